@@ -1,0 +1,73 @@
+"""The five synthetic workloads the attention path is checked and measured on.
+
+Shapes follow the page's statement of the operation (Q, K, V in R^{B x H x L x d},
+g: R^d -> R_+^M) with a user-chosen slice count; "chunks" is the number of
+slices N and the slice (chunk) length is ceil(L / N).  Inputs are Gaussian as
+listed; ``qkv_scale`` multiplies N(0, 1) draws of Q, K, V, and dY is N(0, 1).
+Where a workload leaves a choice open (W draw, distribution) the plainest
+reading is taken: W iid N(0, 1) unless "orthogonal" is named.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    L: int
+    d: int
+    M: int
+    chunks: int          # number of slices N; slice length = ceil(L / N)
+    dtype: str           # "f32" or "bf16": dtype of Q, K, V, W, dY, Y, dQ, dK, dV
+    feat: str            # "favor" or "elu1"
+    w_kind: str          # "gaussian" or "orthogonal" (FAVOR+ only)
+    qkv_scale: float
+    seed: int
+    backward: bool = True
+
+    @property
+    def chunk_len(self) -> int:
+        return -(-self.L // self.chunks)
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.L
+
+    @property
+    def head_tokens(self) -> int:
+        return self.B * self.H * self.L
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        # fp32 forward, L=256, d=M=16, four slices of 64, W ~ N(0,1), Q,K,V ~ N(0, 0.5^2)
+        Workload("favor_f32_L256_d16_M16", 1, 1, 256, 16, 16, 4, "f32", "favor", "gaussian", 0.5, 1,
+                 backward=False),
+        # fp32 fwd+bwd, orthogonal random features, slices of 256
+        Workload("favor_ortho_f32_L4096_d64_M128", 2, 8, 4096, 64, 128, 16, "f32", "favor",
+                 "orthogonal", 64 ** -0.25, 2),
+        # bf16 fwd+bwd, fp32 state/accumulation, slices of 512 (the headline measurement)
+        Workload("favor_bf16_L16384_d64_M256", 4, 16, 16384, 64, 256, 32, "bf16", "favor", "gaussian",
+                 64 ** -0.25, 3),
+        # bf16 long context, 2048 slices of 512
+        Workload("favor_bf16_L1048576_d64_M64", 1, 8, 1 << 20, 64, 64, 2048, "bf16", "favor",
+                 "gaussian", 64 ** -0.25, 4),
+        # bf16 elementwise elu(x)+1, M = d = 128, slices of 256
+        Workload("elu1_bf16_L8192_d128", 8, 12, 8192, 128, 128, 32, "bf16", "elu1", "gaussian", 1.0, 5),
+    ]
+}
+
+HEADLINE = "favor_bf16_L16384_d64_M256"
+
+
+def io_bytes_per_head_token(w: Workload, backward: bool = True) -> float:
+    """Minimum HBM traffic per (token, head): read Q, K, V (+ dY) and write Y
+    (+ dQ, dK, dV) once, in the I/O dtype."""
+    s = 4 if w.dtype == "f32" else 2
+    n = 11 if backward else 4
+    return n * w.d * s

@@ -1,0 +1,351 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Every function raises AssertionError when the oracle disagrees with:
+  * hand-worked closed forms of the definition (tests/golden/hand_examples.json),
+  * special cases that reduce to a plain average or to the inputs,
+  * causality (page "Sub-Linear Memory: How to Make Performers SLiM",
+    Subsection 2.1: output l depends only on indices 1..l),
+  * associativity: the masked quadratic form equals the prefix-sum recurrence
+    (the second transition of eq. (2), Subsection 2.1) -- two separately
+    written evaluations,
+  * FAVOR+ unbiasedness for exp(q.k) (Subsection 2.1 cites it as an unbiased
+    approximation of exponential attention) and the M^{-1/2} convergence of
+    FAVOR+ attention to exact softmax attention,
+  * central finite differences of every gradient.
+
+The functions are shared by tests/test_oracle_pins.py and by the mutation
+check (tests/test_oracle_mutants.py), which plants mistakes in copies of
+oracle.c and requires each one to fail at least one pin.  `main(path)` runs
+all pins against the library at `path` and exits with the failure count.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_examples.json")
+
+
+def _ev(expr: str) -> float:
+    return float(eval(expr, {"__builtins__": {}}, {"exp": math.exp, "sqrt": math.sqrt}))
+
+
+def _arr(x):
+    return np.asarray(x, dtype=np.float64)[None, None]
+
+
+def _rand(seed, *shape, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _relerr(a, b):
+    return float(np.linalg.norm(np.ravel(a - b)) / max(np.linalg.norm(np.ravel(b)), 1e-300))
+
+
+# ------------------------------------------------------------ feature map ---
+
+def pin_featmap_golden():
+    cases = json.load(open(GOLDEN))["cases"]
+    for c in cases:
+        if "Phi" not in c:
+            continue
+        phi = oracle.featmap(np.array(c["X"]), np.array(c["W"]), c["feat"])
+        want = np.array([_ev(e) for e in c["Phi"]])
+        assert np.allclose(phi[0], want, rtol=1e-14, atol=0), (c["name"], phi, want)
+
+
+def pin_featmap_zero_input():
+    # x = 0: every FAVOR+ feature is exp(0)/sqrt(M) whatever W is.
+    W = _rand(1, 7, 5)
+    phi = oracle.featmap(np.zeros((2, 5)), W, "favor")
+    assert np.allclose(phi, 1 / math.sqrt(7), rtol=1e-15), phi
+
+
+def pin_elu1_values():
+    x = np.array([[2.0, -1.0, 0.0, 1e-3, -3.5]])
+    want = np.array([3.0, math.exp(-1.0), 1.0, 1.001, math.exp(-3.5)])
+    phi = oracle.featmap(x, None, "elu1")
+    assert np.allclose(phi[0], want, rtol=1e-15), phi
+
+
+def pin_favor_unbiased():
+    # E_w[g(q).g(k)] = E_w[exp(w.(q+k) - (|q|^2+|k|^2)/2)] = exp(q.k)  (Gaussian MGF).
+    # One W with many rows is a Monte-Carlo estimate; check it within 6 sigma.
+    d, M = 4, 400000
+    rng = np.random.default_rng(7)
+    W = rng.standard_normal((M, d))
+    q = np.array([0.3, -0.2, 0.5, 0.1])
+    k = np.array([-0.1, 0.4, 0.2, -0.3])
+    est = float(oracle.featmap(q[None], W)[0] @ oracle.featmap(k[None], W)[0])
+    u = q + k
+    var = math.exp(2 * float(u @ u)) - math.exp(float(u @ u))  # var of exp(w.u)
+    sigma = math.exp(-0.5 * float(q @ q + k @ k)) * math.sqrt(var / M)
+    exact = math.exp(float(q @ k))
+    assert abs(est - exact) < 6 * sigma, (est, exact, sigma)
+    # and resolved well enough to reject a plausible wrong value (half the exponent)
+    assert abs(est - math.exp(0.5 * float(q @ k))) > 6 * sigma
+
+
+def pin_featmap_vjp_fd():
+    for feat, d, M in (("favor", 4, 6), ("elu1", 5, 5)):
+        rng = np.random.default_rng(3)
+        X = rng.standard_normal((3, d)) * 0.7
+        X[np.abs(X) < 1e-2] += 0.05  # stay away from the elu kink
+        W = rng.standard_normal((M, d))
+        dPhi = rng.standard_normal((3, M))
+        got = oracle.featmap_vjp(X, W, dPhi, feat)
+        h = 1e-6
+        fd = np.zeros_like(X)
+        for r in range(3):
+            for e in range(d):
+                Xp, Xm = X.copy(), X.copy()
+                Xp[r, e] += h
+                Xm[r, e] -= h
+                fd[r, e] = np.sum(dPhi * (oracle.featmap(Xp, W, feat) - oracle.featmap(Xm, W, feat))) / (2 * h)
+        assert _relerr(got, fd) < 1e-7, (feat, got, fd)
+
+
+# --------------------------------------------------------------- forward ---
+
+def pin_fwd_golden():
+    for c in json.load(open(GOLDEN))["cases"]:
+        if "Y" not in c:
+            continue
+        W = np.array(c["W"]) if "W" in c else None
+        want = np.array([_ev(e) for e in c["Y"]])
+        for form in ("quadratic", "prefix"):
+            Y = oracle.attn_fwd(_arr(c["Q"]), _arr(c["K"]), _arr(c["V"]), W, c["feat"], form=form)[0]
+            assert np.allclose(Y[0, 0, :, 0], want, rtol=1e-13), (c["name"], form, Y, want)
+
+
+def _qkv(seed, L, d, M, scale=0.5):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((1, 2, L, d)) * scale
+    K = rng.standard_normal((1, 2, L, d)) * scale
+    V = rng.standard_normal((1, 2, L, d))
+    W = rng.standard_normal((M, d))
+    return Q, K, V, W
+
+
+def pin_single_row_is_value():
+    # L = 1: the only weight is on V_1, so Y_1 = V_1 for any positive g.
+    for feat, d, M in (("favor", 3, 5), ("elu1", 4, 4)):
+        Q, K, V, W = _qkv(11, 1, d, M)
+        for form in ("quadratic", "prefix"):
+            Y = oracle.attn_fwd(Q, K, V, W, feat, form=form)[0]
+            assert np.allclose(Y, V, rtol=1e-14), (feat, form)
+
+
+def pin_identical_keys_give_running_mean():
+    # All keys equal => all weights in row l equal => Y_l = mean(V_1..V_l), diagonal included.
+    for feat, d, M in (("favor", 3, 6), ("elu1", 3, 3)):
+        Q, K, V, W = _qkv(12, 9, d, M)
+        K[:] = K[:, :, :1, :]
+        want = np.cumsum(V, axis=2) / np.arange(1, 10)[None, None, :, None]
+        for form in ("quadratic", "prefix"):
+            Y = oracle.attn_fwd(Q, K, V, W, feat, form=form)[0]
+            assert np.allclose(Y, want, rtol=1e-12), (feat, form)
+
+
+def pin_constant_values():
+    # V_i = v for all i => Y_l = v (weights sum to one).
+    Q, K, V, W = _qkv(13, 8, 3, 4)
+    V[:] = np.array([1.5, -2.0, 0.25])
+    for form in ("quadratic", "prefix"):
+        Y = oracle.attn_fwd(Q, K, V, W, "favor", form=form)[0]
+        assert np.allclose(Y, V, rtol=1e-13), form
+
+
+def pin_causality():
+    # Perturbing row j of Q, K or V leaves Y_l, l < j, bitwise unchanged and changes row j.
+    Q, K, V, W = _qkv(14, 12, 4, 6)
+    Y0 = oracle.attn_fwd(Q, K, V, W, "favor")[0]
+    for which in range(3):
+        X = [Q.copy(), K.copy(), V.copy()]
+        X[which][:, :, 7, :] += 0.3
+        Y1 = oracle.attn_fwd(*X, W, "favor")[0]
+        assert np.array_equal(Y0[:, :, :7], Y1[:, :, :7]), which
+        assert not np.allclose(Y0[:, :, 7], Y1[:, :, 7]), which
+
+
+def pin_convex_hull():
+    # Y_l is a convex combination of V_1..V_l: every coordinate lies within their range.
+    Q, K, V, W = _qkv(15, 16, 3, 5, scale=1.0)
+    Y = oracle.attn_fwd(Q, K, V, W, "favor")[0]
+    lo = np.minimum.accumulate(V, axis=2)
+    hi = np.maximum.accumulate(V, axis=2)
+    assert np.all(Y >= lo - 1e-12) and np.all(Y <= hi + 1e-12)
+
+
+def pin_quadratic_equals_prefix():
+    # Associativity (eq. (2), second transition): the masked quadratic form and the
+    # prefix-sum recurrence agree, including states and initial states.
+    for feat, d, M in (("favor", 4, 8), ("elu1", 5, 5)):
+        Q, K, V, W = _qkv(16, 33, d, M)
+        R0 = _rand(17, 1, 2, d, M)
+        S0 = np.abs(_rand(18, 1, 2, M)) + 0.5
+        a = oracle.attn_fwd(Q, K, V, W, feat, R0=R0, S0=S0, form="quadratic")
+        b = oracle.attn_fwd(Q, K, V, W, feat, R0=R0, S0=S0, form="prefix")
+        for x, y in zip(a, b):
+            assert _relerr(x, y) < 1e-12, feat
+
+
+def pin_initial_state_is_a_prefix():
+    # Running on [P; X] equals running on X from the state of P (slice recurrence,
+    # Subsection 3.2: each slice starts from the previous slice's last prefix value).
+    Q, K, V, W = _qkv(19, 20, 3, 5)
+    Yfull, _, Rf, Sf = oracle.attn_fwd(Q, K, V, W, "favor")
+    _, _, Rp, Sp = oracle.attn_fwd(Q[:, :, :8], K[:, :, :8], V[:, :, :8], W, "favor")
+    Y2, _, R2, S2 = oracle.attn_fwd(Q[:, :, 8:], K[:, :, 8:], V[:, :, 8:], W, "favor", R0=Rp, S0=Sp)
+    assert _relerr(Y2, Yfull[:, :, 8:]) < 1e-13
+    assert _relerr(R2, Rf) < 1e-13 and _relerr(S2, Sf) < 1e-13
+
+
+def pin_rows_match_full():
+    Q, K, V, W = _qkv(20, 40, 4, 6)
+    Y = oracle.attn_fwd(Q, K, V, W, "favor")[0]
+    rows = np.array([0, 1, 17, 39])
+    Yr, _ = oracle.attn_fwd_rows(Q[0, 1], K[0, 1], V[0, 1], W, rows, "favor")
+    assert _relerr(Yr, Y[0, 1, rows]) < 1e-14
+
+
+def pin_softmax_special_cases():
+    Q, K, V, _ = _qkv(21, 10, 3, 1)
+    # Q = 0 => all scores equal => running mean
+    Y = oracle.softmax_fwd(np.zeros_like(Q), K, V)
+    want = np.cumsum(V, axis=2) / np.arange(1, 11)[None, None, :, None]
+    assert np.allclose(Y, want, rtol=1e-13)
+    # two rows by hand: Y_2 = (e^{q2.k1} V_1 + e^{q2.k2} V_2)/(e^{q2.k1}+e^{q2.k2})
+    q2, k1, k2 = Q[0, 0, 1], K[0, 0, 0], K[0, 0, 1]
+    a, b = math.exp(q2 @ k1), math.exp(q2 @ k2)
+    Y = oracle.softmax_fwd(Q[:, :, :2], K[:, :, :2], V[:, :, :2])
+    assert np.allclose(Y[0, 0, 1], (a * V[0, 0, 0] + b * V[0, 0, 1]) / (a + b), rtol=1e-13)
+
+
+def pin_favor_converges_to_softmax():
+    # FAVOR+ attention -> exact exponential attention as M grows, error ~ M^{-1/2}.
+    L, d = 24, 4
+    rng = np.random.default_rng(22)
+    Q = rng.standard_normal((1, 1, L, d)) * 0.4
+    K = rng.standard_normal((1, 1, L, d)) * 0.4
+    V = rng.standard_normal((1, 1, L, d))
+    Ys = oracle.softmax_fwd(Q, K, V)
+    Ms = [64, 256, 1024, 4096, 16384]
+    errs = []
+    for M in Ms:
+        e = []
+        for s in range(6):
+            W = np.random.default_rng(1000 + 31 * s + M).standard_normal((M, d))
+            e.append(_relerr(oracle.attn_fwd(Q, K, V, W, "favor")[0], Ys))
+        errs.append(np.mean(e))
+    slope = np.polyfit(np.log(Ms), np.log(errs), 1)[0]
+    assert -0.75 < slope < -0.3, (slope, errs)
+    assert errs[-1] < 0.02, errs
+
+
+# -------------------------------------------------------------- backward ---
+
+def _loss(Q, K, V, W, feat, R0, S0, dY, dR, dS, form):
+    Y, _, R, S = oracle.attn_fwd(Q, K, V, W, feat, R0=R0, S0=S0, form=form)
+    return float(np.sum(dY * Y) + np.sum(dR * R) + np.sum(dS * S))
+
+
+def pin_bwd_finite_differences():
+    for feat, d, M in (("favor", 3, 5), ("elu1", 3, 3)):
+        rng = np.random.default_rng(23)
+        L = 6
+        Q = rng.standard_normal((1, 1, L, d)) * 0.6
+        K = rng.standard_normal((1, 1, L, d)) * 0.6
+        for X in (Q, K):
+            X[np.abs(X) < 2e-2] += 0.05
+        V = rng.standard_normal((1, 1, L, d))
+        W = rng.standard_normal((M, d))
+        R0 = rng.standard_normal((1, 1, d, M)) * 0.5
+        S0 = np.abs(rng.standard_normal((1, 1, M))) + 0.5
+        dY = rng.standard_normal((1, 1, L, d))
+        dR = rng.standard_normal((1, 1, d, M))
+        dS = rng.standard_normal((1, 1, M))
+        for form in ("quadratic", "prefix"):
+            grads = oracle.attn_bwd(Q, K, V, W, dY, feat, R0=R0, S0=S0, dRout=dR, dSout=dS, form=form)
+            args = [Q, K, V, R0, S0]
+            h = 1e-6
+            for a, g in zip(args, grads):
+                fd = np.zeros_like(a)
+                for idx in np.ndindex(a.shape):
+                    keep = a[idx]
+                    a[idx] = keep + h
+                    fp = _loss(Q, K, V, W, feat, R0, S0, dY, dR, dS, "quadratic")
+                    a[idx] = keep - h
+                    fm = _loss(Q, K, V, W, feat, R0, S0, dY, dR, dS, "quadratic")
+                    a[idx] = keep
+                    fd[idx] = (fp - fm) / (2 * h)
+                assert _relerr(g, fd) < 1e-6, (feat, form, g, fd)
+
+
+def pin_bwd_special_cases():
+    Q, K, V, W = _qkv(24, 1, 3, 4)
+    dY = _rand(25, 1, 2, 1, 3)
+    for form in ("quadratic", "prefix"):
+        # L = 1: Y = V, so dQ = dK = 0 and dV = dY.
+        dQ, dK, dV, _, _ = oracle.attn_bwd(Q, K, V, W, dY, "favor", form=form)
+        assert np.allclose(dQ, 0, atol=1e-14) and np.allclose(dK, 0, atol=1e-14)
+        assert np.allclose(dV, dY, rtol=1e-14)
+    # constant V: Y = V whatever Q, K are, so dQ = dK = 0.
+    Q, K, V, W = _qkv(26, 9, 3, 4)
+    V[:] = np.array([0.5, -1.0, 2.0])
+    dY = _rand(27, 1, 2, 9, 3)
+    for form in ("quadratic", "prefix"):
+        dQ, dK, dV, _, _ = oracle.attn_bwd(Q, K, V, W, dY, "favor", form=form)
+        assert np.allclose(dQ, 0, atol=1e-12) and np.allclose(dK, 0, atol=1e-12), form
+
+
+def pin_bwd_quadratic_equals_prefix():
+    for feat, d, M in (("favor", 4, 8), ("elu1", 4, 4)):
+        Q, K, V, W = _qkv(28, 30, d, M)
+        dY = _rand(29, 1, 2, 30, d)
+        dR = _rand(30, 1, 2, d, M)
+        dS = _rand(31, 1, 2, M)
+        R0 = _rand(32, 1, 2, d, M)
+        S0 = np.abs(_rand(33, 1, 2, M)) + 0.5
+        a = oracle.attn_bwd(Q, K, V, W, dY, feat, R0, S0, dR, dS, form="quadratic")
+        b = oracle.attn_bwd(Q, K, V, W, dY, feat, R0, S0, dR, dS, form="prefix")
+        for x, y in zip(a, b):
+            assert _relerr(x, y) < 1e-11, feat
+
+
+ALL_PINS = [
+    pin_featmap_golden, pin_featmap_zero_input, pin_elu1_values, pin_favor_unbiased,
+    pin_featmap_vjp_fd, pin_fwd_golden, pin_single_row_is_value, pin_identical_keys_give_running_mean,
+    pin_constant_values, pin_causality, pin_convex_hull, pin_quadratic_equals_prefix,
+    pin_initial_state_is_a_prefix, pin_rows_match_full, pin_softmax_special_cases,
+    pin_favor_converges_to_softmax, pin_bwd_finite_differences, pin_bwd_special_cases,
+    pin_bwd_quadratic_equals_prefix,
+]
+
+
+def main(path=None) -> int:
+    if path:
+        oracle._lib = oracle.load(path)
+    failed = []
+    for p in ALL_PINS:
+        try:
+            p()
+        except Exception as e:  # noqa: BLE001 - a mutant may raise anything
+            failed.append(p.__name__)
+            print("FAIL", p.__name__, type(e).__name__, str(e)[:200])
+    print("FAILED_PINS", len(failed), ",".join(failed))
+    return len(failed)
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1] if len(sys.argv) > 1 else None))
