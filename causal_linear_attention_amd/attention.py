@@ -1,0 +1,148 @@
+"""PyTorch front end of libslim: device memory, streams and autograd wiring.
+
+Every step of the computation runs in the HIP kernels behind the C ABI; this
+module only checks tensors, allocates outputs/workspace with PyTorch's caching
+allocator (so ``torch.cuda.max_memory_allocated`` sees all of it) and passes
+pointers plus the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.SLIM_F32, torch.bfloat16: _lib.SLIM_BF16}
+_FEAT = {"favor": _lib.SLIM_FEAT_FAVOR, "elu1": _lib.SLIM_FEAT_ELU1}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check_io(name, t, dtype, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def make_desc(q, M, feat, num_chunks, window_chunks=0):
+    B, H, L, d = q.shape
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return _lib.desc(B, H, L, d, M, num_chunks, window_chunks, _DT[q.dtype], _FEAT[feat])
+
+
+def _feat_M(W, feat, d):
+    if feat == "favor":
+        if W is None:
+            raise ValueError("FAVOR+ needs W")
+        return W.shape[0]
+    if W is not None:
+        raise ValueError("elu1 takes no W")
+    return d
+
+
+def workspace_bytes(desc, pass_):
+    n = _lib.lib().slim_workspace_bytes(ctypes.byref(desc), pass_)
+    if n == 0 and pass_ != _lib.SLIM_PASS_FEATMAP:
+        _lib.check(_lib.lib().slim_validate(ctypes.byref(desc), pass_), "slim_workspace_bytes")
+    return n
+
+
+def featmap(x, W=None, feat="favor", row_offset=False):
+    """g(x) in fp32: x [B, H, L, d] -> [B, H, L, M] (and the per-row offsets)."""
+    B, H, L, d = x.shape
+    M = _feat_M(W, feat, d)
+    _check_io("x", x, x.dtype)
+    if W is not None:
+        _check_io("W", W, x.dtype, (M, d))
+    dsc = make_desc(x, M, feat, 1)
+    phi = torch.empty((B, H, L, M), dtype=torch.float32, device=x.device)
+    off = torch.empty((B, H, L), dtype=torch.float32, device=x.device) if row_offset else None
+    _lib.check(_lib.lib().slim_featmap(ctypes.byref(dsc), _ptr(x), _ptr(W), _ptr(phi), _ptr(off), _stream()),
+               "slim_featmap")
+    return (phi, off) if row_offset else phi
+
+
+def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, window_chunks=0):
+    """Forward.  Returns (Y, R_out [B,H,d,M] fp32, S_out [B,H,M] fp32)."""
+    B, H, L, d = q.shape
+    M = _feat_M(W, feat, d)
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_io(n, t, q.dtype, q.shape)
+    if W is not None:
+        _check_io("W", W, q.dtype, (M, d))
+    if R_in is not None:
+        _check_io("R_in", R_in, torch.float32, (B, H, d, M))
+        _check_io("S_in", S_in, torch.float32, (B, H, M))
+    dsc = make_desc(q, M, feat, num_chunks, window_chunks)
+    ws = torch.empty(max(1, workspace_bytes(dsc, _lib.SLIM_PASS_FWD)), dtype=torch.uint8, device=q.device)
+    Y = torch.empty_like(q)
+    R = torch.empty((B, H, d, M), dtype=torch.float32, device=q.device)
+    S = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    _lib.check(_lib.lib().slim_attn_fwd(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(R_in),
+                                        _ptr(S_in), _ptr(Y), _ptr(R), _ptr(S), _ptr(ws), ws.numel(), _stream()),
+               "slim_attn_fwd")
+    return Y, R, S
+
+
+def attn_bwd(q, k, v, W, dY, R_out, S_out, feat="favor", num_chunks=1, dR_out=None, dS_out=None,
+             want_state_grad=False, window_chunks=0):
+    """Backward.  Returns (dQ, dK, dV, dR_in, dS_in); the last two are None
+    unless want_state_grad."""
+    B, H, L, d = q.shape
+    M = _feat_M(W, feat, d)
+    for n, t in (("q", q), ("k", k), ("v", v), ("dY", dY)):
+        _check_io(n, t, q.dtype, q.shape)
+    _check_io("R_out", R_out, torch.float32, (B, H, d, M))
+    _check_io("S_out", S_out, torch.float32, (B, H, M))
+    if dR_out is not None:
+        _check_io("dR_out", dR_out, torch.float32, (B, H, d, M))
+        _check_io("dS_out", dS_out, torch.float32, (B, H, M))
+    dsc = make_desc(q, M, feat, num_chunks, window_chunks)
+    ws = torch.empty(max(1, workspace_bytes(dsc, _lib.SLIM_PASS_BWD)), dtype=torch.uint8, device=q.device)
+    dQ, dK, dV = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dR = dS = None
+    if want_state_grad:
+        dR = torch.empty((B, H, d, M), dtype=torch.float32, device=q.device)
+        dS = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    _lib.check(_lib.lib().slim_attn_bwd(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(dY),
+                                        _ptr(R_out), _ptr(S_out), _ptr(dR_out), _ptr(dS_out), _ptr(dQ), _ptr(dK),
+                                        _ptr(dV), _ptr(dR), _ptr(dS), _ptr(ws), ws.numel(), _stream()),
+               "slim_attn_bwd")
+    return dQ, dK, dV, dR, dS
+
+
+class _SlimAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, W, feat, num_chunks, window_chunks):
+        Y, R, S = attn_fwd(q, k, v, W, feat, num_chunks, window_chunks=window_chunks)
+        # Only the inputs and the final state are kept for the backward (the
+        # reverse walk recovers every slice's entry state from R, S).
+        ctx.save_for_backward(q, k, v, W if W is not None else torch.empty(0), R, S)
+        ctx.feat, ctx.num_chunks, ctx.window_chunks, ctx.has_w = feat, num_chunks, window_chunks, W is not None
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        q, k, v, W, R, S = ctx.saved_tensors
+        dQ, dK, dV, _, _ = attn_bwd(q, k, v, W if ctx.has_w else None, dY.contiguous(), R, S, ctx.feat,
+                                    ctx.num_chunks, window_chunks=ctx.window_chunks)
+        return dQ, dK, dV, None, None, None, None
+
+
+def slim_attention(q, k, v, W=None, feat="favor", num_chunks=1, window_chunks=0):
+    """Causal linear attention with autograd (gradients for q, k, v; W is a
+    fixed random projection and gets none)."""
+    return _SlimAttention.apply(q, k, v, W, feat, num_chunks, window_chunks)

@@ -1,0 +1,186 @@
+// slim_device.h -- device building blocks of the gfx950 kernels: operand
+// fragments for the 16x16 MFMA shapes, tile staging through LDS, and the
+// feature map g evaluated straight into MFMA register layouts.
+//
+// Fragment convention.  Every 16x16 fp32 accumulator block ("C block") held
+// by a wave gives lane i the four entries (row 4*(i/16)+j, col i%16), j=0..3.
+// An operand fragment Frag<T> carries, for one lane, four consecutive
+// contraction indices 4*(i/16)..4*(i/16)+3 of one 16-wide contraction block,
+// for the free index i%16.  Hence
+//   * a C block Z (rows r, cols c) converts in registers into the operand of
+//     any product that contracts over Z's rows, with Z's columns as the free
+//     index (as the A operand of Z^T U or the B operand of U Z);
+//   * an LDS array stored [n][k] (k contiguous) yields the operand for
+//     contraction index k and free index n with one 8- or 16-byte read.
+// Two 16-deep bf16 contraction blocks make one v_mfma_f32_16x16x32_bf16 (a lone
+// block is zero-padded to 32); one fp32 block is four v_mfma_f32_16x16x4_f32
+// (one per j).  A and B always pair the same physical indices, so
+// the order in which an instruction walks its K dimension does not matter.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace slim {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+enum { FEAT_FAVOR = 0, FEAT_ELU1 = 1 };
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int lcol() { return threadIdx.x & 15; }        // i % 16
+__device__ __forceinline__ int lgrp() { return (threadIdx.x >> 4) & 3; }  // i / 16 (within the wave)
+
+template <typename T> struct Frag;
+template <> struct Frag<float> { f4 v; };
+template <> struct Frag<__bf16> { bf4 v; };
+
+__device__ __forceinline__ f4 f4zero() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
+template <typename T> __device__ __forceinline__ Frag<T> cfrag(f4 c);
+template <> __device__ __forceinline__ Frag<float> cfrag<float>(f4 c) { return Frag<float>{c}; }
+template <> __device__ __forceinline__ Frag<__bf16> cfrag<__bf16>(f4 c)
+{
+    Frag<__bf16> r;
+    r.v[0] = (__bf16)c[0];
+    r.v[1] = (__bf16)c[1];
+    r.v[2] = (__bf16)c[2];
+    r.v[3] = (__bf16)c[3];
+    return r;
+}
+
+template <typename T> __device__ __forceinline__ f4 frag_to_f4(Frag<T> a);
+template <> __device__ __forceinline__ f4 frag_to_f4<float>(Frag<float> a) { return a.v; }
+template <> __device__ __forceinline__ f4 frag_to_f4<__bf16>(Frag<__bf16> a)
+{
+    return f4{(float)a.v[0], (float)a.v[1], (float)a.v[2], (float)a.v[3]};
+}
+
+// acc += A(16 x 16) * B(16 x 16) over one contraction block.
+__device__ __forceinline__ void mma1(f4 &acc, Frag<float> a, Frag<float> b)
+{
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[0], b.v[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[1], b.v[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[2], b.v[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[3], b.v[3], acc, 0, 0, 0);
+}
+// bf16: a single 16-deep block also goes through v_mfma_f32_16x16x32_bf16, with the
+// second half of both operands zero.  Every bf16 product therefore uses one MFMA
+// kind: chaining v_mfma_f32_16x16x16_bf16 and v_mfma_f32_16x16x32_bf16 on the same
+// accumulator was compiled without the wait states the hand-off needs on gfx950
+// and produced wrong sums.
+__device__ __forceinline__ void mma1(f4 &acc, Frag<__bf16> a, Frag<__bf16> b)
+{
+    const __bf16 z = (__bf16)0.f;
+    bf8 a8 = {a.v[0], a.v[1], a.v[2], a.v[3], z, z, z, z};
+    bf8 b8 = {b.v[0], b.v[1], b.v[2], b.v[3], z, z, z, z};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc, 0, 0, 0);
+}
+// acc += over two contraction blocks.
+__device__ __forceinline__ void mma2(f4 &acc, Frag<float> a0, Frag<float> a1, Frag<float> b0, Frag<float> b1)
+{
+    mma1(acc, a0, b0);
+    mma1(acc, a1, b1);
+}
+__device__ __forceinline__ void mma2(f4 &acc, Frag<__bf16> a0, Frag<__bf16> a1, Frag<__bf16> b0,
+                                     Frag<__bf16> b1)
+{
+    bf8 a = {a0.v[0], a0.v[1], a0.v[2], a0.v[3], a1.v[0], a1.v[1], a1.v[2], a1.v[3]};
+    bf8 b = {b0.v[0], b0.v[1], b0.v[2], b0.v[3], b1.v[0], b1.v[1], b1.v[2], b1.v[3]};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+// acc += sum over contraction blocks kb = k0..k1-1 of A(kb) * B(kb); fa/fb return Frag<T>.
+template <typename T, typename FA, typename FB>
+__device__ __forceinline__ void mma_range(f4 &acc, int k0, int k1, FA fa, FB fb)
+{
+    int kb = k0;
+    for (; kb + 1 < k1; kb += 2) mma2(acc, fa(kb), fa(kb + 1), fb(kb), fb(kb + 1));
+    if (kb < k1) mma1(acc, fa(kb), fb(kb));
+}
+
+// Operand fragment from an LDS array stored [n][k] with row stride ld elements:
+// free index n0 + i%16, contraction indices k0 + 4*(i/16) .. +3.
+template <typename T> __device__ __forceinline__ Frag<T> lds_frag(const T *base, int ld, int n0, int k0)
+{
+    const T *p = base + (n0 + lcol()) * ld + k0 + 4 * lgrp();
+    return *reinterpret_cast<const Frag<T> *>(p);
+}
+
+// Sum over the four lane groups (lanes i, i^16, i^32, i^48) of the same column.
+__device__ __forceinline__ float sum_groups(float v)
+{
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+__device__ __forceinline__ float max_groups(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+__device__ __forceinline__ float fast_exp(float x)
+{
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+__device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : fast_exp(x); }
+__device__ __forceinline__ float elu1_grad(float x) { return x > 0.f ? 1.f : fast_exp(x); }
+
+// 16-byte vector of the I/O type.
+template <typename T> struct Vec16;
+template <> struct Vec16<float> { typedef f4 type; static constexpr int N = 4; };
+template <> struct Vec16<__bf16> { typedef bf8 type; static constexpr int N = 8; };
+
+// Stage rows [0, TT) of a row-major [rows][D] tile (src points at its first row) into
+// LDS dst[TT][ldx] (skipped if dst is null); rows >= nvalid read as zero.  If dstT is non-null the transposed
+// tile dstT[D][ldt] is written as well.  If rowscale is non-null, row t is multiplied
+// by rowscale[t] (in fp32) before it is stored.
+template <typename T, int D, int TT, int NT>
+__device__ __forceinline__ void stage_tile(T *dst, int ldx, T *dstT, int ldt, const T *__restrict__ src, int nvalid,
+                                           const float *rowscale)
+{
+    typedef typename Vec16<T>::type V;
+    constexpr int EPV = Vec16<T>::N;
+    constexpr int VPR = D / EPV;
+    for (int v = threadIdx.x; v < TT * VPR; v += NT) {
+        const int t = v / VPR, c = (v % VPR) * EPV;
+        V x;
+        if (t < nvalid) {
+            x = *reinterpret_cast<const V *>(src + (size_t)t * D + c);
+            if (rowscale) {
+                const float s = rowscale[t];
+#pragma unroll
+                for (int j = 0; j < EPV; ++j) x[j] = (T)((float)x[j] * s);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < EPV; ++j) x[j] = (T)0.f;
+        }
+        if (dst) *reinterpret_cast<V *>(dst + t * ldx + c) = x;
+        if (dstT) {
+#pragma unroll
+            for (int j = 0; j < EPV; ++j) dstT[(c + j) * ldt + t] = x[j];
+        }
+    }
+}
+
+// |x_t|^2 of every row of an LDS tile [TT][ldx] (io type), written to out[t].
+template <typename T, int D, int TT, int NT>
+__device__ __forceinline__ void row_sqnorm(const T *x, int ldx, float *out)
+{
+    for (int t = threadIdx.x; t < TT; t += NT) {
+        float s = 0.f;
+        for (int e = 0; e < D; ++e) {
+            const float v = (float)x[t * ldx + e];
+            s += v * v;
+        }
+        out[t] = s;
+    }
+}
+
+}  // namespace slim

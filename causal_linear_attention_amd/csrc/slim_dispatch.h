@@ -1,0 +1,25 @@
+// slim_dispatch.h -- per-shape kernel tables (internal to libslim).
+#pragma once
+#include <hip/hip_runtime.h>
+#include "slim_kernels.h"
+
+namespace slim {
+
+struct KernelTable {
+    int nt;  // threads per workgroup
+    int tt;  // rows per tile
+    void (*featmap)(dim3, hipStream_t, const void *, const void *, float *, float *, long long);
+    void (*state)(dim3, hipStream_t, const ChunkArgs &);
+    void (*fwd)(dim3, hipStream_t, const ChunkArgs &);
+    void (*stats)(dim3, hipStream_t, const ChunkArgs &);
+    void (*bwdq)(dim3, hipStream_t, const ChunkArgs &);
+    void (*bwdkv)(dim3, hipStream_t, const ChunkArgs &);
+};
+
+// One lookup per (dtype, feature map) translation unit; NULL if the shape is not compiled.
+const KernelTable *table_f32_favor(int D, int M);
+const KernelTable *table_bf16_favor(int D, int M);
+const KernelTable *table_f32_elu1(int D, int M);
+const KernelTable *table_bf16_elu1(int D, int M);
+
+}  // namespace slim

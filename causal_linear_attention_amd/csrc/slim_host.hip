@@ -1,0 +1,274 @@
+// slim_host.hip -- the C ABI of libslim (include/slim.h): host-side validation,
+// workspace planning and the slice-window launch sequence, plus the two small
+// shape-independent kernels (state scan, copy/zero).
+//
+// Launch sequence (page "Sub-Linear Memory: How to Make Performers SLiM"):
+//   forward  (Subsection 3.2): for each window of P slices in order:
+//       state -> forward prefix scan (carry = running final state) -> fwd
+//   backward (Subsection 3.3): for each window in reverse order:
+//       state -> reverse scan (entry states by subtraction from the carry,
+//       update (19)) -> stats (recompute forward, per-row statistics, the
+//       slice's gradient w.r.t. its entry state) -> gradient suffix scan
+//       (update (20)) -> dQ -> dK, dV
+// Only the carries (d x M + M per head) live across windows, so the workspace
+// is bounded by the window, not by L.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/slim.h"
+#include "slim_dispatch.h"
+
+namespace slim {
+
+__global__ __launch_bounds__(256) void copy_or_zero_kernel(float *dst, const float *src, long long n)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+static void copy_or_zero(float *dst, const float *src, long long n, hipStream_t s)
+{
+    if (n <= 0) return;
+    hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, src, n);
+}
+
+// scan_kernel lives in slim_kernels.h (instantiated here once).
+static void scan(int mode, float *slots, float *cR, float *cS, int D, int M, int P, int np, int BH, hipStream_t s)
+{
+    const int SZ = (D + 1) * M;
+    dim3 grid((unsigned)((SZ / 4 + 255) / 256), (unsigned)BH);
+    if (mode == 0)
+        hipLaunchKernelGGL(scan_kernel<0>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np);
+    else if (mode == 1)
+        hipLaunchKernelGGL(scan_kernel<1>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np);
+    else
+        hipLaunchKernelGGL(scan_kernel<2>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np);
+}
+
+static const KernelTable *find(const slim_desc *d)
+{
+    if (d->d > 1024 || d->M > 1024) return nullptr;
+    const int D = (int)d->d, M = (int)d->M;
+    if (d->dtype == SLIM_F32) return d->feat == SLIM_FEAT_FAVOR ? table_f32_favor(D, M) : table_f32_elu1(D, M);
+    return d->feat == SLIM_FEAT_FAVOR ? table_bf16_favor(D, M) : table_bf16_elu1(D, M);
+}
+
+struct Plan {
+    long long BH, c, nchunks, P, SZ;
+    size_t slots_off, gslots_off, stats_off, cR_off, cS_off, gR_off, gS_off, total;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static long long resolve_window(const slim_desc *d, long long nchunks)
+{
+    long long P = d->window_chunks;
+    if (P <= 0) {
+        const long long BH = d->B * d->H;
+        P = (4096 + BH - 1) / BH;  // about 4096 workgroups per launch
+    }
+    if (P > nchunks) P = nchunks;
+    if (P < 1) P = 1;
+    if (P > 65535) P = 65535;
+    return P;
+}
+
+static Plan plan(const slim_desc *d, int pass)
+{
+    Plan p;
+    memset(&p, 0, sizeof(p));
+    p.BH = d->B * d->H;
+    p.c = (d->L + d->num_chunks - 1) / d->num_chunks;
+    p.nchunks = (d->L + p.c - 1) / p.c;
+    p.P = resolve_window(d, p.nchunks);
+    p.SZ = (d->d + 1) * d->M;
+    const size_t slots = (size_t)p.BH * (p.P + 1) * p.SZ * 4;
+    size_t off = 0;
+    p.slots_off = off;
+    off = align256(off + slots);
+    if (pass == SLIM_PASS_BWD) {
+        p.gslots_off = off;
+        off = align256(off + slots);
+        p.stats_off = off;
+        off = align256(off + (size_t)p.BH * p.P * p.c * 2 * 4);
+        p.cR_off = off;
+        off = align256(off + (size_t)p.BH * d->d * d->M * 4);
+        p.cS_off = off;
+        off = align256(off + (size_t)p.BH * d->M * 4);
+        p.gR_off = off;
+        off = align256(off + (size_t)p.BH * d->d * d->M * 4);
+        p.gS_off = off;
+        off = align256(off + (size_t)p.BH * d->M * 4);
+    }
+    p.total = pass == SLIM_PASS_FEATMAP ? 0 : off;
+    return p;
+}
+
+static bool misaligned(const void *p, uintptr_t a) { return p && ((uintptr_t)p % a) != 0; }
+
+}  // namespace slim
+
+using namespace slim;
+
+extern "C" {
+
+int slim_version(void) { return (1 << 16) | 0; }
+
+const char *slim_status_string(slim_status s)
+{
+    switch (s) {
+    case SLIM_OK: return "ok";
+    case SLIM_ERR_NULL: return "required pointer is NULL";
+    case SLIM_ERR_SHAPE: return "shape or slice count out of range";
+    case SLIM_ERR_DTYPE: return "unknown dtype or feature map";
+    case SLIM_ERR_UNSUPPORTED: return "shape not supported by the compiled kernels";
+    case SLIM_ERR_WORKSPACE: return "workspace too small";
+    case SLIM_ERR_ALIGN: return "misaligned pointer";
+    case SLIM_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+slim_status slim_validate(const slim_desc *d, int pass)
+{
+    if (!d) return SLIM_ERR_NULL;
+    if (d->dtype != SLIM_F32 && d->dtype != SLIM_BF16) return SLIM_ERR_DTYPE;
+    if (d->feat != SLIM_FEAT_FAVOR && d->feat != SLIM_FEAT_ELU1) return SLIM_ERR_DTYPE;
+    if (pass < SLIM_PASS_FEATMAP || pass > SLIM_PASS_BWD) return SLIM_ERR_SHAPE;
+    if (d->B < 1 || d->H < 1 || d->L < 1 || d->d < 1 || d->M < 1) return SLIM_ERR_SHAPE;
+    if (d->L >= (1LL << 31) || d->B > (1LL << 31) || d->H > (1LL << 31)) return SLIM_ERR_SHAPE;
+    if (pass != SLIM_PASS_FEATMAP && (d->num_chunks < 1 || d->num_chunks > d->L)) return SLIM_ERR_SHAPE;
+    if (d->window_chunks < 0) return SLIM_ERR_SHAPE;
+    if (d->feat == SLIM_FEAT_ELU1 && d->M != d->d) return SLIM_ERR_SHAPE;
+    const long long BH = d->B * d->H;
+    if (BH > 65535 && pass != SLIM_PASS_FEATMAP) return SLIM_ERR_UNSUPPORTED;
+    if ((double)BH * (double)d->L * (double)(d->d > d->M ? d->d : d->M) > 4.0e18) return SLIM_ERR_SHAPE;
+    if (!find(d)) return SLIM_ERR_UNSUPPORTED;
+    return SLIM_OK;
+}
+
+size_t slim_workspace_bytes(const slim_desc *d, int pass)
+{
+    if (slim_validate(d, pass) != SLIM_OK) return 0;
+    return plan(d, pass).total;
+}
+
+int64_t slim_window_chunks(const slim_desc *d)
+{
+    if (slim_validate(d, SLIM_PASS_FWD) != SLIM_OK) return 0;
+    return plan(d, SLIM_PASS_FWD).P;
+}
+
+slim_status slim_featmap(const slim_desc *d, const void *X, const void *W, float *phi, float *row_offset,
+                         void *stream)
+{
+    slim_status st = slim_validate(d, SLIM_PASS_FEATMAP);
+    if (st != SLIM_OK) return st;
+    if (!X || !phi) return SLIM_ERR_NULL;
+    if (d->feat == SLIM_FEAT_FAVOR && !W) return SLIM_ERR_NULL;
+    if (d->feat == SLIM_FEAT_ELU1 && (W || row_offset)) return SLIM_ERR_SHAPE;
+    if (misaligned(X, 16) || misaligned(W, 16) || misaligned(phi, 16) || misaligned(row_offset, 4))
+        return SLIM_ERR_ALIGN;
+    const KernelTable *kt = find(d);
+    const long long rows = d->B * d->H * d->L;
+    const long long nblk = (rows + kt->tt - 1) / kt->tt;
+    if (nblk > 0x7fffffffLL) return SLIM_ERR_SHAPE;
+    kt->featmap(dim3((unsigned)nblk), (hipStream_t)stream, X, W, phi, row_offset, rows);
+    return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
+}
+
+slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
+                          const float *R_in, const float *S_in, void *Y, float *R_out, float *S_out, void *ws,
+                          size_t ws_bytes, void *stream)
+{
+    slim_status st = slim_validate(d, SLIM_PASS_FWD);
+    if (st != SLIM_OK) return st;
+    if (!Q || !K || !V || !Y || !R_out || !S_out || !ws) return SLIM_ERR_NULL;
+    if (d->feat == SLIM_FEAT_FAVOR && !W) return SLIM_ERR_NULL;
+    if (d->feat == SLIM_FEAT_ELU1 && W) return SLIM_ERR_SHAPE;
+    if ((R_in == nullptr) != (S_in == nullptr)) return SLIM_ERR_NULL;
+    if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(W, 16) || misaligned(Y, 16) ||
+        misaligned(R_out, 16) || misaligned(S_out, 16) || misaligned(R_in, 16) || misaligned(S_in, 16) ||
+        misaligned(ws, 256))
+        return SLIM_ERR_ALIGN;
+    const Plan p = plan(d, SLIM_PASS_FWD);
+    if (ws_bytes < p.total) return SLIM_ERR_WORKSPACE;
+    const KernelTable *kt = find(d);
+    hipStream_t s = (hipStream_t)stream;
+    const int D = (int)d->d, M = (int)d->M, BH = (int)p.BH;
+    char *base = (char *)ws;
+    ChunkArgs a;
+    memset(&a, 0, sizeof(a));
+    a.Q = Q; a.K = K; a.V = V; a.W = W; a.out0 = Y;
+    a.slots = (float *)(base + p.slots_off);
+    a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
+    copy_or_zero(R_out, R_in, p.BH * D * M, s);
+    copy_or_zero(S_out, S_in, p.BH * M, s);
+    for (long long n0 = 0; n0 < p.nchunks; n0 += p.P) {
+        const int np = (int)(p.nchunks - n0 < p.P ? p.nchunks - n0 : p.P);
+        a.n0 = (int)n0;
+        kt->state(dim3(np, BH), s, a);
+        scan(0, a.slots, R_out, S_out, D, M, (int)p.P, np, BH, s);
+        kt->fwd(dim3(np, BH), s, a);
+    }
+    return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
+}
+
+slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
+                          const void *dY, const float *R_out, const float *S_out, const float *dR_out,
+                          const float *dS_out, void *dQ, void *dK, void *dV, float *dR_in, float *dS_in, void *ws,
+                          size_t ws_bytes, void *stream)
+{
+    slim_status st = slim_validate(d, SLIM_PASS_BWD);
+    if (st != SLIM_OK) return st;
+    if (!Q || !K || !V || !dY || !R_out || !S_out || !dQ || !dK || !dV || !ws) return SLIM_ERR_NULL;
+    if (d->feat == SLIM_FEAT_FAVOR && !W) return SLIM_ERR_NULL;
+    if (d->feat == SLIM_FEAT_ELU1 && W) return SLIM_ERR_SHAPE;
+    if ((dR_out == nullptr) != (dS_out == nullptr)) return SLIM_ERR_NULL;
+    if ((dR_in == nullptr) != (dS_in == nullptr)) return SLIM_ERR_NULL;
+    if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(W, 16) || misaligned(dY, 16) ||
+        misaligned(R_out, 16) || misaligned(S_out, 16) || misaligned(dR_out, 16) || misaligned(dS_out, 16) ||
+        misaligned(dQ, 16) || misaligned(dK, 16) || misaligned(dV, 16) || misaligned(dR_in, 16) ||
+        misaligned(dS_in, 16) || misaligned(ws, 256))
+        return SLIM_ERR_ALIGN;
+    const Plan p = plan(d, SLIM_PASS_BWD);
+    if (ws_bytes < p.total) return SLIM_ERR_WORKSPACE;
+    const KernelTable *kt = find(d);
+    hipStream_t s = (hipStream_t)stream;
+    const int D = (int)d->d, M = (int)d->M, BH = (int)p.BH;
+    char *base = (char *)ws;
+    ChunkArgs a;
+    memset(&a, 0, sizeof(a));
+    a.Q = Q; a.K = K; a.V = V; a.W = W; a.dY = dY;
+    a.out0 = dQ; a.out1 = dK; a.out2 = dV;
+    a.slots = (float *)(base + p.slots_off);
+    a.gslots = (float *)(base + p.gslots_off);
+    a.stats = (float *)(base + p.stats_off);
+    a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
+    float *cR = (float *)(base + p.cR_off), *cS = (float *)(base + p.cS_off);
+    float *gR = (float *)(base + p.gR_off), *gS = (float *)(base + p.gS_off);
+    copy_or_zero(cR, R_out, p.BH * D * M, s);
+    copy_or_zero(cS, S_out, p.BH * M, s);
+    copy_or_zero(gR, dR_out, p.BH * D * M, s);
+    copy_or_zero(gS, dS_out, p.BH * M, s);
+    const long long nwin = (p.nchunks + p.P - 1) / p.P;
+    for (long long wi = nwin - 1; wi >= 0; --wi) {
+        const long long n0 = wi * p.P;
+        const int np = (int)(p.nchunks - n0 < p.P ? p.nchunks - n0 : p.P);
+        a.n0 = (int)n0;
+        kt->state(dim3(np, BH), s, a);
+        scan(1, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
+        kt->stats(dim3(np, BH), s, a);
+        scan(2, a.gslots, gR, gS, D, M, (int)p.P, np, BH, s);
+        kt->bwdq(dim3(np, BH), s, a);
+        kt->bwdkv(dim3(np, BH), s, a);
+    }
+    if (dR_in) {
+        copy_or_zero(dR_in, gR, p.BH * D * M, s);
+        copy_or_zero(dS_in, gS, p.BH * M, s);
+    }
+    return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
+}
+
+}  // extern "C"

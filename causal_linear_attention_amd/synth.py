@@ -68,4 +68,4 @@ def projection(seed: int, M: int, d: int, kind: str = "gaussian") -> np.ndarray:
         blocks.append(q.T)  # rows orthonormal
     Wo = np.concatenate(blocks, axis=0)[:M]
     norms = np.linalg.norm(g.standard_normal((M, d)), axis=1)
-    return (Wo * norms[:, None]).astype(np.float32)
+    return np.ascontiguousarray((Wo * norms[:, None]).astype(np.float32))

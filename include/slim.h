@@ -1,0 +1,135 @@
+/*
+ * slim.h -- C ABI of the MI355X (gfx950) causal linear self-attention library
+ * (libslim.so).
+ *
+ * The operation (page "Sub-Linear Memory: How to Make Performers SLiM",
+ * Subsection 2.1, eq. (2)-(4)):  for every batch b and head h, with a
+ * feature map g: R^d -> R_+^M,
+ *     R_l = R_0 + sum_{i<=l} V_i g(K_i)^T      (d x M)
+ *     S_l = S_0 + sum_{i<=l} g(K_i)            (M)
+ *     Y_l = R_l g(Q_l) / (S_l . g(Q_l))         l = 1..L
+ * i.e. the causal (diagonal included) g(Q_l).g(K_i)-weighted average of the
+ * values.  (R_0, S_0) is an optional initial state (zero by default), which
+ * lets one long sequence be streamed through several calls.
+ *
+ * Evaluation follows the page's sliced scheme (Subsection 3.2, eq. (14)-(18)):
+ * the sequence is cut into num_chunks slices of length c = ceil(L/num_chunks)
+ * (the last one may be shorter); the backward (Subsection 3.3, updates
+ * (19)-(20)) walks the slices in reverse, recomputing each slice's forward,
+ * recovering each slice's entry state from the final state by subtraction and
+ * carrying the gradient of the state.  No L x d x M prefix tensor is stored:
+ * the workspace holds per-slice states for a bounded window of slices, so it
+ * does not grow with L once L exceeds window_chunks * c.
+ *
+ * Feature maps (Subsection 2.1 names both kinds):
+ *   SLIM_FEAT_FAVOR: g(x)_m = exp(w_m . x - |x|^2/2) / sqrt(M), w_m = row m of
+ *                    W [M][d] (FAVOR+ positive random features; W is an input,
+ *                    drawn by the caller, Gaussian or orthogonal).
+ *   SLIM_FEAT_ELU1 : g(x)_j = elu(x_j) + 1, M must equal d, W must be NULL.
+ *
+ * Conventions for every entry point:
+ *   - Layout: Q, K, V, Y, dY, dQ, dK, dV are contiguous row-major
+ *     [B][H][L][d]; W is [M][d]; states R are [B][H][d][M] fp32, S [B][H][M]
+ *     fp32; phi is [B][H][L][M] fp32.
+ *   - dtype: SLIM_F32 or SLIM_BF16 is the element type of Q, K, V, W, Y, dY,
+ *     dQ, dK, dV.  States, statistics and all accumulation are fp32.
+ *   - All pointers are device pointers (HIP).  The caller owns every buffer;
+ *     the library never allocates, frees or synchronises.  Work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the default stream) and runs
+ *     asynchronously.  Buffers must stay valid until the work completes.
+ *   - Alignment: every tensor pointer and the workspace must be 16-byte
+ *     aligned (256-byte for the workspace).
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; a failing check returns a status and enqueues nothing.
+ *     SLIM_ERR_HIP means a launch failed (hipGetLastError); work enqueued
+ *     before the failure may have run.  No exception crosses the ABI.
+ *   - Supported shapes: d in {16, 32, 64, 128}; M in {16, 32, 64, 128, 256}
+ *     (FAVOR+) or M == d (elu+1); 1 <= num_chunks <= L; L < 2^31.  Other
+ *     shapes return SLIM_ERR_UNSUPPORTED.
+ *   - Results are deterministic: no atomics, fixed reduction order.
+ */
+#ifndef SLIM_H
+#define SLIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum slim_status {
+    SLIM_OK = 0,
+    SLIM_ERR_NULL = 1,        /* a required pointer is NULL */
+    SLIM_ERR_SHAPE = 2,       /* B, H, L, d, M or num_chunks out of range */
+    SLIM_ERR_DTYPE = 3,       /* unknown dtype or feature-map kind */
+    SLIM_ERR_UNSUPPORTED = 4, /* valid but not compiled: see supported shapes */
+    SLIM_ERR_WORKSPACE = 5,   /* workspace smaller than slim_workspace_bytes() */
+    SLIM_ERR_ALIGN = 6,       /* misaligned pointer */
+    SLIM_ERR_HIP = 7          /* a HIP launch failed */
+} slim_status;
+
+typedef enum slim_dtype { SLIM_F32 = 0, SLIM_BF16 = 1 } slim_dtype;
+typedef enum slim_feat { SLIM_FEAT_FAVOR = 0, SLIM_FEAT_ELU1 = 1 } slim_feat;
+typedef enum slim_pass { SLIM_PASS_FEATMAP = 0, SLIM_PASS_FWD = 1, SLIM_PASS_BWD = 2 } slim_pass;
+
+typedef struct slim_desc {
+    int64_t B, H, L;       /* batch, heads, sequence length */
+    int64_t d, M;          /* head dim, number of features */
+    int64_t num_chunks;    /* N slices; slice length c = ceil(L / N) */
+    int64_t window_chunks; /* slices whose states are held at once; 0 = auto */
+    int32_t dtype;         /* slim_dtype */
+    int32_t feat;          /* slim_feat */
+} slim_desc;
+
+/* Host-only check of a descriptor for a pass; touches no GPU. */
+slim_status slim_validate(const slim_desc *desc, int pass);
+
+/* Workspace bytes the pass needs (0 for SLIM_PASS_FEATMAP); 0 if the
+ * descriptor is invalid.  Host-only. */
+size_t slim_workspace_bytes(const slim_desc *desc, int pass);
+
+/* Slices whose states one window holds (the resolved window_chunks). */
+int64_t slim_window_chunks(const slim_desc *desc);
+
+/* Feature map (Subsection 2.1): phi[r][m] = g(X_r)_m in fp32 for the
+ * B*H*L rows of X ([B][H][L][d], desc dtype).  FAVOR+: if row_offset is
+ * non-NULL, row r is scaled by exp(-row_offset[r]) with
+ * row_offset[r] = max_m (w_m . X_r - |X_r|^2/2) (so every value is at most
+ * 1/sqrt(M)); if NULL, the unscaled value.  row_offset must be NULL for elu+1.
+ * num_chunks is ignored. */
+slim_status slim_featmap(const slim_desc *desc, const void *X, const void *W, float *phi, float *row_offset,
+                         void *stream);
+
+/* Forward (eq. (2) evaluated slice by slice, Subsection 3.2).
+ * In : Q, K, V, W (NULL for elu+1); R_in, S_in = initial state (both NULL =
+ *      zero, or both given).
+ * Out: Y; R_out, S_out = final state R_L, S_L (required: the backward starts
+ *      from it).  R_out/S_out may not alias R_in/S_in.
+ * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_FWD). */
+slim_status slim_attn_fwd(const slim_desc *desc, const void *Q, const void *K, const void *V, const void *W,
+                          const float *R_in, const float *S_in, void *Y, float *R_out, float *S_out, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* Backward of the loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out>
+ * (Subsection 3.3: reverse walk over slices, entry states recovered from the
+ * final state R_out/S_out of the forward by subtraction).
+ * In : Q, K, V, W as in the forward; dY; R_out, S_out from the forward;
+ *      dR_out, dS_out = incoming gradient of the final state (both NULL = zero).
+ * Out: dQ, dK, dV; dR_in, dS_in = gradient w.r.t. the initial state (both NULL
+ *      = not wanted, or both given).  dW is not computed.
+ * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_BWD). */
+slim_status slim_attn_bwd(const slim_desc *desc, const void *Q, const void *K, const void *V, const void *W,
+                          const void *dY, const float *R_out, const float *S_out, const float *dR_out,
+                          const float *dS_out, void *dQ, void *dK, void *dV, float *dR_in, float *dS_in, void *ws,
+                          size_t ws_bytes, void *stream);
+
+const char *slim_status_string(slim_status s);
+
+/* ABI version: (major << 16) | minor. */
+int slim_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SLIM_H */

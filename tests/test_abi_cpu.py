@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/slim.h declares, and its validation / workspace
+planning behave as documented.  Nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from causal_linear_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "slim.h")
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(slim_[a-z_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libslim.so not built")
+    return _lib.lib()
+
+
+def test_header_lists_the_binding_exports():
+    assert header_functions() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.slim_version() >> 16 == 1
+    for code in range(8):
+        assert lib.slim_status_string(code)
+    assert lib.slim_status_string(0) == b"ok"
+
+
+def d_(**kw):
+    base = dict(B=2, H=3, L=1000, d=64, M=128, num_chunks=8, window_chunks=0, dtype=_lib.SLIM_BF16,
+                feat=_lib.SLIM_FEAT_FAVOR)
+    base.update(kw)
+    return _lib.desc(**base)
+
+
+def validate(lib, pass_=_lib.SLIM_PASS_FWD, **kw):
+    return lib.slim_validate(ctypes.byref(d_(**kw)), pass_)
+
+
+def test_validate_ok(lib):
+    for p in (0, 1, 2):
+        assert validate(lib, p) == 0
+    assert validate(lib, feat=_lib.SLIM_FEAT_ELU1, M=64) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 2), (dict(H=-1), 2), (dict(L=0), 2), (dict(num_chunks=0), 2), (dict(num_chunks=1001), 2),
+    (dict(window_chunks=-1), 2), (dict(L=1 << 31), 2), (dict(dtype=7), 3), (dict(feat=9), 3),
+    (dict(feat=_lib.SLIM_FEAT_ELU1), 2),            # elu+1 needs M == d
+    (dict(d=48), 4), (dict(M=96), 4), (dict(M=512), 4), (dict(d=256, M=256), 4),
+])
+def test_validate_errors(lib, kw, code):
+    assert validate(lib, **kw) == code
+
+
+def test_validate_null(lib):
+    assert lib.slim_validate(None, 1) == 1
+
+
+def test_entry_points_reject_before_any_launch(lib):
+    d = d_()
+    # NULL inputs / workspace: rejected on the host, nothing enqueued
+    assert lib.slim_attn_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 0,
+                           None) == 1
+    p = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    assert lib.slim_attn_fwd(ctypes.byref(d), p, p, p, p, None, None, p, p, p, p, 0, None) == 5
+    bad = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.slim_attn_fwd(ctypes.byref(d), bad, p, p, p, None, None, p, p, p, p, 1 << 40, None) == 6
+    assert lib.slim_attn_bwd(ctypes.byref(d_(num_chunks=0)), p, p, p, p, p, p, p, None, None, p, p, p, None, None,
+                           p, 1 << 40, None) == 2
+    # only one of the paired initial-state pointers
+    assert lib.slim_attn_fwd(ctypes.byref(d), p, p, p, p, p, None, p, p, p, p, 1 << 40, None) == 1
+    # elu+1 takes no W
+    de = d_(feat=_lib.SLIM_FEAT_ELU1, M=64)
+    assert lib.slim_attn_fwd(ctypes.byref(de), p, p, p, p, None, None, p, p, p, p, 1 << 40, None) == 2
+    assert lib.slim_featmap(ctypes.byref(de), p, None, p, p, None) == 2
+
+
+def ws(lib, pass_, **kw):
+    return lib.slim_workspace_bytes(ctypes.byref(d_(**kw)), pass_)
+
+
+def test_workspace_sizes(lib):
+    assert ws(lib, 0) == 0
+    assert 0 < ws(lib, 1) < ws(lib, 2)
+    assert ws(lib, 1, B=0) == 0
+    # forward: (window + 1) slots of (d + 1) * M fp32 per head
+    d = d_(L=4096, num_chunks=16, window_chunks=16)
+    assert lib.slim_workspace_bytes(ctypes.byref(d), 1) >= 6 * 17 * 65 * 128 * 4
+
+
+def test_workspace_does_not_grow_with_L_at_fixed_slice_and_window(lib):
+    # slice length 512, window of 64 slices: once L exceeds 64 * 512 the workspace is flat
+    sizes = [ws(lib, 2, B=1, H=8, L=n, d=64, M=64, num_chunks=n // 512, window_chunks=64)
+             for n in (1 << 15, 1 << 16, 1 << 18, 1 << 20)]
+    assert len(set(sizes)) == 1, sizes
+    fw = [ws(lib, 1, B=1, H=8, L=n, d=64, M=64, num_chunks=n // 512, window_chunks=64) for n in (1 << 15, 1 << 20)]
+    assert fw[0] == fw[1]
+
+
+def test_auto_window(lib):
+    d = d_(B=4, H=16, L=16384, d=64, M=256, num_chunks=32)
+    assert lib.slim_window_chunks(ctypes.byref(d)) == 32
+    d = d_(B=1, H=8, L=1 << 20, d=64, M=64, num_chunks=2048)
+    assert lib.slim_window_chunks(ctypes.byref(d)) == 512

@@ -1,0 +1,185 @@
+"""GPU (HIP, gfx950) against the fp64 oracle, element by element on the same
+seeded inputs, through the C ABI.  Tolerance: normwise relative error per
+(batch, head) and tensor, 1e-4 for fp32 inputs and 2e-2 for bf16 inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from causal_linear_attention_amd import attention as A
+from gpu_util import DT, TOL, host64, inputs, relerr, relerr_heads
+
+pytestmark = pytest.mark.gpu
+
+# (B, H, L, d, M, chunks, dtype, feat): several tiles per chunk, ragged tails,
+# a single chunk (pure intra-chunk), one-row chunks, partial last chunk.
+CASES = [
+    (1, 1, 256, 16, 16, 4, "f32", "favor"),    # the small fp32 forward workload
+    (1, 2, 200, 16, 32, 3, "f32", "favor"),    # chunk 67: ragged tiles and ragged last chunk
+    (2, 2, 160, 32, 64, 1, "f32", "favor"),    # one chunk
+    (1, 2, 96, 64, 128, 96, "f32", "favor"),   # one-row chunks
+    (1, 2, 333, 64, 256, 5, "f32", "favor"),
+    (1, 2, 300, 64, 64, 7, "bf16", "favor"),
+    (1, 2, 257, 64, 256, 2, "bf16", "favor"),
+    (2, 1, 190, 64, 128, 4, "bf16", "favor"),
+    (1, 2, 150, 32, 32, 3, "f32", "elu1"),
+    (1, 2, 270, 64, 64, 4, "bf16", "elu1"),
+    (1, 1, 200, 128, 128, 3, "bf16", "elu1"),
+    (1, 1, 100, 128, 128, 2, "f32", "elu1"),
+    (1, 1, 64, 16, 16, 64, "bf16", "elu1"),
+]
+
+
+def _id(c):
+    return "B%dH%dL%d_d%dM%d_C%d_%s_%s" % c
+
+
+def _supported(d, M, dtype, feat):
+    from causal_linear_attention_amd import _lib
+    import ctypes
+    dsc = _lib.desc(1, 1, 16, d, M, 1, 0, _lib.SLIM_F32 if dtype == "f32" else _lib.SLIM_BF16,
+                    _lib.SLIM_FEAT_FAVOR if feat == "favor" else _lib.SLIM_FEAT_ELU1)
+    return _lib.lib().slim_validate(ctypes.byref(dsc), 1) == 0
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_forward_matches_oracle(case):
+    B, H, L, d, M, C, dt, feat = case
+    if not _supported(d, M, dt, feat):
+        pytest.skip("shape not compiled")
+    dtype = DT[dt]
+    x = inputs(B, H, L, d, M, dtype, feat, seed=11, dy=False)
+    print("fwd", _id(case), flush=True)
+    Y, R, S = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], feat, C)
+    torch.cuda.synchronize()
+    Yo, _, Ro, So = oracle.attn_fwd(host64(x["q"]), host64(x["k"]), host64(x["v"]),
+                                    None if x["W"] is None else host64(x["W"]), feat)
+    tol = TOL[dtype]
+    assert relerr_heads(host64(Y), Yo) < tol
+    assert relerr_heads(host64(R), Ro) < tol
+    assert relerr_heads(host64(S), So) < tol
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_backward_matches_oracle(case):
+    B, H, L, d, M, C, dt, feat = case
+    if not _supported(d, M, dt, feat):
+        pytest.skip("shape not compiled")
+    dtype = DT[dt]
+    x = inputs(B, H, L, d, M, dtype, feat, seed=12)
+    print("bwd", _id(case), flush=True)
+    Y, R, S = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], feat, C)
+    dQ, dK, dV, _, _ = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], R, S, feat, C)
+    torch.cuda.synchronize()
+    Wh = None if x["W"] is None else host64(x["W"])
+    g = oracle.attn_bwd(host64(x["q"]), host64(x["k"]), host64(x["v"]), Wh, host64(x["dy"]), feat)
+    tol = TOL[dtype]
+    for name, got, ref in (("dQ", dQ, g[0]), ("dK", dK, g[1]), ("dV", dV, g[2])):
+        e = relerr_heads(host64(got), ref)
+        assert e < tol, (name, e)
+
+
+@pytest.mark.parametrize("dt,feat,d,M", [("f32", "favor", 64, 128), ("bf16", "favor", 64, 256),
+                                         ("bf16", "elu1", 64, 64)])
+def test_featmap_matches_oracle(dt, feat, d, M):
+    dtype = DT[dt]
+    x = inputs(2, 3, 77, d, M, dtype, feat, seed=13, dy=False)
+    phi = A.featmap(x["q"], x["W"], feat)
+    Wh = None if x["W"] is None else host64(x["W"])
+    ref = oracle.featmap(host64(x["q"]), Wh, feat)
+    assert relerr(host64(phi), ref) < (1e-5 if dt == "f32" else 1e-5 * 4)
+    if feat == "favor":
+        phi2, off = A.featmap(x["q"], x["W"], feat, row_offset=True)
+        back = host64(phi2) * np.exp(host64(off))[..., None]
+        assert relerr(back, ref) < 1e-4
+        assert float(host64(phi2).max()) <= 1.0 / np.sqrt(M) * (1 + 1e-5)
+
+
+def test_initial_state_and_state_gradients():
+    # Streaming: run [P; X] in one call vs X from the state of P; gradients of the
+    # initial state against the oracle with a nonzero incoming state gradient.
+    B, H, L, d, M = 1, 2, 192, 64, 128
+    dtype = torch.float32
+    x = inputs(B, H, L, d, M, dtype, "favor", seed=14)
+    q, k, v, W, dy = x["q"], x["k"], x["v"], x["W"], x["dy"]
+    Yf, Rf, Sf = A.attn_fwd(q, k, v, W, "favor", 3)
+    _, Rp, Sp = A.attn_fwd(q[:, :, :64].contiguous(), k[:, :, :64].contiguous(), v[:, :, :64].contiguous(), W,
+                           "favor", 2)
+    Y2, R2, S2 = A.attn_fwd(q[:, :, 64:].contiguous(), k[:, :, 64:].contiguous(), v[:, :, 64:].contiguous(), W,
+                            "favor", 2, R_in=Rp, S_in=Sp)
+    torch.cuda.synchronize()
+    assert relerr_heads(host64(Y2), host64(Yf[:, :, 64:])) < 1e-5
+    assert relerr_heads(host64(R2), host64(Rf)) < 1e-5
+    rng = np.random.default_rng(5)
+    dRo = torch.from_numpy(rng.standard_normal((B, H, d, M)).astype(np.float32)).cuda() * 1e-3
+    dSo = torch.from_numpy(rng.standard_normal((B, H, M)).astype(np.float32)).cuda() * 1e-3
+    qs, ks, vs, dys = (t[:, :, 64:].contiguous() for t in (q, k, v, dy))
+    dQ, dK, dV, dR0, dS0 = A.attn_bwd(qs, ks, vs, W, dys, R2, S2, "favor", 2, dR_out=dRo, dS_out=dSo,
+                                      want_state_grad=True)
+    torch.cuda.synchronize()
+    g = oracle.attn_bwd(host64(qs), host64(ks), host64(vs), host64(W), host64(dys), "favor", R0=host64(Rp),
+                        S0=host64(Sp), dRout=host64(dRo), dSout=host64(dSo))
+    for name, got, ref in (("dQ", dQ, g[0]), ("dK", dK, g[1]), ("dV", dV, g[2]), ("dR0", dR0, g[3]),
+                           ("dS0", dS0, g[4])):
+        e = relerr_heads(host64(got), ref)
+        assert e < 1e-4, (name, e)
+
+
+def test_chunk_count_invariance_and_windows():
+    # The sliced result does not depend on the slice count or the window (up to rounding).
+    B, H, L, d, M = 1, 2, 1024, 64, 64
+    x = inputs(B, H, L, d, M, torch.float32, "favor", seed=15)
+    ref = None
+    for C, P in ((1, 0), (4, 0), (16, 0), (16, 3), (64, 5), (1024, 100)):
+        Y, R, S = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], "favor", C, window_chunks=P)
+        dQ, dK, dV, _, _ = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], R, S, "favor", C, window_chunks=P)
+        cur = [host64(t) for t in (Y, dQ, dK, dV)]
+        if ref is None:
+            ref = cur
+            g = oracle.attn_bwd(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(x["W"]), host64(x["dy"]),
+                                "favor")
+            Yo = oracle.attn_fwd(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(x["W"]), "favor")[0]
+            oref = [Yo, g[0], g[1], g[2]]
+        errs = [relerr_heads(a, b) for a, b in zip(cur, ref)]
+        oerrs = [relerr_heads(a, b) for a, b in zip(cur, oref)]
+        print("slices", C, "window", P, "vs one slice", ["%.2e" % e for e in errs],
+              "vs oracle", ["%.2e" % e for e in oerrs], flush=True)
+        # each chunking matches the oracle, hence the others, within the fp32 bound
+        assert max(oerrs) < 1e-4, (C, P, oerrs)
+        assert max(errs) < 2e-4, (C, P, errs)
+
+
+def test_deterministic():
+    x = inputs(1, 2, 700, 64, 256, torch.bfloat16, "favor", seed=16)
+    outs = []
+    for _ in range(2):
+        Y, R, S = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], "favor", 3)
+        dQ, dK, dV, _, _ = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], R, S, "favor", 3)
+        outs.append([t.clone() for t in (Y, R, dQ, dK, dV)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_causality():
+    # Perturbing row j leaves outputs before j bitwise unchanged.
+    x = inputs(1, 1, 256, 64, 64, torch.float32, "favor", seed=17, dy=False)
+    Y0, _, _ = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], "favor", 4)
+    for name in ("q", "k", "v"):
+        y = dict(x)
+        t = x[name].clone()
+        t[:, :, 150] += 0.5
+        y[name] = t
+        Y1, _, _ = A.attn_fwd(y["q"], y["k"], y["v"], y["W"], "favor", 4)
+        torch.cuda.synchronize()
+        assert torch.equal(Y0[:, :, :150], Y1[:, :, :150]), name
+        assert not torch.equal(Y0[:, :, 150], Y1[:, :, 150]), name
+
+
+def test_autograd_function():
+    x = inputs(1, 2, 130, 32, 64, torch.float32, "favor", seed=18)
+    q, k, v = (x[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    Y = A.slim_attention(q, k, v, x["W"], "favor", 3)
+    (Y * x["dy"]).sum().backward()
+    g = oracle.attn_bwd(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(x["W"]), host64(x["dy"]), "favor")
+    for got, ref in ((q.grad, g[0]), (k.grad, g[1]), (v.grad, g[2])):
+        assert relerr_heads(host64(got), ref) < 1e-4
