@@ -19,7 +19,8 @@ STATUS = {0: "SLIM_OK", 1: "SLIM_ERR_NULL", 2: "SLIM_ERR_SHAPE", 3: "SLIM_ERR_DT
 
 # every symbol declared in include/slim.h
 EXPORTS = ["slim_validate", "slim_workspace_bytes", "slim_window_chunks", "slim_featmap", "slim_attn_fwd",
-           "slim_attn_bwd", "slim_status_string", "slim_version"]
+           "slim_attn_bwd", "slim_status_string", "slim_version", "slim_prof_enable", "slim_prof_count",
+           "slim_prof_entry"]
 
 
 class SlimDesc(ctypes.Structure):
@@ -65,6 +66,13 @@ def lib(path: str | None = None):
     L.slim_status_string.restype = ctypes.c_char_p
     L.slim_version.argtypes = []
     L.slim_version.restype = i32
+    L.slim_prof_enable.argtypes = [i32]
+    L.slim_prof_enable.restype = i32
+    L.slim_prof_count.argtypes = []
+    L.slim_prof_count.restype = i32
+    L.slim_prof_entry.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                  ctypes.POINTER(ctypes.c_int64)]
+    L.slim_prof_entry.restype = i32
     if path is None:
         _lib = L
     return L
@@ -85,3 +93,18 @@ def check(code: int, where: str):
 def desc(B, H, L, d, M, num_chunks=1, window_chunks=0, dtype=SLIM_F32, feat=SLIM_FEAT_FAVOR) -> SlimDesc:
     return SlimDesc(int(B), int(H), int(L), int(d), int(M), int(num_chunks), int(window_chunks), int(dtype),
                     int(feat))
+
+
+def prof_enable(on: bool):
+    check(lib().slim_prof_enable(1 if on else 0), "slim_prof_enable")
+
+
+def prof_read() -> dict:
+    """{kernel name: (total GPU ms, launches)} since the last prof_enable(True)."""
+    L = lib()
+    out = {}
+    for i in range(L.slim_prof_count()):
+        name, ms, n = ctypes.c_char_p(), ctypes.c_double(), ctypes.c_int64()
+        check(L.slim_prof_entry(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(n)), "slim_prof_entry")
+        out[name.value.decode()] = (ms.value, n.value)
+    return out

@@ -16,10 +16,92 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
 #include "../../include/slim.h"
 #include "slim_dispatch.h"
 
 namespace slim {
+
+// Kernel timing (diagnostics): when enabled, each launch below is bracketed by
+// a pair of hipEvents recorded on the launch stream; slim_prof_entry() waits
+// for the pending pairs and accumulates elapsed time per kernel name.
+namespace prof {
+struct Pending {
+    std::string name;
+    hipEvent_t a, b;
+};
+struct Total {
+    double ms = 0.0;
+    long long n = 0;
+};
+static std::mutex mu;
+static bool on = false;
+static std::vector<Pending> pending;
+static std::vector<hipEvent_t> pool;
+static std::map<std::string, Total> totals;
+static std::vector<std::string> order;
+
+static hipEvent_t take()
+{
+    if (!pool.empty()) {
+        hipEvent_t e = pool.back();
+        pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+struct Scope {
+    bool active = false;
+    Pending p;
+    hipStream_t s;
+    Scope(const char *name, hipStream_t st) : s(st)
+    {
+        std::lock_guard<std::mutex> g(mu);
+        if (!on) return;
+        p.name = name;
+        p.a = take();
+        p.b = take();
+        if (!p.a || !p.b) return;
+        active = hipEventRecord(p.a, s) == hipSuccess;
+    }
+    ~Scope()
+    {
+        if (!active) return;
+        std::lock_guard<std::mutex> g(mu);
+        hipEventRecord(p.b, s);
+        pending.push_back(p);
+    }
+};
+
+static void collect()
+{
+    for (auto &p : pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+            if (!totals.count(p.name)) order.push_back(p.name);
+            Total &t = totals[p.name];
+            t.ms += ms;
+            t.n += 1;
+        }
+        pool.push_back(p.a);
+        pool.push_back(p.b);
+    }
+    pending.clear();
+}
+}  // namespace prof
+
+#define SLIM_TIMED(name, s, call) \
+    do {                          \
+        prof::Scope _ps(name, s); \
+        call;                     \
+    } while (0)
 
 __global__ __launch_bounds__(256) void copy_or_zero_kernel(float *dst, const float *src, long long n)
 {
@@ -38,6 +120,7 @@ static void scan(int mode, float *slots, float *cR, float *cS, int D, int M, int
 {
     const int SZ = (D + 1) * M;
     dim3 grid((unsigned)((SZ / 4 + 255) / 256), (unsigned)BH);
+    prof::Scope ps(mode == 0 ? "scan_prefix" : mode == 1 ? "scan_reverse" : "scan_grad", s);
     if (mode == 0)
         hipLaunchKernelGGL(scan_kernel<0>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np);
     else if (mode == 1)
@@ -113,7 +196,39 @@ using namespace slim;
 
 extern "C" {
 
-int slim_version(void) { return (1 << 16) | 0; }
+int slim_version(void) { return (1 << 16) | 1; }
+
+slim_status slim_prof_enable(int enable)
+{
+    std::lock_guard<std::mutex> g(prof::mu);
+    prof::collect();
+    if (enable) {
+        prof::totals.clear();
+        prof::order.clear();
+    }
+    prof::on = enable != 0;
+    return SLIM_OK;
+}
+
+int slim_prof_count(void)
+{
+    std::lock_guard<std::mutex> g(prof::mu);
+    prof::collect();
+    return (int)prof::order.size();
+}
+
+slim_status slim_prof_entry(int i, const char **name, double *total_ms, int64_t *launches)
+{
+    std::lock_guard<std::mutex> g(prof::mu);
+    prof::collect();
+    if (i < 0 || i >= (int)prof::order.size()) return SLIM_ERR_SHAPE;
+    if (!name || !total_ms || !launches) return SLIM_ERR_NULL;
+    const prof::Total &t = prof::totals[prof::order[i]];
+    *name = prof::order[i].c_str();
+    *total_ms = t.ms;
+    *launches = t.n;
+    return SLIM_OK;
+}
 
 const char *slim_status_string(slim_status s)
 {
@@ -174,7 +289,8 @@ slim_status slim_featmap(const slim_desc *d, const void *X, const void *W, float
     const long long rows = d->B * d->H * d->L;
     const long long nblk = (rows + kt->tt - 1) / kt->tt;
     if (nblk > 0x7fffffffLL) return SLIM_ERR_SHAPE;
-    kt->featmap(dim3((unsigned)nblk), (hipStream_t)stream, X, W, phi, row_offset, rows);
+    SLIM_TIMED("featmap", (hipStream_t)stream,
+               kt->featmap(dim3((unsigned)nblk), (hipStream_t)stream, X, W, phi, row_offset, rows));
     return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
 
@@ -208,9 +324,9 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
     for (long long n0 = 0; n0 < p.nchunks; n0 += p.P) {
         const int np = (int)(p.nchunks - n0 < p.P ? p.nchunks - n0 : p.P);
         a.n0 = (int)n0;
-        kt->state(dim3(np, BH), s, a);
+        SLIM_TIMED("state", s, kt->state(dim3(np, BH), s, a));
         scan(0, a.slots, R_out, S_out, D, M, (int)p.P, np, BH, s);
-        kt->fwd(dim3(np, BH), s, a);
+        SLIM_TIMED("fwd", s, kt->fwd(dim3(np, BH), s, a));
     }
     return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
@@ -257,12 +373,12 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
         const long long n0 = wi * p.P;
         const int np = (int)(p.nchunks - n0 < p.P ? p.nchunks - n0 : p.P);
         a.n0 = (int)n0;
-        kt->state(dim3(np, BH), s, a);
+        SLIM_TIMED("state", s, kt->state(dim3(np, BH), s, a));
         scan(1, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
-        kt->stats(dim3(np, BH), s, a);
+        SLIM_TIMED("stats", s, kt->stats(dim3(np, BH), s, a));
         scan(2, a.gslots, gR, gS, D, M, (int)p.P, np, BH, s);
-        kt->bwdq(dim3(np, BH), s, a);
-        kt->bwdkv(dim3(np, BH), s, a);
+        SLIM_TIMED("bwdq", s, kt->bwdq(dim3(np, BH), s, a));
+        SLIM_TIMED("bwdkv", s, kt->bwdkv(dim3(np, BH), s, a));
     }
     if (dR_in) {
         copy_or_zero(dR_in, gR, p.BH * D * M, s);

@@ -71,3 +71,36 @@ def io_bytes_per_head_token(w: Workload, backward: bool = True) -> float:
     s = 4 if w.dtype == "f32" else 2
     n = 11 if backward else 4
     return n * w.d * s
+
+
+def kernel_flops(w: Workload, tile: int) -> dict:
+    """Useful MFMA floating-point work per (token, head) of each kernel, as the
+    kernels evaluate it: every chunk is walked in `tile`-row tiles carrying the
+    d x M state, so the intra-tile causal products cost about (tile+1) M and
+    (tile+1) d per row, and every state-sized product (a d x M contraction per
+    row) costs 2 d M.  A FAVOR+ feature-map projection is one more 2 d M per row
+    and orientation computed (elu+1 needs none).  Zero padding, masked-out
+    upper triangles and elementwise work are not counted."""
+    d, M = w.d, w.M
+    favor = w.feat == "favor"
+    P = 2 * d * M if favor else 0        # one feature-map projection
+    dm = 2 * d * M                       # one state-sized contraction
+    tm = (tile + 1) * M                  # causal tile x tile x M product, per row
+    td = (tile + 1) * d                  # causal tile x tile x d product, per row
+    vjp = dm if favor else 0             # FAVOR+ chain rule through W
+    return {
+        "state": P + dm,                                   # g(K); dR = V^T g(K)
+        "fwd": 3 * P + tm + td + 2 * dm,                   # g(Q)^T, g(K)^T, g(K); P^T; V^T P^T; R g(Q); state
+        "stats": 4 * P + tm + td + 3 * dm,                 # fwd + g(Q) rows-major + dG
+        "bwdq": 2 * P + tm + td + 2 * dm + vjp,            # g(Q)^T, g(K); A^T; A g(K); dNum R; W chain; R
+        "bwdkv": 3 * P + 2 * tm + 2 * td + 4 * dm + vjp,   # g(Q)^T, g(Q), g(K)^T; P; A; A^T g(Q); dR V; chain;
+                                                            # P^T dNum; g(K) dR^T; dR, dR^T updates
+    }
+
+
+def survey_flops(w: Workload) -> float:
+    """The per-(token, head) fwd+bwd count of the unsliced-tile accounting:
+    28 d M + 4 c (M + d) for FAVOR+, 16 d M + 4 c (M + d) for elu+1."""
+    c = w.chunk_len
+    base = 28 if w.feat == "favor" else 16
+    return base * w.d * w.M + 4 * c * (w.M + w.d)

@@ -126,6 +126,20 @@ slim_status slim_attn_bwd(const slim_desc *desc, const void *Q, const void *K, c
 
 const char *slim_status_string(slim_status s);
 
+/* Kernel timing, for measurement tools.  slim_prof_enable(1) clears the
+ * totals and starts bracketing every kernel the library launches with a pair
+ * of hipEvents on the launch stream (a small, constant overhead per launch);
+ * slim_prof_enable(0) stops.  slim_prof_count() and slim_prof_entry() first
+ * wait for the recorded events to complete (they synchronise with those
+ * events), then report per kernel name ("state", "scan_prefix", "fwd",
+ * "scan_reverse", "stats", "scan_grad", "bwdq", "bwdkv", "featmap") the summed
+ * GPU time in milliseconds and the number of launches.  The name pointer stays
+ * valid until the next slim_prof_enable(1).  Guarded by a process-wide mutex;
+ * the timings are global to the process, not per stream. */
+slim_status slim_prof_enable(int enable);
+int slim_prof_count(void);
+slim_status slim_prof_entry(int i, const char **name, double *total_ms, int64_t *launches);
+
 /* ABI version: (major << 16) | minor. */
 int slim_version(void);
 
