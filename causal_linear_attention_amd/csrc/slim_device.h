@@ -136,51 +136,98 @@ template <typename T> struct Vec16;
 template <> struct Vec16<float> { typedef f4 type; static constexpr int N = 4; };
 template <> struct Vec16<__bf16> { typedef bf8 type; static constexpr int N = 8; };
 
-// Stage rows [0, TT) of a row-major [rows][D] tile (src points at its first row) into
-// LDS dst[TT][ldx] (skipped if dst is null); rows >= nvalid read as zero.  If dstT is non-null the transposed
-// tile dstT[D][ldt] is written as well.  If rowscale is non-null, row t is multiplied
-// by rowscale[t] (in fp32) before it is stored.
-template <typename T, int D, int TT, int NT>
-__device__ __forceinline__ void stage_tile(T *dst, int ldx, T *dstT, int ldt, const T *__restrict__ src, int nvalid,
-                                           const float *rowscale)
+template <typename T> __device__ __forceinline__ typename Vec16<T>::type zero16()
 {
-    typedef typename Vec16<T>::type V;
-    constexpr int EPV = Vec16<T>::N;
-    constexpr int VPR = D / EPV;
-    for (int v = threadIdx.x; v < TT * VPR; v += NT) {
-        const int t = v / VPR, c = (v % VPR) * EPV;
-        V x;
-        if (t < nvalid) {
-            x = *reinterpret_cast<const V *>(src + (size_t)t * D + c);
-            if (rowscale) {
-                const float s = rowscale[t];
+    typename Vec16<T>::type z;
 #pragma unroll
-                for (int j = 0; j < EPV; ++j) x[j] = (T)((float)x[j] * s);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < EPV; ++j) x[j] = (T)0.f;
-        }
-        if (dst) *reinterpret_cast<V *>(dst + t * ldx + c) = x;
-        if (dstT) {
-#pragma unroll
-            for (int j = 0; j < EPV; ++j) dstT[(c + j) * ldt + t] = x[j];
-        }
-    }
+    for (int j = 0; j < Vec16<T>::N; ++j) z[j] = (T)0.f;
+    return z;
 }
 
-// |x_t|^2 of every row of an LDS tile [TT][ldx] (io type), written to out[t].
-template <typename T, int D, int TT, int NT>
-__device__ __forceinline__ void row_sqnorm(const T *x, int ldx, float *out)
+// 16-byte vector store into an LDS row whose stride is only 8-byte aligned.
+__device__ __forceinline__ void store16(float *p, f4 x) { *reinterpret_cast<f4 *>(p) = x; }
+__device__ __forceinline__ void store16(__bf16 *p, bf8 x)
 {
-    for (int t = threadIdx.x; t < TT; t += NT) {
-        float s = 0.f;
-        for (int e = 0; e < D; ++e) {
-            const float v = (float)x[t * ldx + e];
-            s += v * v;
-        }
-        out[t] = s;
-    }
+    reinterpret_cast<bf4 *>(p)[0] = bf4{x[0], x[1], x[2], x[3]};
+    reinterpret_cast<bf4 *>(p)[1] = bf4{x[4], x[5], x[6], x[7]};
 }
+
+// A [TT][D] tile of a row-major tensor held in registers: thread i owns the
+// 16-byte vectors i, i+NT, ... (row t = idx / VPR, columns c..c+EPV-1).  load()
+// issues the global reads (rows >= nvalid read as zero) and returns at once, so a
+// tile can be fetched while the previous one is being computed; store() moves it
+// into LDS once the data is needed.
+template <typename T, int D, int TT, int NT> struct TileRegs {
+    typedef typename Vec16<T>::type V;
+    static constexpr int EPV = Vec16<T>::N;
+    static constexpr int VPR = D / EPV;
+    static constexpr int NV = TT * VPR;
+    static constexpr int PER = (NV + NT - 1) / NT;
+    V v[PER];
+    float s[PER];
+
+    // stats (optional): per-row (scale, unused) pairs; row t's scale goes with its vectors.
+    __device__ __forceinline__ void load(const T *__restrict__ src, int nvalid, const float *stats = nullptr)
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            const int t = idx / VPR, c = (idx % VPR) * EPV;
+            const bool ok = idx < NV && t < nvalid;
+            v[i] = ok ? *reinterpret_cast<const V *>(src + (size_t)t * D + c) : zero16<T>();
+            if (stats) s[i] = ok ? stats[(size_t)t * 2] : 0.f;
+        }
+    }
+    // Write to dst[TT][ldx] (if non-null) and the transposed dstT[D][ldt] (if
+    // non-null); scaled: multiply row t by its stats scale first; sq (if non-null)
+    // receives |row t|^2 (summed over the VPR lanes of the row with shuffles).
+    __device__ __forceinline__ void store(T *dst, int ldx, T *dstT, int ldt, bool scaled, float *sq) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            const int t = idx / VPR, c = (idx % VPR) * EPV;
+            V x = v[i];
+            if (scaled) {
+#pragma unroll
+                for (int j = 0; j < EPV; ++j) x[j] = (T)((float)x[j] * s[i]);
+            }
+            if (idx < NV) {
+                if (dst) store16(dst + t * ldx + c, x);
+                if (dstT) {
+#pragma unroll
+                    for (int j = 0; j < EPV; ++j) dstT[(c + j) * ldt + t] = x[j];
+                }
+            }
+            if (sq) {
+                float q = 0.f;
+#pragma unroll
+                for (int j = 0; j < EPV; ++j) q += (float)x[j] * (float)x[j];
+#pragma unroll
+                for (int o = 1; o < VPR; o <<= 1) q += __shfl_xor(q, o, 64);
+                if (idx < NV && c == 0) sq[t] = q;
+            }
+        }
+    }
+};
+
+// Per-row statistics of a tile held in registers by threads 0..TT-1.
+template <int TT> struct RowStatRegs {
+    float inv, dd;
+    __device__ __forceinline__ void load(const float *st, int nvalid)
+    {
+        const int t = threadIdx.x;
+        const bool ok = t < TT && t < nvalid;
+        inv = ok ? st[(size_t)t * 2] : 0.f;
+        dd = ok ? st[(size_t)t * 2 + 1] : 0.f;
+    }
+    __device__ __forceinline__ void store(float *invl, float *ddl) const
+    {
+        if (threadIdx.x < TT) {
+            invl[threadIdx.x] = inv;
+            ddl[threadIdx.x] = dd;
+        }
+    }
+};
 
 }  // namespace slim

@@ -47,21 +47,23 @@ struct ChunkArgs {
     int P;   // window capacity (slot stride)
 };
 
-template <typename T_, int D_, int M_, int FEAT_, int TT_> struct KCfg {
+template <typename T_, int D_, int M_, int FEAT_, int TT_, int MW_ = 32> struct KCfg {
     typedef T_ T;
     static constexpr int D = D_, M = M_, FEAT = FEAT_, TT = TT_;
-    static constexpr int NW = M >= 64 ? 4 : M / 16;  // waves per workgroup
+    static constexpr int MW = M >= MW_ ? MW_ : M;  // features per wave
+    static constexpr int NW = M / MW;            // waves per workgroup
     static constexpr int NT = NW * 64;
-    static constexpr int MW = M / NW;  // features per wave
     static constexpr int NFB = MW / 16;
     static constexpr int NEB = D / 16;
     static constexpr int NTB = TT / 16;
-    static constexpr int PADE = 16 / (int)sizeof(T);
-    static constexpr int LDX = D + PADE;   // [TT][D] tiles
-    static constexpr int LDT = TT + PADE;  // [D][TT] transposed tiles
-    static constexpr int LDR = D + 4;      // fp32 reduction rows
+    // LDS row strides: 4 elements of padding make the rows of a 16-row operand
+    // read land in distinct banks (stride = 8 bytes mod 128 for bf16, 16 for fp32).
+    static constexpr int LDX = D + 4;   // [TT][D] tiles
+    static constexpr int LDT = TT + 4;  // [D][TT] transposed tiles
+    static constexpr int LDR = D + 4;   // fp32 reduction rows
     static constexpr int SZ = (D + 1) * M;
     static constexpr bool FAVOR = FEAT == FEAT_FAVOR;
+    typedef TileRegs<T, D, TT, NT> Tile;
     static_assert(FEAT == FEAT_FAVOR || D == M, "elu+1 needs M == d");
     static_assert(MW % 16 == 0 && D % 16 == 0 && TT % 16 == 0, "block sizes");
 };
@@ -291,9 +293,11 @@ __global__ __launch_bounds__(C::NT) void featmap_kernel(const void *Xv, const vo
     const T *X = (const T *)Xv + r0 * C::D;
     Frag<T> wf[C::NFB][C::NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, Wv);
-    stage_tile<T, C::D, C::TT, C::NT>(xs, C::LDX, nullptr, 0, X, nv, nullptr);
-    __syncthreads();
-    if constexpr (C::FAVOR) row_sqnorm<T, C::D, C::TT, C::NT>(xs, C::LDX, kn);
+    {
+        typename C::Tile rx;
+        rx.load(X, nv);
+        rx.store(xs, C::LDX, nullptr, 0, false, C::FAVOR ? kn : nullptr);
+    }
     __syncthreads();
     f4 ph[C::NFB][C::NTB];
     feat_T<C>(ph, xs, wf);
@@ -375,14 +379,18 @@ template <class C> __global__ __launch_bounds__(C::NT) void state_kernel(ChunkAr
 #pragma unroll
         for (int eb = 0; eb < NEB; ++eb) rt[fb][eb] = f4zero();
     }
+    typename C::Tile rk, rv;
+    rk.load(K, min(TT, G.len));
+    rv.load(V, min(TT, G.len));
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        stage_tile<T, C::D, TT, C::NT>(xk, C::LDX, C::FAVOR ? nullptr : kt, C::LDT, K + (size_t)t0 * C::D, nv, nullptr);
-        stage_tile<T, C::D, TT, C::NT>(nullptr, 0, vt, C::LDT, V + (size_t)t0 * C::D, nv, nullptr);
+        rk.store(xk, C::LDX, C::FAVOR ? nullptr : kt, C::LDT, false, C::FAVOR ? kn : nullptr);
+        rv.store(nullptr, 0, vt, C::LDT, false, nullptr);
         __syncthreads();
-        if constexpr (C::FAVOR) {
-            row_sqnorm<T, C::D, TT, C::NT>(xk, C::LDX, kn);
-            __syncthreads();
+        if (t0 + TT < G.len) {  // prefetch the next tile while this one is computed
+            const int nv1 = min(TT, G.len - t0 - TT);
+            rk.load(K + (size_t)(t0 + TT) * C::D, nv1);
+            rv.load(V + (size_t)(t0 + TT) * C::D, nv1);
         }
         f4 pk[NTB][NFB];
         feat_S<C>(pk, xk, kt, wf);
@@ -565,21 +573,24 @@ __device__ __forceinline__ void load_state_T(f4 (&rt)[C::NFB][C::NEB], float *Sl
     for (int m = threadIdx.x; m < C::M; m += C::NT) Sl[m] = slot[C::D * C::M + m];
 }
 
-template <class C>
-__device__ __forceinline__ void stage_fwd_inputs(FwdSmem<C> &sm, const typename C::T *Q, const typename C::T *K,
-                                                 const typename C::T *V, int nv, bool q_transposed)
-{
+// Q, K, V tiles of the chunk forward, held in registers between prefetch and use.
+template <class C> struct FwdRegs {
     typedef typename C::T T;
-    stage_tile<T, C::D, C::TT, C::NT>(sm.xq, C::LDX, (!C::FAVOR && q_transposed) ? sm.qt : nullptr, C::LDT, Q, nv,
-                                      nullptr);
-    stage_tile<T, C::D, C::TT, C::NT>(sm.xk, C::LDX, C::FAVOR ? nullptr : sm.kt, C::LDT, K, nv, nullptr);
-    stage_tile<T, C::D, C::TT, C::NT>(nullptr, 0, sm.vt, C::LDT, V, nv, nullptr);
-    __syncthreads();
-    if constexpr (C::FAVOR) {
-        row_sqnorm<T, C::D, C::TT, C::NT>(sm.xk, C::LDX, sm.kn);
-        __syncthreads();
+    typename C::Tile q, k, v;
+    __device__ __forceinline__ void load(const T *Q, const T *K, const T *V, int t0, int len)
+    {
+        const int nv = min(C::TT, len - t0);
+        q.load(Q + (size_t)t0 * C::D, nv);
+        k.load(K + (size_t)t0 * C::D, nv);
+        v.load(V + (size_t)t0 * C::D, nv);
     }
-}
+    __device__ __forceinline__ void store(FwdSmem<C> &sm, bool q_transposed) const
+    {
+        q.store(sm.xq, C::LDX, (!C::FAVOR && q_transposed) ? sm.qt : nullptr, C::LDT, false, nullptr);
+        k.store(sm.xk, C::LDX, C::FAVOR ? nullptr : sm.kt, C::LDT, false, C::FAVOR ? sm.kn : nullptr);
+        v.store(nullptr, 0, sm.vt, C::LDT, false, nullptr);
+    }
+};
 
 // fwd_kernel: Y of one chunk from its entry state slot[n].
 template <class C> __global__ __launch_bounds__(C::NT) void fwd_kernel(ChunkArgs a)
@@ -594,9 +605,13 @@ template <class C> __global__ __launch_bounds__(C::NT) void fwd_kernel(ChunkArgs
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
     f4 rt[NFB][NEB];
     load_state_T<C>(rt, sm.Sl, slot_ptr<C>(a.slots, a, G.bh, G.nl));
+    FwdRegs<C> rg;
+    rg.load(Q, K, V, 0, G.len);
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        stage_fwd_inputs<C>(sm, Q + (size_t)t0 * C::D, K + (size_t)t0 * C::D, V + (size_t)t0 * C::D, nv, false);
+        rg.store(sm, false);
+        __syncthreads();
+        if (t0 + TT < G.len) rg.load(Q, K, V, t0 + TT, G.len);
         f4 pq[NFB][NTB], pk[NTB][NFB];
         fwd_tile<C>(sm, wf, rt, nv, pq, pk);
         reduce_rows<C>(sm.red, nv, [&](int t, int e, f4 s, bool ok) {

@@ -45,10 +45,19 @@ template <class C> __global__ __launch_bounds__(C::NT) void stats_kernel(ChunkAr
 #pragma unroll
         for (int eb = 0; eb < NEB; ++eb) dg[fb][eb] = f4zero();
     }
+    FwdRegs<C> rg;
+    typename C::Tile rdy;
+    rg.load(Q, K, V, 0, G.len);
+    rdy.load(dY, min(TT, G.len));
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        stage_tile<T, D, TT, C::NT>(xdy, C::LDX, nullptr, 0, dY + (size_t)t0 * D, nv, nullptr);
-        stage_fwd_inputs<C>(sm, Q + (size_t)t0 * D, K + (size_t)t0 * D, V + (size_t)t0 * D, nv, true);
+        rg.store(sm, true);
+        rdy.store(xdy, C::LDX, nullptr, 0, false, nullptr);
+        __syncthreads();
+        if (t0 + TT < G.len) {
+            rg.load(Q, K, V, t0 + TT, G.len);
+            rdy.load(dY + (size_t)(t0 + TT) * D, min(TT, G.len - t0 - TT));
+        }
         f4 pq[NFB][NTB], pk[NTB][NFB];
         fwd_tile<C>(sm, wf, rt, nv, pq, pk);
         reduce_rows<C>(sm.red, nv, [&](int t, int e, f4 s, bool ok) {
@@ -104,16 +113,6 @@ template <class C> __global__ __launch_bounds__(C::NT) void stats_kernel(ChunkAr
     }
 }
 
-// Per-row statistics of a tile: inv[t] = 1/den, dd[t] = dden (0 beyond nv).
-__device__ __forceinline__ void load_row_stats(const float *st, int t0, int nv, int TT, float *inv, float *dd)
-{
-    for (int t = threadIdx.x; t < TT; t += blockDim.x) {
-        const bool ok = t < nv;
-        inv[t] = ok ? st[(size_t)(t0 + t) * 2] : 0.f;
-        dd[t] = ok ? st[(size_t)(t0 + t) * 2 + 1] : 0.f;
-    }
-}
-
 // bwdq_kernel: dQ of one chunk.  Tiles in forward order, carrying the entry
 // state R (blocks with rows e, cols m) and S from slot[n].
 template <class C> __global__ __launch_bounds__(C::NT) void bwdq_kernel(ChunkArgs a)
@@ -149,16 +148,26 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdq_kernel(ChunkArg
             for (int j = 0; j < 4; ++j) r[eb][fb][j] = slot[(size_t)(eb * 16 + 4 * g + j) * M + w * MW + fb * 16 + lc];
     for (int m = threadIdx.x; m < M; m += C::NT) Sl[m] = slot[D * M + m];
 
+    typename C::Tile rq, rk, rv, rdy;
+    RowStatRegs<TT> rs;
+    auto prefetch = [&](int t) {
+        const int n = min(TT, G.len - t);
+        rq.load(Q + (size_t)t * D, n);
+        rk.load(K + (size_t)t * D, n);
+        rv.load(V + (size_t)t * D, n);
+        rdy.load(dY + (size_t)t * D, n, st + (size_t)t * 2);
+        rs.load(st + (size_t)t * 2, n);
+    };
+    prefetch(0);
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        load_row_stats(st, t0, nv, TT, invl, ddl);
+        rq.store(xq, C::LDX, nullptr, 0, false, nullptr);
+        rk.store(xk, C::LDX, C::FAVOR ? nullptr : kt, C::LDT, false, C::FAVOR ? kn : nullptr);
+        rv.store(xv, C::LDX, vt, C::LDT, false, nullptr);
+        rdy.store(dn, C::LDX, nullptr, 0, true, nullptr);
+        rs.store(invl, ddl);
         __syncthreads();
-        stage_tile<T, D, TT, C::NT>(xq, C::LDX, nullptr, 0, Q + (size_t)t0 * D, nv, nullptr);
-        stage_tile<T, D, TT, C::NT>(xk, C::LDX, C::FAVOR ? nullptr : kt, C::LDT, K + (size_t)t0 * D, nv, nullptr);
-        stage_tile<T, D, TT, C::NT>(xv, C::LDX, vt, C::LDT, V + (size_t)t0 * D, nv, nullptr);
-        stage_tile<T, D, TT, C::NT>(dn, C::LDX, nullptr, 0, dY + (size_t)t0 * D, nv, invl);
-        __syncthreads();
-        if constexpr (C::FAVOR) row_sqnorm<T, D, TT, C::NT>(xk, C::LDX, kn);
+        if (t0 + TT < G.len) prefetch(t0 + TT);
         f4 pq[NFB][NTB], pk[NTB][NFB];
         feat_T<C>(pq, xq, wf);
         if constexpr (C::FAVOR) q_partial_max<C>(pq, qmax);
@@ -285,73 +294,124 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdkv_kernel(ChunkAr
     for (int m = threadIdx.x; m < M; m += C::NT) dSl[m] = gsl[D * M + m];
 
     const int last = ((G.len - 1) / TT) * TT;
+    typename C::Tile rq, rk, rv, rdy;
+    RowStatRegs<TT> rs;
+    auto prefetch = [&](int t) {
+        const int n = min(TT, G.len - t);
+        rq.load(Q + (size_t)t * D, n);
+        rk.load(K + (size_t)t * D, n);
+        rv.load(V + (size_t)t * D, n);
+        rdy.load(dY + (size_t)t * D, n, st + (size_t)t * 2);
+        rs.load(st + (size_t)t * 2, n);
+    };
+    prefetch(last);
     for (int t0 = last; t0 >= 0; t0 -= TT) {
         const int nv = min(TT, G.len - t0);
-        load_row_stats(st, t0, nv, TT, invl, ddl);
+        rq.store(xq, C::LDX, C::FAVOR ? nullptr : qt, C::LDT, false, nullptr);
+        rk.store(xk, C::LDX, nullptr, 0, false, C::FAVOR ? kn : nullptr);
+        rv.store(xv, C::LDX, nullptr, 0, false, nullptr);
+        rdy.store(dn, C::LDX, dnt, C::LDT, true, nullptr);
+        rs.store(invl, ddl);
         __syncthreads();
-        stage_tile<T, D, TT, C::NT>(xq, C::LDX, C::FAVOR ? nullptr : qt, C::LDT, Q + (size_t)t0 * D, nv, nullptr);
-        stage_tile<T, D, TT, C::NT>(xk, C::LDX, nullptr, 0, K + (size_t)t0 * D, nv, nullptr);
-        stage_tile<T, D, TT, C::NT>(xv, C::LDX, nullptr, 0, V + (size_t)t0 * D, nv, nullptr);
-        stage_tile<T, D, TT, C::NT>(dn, C::LDX, dnt, C::LDT, dY + (size_t)t0 * D, nv, invl);
-        __syncthreads();
-        if constexpr (C::FAVOR) row_sqnorm<T, D, TT, C::NT>(xk, C::LDX, kn);
-        f4 pq[NFB][NTB], pqS[NTB][NFB], pkT[NFB][NTB];
-        feat_T<C>(pq, xq, wf);
-        if constexpr (C::FAVOR) q_partial_max<C>(pq, qmax);
-        __syncthreads();
-        q_finish_T<C>(pq, qmax);
-        feat_S<C>(pqS, xq, qt, wf);
-        q_finish_S<C>(pqS, qmax);
-        feat_T<C>(pkT, xk, wf);
-        k_finish_T<C>(pkT, kn, nv);
-        // P and A blocks (rows t, cols s), s <= t
-        f4 p[NTB][NTB], ap[NTB][NTB];
+        if (t0 > 0) prefetch(t0 - TT);
+        // Features, kept as MFMA operand fragments (the fp32 blocks die at once).
+        Frag<T> fq[NFB][NTB], fqS[NTB][NFB], fkT[NFB][NTB];
+        {
+            f4 pq[NFB][NTB];
+            feat_T<C>(pq, xq, wf);
+            if constexpr (C::FAVOR) q_partial_max<C>(pq, qmax);
+            __syncthreads();
+            q_finish_T<C>(pq, qmax);
+            to_frags<C>(fq, pq);
+        }
+        {
+            f4 pqS[NTB][NFB];
+            feat_S<C>(pqS, xq, qt, wf);
+            q_finish_S<C>(pqS, qmax);
+            to_frags<C>(fqS, pqS);
+        }
+        {
+            f4 pkT[NFB][NTB];
+            feat_T<C>(pkT, xk, wf);
+            k_finish_T<C>(pkT, kn, nv);
+            to_frags<C>(fkT, pkT);
+        }
+        // dV^T blocks (rows e, cols s): dNum^T P + dR g(K)^T, reduced across waves.
+        // P[t][s] = g(Q_t).g(K_s) over this wave's features, s <= t.
+        {
+            Frag<T> fp[NTB][NTB];
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb)
+            for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-            for (int sb = 0; sb <= tb; ++sb) {
-                f4 acc = f4zero(), acc2 = f4zero();
-                mma_range<T>(acc, 0, NFB, [&](int fb) { return cfrag<T>(pq[fb][tb]); },
-                             [&](int fb) { return cfrag<T>(pkT[fb][sb]); });
-                mma_range<T>(acc2, 0, NEB, [&](int kb) { return lds_frag<T>(dn, C::LDX, tb * 16, kb * 16); },
-                             [&](int kb) { return lds_frag<T>(xv, C::LDX, sb * 16, kb * 16); });
+                for (int sb = 0; sb <= tb; ++sb) {
+                    f4 acc = f4zero();
+                    mma_range<T>(acc, 0, NFB, [&](int fb) { return fq[fb][tb]; }, [&](int fb) { return fkT[fb][sb]; });
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool keep = !(sb == tb && lc > 4 * g + j);
-                    acc[j] = keep ? acc[j] : 0.f;
-                    acc2[j] = keep ? acc2[j] + ddl[tb * 16 + 4 * g + j] : 0.f;
+                    for (int j = 0; j < 4; ++j)
+                        if (sb == tb && lc > 4 * g + j) acc[j] = 0.f;
+                    fp[tb][sb] = cfrag<T>(acc);
                 }
-                p[tb][sb] = acc;
-                ap[tb][sb] = acc2;
-            }
-        // dg(K)^T blocks (rows m, cols s)
+#pragma unroll
+            for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+                for (int sb = 0; sb < NTB; ++sb) {
+                    f4 acc = f4zero();
+                    mma_range<T>(acc, sb, NTB, [&](int tb) { return lds_frag<T>(dnt, C::LDT, eb * 16, tb * 16); },
+                                 [&](int tb) { return fp[tb][sb]; });
+                    mma_range<T>(acc, 0, NFB, [&](int fb) { return cfrag<T>(drt[fb][eb]); },
+                                 [&](int fb) { return fkT[fb][sb]; });
+                    *reinterpret_cast<f4 *>(red + (w * TT + sb * 16 + lc) * C::LDR + eb * 16 + 4 * g) = acc;
+                }
+        }
+        __syncthreads();
+        reduce_rows<C>(red, nv, [&](int s, int e, f4 v, bool ok) {
+            if (ok) store4<T>(dV + (size_t)(t0 + s) * D + e, v);
+        });
+        __syncthreads();
+        // dg(K)^T blocks (rows m, cols s): A^T g(Q) + dR^T V + dS, with
+        // A[t][s] = dNum_t . V_s + dden_t for s <= t (the full sum over d, every wave).
         f4 dk[NFB][NTB];
+        {
+            Frag<T> fa[NTB][NTB];
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb)
+            for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-            for (int sb = 0; sb < NTB; ++sb) {
-                f4 acc = f4zero();
-                mma_range<T>(acc, sb, NTB, [&](int tb) { return cfrag<T>(pqS[tb][fb]); },
-                             [&](int tb) { return cfrag<T>(ap[tb][sb]); });
-                mma_range<T>(acc, 0, NEB, [&](int eb) { return cfrag<T>(dr[eb][fb]); },
-                             [&](int eb) { return lds_frag<T>(xv, C::LDX, sb * 16, eb * 16); });
+                for (int sb = 0; sb <= tb; ++sb) {
+                    f4 acc = f4zero();
+                    mma_range<T>(acc, 0, NEB, [&](int kb) { return lds_frag<T>(dn, C::LDX, tb * 16, kb * 16); },
+                                 [&](int kb) { return lds_frag<T>(xv, C::LDX, sb * 16, kb * 16); });
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] += dSl[w * MW + fb * 16 + 4 * g + j];
-                dk[fb][sb] = acc;
-            }
+                    for (int j = 0; j < 4; ++j)
+                        acc[j] = (sb == tb && lc > 4 * g + j) ? 0.f : acc[j] + ddl[tb * 16 + 4 * g + j];
+                    fa[tb][sb] = cfrag<T>(acc);
+                }
+#pragma unroll
+            for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+                for (int sb = 0; sb < NTB; ++sb) {
+                    f4 acc = f4zero();
+                    mma_range<T>(acc, sb, NTB, [&](int tb) { return fqS[tb][fb]; }, [&](int tb) { return fa[tb][sb]; });
+                    mma_range<T>(acc, 0, NEB, [&](int eb) { return cfrag<T>(dr[eb][fb]); },
+                                 [&](int eb) { return lds_frag<T>(xv, C::LDX, sb * 16, eb * 16); });
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] += dSl[w * MW + fb * 16 + 4 * g + j];
+                    dk[fb][sb] = acc;
+                }
+        }
         if constexpr (C::FAVOR) {
+            // dK = (dg(K) . g(K)) W - K * rowsum(dg(K) . g(K)), reduced across waves
             Frag<T> gk[NFB][NTB];
 #pragma unroll
             for (int sb = 0; sb < NTB; ++sb) {
-                float rs = 0.f;
+                float rsum = 0.f;
 #pragma unroll
                 for (int fb = 0; fb < NFB; ++fb) {
-                    const f4 gg = dk[fb][sb] * pkT[fb][sb];
-                    rs += gg[0] + gg[1] + gg[2] + gg[3];
+                    const f4 gg = dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]);
+                    rsum += gg[0] + gg[1] + gg[2] + gg[3];
                     gk[fb][sb] = cfrag<T>(gg);
                 }
-                rs = sum_groups(rs);
-                if (g == 0) redk[w * TT + sb * 16 + lc] = rs;
+                rsum = sum_groups(rsum);
+                if (g == 0) redk[w * TT + sb * 16 + lc] = rsum;
             }
 #pragma unroll
             for (int eb = 0; eb < NEB; ++eb)
@@ -364,13 +424,12 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdkv_kernel(ChunkAr
             __syncthreads();
             reduce_rows<C>(red, nv, [&](int s, int e, f4 v, bool ok) {
                 if (!ok) return;
-                float rs = redk[s];
+                float rsum = redk[s];
 #pragma unroll
-                for (int ww = 1; ww < C::NW; ++ww) rs += redk[ww * TT + s];
+                for (int ww = 1; ww < C::NW; ++ww) rsum += redk[ww * TT + s];
                 const f4 kk = load4<T>(xk + s * C::LDX + e);
-                store4<T>(dK + (size_t)(t0 + s) * D + e, v - kk * rs);
+                store4<T>(dK + (size_t)(t0 + s) * D + e, v - kk * rsum);
             });
-            __syncthreads();
         } else {
 #pragma unroll
             for (int fb = 0; fb < NFB; ++fb)
@@ -384,25 +443,7 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdkv_kernel(ChunkAr
                     if (s < nv) store4<T>(dK + (size_t)(t0 + s) * D + w * MW + fb * 16 + 4 * g, v);
                 }
         }
-        // dV^T blocks (rows e, cols s): dNum^T P + dR g(K)^T, reduced across waves
-#pragma unroll
-        for (int eb = 0; eb < NEB; ++eb)
-#pragma unroll
-            for (int sb = 0; sb < NTB; ++sb) {
-                f4 acc = f4zero();
-                mma_range<T>(acc, sb, NTB, [&](int tb) { return lds_frag<T>(dnt, C::LDT, eb * 16, tb * 16); },
-                             [&](int tb) { return cfrag<T>(p[tb][sb]); });
-                mma_range<T>(acc, 0, NFB, [&](int fb) { return cfrag<T>(drt[fb][eb]); },
-                             [&](int fb) { return cfrag<T>(pkT[fb][sb]); });
-                *reinterpret_cast<f4 *>(red + (w * TT + sb * 16 + lc) * C::LDR + eb * 16 + 4 * g) = acc;
-            }
-        __syncthreads();
-        reduce_rows<C>(red, nv, [&](int s, int e, f4 v, bool ok) {
-            if (ok) store4<T>(dV + (size_t)(t0 + s) * D + e, v);
-        });
         // gradient state: dR += dNum^T g(Q), dS += sum dden g(Q) (after use)
-        Frag<T> fqS[NTB][NFB];
-        to_frags<C>(fqS, pqS);
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb) {
 #pragma unroll
@@ -414,9 +455,11 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdkv_kernel(ChunkAr
             }
             float s = 0.f;
 #pragma unroll
-            for (int tb = 0; tb < NTB; ++tb)
+            for (int tb = 0; tb < NTB; ++tb) {
+                const f4 q4 = frag_to_f4<T>(fqS[tb][fb]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) s += pqS[tb][fb][j] * ddl[tb * 16 + 4 * g + j];
+                for (int j = 0; j < 4; ++j) s += q4[j] * ddl[tb * 16 + 4 * g + j];
+            }
             s = sum_groups(s);
             if (g == 0) dSl[w * MW + fb * 16 + lc] += s;
         }
