@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace slim {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -152,6 +154,96 @@ __device__ __forceinline__ void store16(__bf16 *p, bf8 x)
     reinterpret_cast<bf4 *>(p)[1] = bf4{x[4], x[5], x[6], x[7]};
 }
 
+// Row-major matrix in LDS, ROWS x COLS of the operand type T (COLS a multiple of 16).
+// Operand fragments can contract over either index:
+//   frag_c(n0, k0): free index = row n0 + i%16, contraction = columns k0 + 4g..+3;
+//   frag_r(n0, k0): free index = column n0 + i%16, contraction = rows k0 + 4g..+3.
+// bf16: rows are packed and the 8-byte chunk q of row r is stored at chunk
+// q ^ swz(r), swz(r) = ((r&3)<<2 | (r>>2)&3) mod (COLS/4), which keeps both read
+// patterns free of bank conflicts; frag_r is one ds_read_b64_tr_b16 (within each
+// 16-lane group, lane i receives element i%4 of the chunks addressed by lanes
+// i/4, 4+i/4, 8+i/4, 12+i/4, so lane L points at row k0+4g+L/4, column
+// n0+4(L%4)).  fp32: rows padded by 4 elements, frag_r is four 4-byte reads.
+template <typename T, int ROWS, int COLS> struct LMat {
+    static constexpr bool BF = sizeof(T) == 2;
+    static constexpr int LD = BF ? COLS : COLS + 4;
+    static constexpr int NCH = COLS / 4;
+    static constexpr int SIZE = ROWS * LD;
+    static_assert(COLS % 16 == 0 && (NCH & (NCH - 1)) == 0, "columns: power-of-two multiple of 16");
+    T *p;
+    __device__ __forceinline__ explicit LMat(T *base) : p(base) {}
+    __device__ static __forceinline__ int off(int r, int c)  // c % 4 == 0
+    {
+        if constexpr (BF) {
+            const int f = (((r & 3) << 2) | ((r >> 2) & 3)) & (NCH - 1);
+            return r * COLS + ((((c >> 2) ^ f)) << 2);
+        } else {
+            return r * LD + c;
+        }
+    }
+    // four consecutive columns c..c+3 of row r
+    __device__ __forceinline__ void put4(int r, int c, f4 v) const
+    {
+        if constexpr (BF)
+            *reinterpret_cast<bf4 *>(p + off(r, c)) = bf4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        else
+            *reinterpret_cast<f4 *>(p + off(r, c)) = v;
+    }
+    __device__ __forceinline__ void put_frag(int r, int c, Frag<T> v) const
+    {
+        *reinterpret_cast<Frag<T> *>(p + off(r, c)) = v;
+    }
+    // one 16-byte vector of the I/O type at columns c..c+EPV-1 (c % EPV == 0)
+    __device__ __forceinline__ void put16(int r, int c, typename Vec16<T>::type x) const
+    {
+        if constexpr (BF) {
+            *reinterpret_cast<bf4 *>(p + off(r, c)) = bf4{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<bf4 *>(p + off(r, c + 4)) = bf4{x[4], x[5], x[6], x[7]};
+        } else {
+            *reinterpret_cast<f4 *>(p + off(r, c)) = x;
+        }
+    }
+    __device__ __forceinline__ f4 get4(int r, int c) const
+    {
+        if constexpr (BF) {
+            const bf4 v = *reinterpret_cast<const bf4 *>(p + off(r, c));
+            return f4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+        } else {
+            return *reinterpret_cast<const f4 *>(p + off(r, c));
+        }
+    }
+    __device__ __forceinline__ Frag<T> frag_c(int n0, int k0) const
+    {
+        return *reinterpret_cast<const Frag<T> *>(p + off(n0 + lcol(), k0 + 4 * lgrp()));
+    }
+    __device__ __forceinline__ Frag<T> frag_r(int n0, int k0) const
+    {
+        if constexpr (BF) {
+            const int L = lcol();
+            const T *a = p + off(k0 + 4 * lgrp() + (L >> 2), n0 + 4 * (L & 3));
+            typedef __attribute__((address_space(3))) bf4 lds_bf4;
+            Frag<T> f;
+            f.v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf4 *)(a));
+            return f;
+        } else {
+            Frag<T> f;
+            const int r = k0 + 4 * lgrp(), c = n0 + lcol();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f.v[j] = p[(r + j) * LD + c];
+            return f;
+        }
+    }
+};
+
+// Orders this wave's LDS writes before its later LDS reads of the same
+// locations (per-wave scratch in LDS, no other wave involved).
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // A [TT][D] tile of a row-major tensor held in registers: thread i owns the
 // 16-byte vectors i, i+NT, ... (row t = idx / VPR, columns c..c+EPV-1).  load()
 // issues the global reads (rows >= nvalid read as zero) and returns at once, so a
@@ -178,10 +270,11 @@ template <typename T, int D, int TT, int NT> struct TileRegs {
             if (stats) s[i] = ok ? stats[(size_t)t * 2] : 0.f;
         }
     }
-    // Write to dst[TT][ldx] (if non-null) and the transposed dstT[D][ldt] (if
-    // non-null); scaled: multiply row t by its stats scale first; sq (if non-null)
-    // receives |row t|^2 (summed over the VPR lanes of the row with shuffles).
-    __device__ __forceinline__ void store(T *dst, int ldx, T *dstT, int ldt, bool scaled, float *sq) const
+    // Move the tile into an LDS matrix (rows t, columns e); scaled: multiply row t
+    // by its stats scale first; rowfn (if not null) is called by one lane per
+    // row as rowfn(t, |row t|^2) (summed over the VPR lanes of the row).
+    template <class MAT, class RF>
+    __device__ __forceinline__ void store(const MAT &dst, bool scaled, RF rowfn) const
     {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -192,20 +285,26 @@ template <typename T, int D, int TT, int NT> struct TileRegs {
 #pragma unroll
                 for (int j = 0; j < EPV; ++j) x[j] = (T)((float)x[j] * s[i]);
             }
-            if (idx < NV) {
-                if (dst) store16(dst + t * ldx + c, x);
-                if (dstT) {
-#pragma unroll
-                    for (int j = 0; j < EPV; ++j) dstT[(c + j) * ldt + t] = x[j];
-                }
-            }
-            if (sq) {
+            if (idx < NV) dst.put16(t, c, x);
+            if constexpr (!std::is_same<RF, std::nullptr_t>::value) {
                 float q = 0.f;
 #pragma unroll
                 for (int j = 0; j < EPV; ++j) q += (float)x[j] * (float)x[j];
 #pragma unroll
                 for (int o = 1; o < VPR; o <<= 1) q += __shfl_xor(q, o, 64);
-                if (idx < NV && c == 0) sq[t] = q;
+                if (idx < NV && c == 0) rowfn(t, q);
+            }
+        }
+    }
+    // rows t >= nvalid of the tile hold `fill` instead of zero after load()
+    __device__ __forceinline__ void fill_invalid(int nvalid, float fill)
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            if (idx / VPR >= nvalid) {
+#pragma unroll
+                for (int j = 0; j < EPV; ++j) v[i][j] = (T)fill;
             }
         }
     }

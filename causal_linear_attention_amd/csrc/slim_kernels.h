@@ -19,6 +19,15 @@
 // gradients) in MFMA accumulator layout, and reduces the feature-contracted
 // outputs (numerators, dQ, dK, dV) across waves through LDS.
 //
+// Augmented value index.  V, the state R, dNum and dR carry one extra 16-wide
+// block of the value index e whose first column is 1 (V), S (R), dden (dNum) or
+// dS (dR), the rest zero.  With it the MFMAs produce, as that extra column, the
+// denominators (sum_s P[t][s] + g(Q_t).S), S += sum g(K), the dden.S and dS terms
+// of the gradients and the rank-one part of A = dNum V^T + dden 1^T.
+//
+// Every LDS tile is stored row-major only; fragments that contract over its rows
+// use gfx950's transposing LDS read (LMat::frag_r).
+//
 // Kernels (all launched on a grid (chunks in window, B*H)):
 //   featmap_kernel : standalone g(X), optional per-row max offset.
 //   state_kernel   : dR_n = sum_{rows of chunk n} V g(K)^T, dS_n = sum g(K).
@@ -47,25 +56,53 @@ struct ChunkArgs {
     int P;   // window capacity (slot stride)
 };
 
+constexpr float LOG2E = 1.4426950408889634f;
+
 template <typename T_, int D_, int M_, int FEAT_, int TT_, int MW_ = 32> struct KCfg {
     typedef T_ T;
     static constexpr int D = D_, M = M_, FEAT = FEAT_, TT = TT_;
     static constexpr int MW = M >= MW_ ? MW_ : M;  // features per wave
-    static constexpr int NW = M / MW;            // waves per workgroup
+    static constexpr int NW = M / MW;              // waves per workgroup
     static constexpr int NT = NW * 64;
     static constexpr int NFB = MW / 16;
     static constexpr int NEB = D / 16;
+    static constexpr int NEA = NEB + 1;  // value blocks including the auxiliary one
     static constexpr int NTB = TT / 16;
-    // LDS row strides: 4 elements of padding make the rows of a 16-row operand
-    // read land in distinct banks (stride = 8 bytes mod 128 for bf16, 16 for fp32).
-    static constexpr int LDX = D + 4;   // [TT][D] tiles
-    static constexpr int LDT = TT + 4;  // [D][TT] transposed tiles
-    static constexpr int LDR = D + 4;   // fp32 reduction rows
+    static constexpr int LDR = D + 4;  // fp32 reduction rows; column D = denominator / row sum
     static constexpr int SZ = (D + 1) * M;
     static constexpr bool FAVOR = FEAT == FEAT_FAVOR;
     typedef TileRegs<T, D, TT, NT> Tile;
+    typedef LMat<T, TT, D> XMat;     // [TT][D] input tile
+    typedef LMat<T, TT, 16> AuxMat;  // auxiliary value block of a tile (column 0 used)
+    typedef LMat<T, TT, MW> FMat;    // one wave's features of a tile: rows t, columns m
     static_assert(FEAT == FEAT_FAVOR || D == M, "elu+1 needs M == d");
     static_assert(MW % 16 == 0 && D % 16 == 0 && TT % 16 == 0, "block sizes");
+};
+
+// A value-indexed tile (V or dNum) with its auxiliary block.
+template <class C> struct AugTile {
+    typedef typename C::T T;
+    typename C::XMat x;
+    typename C::AuxMat a;
+    __device__ __forceinline__ AugTile(T *main, T *aux) : x(main), a(aux) {}
+    // free index row n0 + i%16, contraction over value block eb
+    __device__ __forceinline__ Frag<T> fc(int n0, int eb) const
+    {
+        return eb < C::NEB ? x.frag_c(n0, eb * 16) : a.frag_c(n0, 0);
+    }
+    // free index value block eb, contraction over rows k0 + 4g..
+    __device__ __forceinline__ Frag<T> fr(int eb, int k0) const
+    {
+        return eb < C::NEB ? x.frag_r(eb * 16, k0) : a.frag_r(0, k0);
+    }
+    // row t of the auxiliary block: (v, 0, ..., 0); one lane per row.
+    __device__ __forceinline__ void set_aux(int t, float v) const
+    {
+        a.put4(t, 0, f4{v, 0.f, 0.f, 0.f});
+        a.put4(t, 4, f4zero());
+        a.put4(t, 8, f4zero());
+        a.put4(t, 12, f4zero());
+    }
 };
 
 // ------------------------------------------------------------------ g(X) ---
@@ -87,21 +124,24 @@ __device__ __forceinline__ void load_wfrag(Frag<typename C::T> (&wf)[C::NFB][C::
 }
 
 // W^T fragments: wt[eb][fb] holds W[m][e] for m = w*MW + fb*16 + 4g + j, e = eb*16 + i%16
-// (free index e, contraction over this wave's features).
-template <class C>
-__device__ __forceinline__ void load_wtfrag(Frag<typename C::T> (&wt)[C::NEB][C::NFB], const void *Wv)
+// (free index e, contraction over this wave's features).  Block eb = NEB (if
+// present) is the auxiliary column of ones (e = D), which turns the product into
+// the row sum over m.
+template <class C, int NE>
+__device__ __forceinline__ void load_wtfrag(Frag<typename C::T> (&wt)[NE][C::NFB], const void *Wv)
 {
     typedef typename C::T T;
     const T *W = (const T *)Wv;
     const int w = wave_id();
 #pragma unroll
-    for (int eb = 0; eb < C::NEB; ++eb)
+    for (int eb = 0; eb < NE; ++eb)
 #pragma unroll
         for (int fb = 0; fb < C::NFB; ++fb) {
             Frag<T> f;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                f.v[j] = W[(size_t)(w * C::MW + fb * 16 + 4 * lgrp() + j) * C::D + eb * 16 + lcol()];
+                f.v[j] = eb < C::NEB ? W[(size_t)(w * C::MW + fb * 16 + 4 * lgrp() + j) * C::D + eb * 16 + lcol()]
+                                     : (T)(lcol() == 0 ? 1.f : 0.f);
             wt[eb][fb] = f;
         }
 }
@@ -109,7 +149,7 @@ __device__ __forceinline__ void load_wtfrag(Frag<typename C::T> (&wt)[C::NEB][C:
 // Feature blocks in "transposed" orientation: ph[fb][tb] has rows m = w*MW + fb*16 + 4g + j
 // and columns t = tb*16 + i%16.  FAVOR+: the raw projection w_m . x_t.  elu+1: g itself.
 template <class C>
-__device__ __forceinline__ void feat_T(f4 (&ph)[C::NFB][C::NTB], const typename C::T *xs,
+__device__ __forceinline__ void feat_T(f4 (&ph)[C::NFB][C::NTB], const typename C::XMat &xs,
                                        const Frag<typename C::T> (&wf)[C::NFB][C::NEB])
 {
     typedef typename C::T T;
@@ -120,19 +160,19 @@ __device__ __forceinline__ void feat_T(f4 (&ph)[C::NFB][C::NTB], const typename 
             if constexpr (C::FAVOR) {
                 f4 acc = f4zero();
                 mma_range<T>(acc, 0, C::NEB, [&](int kb) { return wf[fb][kb]; },
-                             [&](int kb) { return lds_frag<T>(xs, C::LDX, tb * 16, kb * 16); });
+                             [&](int kb) { return xs.frag_c(tb * 16, kb * 16); });
                 ph[fb][tb] = acc;
             } else {
-                f4 x = frag_to_f4<T>(lds_frag<T>(xs, C::LDX, tb * 16, wave_id() * C::MW + fb * 16));
+                f4 x = frag_to_f4<T>(xs.frag_c(tb * 16, wave_id() * C::MW + fb * 16));
                 ph[fb][tb] = f4{elu1(x[0]), elu1(x[1]), elu1(x[2]), elu1(x[3])};
             }
         }
 }
 
 // Feature blocks in "token" orientation: ph[tb][fb] has rows t = tb*16 + 4g + j and
-// columns m = w*MW + fb*16 + i%16.  elu+1 reads the transposed tile xt[D][TT].
+// columns m = w*MW + fb*16 + i%16 (elu+1 reads the tile transposed).
 template <class C>
-__device__ __forceinline__ void feat_S(f4 (&ph)[C::NTB][C::NFB], const typename C::T *xs, const typename C::T *xt,
+__device__ __forceinline__ void feat_S(f4 (&ph)[C::NTB][C::NFB], const typename C::XMat &xs,
                                        const Frag<typename C::T> (&wf)[C::NFB][C::NEB])
 {
     typedef typename C::T T;
@@ -142,11 +182,11 @@ __device__ __forceinline__ void feat_S(f4 (&ph)[C::NTB][C::NFB], const typename 
         for (int fb = 0; fb < C::NFB; ++fb) {
             if constexpr (C::FAVOR) {
                 f4 acc = f4zero();
-                mma_range<T>(acc, 0, C::NEB, [&](int kb) { return lds_frag<T>(xs, C::LDX, tb * 16, kb * 16); },
+                mma_range<T>(acc, 0, C::NEB, [&](int kb) { return xs.frag_c(tb * 16, kb * 16); },
                              [&](int kb) { return wf[fb][kb]; });
                 ph[tb][fb] = acc;
             } else {
-                f4 x = frag_to_f4<T>(lds_frag<T>(xt, C::LDT, wave_id() * C::MW + fb * 16, tb * 16));
+                f4 x = frag_to_f4<T>(xs.frag_r(wave_id() * C::MW + fb * 16, tb * 16));
                 ph[tb][fb] = f4{elu1(x[0]), elu1(x[1]), elu1(x[2]), elu1(x[3])};
             }
         }
@@ -166,13 +206,6 @@ template <class C> __device__ __forceinline__ void q_partial_max(const f4 (&ph)[
         if (lgrp() == 0) qmax[wave_id() * C::TT + tb * 16 + lcol()] = m;
     }
 }
-template <class C> __device__ __forceinline__ float q_offset(const float *qmax, int t)
-{
-    float m = qmax[t];
-#pragma unroll
-    for (int w = 1; w < C::NW; ++w) m = fmaxf(m, qmax[w * C::TT + t]);
-    return m;
-}
 
 // g(Q) up to a per-row positive factor: exp(w_m.q_t - max_m' w_m'.q_t).  The factor
 // cancels in Y and in dQ (Y is homogeneous of degree 0 in each g(Q_l)).
@@ -181,60 +214,68 @@ template <class C> __device__ __forceinline__ void q_finish_T(f4 (&ph)[C::NFB][C
     if constexpr (C::FAVOR) {
 #pragma unroll
         for (int tb = 0; tb < C::NTB; ++tb) {
-            const float off = q_offset<C>(qmax, tb * 16 + lcol());
+            const int t = tb * 16 + lcol();
+            float m = qmax[t];
+#pragma unroll
+            for (int w = 1; w < C::NW; ++w) m = fmaxf(m, qmax[w * C::TT + t]);
+            const float off = -m * LOG2E;
 #pragma unroll
             for (int fb = 0; fb < C::NFB; ++fb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) ph[fb][tb][j] = fast_exp(ph[fb][tb][j] - off);
+                for (int j = 0; j < 4; ++j) ph[fb][tb][j] = __builtin_amdgcn_exp2f(fmaf(ph[fb][tb][j], LOG2E, off));
         }
     }
 }
-template <class C> __device__ __forceinline__ void q_finish_S(f4 (&ph)[C::NTB][C::NFB], const float *qmax)
+
+// g(K) exactly: exp(w_m.k_t - |k_t|^2/2) / sqrt(M) = 2^(log2e w_m.k_t - kn2[t]) with
+// kn2[t] = log2e (|k_t|^2/2 + ln(M)/2), +inf for rows beyond the chunk (g = 0 there).
+// elu+1 rows beyond the chunk were staged as -inf, so g = 0 there too.
+template <class C> __device__ __forceinline__ void k_finish_T(f4 (&ph)[C::NFB][C::NTB], const float *kn2)
+{
+    if constexpr (C::FAVOR) {
+#pragma unroll
+        for (int tb = 0; tb < C::NTB; ++tb) {
+            const float off = -kn2[tb * 16 + lcol()];
+#pragma unroll
+            for (int fb = 0; fb < C::NFB; ++fb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ph[fb][tb][j] = __builtin_amdgcn_exp2f(fmaf(ph[fb][tb][j], LOG2E, off));
+        }
+    }
+}
+template <class C> __device__ __forceinline__ void k_finish_S(f4 (&ph)[C::NTB][C::NFB], const float *kn2)
 {
     if constexpr (C::FAVOR) {
 #pragma unroll
         for (int tb = 0; tb < C::NTB; ++tb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float off = q_offset<C>(qmax, tb * 16 + 4 * lgrp() + j);
+                const float off = -kn2[tb * 16 + 4 * lgrp() + j];
 #pragma unroll
-                for (int fb = 0; fb < C::NFB; ++fb) ph[tb][fb][j] = fast_exp(ph[tb][fb][j] - off);
+                for (int fb = 0; fb < C::NFB; ++fb)
+                    ph[tb][fb][j] = __builtin_amdgcn_exp2f(fmaf(ph[tb][fb][j], LOG2E, off));
             }
     }
 }
 
-// g(K) exactly: exp(w_m.k_t - |k_t|^2/2) / sqrt(M) (FAVOR+), zero for rows t >= nv.
-template <class C>
-__device__ __forceinline__ void k_finish_T(f4 (&ph)[C::NFB][C::NTB], const float *kn, int nv)
-{
-    const float lns = 0.5f * __logf((float)C::M);
-#pragma unroll
-    for (int tb = 0; tb < C::NTB; ++tb) {
-        const int t = tb * 16 + lcol();
-        const bool ok = t < nv;
-        const float off = C::FAVOR ? 0.5f * kn[t] + lns : 0.f;
-#pragma unroll
-        for (int fb = 0; fb < C::NFB; ++fb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                ph[fb][tb][j] = !ok ? 0.f : (C::FAVOR ? fast_exp(ph[fb][tb][j] - off) : ph[fb][tb][j]);
+// Row function for staging K: kn2[t] as above.
+template <class C> struct KnormFn {
+    float *kn2;
+    int nv;
+    __device__ __forceinline__ void operator()(int t, float q) const
+    {
+        kn2[t] = t < nv ? (0.5f * q + 0.5f * __logf((float)C::M)) * LOG2E : __builtin_inff();
     }
-}
+};
+
+// Write this wave's feature blocks ph[fb][tb] (rows m, cols t) into F (rows t, cols m).
 template <class C>
-__device__ __forceinline__ void k_finish_S(f4 (&ph)[C::NTB][C::NFB], const float *kn, int nv)
+__device__ __forceinline__ void put_features(const typename C::FMat &F, const f4 (&ph)[C::NFB][C::NTB])
 {
-    const float lns = 0.5f * __logf((float)C::M);
 #pragma unroll
-    for (int tb = 0; tb < C::NTB; ++tb)
+    for (int fb = 0; fb < C::NFB; ++fb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = tb * 16 + 4 * lgrp() + j;
-            const bool ok = t < nv;
-            const float off = C::FAVOR ? 0.5f * kn[t] + lns : 0.f;
-#pragma unroll
-            for (int fb = 0; fb < C::NFB; ++fb)
-                ph[tb][fb][j] = !ok ? 0.f : (C::FAVOR ? fast_exp(ph[tb][fb][j] - off) : ph[tb][fb][j]);
-        }
+        for (int tb = 0; tb < C::NTB; ++tb) F.put4(tb * 16 + lcol(), fb * 16 + 4 * lgrp(), ph[fb][tb]);
 }
 
 template <class C, int A, int B>
@@ -246,8 +287,8 @@ __device__ __forceinline__ void to_frags(Frag<typename C::T> (&f)[A][B], const f
         for (int b = 0; b < B; ++b) f[a][b] = cfrag<typename C::T>(c[a][b]);
 }
 
-// Sum the NW per-wave fp32 partials red[w][t][e] for tile rows, divide by den (if
-// given) and hand (t, e..e+3, value) to `emit` for every valid row.
+// Sum the NW per-wave fp32 partials red[w][t][e] for tile rows and hand
+// (t, e..e+3, value, row valid) to `emit`.
 template <class C, typename F>
 __device__ __forceinline__ void reduce_rows(const float *red, int nv, F emit)
 {
@@ -260,6 +301,24 @@ __device__ __forceinline__ void reduce_rows(const float *red, int nv, F emit)
         emit(t, e, s, t < nv);
     }
 }
+// Sum over waves of column D of the reduction rows (denominator / row sum) of row t.
+template <class C> __device__ __forceinline__ float reduce_col(const float *red, int t)
+{
+    float s = red[t * C::LDR + C::D];
+#pragma unroll
+    for (int w = 1; w < C::NW; ++w) s += red[(w * C::TT + t) * C::LDR + C::D];
+    return s;
+}
+// Write a value-indexed block acc (rows e = eb*16 + 4g + j, cols t = tb*16 + i%16) of
+// this wave's partial to red; the auxiliary block contributes only column D.
+template <class C> __device__ __forceinline__ void put_red(float *red, int eb, int tb, f4 acc)
+{
+    const int row = (wave_id() * C::TT + tb * 16 + lcol()) * C::LDR;
+    if (eb < C::NEB)
+        *reinterpret_cast<f4 *>(red + row + eb * 16 + 4 * lgrp()) = acc;
+    else if (lgrp() == 0)
+        red[row + C::D] = acc[0];
+}
 
 template <typename T> __device__ __forceinline__ void store4(T *p, f4 v);
 template <> __device__ __forceinline__ void store4<float>(float *p, f4 v) { *reinterpret_cast<f4 *>(p) = v; }
@@ -267,13 +326,6 @@ template <> __device__ __forceinline__ void store4<__bf16>(__bf16 *p, f4 v)
 {
     bf4 r = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
     *reinterpret_cast<bf4 *>(p) = r;
-}
-template <typename T> __device__ __forceinline__ f4 load4(const T *p);
-template <> __device__ __forceinline__ f4 load4<float>(const float *p) { return *reinterpret_cast<const f4 *>(p); }
-template <> __device__ __forceinline__ f4 load4<__bf16>(const __bf16 *p)
-{
-    bf4 r = *reinterpret_cast<const bf4 *>(p);
-    return f4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
 }
 
 // ----------------------------------------------------------- featmap ---
@@ -285,9 +337,10 @@ __global__ __launch_bounds__(C::NT) void featmap_kernel(const void *Xv, const vo
                                                         long long rows)
 {
     typedef typename C::T T;
-    __shared__ __align__(16) T xs[C::TT * C::LDX];
+    __shared__ __align__(16) T xs_[C::XMat::SIZE];
     __shared__ float kn[C::TT];
     __shared__ float qmax[C::NW * C::TT];
+    const typename C::XMat xs(xs_);
     const long long r0 = (long long)blockIdx.x * C::TT;
     const int nv = (int)min((long long)C::TT, rows - r0);
     const T *X = (const T *)Xv + r0 * C::D;
@@ -296,7 +349,10 @@ __global__ __launch_bounds__(C::NT) void featmap_kernel(const void *Xv, const vo
     {
         typename C::Tile rx;
         rx.load(X, nv);
-        rx.store(xs, C::LDX, nullptr, 0, false, C::FAVOR ? kn : nullptr);
+        if constexpr (C::FAVOR)
+            rx.store(xs, false, [&](int t, float q) { kn[t] = q; });
+        else
+            rx.store(xs, false, nullptr);
     }
     __syncthreads();
     f4 ph[C::NFB][C::NTB];
@@ -314,12 +370,18 @@ __global__ __launch_bounds__(C::NT) void featmap_kernel(const void *Xv, const vo
 #pragma unroll
         for (int tb = 0; tb < C::NTB; ++tb) {
             const int t = tb * 16 + lcol();
-            const float off = row_off ? q_offset<C>(qmax, t) : 0.f;
-            if (row_off && wave_id() == 0 && lgrp() == 0 && t < nv) row_off[r0 + t] = off;
+            float off = 0.f;
+            if (row_off) {
+                off = qmax[t];
+#pragma unroll
+                for (int w = 1; w < C::NW; ++w) off = fmaxf(off, qmax[w * C::TT + t]);
+                if (wave_id() == 0 && lgrp() == 0 && t < nv) row_off[r0 + t] = off;
+            }
+            const float o2 = -(off + lns) * LOG2E;
 #pragma unroll
             for (int fb = 0; fb < C::NFB; ++fb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) ph[fb][tb][j] = fast_exp(ph[fb][tb][j] - off - lns);
+                for (int j = 0; j < 4; ++j) ph[fb][tb][j] = __builtin_amdgcn_exp2f(fmaf(ph[fb][tb][j], LOG2E, o2));
         }
     }
 #pragma unroll
@@ -340,7 +402,7 @@ struct ChunkGeom {
     int bh;          // head
     long long row0;  // first row of the chunk
     int len;         // rows in the chunk
-    size_t hb;       // element offset of the head in a [B,H,L,D] tensor
+    size_t hb;       // element offset of the chunk's first row in a [B,H,L,D] tensor
 };
 template <class C> __device__ __forceinline__ ChunkGeom chunk_geom(const ChunkArgs &a)
 {
@@ -357,67 +419,100 @@ template <class C> __device__ __forceinline__ float *slot_ptr(float *base, const
     return base + ((size_t)bh * (a.P + 1) + s) * C::SZ;
 }
 
+// Stage a K tile: rows past the chunk give g = 0 (kn2 = +inf for FAVOR+, -inf
+// inputs for elu+1).
+template <class C>
+__device__ __forceinline__ void store_k_tile(typename C::Tile &rk, const typename C::XMat &xk, float *kn2, int nv)
+{
+    if constexpr (C::FAVOR) {
+        rk.store(xk, false, KnormFn<C>{kn2, nv});
+    } else {
+        rk.fill_invalid(nv, -__builtin_inff());
+        rk.store(xk, false, nullptr);
+    }
+}
+// Stage a V tile and its auxiliary column of ones (zero past the chunk).
+template <class C>
+__device__ __forceinline__ void store_v_tile(const typename C::Tile &rv, const AugTile<C> &V, int nv)
+{
+    rv.store(V.x, false, nullptr);
+    if (threadIdx.x < C::TT) V.set_aux(threadIdx.x, threadIdx.x < nv ? 1.f : 0.f);
+}
+
+// State block of a wave (rows m, cols e) from a slot stored [e][m] (row D = S);
+// the auxiliary block holds S in column D.
+template <class C> __device__ __forceinline__ void load_state_T(f4 (&rt)[C::NFB][C::NEA], const float *slot)
+{
+    const int w = wave_id();
+#pragma unroll
+    for (int fb = 0; fb < C::NFB; ++fb) {
+        const int m = w * C::MW + fb * 16 + 4 * lgrp();
+#pragma unroll
+        for (int eb = 0; eb < C::NEB; ++eb)
+            rt[fb][eb] = *reinterpret_cast<const f4 *>(slot + (size_t)(eb * 16 + lcol()) * C::M + m);
+        rt[fb][C::NEB] = lcol() == 0 ? *reinterpret_cast<const f4 *>(slot + (size_t)C::D * C::M + m) : f4zero();
+    }
+}
+template <class C> __device__ __forceinline__ void store_state_T(float *slot, const f4 (&rt)[C::NFB][C::NEA])
+{
+    const int w = wave_id();
+#pragma unroll
+    for (int fb = 0; fb < C::NFB; ++fb) {
+        const int m = w * C::MW + fb * 16 + 4 * lgrp();
+#pragma unroll
+        for (int eb = 0; eb < C::NEB; ++eb)
+            *reinterpret_cast<f4 *>(slot + (size_t)(eb * 16 + lcol()) * C::M + m) = rt[fb][eb];
+        if (lcol() == 0) *reinterpret_cast<f4 *>(slot + (size_t)C::D * C::M + m) = rt[fb][C::NEB];
+    }
+}
+
 // state_kernel: slot[n+1] = (dR_n, dS_n) of chunk n (R part stored [e][m]).
 template <class C> __global__ __launch_bounds__(C::NT) void state_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
-    constexpr int NFB = C::NFB, NEB = C::NEB, NTB = C::NTB, TT = C::TT;
-    __shared__ __align__(16) T xk[TT * C::LDX];
-    __shared__ __align__(16) T kt[C::FAVOR ? 8 : C::D * C::LDT];
-    __shared__ __align__(16) T vt[C::D * C::LDT];
-    __shared__ float kn[TT];
+    constexpr int NFB = C::NFB, NEA = C::NEA, NTB = C::NTB, TT = C::TT;
+    __shared__ __align__(16) T xk_[C::XMat::SIZE];
+    __shared__ __align__(16) T xv_[C::XMat::SIZE];
+    __shared__ __align__(16) T xva_[C::AuxMat::SIZE];
+    __shared__ float kn2[TT];
+    const typename C::XMat xk(xk_);
+    const AugTile<C> V(xv_, xva_);
     const ChunkGeom G = chunk_geom<C>(a);
-    const int w = wave_id(), g = lgrp(), lc = lcol();
-    const T *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
-    Frag<T> wf[NFB][NEB];
+    const T *Kp = (const T *)a.K + G.hb, *Vp = (const T *)a.V + G.hb;
+    Frag<T> wf[NFB][C::NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
-    f4 rt[NFB][NEB];
-    float sacc[NFB];
+    f4 rt[NFB][NEA];
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) {
-        sacc[fb] = 0.f;
+    for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-        for (int eb = 0; eb < NEB; ++eb) rt[fb][eb] = f4zero();
-    }
+        for (int eb = 0; eb < NEA; ++eb) rt[fb][eb] = f4zero();
     typename C::Tile rk, rv;
-    rk.load(K, min(TT, G.len));
-    rv.load(V, min(TT, G.len));
+    rk.load(Kp, min(TT, G.len));
+    rv.load(Vp, min(TT, G.len));
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        rk.store(xk, C::LDX, C::FAVOR ? nullptr : kt, C::LDT, false, C::FAVOR ? kn : nullptr);
-        rv.store(nullptr, 0, vt, C::LDT, false, nullptr);
+        store_k_tile<C>(rk, xk, kn2, nv);
+        store_v_tile<C>(rv, V, nv);
         __syncthreads();
         if (t0 + TT < G.len) {  // prefetch the next tile while this one is computed
             const int nv1 = min(TT, G.len - t0 - TT);
-            rk.load(K + (size_t)(t0 + TT) * C::D, nv1);
-            rv.load(V + (size_t)(t0 + TT) * C::D, nv1);
+            rk.load(Kp + (size_t)(t0 + TT) * C::D, nv1);
+            rv.load(Vp + (size_t)(t0 + TT) * C::D, nv1);
         }
         f4 pk[NTB][NFB];
-        feat_S<C>(pk, xk, kt, wf);
-        k_finish_S<C>(pk, kn, nv);
+        feat_S<C>(pk, xk, wf);
+        k_finish_S<C>(pk, kn2);
         Frag<T> fk[NTB][NFB];
         to_frags<C>(fk, pk);
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb) {
+        for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-            for (int eb = 0; eb < NEB; ++eb)
+            for (int eb = 0; eb < NEA; ++eb)
                 mma_range<T>(rt[fb][eb], 0, NTB, [&](int tb) { return fk[tb][fb]; },
-                             [&](int tb) { return lds_frag<T>(vt, C::LDT, eb * 16, tb * 16); });
-            float s = 0.f;
-#pragma unroll
-            for (int tb = 0; tb < NTB; ++tb) s += pk[tb][fb][0] + pk[tb][fb][1] + pk[tb][fb][2] + pk[tb][fb][3];
-            sacc[fb] += sum_groups(s);
-        }
+                             [&](int tb) { return V.fr(eb, tb * 16); });
         __syncthreads();
     }
-    float *out = slot_ptr<C>(a.slots, a, G.bh, G.nl + 1);
-#pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) {
-#pragma unroll
-        for (int eb = 0; eb < NEB; ++eb)
-            *reinterpret_cast<f4 *>(out + (size_t)(eb * 16 + lc) * C::M + w * C::MW + fb * 16 + 4 * g) = rt[fb][eb];
-        if (g == 0) out[C::D * C::M + w * C::MW + fb * 16 + lc] = sacc[fb];
-    }
+    store_state_T<C>(slot_ptr<C>(a.slots, a, G.bh, G.nl + 1), rt);
 }
 
 // scan_kernel: sweep the window's chunk slots of one head.  Each thread owns 4
@@ -459,119 +554,18 @@ __global__ __launch_bounds__(256) void scan_kernel(float *slots, float *carryR, 
     *reinterpret_cast<f4 *>(cp) = cur;
 }
 
-// Shared LDS layout of the chunk kernels that evaluate a chunk's forward.
+// LDS of the chunk kernels that evaluate a chunk's forward.
 template <class C> struct FwdSmem {
     typedef typename C::T T;
-    __align__(16) T xq[C::TT * C::LDX];
-    __align__(16) T xk[C::TT * C::LDX];
-    __align__(16) T vt[C::D * C::LDT];
-    __align__(16) T kt[C::FAVOR ? 8 : C::D * C::LDT];
-    __align__(16) T qt[C::FAVOR ? 8 : C::D * C::LDT];
+    __align__(16) T xq[C::XMat::SIZE];
+    __align__(16) T xk[C::XMat::SIZE];
+    __align__(16) T xv[C::XMat::SIZE];
+    __align__(16) T xva[C::AuxMat::SIZE];
+    __align__(16) T fk[C::NW * C::FMat::SIZE];
     __align__(16) float red[C::NW * C::TT * C::LDR];
-    float redd[C::NW * C::TT];
     float qmax[C::NW * C::TT];
-    float kn[C::TT];
-    float Sl[C::M];
+    float kn2[C::TT];
 };
-
-// One tile of the chunk forward shared by fwd_kernel and stats_kernel:
-// computes this wave's partial numerator^T / denominator into red/redd (then
-// syncs), leaves g(Q) (transposed blocks), g(K) (token blocks) in the outputs.
-template <class C>
-__device__ __forceinline__ void fwd_tile(FwdSmem<C> &sm, const Frag<typename C::T> (&wf)[C::NFB][C::NEB],
-                                         const f4 (&rt)[C::NFB][C::NEB], int nv, f4 (&pq)[C::NFB][C::NTB],
-                                         f4 (&pk)[C::NTB][C::NFB])
-{
-    typedef typename C::T T;
-    constexpr int NFB = C::NFB, NEB = C::NEB, NTB = C::NTB, TT = C::TT;
-    const int w = wave_id(), g = lgrp(), lc = lcol();
-    f4 pkT[NFB][NTB];
-    feat_T<C>(pq, sm.xq, wf);
-    feat_T<C>(pkT, sm.xk, wf);
-    feat_S<C>(pk, sm.xk, sm.kt, wf);
-    if constexpr (C::FAVOR) q_partial_max<C>(pq, sm.qmax);
-    __syncthreads();
-    q_finish_T<C>(pq, sm.qmax);
-    k_finish_T<C>(pkT, sm.kn, nv);
-    k_finish_S<C>(pk, sm.kn, nv);
-    Frag<T> fq[NFB][NTB], fkT[NFB][NTB];
-    to_frags<C>(fq, pq);
-    to_frags<C>(fkT, pkT);
-    // P^T blocks (rows s, cols t), s-block <= t-block, over this wave's features.
-    f4 pt[NTB][NTB];
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-        for (int sb = 0; sb <= tb; ++sb) {
-            f4 acc = f4zero();
-            mma_range<T>(acc, 0, NFB, [&](int kb) { return fkT[kb][sb]; }, [&](int kb) { return fq[kb][tb]; });
-            if (sb == tb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (4 * g + j > lc) acc[j] = 0.f;
-            pt[sb][tb] = acc;
-        }
-    // partial denominators (per column t): sum_s P^T[s][t] + g(Q_t) . S (own features)
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) {
-        float v = 0.f;
-#pragma unroll
-        for (int sb = 0; sb <= tb; ++sb) v += pt[sb][tb][0] + pt[sb][tb][1] + pt[sb][tb][2] + pt[sb][tb][3];
-#pragma unroll
-        for (int fb = 0; fb < NFB; ++fb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v += pq[fb][tb][j] * sm.Sl[w * C::MW + fb * 16 + 4 * g + j];
-        v = sum_groups(v);
-        if (g == 0) sm.redd[w * TT + tb * 16 + lc] = v;
-    }
-    // partial numerators^T (rows e, cols t): V^T P^T + R g(Q)^T
-#pragma unroll
-    for (int eb = 0; eb < NEB; ++eb)
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            f4 acc = f4zero();
-            mma_range<T>(acc, 0, tb + 1, [&](int sb) { return lds_frag<T>(sm.vt, C::LDT, eb * 16, sb * 16); },
-                         [&](int sb) { return cfrag<T>(pt[sb][tb]); });
-            mma_range<T>(acc, 0, NFB, [&](int fb) { return cfrag<T>(rt[fb][eb]); }, [&](int fb) { return fq[fb][tb]; });
-            *reinterpret_cast<f4 *>(sm.red + (w * TT + tb * 16 + lc) * C::LDR + eb * 16 + 4 * g) = acc;
-        }
-    __syncthreads();
-}
-
-// State update after a tile: R^T += g(K)^T V, S += sum g(K) (own features).
-template <class C>
-__device__ __forceinline__ void state_update_T(FwdSmem<C> &sm, f4 (&rt)[C::NFB][C::NEB], const f4 (&pk)[C::NTB][C::NFB])
-{
-    typedef typename C::T T;
-    constexpr int NFB = C::NFB, NEB = C::NEB, NTB = C::NTB;
-    Frag<T> fk[NTB][NFB];
-    to_frags<C>(fk, pk);
-#pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) {
-#pragma unroll
-        for (int eb = 0; eb < NEB; ++eb)
-            mma_range<T>(rt[fb][eb], 0, NTB, [&](int tb) { return fk[tb][fb]; },
-                         [&](int tb) { return lds_frag<T>(sm.vt, C::LDT, eb * 16, tb * 16); });
-        float s = 0.f;
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) s += pk[tb][fb][0] + pk[tb][fb][1] + pk[tb][fb][2] + pk[tb][fb][3];
-        s = sum_groups(s);
-        if (lgrp() == 0) sm.Sl[wave_id() * C::MW + fb * 16 + lcol()] += s;
-    }
-}
-
-template <class C>
-__device__ __forceinline__ void load_state_T(f4 (&rt)[C::NFB][C::NEB], float *Sl, const float *slot)
-{
-    const int w = wave_id();
-#pragma unroll
-    for (int fb = 0; fb < C::NFB; ++fb)
-#pragma unroll
-        for (int eb = 0; eb < C::NEB; ++eb)
-            rt[fb][eb] = *reinterpret_cast<const f4 *>(slot + (size_t)(eb * 16 + lcol()) * C::M + w * C::MW + fb * 16 +
-                                                        4 * lgrp());
-    for (int m = threadIdx.x; m < C::M; m += C::NT) Sl[m] = slot[C::D * C::M + m];
-}
 
 // Q, K, V tiles of the chunk forward, held in registers between prefetch and use.
 template <class C> struct FwdRegs {
@@ -584,44 +578,106 @@ template <class C> struct FwdRegs {
         k.load(K + (size_t)t0 * C::D, nv);
         v.load(V + (size_t)t0 * C::D, nv);
     }
-    __device__ __forceinline__ void store(FwdSmem<C> &sm, bool q_transposed) const
+    __device__ __forceinline__ void store(FwdSmem<C> &sm, int nv)
     {
-        q.store(sm.xq, C::LDX, (!C::FAVOR && q_transposed) ? sm.qt : nullptr, C::LDT, false, nullptr);
-        k.store(sm.xk, C::LDX, C::FAVOR ? nullptr : sm.kt, C::LDT, false, C::FAVOR ? sm.kn : nullptr);
-        v.store(nullptr, 0, sm.vt, C::LDT, false, nullptr);
+        q.store(typename C::XMat(sm.xq), false, nullptr);
+        store_k_tile<C>(k, typename C::XMat(sm.xk), sm.kn2, nv);
+        store_v_tile<C>(v, AugTile<C>(sm.xv, sm.xva), nv);
     }
 };
+
+// One tile of the chunk forward, shared by fwd_kernel and stats_kernel: writes
+// this wave's partial numerator^T (and denominator, column D) into red and
+// syncs; leaves g(Q) of this wave's features (rows m, cols t) in pq and g(K) in
+// the wave's feature buffer (rows t, cols m).
+template <class C>
+__device__ __forceinline__ void fwd_tile(FwdSmem<C> &sm, const Frag<typename C::T> (&wf)[C::NFB][C::NEB],
+                                         const f4 (&rt)[C::NFB][C::NEA], f4 (&pq)[C::NFB][C::NTB])
+{
+    typedef typename C::T T;
+    constexpr int NFB = C::NFB, NEA = C::NEA, NTB = C::NTB;
+    const int g = lgrp(), lc = lcol();
+    const typename C::XMat xq(sm.xq), xk(sm.xk);
+    const AugTile<C> V(sm.xv, sm.xva);
+    const typename C::FMat Fk(sm.fk + wave_id() * C::FMat::SIZE);
+    f4 pkT[NFB][NTB];
+    feat_T<C>(pq, xq, wf);
+    feat_T<C>(pkT, xk, wf);
+    if constexpr (C::FAVOR) q_partial_max<C>(pq, sm.qmax);
+    __syncthreads();
+    q_finish_T<C>(pq, sm.qmax);
+    k_finish_T<C>(pkT, sm.kn2);
+    put_features<C>(Fk, pkT);
+    Frag<T> fq[NFB][NTB], fkT[NFB][NTB];
+    to_frags<C>(fq, pq);
+    to_frags<C>(fkT, pkT);
+    // P^T blocks (rows s, cols t), s-block <= t-block, over this wave's features.
+    Frag<T> pt[NTB][NTB];
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+        for (int sb = 0; sb <= tb; ++sb) {
+            f4 acc = f4zero();
+            mma_range<T>(acc, 0, NFB, [&](int kb) { return fkT[kb][sb]; }, [&](int kb) { return fq[kb][tb]; });
+            if (sb == tb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (4 * g + j > lc) acc[j] = 0.f;
+            pt[sb][tb] = cfrag<T>(acc);
+        }
+    // partial numerators^T (rows e, cols t; e = D is the denominator): V^T P^T + R g(Q)^T
+#pragma unroll
+    for (int eb = 0; eb < NEA; ++eb)
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            f4 acc = f4zero();
+            mma_range<T>(acc, 0, tb + 1, [&](int sb) { return V.fr(eb, sb * 16); }, [&](int sb) { return pt[sb][tb]; });
+            mma_range<T>(acc, 0, NFB, [&](int fb) { return cfrag<T>(rt[fb][eb]); }, [&](int fb) { return fq[fb][tb]; });
+            put_red<C>(sm.red, eb, tb, acc);
+        }
+    __syncthreads();
+}
+
+// State update after a tile: [R^T | S] += g(K)^T [V | 1] over this wave's features.
+template <class C> __device__ __forceinline__ void state_update_T(FwdSmem<C> &sm, f4 (&rt)[C::NFB][C::NEA])
+{
+    typedef typename C::T T;
+    const AugTile<C> V(sm.xv, sm.xva);
+    const typename C::FMat Fk(sm.fk + wave_id() * C::FMat::SIZE);
+#pragma unroll
+    for (int fb = 0; fb < C::NFB; ++fb)
+#pragma unroll
+        for (int eb = 0; eb < C::NEA; ++eb)
+            mma_range<T>(rt[fb][eb], 0, C::NTB, [&](int tb) { return Fk.frag_r(fb * 16, tb * 16); },
+                         [&](int tb) { return V.fr(eb, tb * 16); });
+}
 
 // fwd_kernel: Y of one chunk from its entry state slot[n].
 template <class C> __global__ __launch_bounds__(C::NT) void fwd_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
-    constexpr int NFB = C::NFB, NEB = C::NEB, NTB = C::NTB, TT = C::TT;
+    constexpr int NFB = C::NFB, NEA = C::NEA, NTB = C::NTB, TT = C::TT;
     __shared__ FwdSmem<C> sm;
     const ChunkGeom G = chunk_geom<C>(a);
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     T *Y = (T *)a.out0 + G.hb;
-    Frag<T> wf[NFB][NEB];
+    Frag<T> wf[NFB][C::NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
-    f4 rt[NFB][NEB];
-    load_state_T<C>(rt, sm.Sl, slot_ptr<C>(a.slots, a, G.bh, G.nl));
+    f4 rt[NFB][NEA];
+    load_state_T<C>(rt, slot_ptr<C>(a.slots, a, G.bh, G.nl));
     FwdRegs<C> rg;
     rg.load(Q, K, V, 0, G.len);
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        rg.store(sm, false);
+        rg.store(sm, nv);
         __syncthreads();
         if (t0 + TT < G.len) rg.load(Q, K, V, t0 + TT, G.len);
-        f4 pq[NFB][NTB], pk[NTB][NFB];
-        fwd_tile<C>(sm, wf, rt, nv, pq, pk);
+        f4 pq[NFB][NTB];
+        fwd_tile<C>(sm, wf, rt, pq);
         reduce_rows<C>(sm.red, nv, [&](int t, int e, f4 s, bool ok) {
-            if (!ok) return;
-            float dn = sm.redd[t];
-#pragma unroll
-            for (int w = 1; w < C::NW; ++w) dn += sm.redd[w * TT + t];
-            store4<T>(Y + (size_t)(t0 + t) * C::D + e, s * (1.f / dn));
+            if (ok) store4<T>(Y + (size_t)(t0 + t) * C::D + e, s * (1.f / reduce_col<C>(sm.red, t)));
         });
-        state_update_T<C>(sm, rt, pk);
+        state_update_T<C>(sm, rt);
         __syncthreads();
     }
 }

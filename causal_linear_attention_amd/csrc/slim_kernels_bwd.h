@@ -11,6 +11,8 @@
 // where R_before is the state entering the tile, dR_after the gradient w.r.t. the
 // state leaving it.  The state gradient is the backwards prefix sum of
 // dNum_t g(Q_t)^T (and dden_t g(Q_t) for S), as Subsection 3.3 notes for PS.
+// With the augmented value index (dNum's extra column = dden, V's = 1, R's = S,
+// dR's = dS) every dden and dS term above is part of an MFMA.
 // FAVOR+ chain: dq = sum_m dg_m g_m (w_m - q) (the -q sum vanishes for queries
 // because Y_t is invariant under rescaling g(Q_t)); elu+1: dx = dg * g'(x).
 #pragma once
@@ -24,57 +26,52 @@ namespace slim {
 template <class C> __global__ __launch_bounds__(C::NT) void stats_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
-    constexpr int NFB = C::NFB, NEB = C::NEB, NTB = C::NTB, TT = C::TT, D = C::D;
+    constexpr int NFB = C::NFB, NEA = C::NEA, NTB = C::NTB, TT = C::TT, D = C::D;
     __shared__ FwdSmem<C> sm;
-    __shared__ __align__(16) T xdy[TT * C::LDX];
-    __shared__ __align__(16) T dnt[D * C::LDT];
-    __shared__ float ddl[TT];
+    __shared__ __align__(16) T dn_[C::XMat::SIZE];
+    __shared__ __align__(16) T dna_[C::AuxMat::SIZE];
+    __shared__ __align__(16) T fq_[C::NW * C::FMat::SIZE];
+    const AugTile<C> DN(dn_, dna_);  // holds dY until the row statistics turn it into dNum
+    const typename C::FMat Fq(fq_ + wave_id() * C::FMat::SIZE);
     const ChunkGeom G = chunk_geom<C>(a);
-    const int w = wave_id(), g = lgrp(), lc = lcol();
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     const T *dY = (const T *)a.dY + G.hb;
     float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * 2;
-    Frag<T> wf[NFB][NEB];
+    Frag<T> wf[NFB][C::NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
-    f4 rt[NFB][NEB], dg[NFB][NEB];
-    float gs[NFB];
-    load_state_T<C>(rt, sm.Sl, slot_ptr<C>(a.slots, a, G.bh, G.nl));
+    f4 rt[NFB][NEA], dg[NFB][NEA];
+    load_state_T<C>(rt, slot_ptr<C>(a.slots, a, G.bh, G.nl));
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) {
-        gs[fb] = 0.f;
+    for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-        for (int eb = 0; eb < NEB; ++eb) dg[fb][eb] = f4zero();
-    }
+        for (int eb = 0; eb < NEA; ++eb) dg[fb][eb] = f4zero();
     FwdRegs<C> rg;
     typename C::Tile rdy;
     rg.load(Q, K, V, 0, G.len);
     rdy.load(dY, min(TT, G.len));
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        rg.store(sm, true);
-        rdy.store(xdy, C::LDX, nullptr, 0, false, nullptr);
+        rg.store(sm, nv);
+        rdy.store(DN.x, false, nullptr);
         __syncthreads();
         if (t0 + TT < G.len) {
             rg.load(Q, K, V, t0 + TT, G.len);
             rdy.load(dY + (size_t)(t0 + TT) * D, min(TT, G.len - t0 - TT));
         }
-        f4 pq[NFB][NTB], pk[NTB][NFB];
-        fwd_tile<C>(sm, wf, rt, nv, pq, pk);
+        f4 pq[NFB][NTB];
+        fwd_tile<C>(sm, wf, rt, pq);
+        put_features<C>(Fq, pq);
         reduce_rows<C>(sm.red, nv, [&](int t, int e, f4 s, bool ok) {
-            float dn = sm.redd[t];
-#pragma unroll
-            for (int ww = 1; ww < C::NW; ++ww) dn += sm.redd[ww * TT + t];
-            const float inv = ok ? 1.f / dn : 0.f;
+            const float inv = ok ? 1.f / reduce_col<C>(sm.red, t) : 0.f;
             const f4 y = s * inv;
-            const f4 dy = load4<T>(xdy + t * C::LDX + e);
+            const f4 dy = DN.x.get4(t, e);
             float p = dy[0] * y[0] + dy[1] * y[1] + dy[2] * y[2] + dy[3] * y[3];
 #pragma unroll
             for (int o = 1; o < D / 4; o <<= 1) p += __shfl_xor(p, o, 64);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dnt[(e + j) * C::LDT + t] = (T)(dy[j] * inv);
+            DN.x.put4(t, e, dy * inv);
             if (e == 0) {
                 const float dd = ok ? -p * inv : 0.f;
-                ddl[t] = dd;
+                DN.set_aux(t, dd);
                 if (ok) {
                     st[(size_t)(t0 + t) * 2] = inv;
                     st[(size_t)(t0 + t) * 2 + 1] = dd;
@@ -82,51 +79,79 @@ template <class C> __global__ __launch_bounds__(C::NT) void stats_kernel(ChunkAr
             }
         });
         __syncthreads();
-        f4 pqS[NTB][NFB];
-        feat_S<C>(pqS, sm.xq, sm.qt, wf);
-        q_finish_S<C>(pqS, sm.qmax);
-        Frag<T> fqS[NTB][NFB];
-        to_frags<C>(fqS, pqS);
+        // [dG | dGs] += g(Q)^T [dNum | dden] over this wave's features
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb) {
+        for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-            for (int eb = 0; eb < NEB; ++eb)
-                mma_range<T>(dg[fb][eb], 0, NTB, [&](int tb) { return fqS[tb][fb]; },
-                             [&](int tb) { return lds_frag<T>(dnt, C::LDT, eb * 16, tb * 16); });
-            float s = 0.f;
-#pragma unroll
-            for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s += pqS[tb][fb][j] * ddl[tb * 16 + 4 * g + j];
-            gs[fb] += sum_groups(s);
-        }
-        state_update_T<C>(sm, rt, pk);
+            for (int eb = 0; eb < NEA; ++eb)
+                mma_range<T>(dg[fb][eb], 0, NTB, [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); },
+                             [&](int tb) { return DN.fr(eb, tb * 16); });
+        state_update_T<C>(sm, rt);
         __syncthreads();
     }
-    float *out = slot_ptr<C>(a.gslots, a, G.bh, G.nl + 1);
+    store_state_T<C>(slot_ptr<C>(a.gslots, a, G.bh, G.nl + 1), dg);
+}
+
+// State block with rows = value index e (incl. the auxiliary block, whose first
+// row is the S / dS vector) and cols = this wave's features, from a slot.
+template <class C> __device__ __forceinline__ void load_state_E(f4 (&r)[C::NEA][C::NFB], const float *slot)
+{
+    const int w = wave_id();
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) {
+    for (int fb = 0; fb < C::NFB; ++fb) {
+        const int m = w * C::MW + fb * 16 + lcol();
 #pragma unroll
-        for (int eb = 0; eb < NEB; ++eb)
-            *reinterpret_cast<f4 *>(out + (size_t)(eb * 16 + lc) * C::M + w * C::MW + fb * 16 + 4 * g) = dg[fb][eb];
-        if (g == 0) out[D * C::M + w * C::MW + fb * 16 + lc] = gs[fb];
+        for (int eb = 0; eb < C::NEB; ++eb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r[eb][fb][j] = slot[(size_t)(eb * 16 + 4 * lgrp() + j) * C::M + m];
+        r[C::NEB][fb] = f4{lgrp() == 0 ? slot[(size_t)C::D * C::M + m] : 0.f, 0.f, 0.f, 0.f};
     }
 }
 
+// Staging of the backward tiles: Q, K, V (+ ones), dNum = dY / den (+ dden).
+template <class C> struct BwdRegs {
+    typedef typename C::T T;
+    typename C::Tile q, k, v, dy;
+    RowStatRegs<C::TT> rs;
+    __device__ __forceinline__ void load(const T *Q, const T *K, const T *V, const T *dY, const float *st, int t0,
+                                         int len)
+    {
+        const int n = min(C::TT, len - t0);
+        q.load(Q + (size_t)t0 * C::D, n);
+        k.load(K + (size_t)t0 * C::D, n);
+        v.load(V + (size_t)t0 * C::D, n);
+        dy.load(dY + (size_t)t0 * C::D, n, st + (size_t)t0 * 2);
+        rs.load(st + (size_t)t0 * 2, n);
+    }
+    __device__ __forceinline__ void store(const typename C::XMat &xq, const typename C::XMat &xk,
+                                          const AugTile<C> &Vt, const AugTile<C> &DN, float *kn2, int nv)
+    {
+        q.store(xq, false, nullptr);
+        store_k_tile<C>(k, xk, kn2, nv);
+        store_v_tile<C>(v, Vt, nv);
+        dy.store(DN.x, true, nullptr);
+        if (threadIdx.x < C::TT) DN.set_aux(threadIdx.x, rs.dd);
+    }
+};
+
 // bwdq_kernel: dQ of one chunk.  Tiles in forward order, carrying the entry
-// state R (blocks with rows e, cols m) and S from slot[n].
+// state [R; S] (rows e, cols m) from slot[n].
 template <class C> __global__ __launch_bounds__(C::NT) void bwdq_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
-    constexpr int NFB = C::NFB, NEB = C::NEB, NTB = C::NTB, TT = C::TT, D = C::D, M = C::M, MW = C::MW;
-    __shared__ __align__(16) T xq[TT * C::LDX];
-    __shared__ __align__(16) T xk[TT * C::LDX];
-    __shared__ __align__(16) T kt[C::FAVOR ? 8 : D * C::LDT];
-    __shared__ __align__(16) T xv[TT * C::LDX];
-    __shared__ __align__(16) T vt[D * C::LDT];
-    __shared__ __align__(16) T dn[TT * C::LDX];
+    constexpr int NFB = C::NFB, NEB = C::NEB, NEA = C::NEA, NTB = C::NTB, TT = C::TT, D = C::D, MW = C::MW;
+    __shared__ __align__(16) T xq_[C::XMat::SIZE];
+    __shared__ __align__(16) T xk_[C::XMat::SIZE];
+    __shared__ __align__(16) T xv_[C::XMat::SIZE];
+    __shared__ __align__(16) T xva_[C::AuxMat::SIZE];
+    __shared__ __align__(16) T dn_[C::XMat::SIZE];
+    __shared__ __align__(16) T dna_[C::AuxMat::SIZE];
+    __shared__ __align__(16) T fk_[C::NW * C::FMat::SIZE];
     __shared__ __align__(16) float red[C::FAVOR ? C::NW * TT * C::LDR : 4];
-    __shared__ float invl[TT], ddl[TT], kn[TT], qmax[C::NW * TT], Sl[M];
+    __shared__ float kn2[TT], qmax[C::NW * TT];
+    const typename C::XMat xq(xq_), xk(xk_);
+    const AugTile<C> Vt(xv_, xva_), DN(dn_, dna_);
+    const typename C::FMat Fk(fk_ + wave_id() * C::FMat::SIZE);
     const ChunkGeom G = chunk_geom<C>(a);
     const int w = wave_id(), g = lgrp(), lc = lcol();
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
@@ -136,73 +161,55 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdq_kernel(ChunkArg
     Frag<T> wf[NFB][NEB], wt[NEB][NFB];
     if constexpr (C::FAVOR) {
         load_wfrag<C>(wf, a.W);
-        load_wtfrag<C>(wt, a.W);
+        load_wtfrag<C, NEB>(wt, a.W);
     }
-    const float *slot = slot_ptr<C>(a.slots, a, G.bh, G.nl);
-    f4 r[NEB][NFB];  // R: rows e, cols m
-#pragma unroll
-    for (int eb = 0; eb < NEB; ++eb)
-#pragma unroll
-        for (int fb = 0; fb < NFB; ++fb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) r[eb][fb][j] = slot[(size_t)(eb * 16 + 4 * g + j) * M + w * MW + fb * 16 + lc];
-    for (int m = threadIdx.x; m < M; m += C::NT) Sl[m] = slot[D * M + m];
-
-    typename C::Tile rq, rk, rv, rdy;
-    RowStatRegs<TT> rs;
-    auto prefetch = [&](int t) {
-        const int n = min(TT, G.len - t);
-        rq.load(Q + (size_t)t * D, n);
-        rk.load(K + (size_t)t * D, n);
-        rv.load(V + (size_t)t * D, n);
-        rdy.load(dY + (size_t)t * D, n, st + (size_t)t * 2);
-        rs.load(st + (size_t)t * 2, n);
-    };
-    prefetch(0);
+    f4 r[NEA][NFB];
+    load_state_E<C>(r, slot_ptr<C>(a.slots, a, G.bh, G.nl));
+    BwdRegs<C> rg;
+    rg.load(Q, K, V, dY, st, 0, G.len);
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        rq.store(xq, C::LDX, nullptr, 0, false, nullptr);
-        rk.store(xk, C::LDX, C::FAVOR ? nullptr : kt, C::LDT, false, C::FAVOR ? kn : nullptr);
-        rv.store(xv, C::LDX, vt, C::LDT, false, nullptr);
-        rdy.store(dn, C::LDX, nullptr, 0, true, nullptr);
-        rs.store(invl, ddl);
+        rg.store(xq, xk, Vt, DN, kn2, nv);
         __syncthreads();
-        if (t0 + TT < G.len) prefetch(t0 + TT);
-        f4 pq[NFB][NTB], pk[NTB][NFB];
+        if (t0 + TT < G.len) rg.load(Q, K, V, dY, st, t0 + TT, G.len);
+        f4 pq[NFB][NTB];
         feat_T<C>(pq, xq, wf);
         if constexpr (C::FAVOR) q_partial_max<C>(pq, qmax);
         __syncthreads();
         q_finish_T<C>(pq, qmax);
-        feat_S<C>(pk, xk, kt, wf);
-        k_finish_S<C>(pk, kn, nv);
-        // A^T blocks (rows s, cols t), s <= t
-        f4 at[NTB][NTB];
+        {
+            f4 pkT[NFB][NTB];
+            feat_T<C>(pkT, xk, wf);
+            k_finish_T<C>(pkT, kn2);
+            put_features<C>(Fk, pkT);
+        }
+        // A^T blocks (rows s, cols t), s <= t: [V | 1] [dNum | dden]^T
+        Frag<T> at[NTB][NTB];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
             for (int sb = 0; sb <= tb; ++sb) {
                 f4 acc = f4zero();
-                mma_range<T>(acc, 0, NEB, [&](int kb) { return lds_frag<T>(xv, C::LDX, sb * 16, kb * 16); },
-                             [&](int kb) { return lds_frag<T>(dn, C::LDX, tb * 16, kb * 16); });
-                const float dd = ddl[tb * 16 + lc];
+                mma_range<T>(acc, 0, NEA, [&](int eb) { return Vt.fc(sb * 16, eb); },
+                             [&](int eb) { return DN.fc(tb * 16, eb); });
+                if (sb == tb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = (sb == tb && 4 * g + j > lc) ? 0.f : acc[j] + dd;
-                at[sb][tb] = acc;
+                    for (int j = 0; j < 4; ++j)
+                        if (4 * g + j > lc) acc[j] = 0.f;
+                at[sb][tb] = cfrag<T>(acc);
             }
-        // dg(Q)^T blocks (rows m, cols t)
+        wave_lds_fence();  // Fk written by this wave above
+        // dg(Q)^T blocks (rows m, cols t) = g(K)^T A^T + [R; S]^T [dNum | dden]^T
         f4 dq[NFB][NTB];
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) {
                 f4 acc = f4zero();
-                mma_range<T>(acc, 0, tb + 1, [&](int sb) { return cfrag<T>(pk[sb][fb]); },
-                             [&](int sb) { return cfrag<T>(at[sb][tb]); });
-                mma_range<T>(acc, 0, NEB, [&](int eb) { return cfrag<T>(r[eb][fb]); },
-                             [&](int eb) { return lds_frag<T>(dn, C::LDX, tb * 16, eb * 16); });
-                const float dd = ddl[tb * 16 + lc];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] += Sl[w * MW + fb * 16 + 4 * g + j] * dd;
+                mma_range<T>(acc, 0, tb + 1, [&](int sb) { return Fk.frag_r(fb * 16, sb * 16); },
+                             [&](int sb) { return at[sb][tb]; });
+                mma_range<T>(acc, 0, NEA, [&](int eb) { return cfrag<T>(r[eb][fb]); },
+                             [&](int eb) { return DN.fc(tb * 16, eb); });
                 dq[fb][tb] = acc;
             }
         if constexpr (C::FAVOR) {
@@ -218,7 +225,7 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdq_kernel(ChunkArg
                 for (int tb = 0; tb < NTB; ++tb) {
                     f4 acc = f4zero();
                     mma_range<T>(acc, 0, NFB, [&](int fb) { return wt[eb][fb]; }, [&](int fb) { return gq[fb][tb]; });
-                    *reinterpret_cast<f4 *>(red + (w * TT + tb * 16 + lc) * C::LDR + eb * 16 + 4 * g) = acc;
+                    put_red<C>(red, eb, tb, acc);
                 }
             __syncthreads();
             reduce_rows<C>(red, nv, [&](int t, int e, f4 s, bool ok) {
@@ -230,137 +237,135 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdq_kernel(ChunkArg
 #pragma unroll
                 for (int tb = 0; tb < NTB; ++tb) {
                     const int t = tb * 16 + lc;
-                    const f4 x = frag_to_f4<T>(lds_frag<T>(xq, C::LDX, tb * 16, w * MW + fb * 16));
+                    const f4 x = frag_to_f4<T>(xq.frag_c(tb * 16, w * MW + fb * 16));
                     f4 v;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) v[j] = dq[fb][tb][j] * elu1_grad(x[j]);
                     if (t < nv) store4<T>(dQ + (size_t)(t0 + t) * D + w * MW + fb * 16 + 4 * g, v);
                 }
         }
-        // R += V^T g(K), S += sum g(K)
+        // [R; S] += [V | 1]^T g(K)
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb) {
+        for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-            for (int eb = 0; eb < NEB; ++eb)
-                mma_range<T>(r[eb][fb], 0, NTB, [&](int tb) { return lds_frag<T>(vt, C::LDT, eb * 16, tb * 16); },
-                             [&](int tb) { return cfrag<T>(pk[tb][fb]); });
-            float s = 0.f;
-#pragma unroll
-            for (int tb = 0; tb < NTB; ++tb) s += pk[tb][fb][0] + pk[tb][fb][1] + pk[tb][fb][2] + pk[tb][fb][3];
-            s = sum_groups(s);
-            if (g == 0) Sl[w * MW + fb * 16 + lc] += s;
-        }
+            for (int eb = 0; eb < NEA; ++eb)
+                mma_range<T>(r[eb][fb], 0, NTB, [&](int tb) { return Vt.fr(eb, tb * 16); },
+                             [&](int tb) { return Fk.frag_r(fb * 16, tb * 16); });
         __syncthreads();
     }
 }
 
 // bwdkv_kernel: dK and dV of one chunk.  Tiles in reverse order, carrying the
-// gradient w.r.t. the state after the tile (dR in both orientations, dS), which
-// starts from gslot[n+1].
+// gradient w.r.t. the state after the tile, [dR; dS] (rows e, cols m), which
+// starts from gslot[n+1].  The dV product also needs dR with the features as the
+// contraction index: a copy of this wave's dR block goes to LDS each tile and is
+// read back transposed (if the copies of all waves fit in 64 KB of LDS;
+// otherwise a second fp32 orientation is carried in registers).
 template <class C> __global__ __launch_bounds__(C::NT) void bwdkv_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
-    constexpr int NFB = C::NFB, NEB = C::NEB, NTB = C::NTB, TT = C::TT, D = C::D, M = C::M, MW = C::MW;
-    __shared__ __align__(16) T xq[TT * C::LDX];
-    __shared__ __align__(16) T qt[C::FAVOR ? 8 : D * C::LDT];
-    __shared__ __align__(16) T xk[TT * C::LDX];
-    __shared__ __align__(16) T xv[TT * C::LDX];
-    __shared__ __align__(16) T dn[TT * C::LDX];
-    __shared__ __align__(16) T dnt[D * C::LDT];
+    constexpr int NFB = C::NFB, NEB = C::NEB, NEA = C::NEA, NTB = C::NTB, TT = C::TT, D = C::D, MW = C::MW;
+    typedef LMat<T, MW, D> DrMat;  // rows m, cols e
+    constexpr bool DR_LDS = (size_t)C::NW * DrMat::SIZE * sizeof(T) <= 64 * 1024;
+    constexpr int NEW = C::FAVOR ? NEA : 1;  // W^T blocks (the auxiliary one gives the row sum)
+    __shared__ __align__(16) T xq_[C::XMat::SIZE];
+    __shared__ __align__(16) T xk_[C::XMat::SIZE];
+    __shared__ __align__(16) T xv_[C::XMat::SIZE];
+    __shared__ __align__(16) T xva_[C::AuxMat::SIZE];
+    __shared__ __align__(16) T dn_[C::XMat::SIZE];
+    __shared__ __align__(16) T dna_[C::AuxMat::SIZE];
+    __shared__ __align__(16) T fq_[C::NW * C::FMat::SIZE];
+    __shared__ __align__(16) T dr_[DR_LDS ? C::NW * DrMat::SIZE : 8];
     __shared__ __align__(16) float red[C::NW * TT * C::LDR];
-    __shared__ float redk[C::NW * TT];
-    __shared__ float invl[TT], ddl[TT], kn[TT], qmax[C::NW * TT], dSl[M];
+    __shared__ float kn2[TT], qmax[C::NW * TT];
+    const typename C::XMat xq(xq_), xk(xk_);
+    const AugTile<C> Vt(xv_, xva_), DN(dn_, dna_);
+    const typename C::FMat Fq(fq_ + wave_id() * C::FMat::SIZE);
+    const DrMat Dr(dr_ + (DR_LDS ? wave_id() * DrMat::SIZE : 0));
     const ChunkGeom G = chunk_geom<C>(a);
     const int w = wave_id(), g = lgrp(), lc = lcol();
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     const T *dY = (const T *)a.dY + G.hb;
     T *dK = (T *)a.out1 + G.hb, *dV = (T *)a.out2 + G.hb;
     const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * 2;
-    Frag<T> wf[NFB][NEB], wt[NEB][NFB];
+    Frag<T> wf[NFB][NEB], wt[NEW][NFB];
     if constexpr (C::FAVOR) {
         load_wfrag<C>(wf, a.W);
-        load_wtfrag<C>(wt, a.W);
+        load_wtfrag<C, NEW>(wt, a.W);
     }
     const float *gsl = slot_ptr<C>(a.gslots, a, G.bh, G.nl + 1);
-    f4 dr[NEB][NFB], drt[NFB][NEB];
+    f4 dr[NEA][NFB];                             // [dR; dS], rows e, cols m
+    f4 drt[DR_LDS ? 1 : NFB][DR_LDS ? 1 : NEB];  // dR^T (rows m, cols e) when not staged in LDS
+    load_state_E<C>(dr, gsl);
+    if constexpr (!DR_LDS) {
 #pragma unroll
-    for (int eb = 0; eb < NEB; ++eb)
+        for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dr[eb][fb][j] = gsl[(size_t)(eb * 16 + 4 * g + j) * M + w * MW + fb * 16 + lc];
-            drt[fb][eb] = *reinterpret_cast<const f4 *>(gsl + (size_t)(eb * 16 + lc) * M + w * MW + fb * 16 + 4 * g);
-        }
-    for (int m = threadIdx.x; m < M; m += C::NT) dSl[m] = gsl[D * M + m];
+            for (int eb = 0; eb < NEB; ++eb)
+                drt[fb][eb] = *reinterpret_cast<const f4 *>(gsl + (size_t)(eb * 16 + lc) * C::M + w * MW + fb * 16 +
+                                                            4 * g);
+    }
 
     const int last = ((G.len - 1) / TT) * TT;
-    typename C::Tile rq, rk, rv, rdy;
-    RowStatRegs<TT> rs;
-    auto prefetch = [&](int t) {
-        const int n = min(TT, G.len - t);
-        rq.load(Q + (size_t)t * D, n);
-        rk.load(K + (size_t)t * D, n);
-        rv.load(V + (size_t)t * D, n);
-        rdy.load(dY + (size_t)t * D, n, st + (size_t)t * 2);
-        rs.load(st + (size_t)t * 2, n);
-    };
-    prefetch(last);
+    BwdRegs<C> rg;
+    rg.load(Q, K, V, dY, st, last, G.len);
     for (int t0 = last; t0 >= 0; t0 -= TT) {
         const int nv = min(TT, G.len - t0);
-        rq.store(xq, C::LDX, C::FAVOR ? nullptr : qt, C::LDT, false, nullptr);
-        rk.store(xk, C::LDX, nullptr, 0, false, C::FAVOR ? kn : nullptr);
-        rv.store(xv, C::LDX, nullptr, 0, false, nullptr);
-        rdy.store(dn, C::LDX, dnt, C::LDT, true, nullptr);
-        rs.store(invl, ddl);
+        rg.store(xq, xk, Vt, DN, kn2, nv);
         __syncthreads();
-        if (t0 > 0) prefetch(t0 - TT);
-        // Features, kept as MFMA operand fragments (the fp32 blocks die at once).
-        Frag<T> fq[NFB][NTB], fqS[NTB][NFB], fkT[NFB][NTB];
+        if (t0 > 0) rg.load(Q, K, V, dY, st, t0 - TT, G.len);
+        Frag<T> fq[NFB][NTB], fkT[NFB][NTB];
         {
             f4 pq[NFB][NTB];
             feat_T<C>(pq, xq, wf);
             if constexpr (C::FAVOR) q_partial_max<C>(pq, qmax);
             __syncthreads();
             q_finish_T<C>(pq, qmax);
+            put_features<C>(Fq, pq);
             to_frags<C>(fq, pq);
-        }
-        {
-            f4 pqS[NTB][NFB];
-            feat_S<C>(pqS, xq, qt, wf);
-            q_finish_S<C>(pqS, qmax);
-            to_frags<C>(fqS, pqS);
         }
         {
             f4 pkT[NFB][NTB];
             feat_T<C>(pkT, xk, wf);
-            k_finish_T<C>(pkT, kn, nv);
+            k_finish_T<C>(pkT, kn2);
             to_frags<C>(fkT, pkT);
         }
+        if constexpr (DR_LDS) {
+#pragma unroll
+            for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+                for (int fb = 0; fb < NFB; ++fb) Dr.put_frag(fb * 16 + lc, eb * 16 + 4 * g, cfrag<T>(dr[eb][fb]));
+        }
         // dV^T blocks (rows e, cols s): dNum^T P + dR g(K)^T, reduced across waves.
-        // P[t][s] = g(Q_t).g(K_s) over this wave's features, s <= t.
         {
-            Frag<T> fp[NTB][NTB];
+            Frag<T> fp[NTB][NTB];  // P[t][s] = g(Q_t).g(K_s) over own features, s <= t
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
                 for (int sb = 0; sb <= tb; ++sb) {
                     f4 acc = f4zero();
                     mma_range<T>(acc, 0, NFB, [&](int fb) { return fq[fb][tb]; }, [&](int fb) { return fkT[fb][sb]; });
+                    if (sb == tb)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (sb == tb && lc > 4 * g + j) acc[j] = 0.f;
+                        for (int j = 0; j < 4; ++j)
+                            if (lc > 4 * g + j) acc[j] = 0.f;
                     fp[tb][sb] = cfrag<T>(acc);
                 }
+            if constexpr (DR_LDS) wave_lds_fence();  // Dr written by this wave above
 #pragma unroll
             for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
                 for (int sb = 0; sb < NTB; ++sb) {
                     f4 acc = f4zero();
-                    mma_range<T>(acc, sb, NTB, [&](int tb) { return lds_frag<T>(dnt, C::LDT, eb * 16, tb * 16); },
+                    mma_range<T>(acc, sb, NTB, [&](int tb) { return DN.fr(eb, tb * 16); },
                                  [&](int tb) { return fp[tb][sb]; });
-                    mma_range<T>(acc, 0, NFB, [&](int fb) { return cfrag<T>(drt[fb][eb]); },
-                                 [&](int fb) { return fkT[fb][sb]; });
-                    *reinterpret_cast<f4 *>(red + (w * TT + sb * 16 + lc) * C::LDR + eb * 16 + 4 * g) = acc;
+                    if constexpr (DR_LDS)
+                        mma_range<T>(acc, 0, NFB, [&](int fb) { return Dr.frag_r(eb * 16, fb * 16); },
+                                     [&](int fb) { return fkT[fb][sb]; });
+                    else
+                        mma_range<T>(acc, 0, NFB, [&](int fb) { return cfrag<T>(drt[fb][eb]); },
+                                     [&](int fb) { return fkT[fb][sb]; });
+                    put_red<C>(red, eb, sb, acc);
                 }
         }
         __syncthreads();
@@ -368,8 +373,8 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdkv_kernel(ChunkAr
             if (ok) store4<T>(dV + (size_t)(t0 + s) * D + e, v);
         });
         __syncthreads();
-        // dg(K)^T blocks (rows m, cols s): A^T g(Q) + dR^T V + dS, with
-        // A[t][s] = dNum_t . V_s + dden_t for s <= t (the full sum over d, every wave).
+        // dg(K)^T blocks (rows m, cols s) = g(Q)^T A + [dR; dS]^T [V | 1]^T,
+        // A[t][s] = [dNum | dden]_t . [V | 1]_s for s <= t.
         f4 dk[NFB][NTB];
         {
             Frag<T> fa[NTB][NTB];
@@ -378,11 +383,12 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdkv_kernel(ChunkAr
 #pragma unroll
                 for (int sb = 0; sb <= tb; ++sb) {
                     f4 acc = f4zero();
-                    mma_range<T>(acc, 0, NEB, [&](int kb) { return lds_frag<T>(dn, C::LDX, tb * 16, kb * 16); },
-                                 [&](int kb) { return lds_frag<T>(xv, C::LDX, sb * 16, kb * 16); });
+                    mma_range<T>(acc, 0, NEA, [&](int eb) { return DN.fc(tb * 16, eb); },
+                                 [&](int eb) { return Vt.fc(sb * 16, eb); });
+                    if (sb == tb)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[j] = (sb == tb && lc > 4 * g + j) ? 0.f : acc[j] + ddl[tb * 16 + 4 * g + j];
+                        for (int j = 0; j < 4; ++j)
+                            if (lc > 4 * g + j) acc[j] = 0.f;
                     fa[tb][sb] = cfrag<T>(acc);
                 }
 #pragma unroll
@@ -390,45 +396,32 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdkv_kernel(ChunkAr
 #pragma unroll
                 for (int sb = 0; sb < NTB; ++sb) {
                     f4 acc = f4zero();
-                    mma_range<T>(acc, sb, NTB, [&](int tb) { return fqS[tb][fb]; }, [&](int tb) { return fa[tb][sb]; });
-                    mma_range<T>(acc, 0, NEB, [&](int eb) { return cfrag<T>(dr[eb][fb]); },
-                                 [&](int eb) { return lds_frag<T>(xv, C::LDX, sb * 16, eb * 16); });
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[j] += dSl[w * MW + fb * 16 + 4 * g + j];
+                    mma_range<T>(acc, sb, NTB, [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); },
+                                 [&](int tb) { return fa[tb][sb]; });
+                    mma_range<T>(acc, 0, NEA, [&](int eb) { return cfrag<T>(dr[eb][fb]); },
+                                 [&](int eb) { return Vt.fc(sb * 16, eb); });
                     dk[fb][sb] = acc;
                 }
         }
         if constexpr (C::FAVOR) {
-            // dK = (dg(K) . g(K)) W - K * rowsum(dg(K) . g(K)), reduced across waves
+            // [dK^T | rowsum] = [W | 1]^T (dg(K) . g(K))^T, reduced across waves;
+            // dK = (dg(K) . g(K)) W - K * rowsum.
             Frag<T> gk[NFB][NTB];
 #pragma unroll
-            for (int sb = 0; sb < NTB; ++sb) {
-                float rsum = 0.f;
+            for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-                for (int fb = 0; fb < NFB; ++fb) {
-                    const f4 gg = dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]);
-                    rsum += gg[0] + gg[1] + gg[2] + gg[3];
-                    gk[fb][sb] = cfrag<T>(gg);
-                }
-                rsum = sum_groups(rsum);
-                if (g == 0) redk[w * TT + sb * 16 + lc] = rsum;
-            }
+                for (int sb = 0; sb < NTB; ++sb) gk[fb][sb] = cfrag<T>(dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]));
 #pragma unroll
-            for (int eb = 0; eb < NEB; ++eb)
+            for (int eb = 0; eb < NEA; ++eb)
 #pragma unroll
                 for (int sb = 0; sb < NTB; ++sb) {
                     f4 acc = f4zero();
                     mma_range<T>(acc, 0, NFB, [&](int fb) { return wt[eb][fb]; }, [&](int fb) { return gk[fb][sb]; });
-                    *reinterpret_cast<f4 *>(red + (w * TT + sb * 16 + lc) * C::LDR + eb * 16 + 4 * g) = acc;
+                    put_red<C>(red, eb, sb, acc);
                 }
             __syncthreads();
             reduce_rows<C>(red, nv, [&](int s, int e, f4 v, bool ok) {
-                if (!ok) return;
-                float rsum = redk[s];
-#pragma unroll
-                for (int ww = 1; ww < C::NW; ++ww) rsum += redk[ww * TT + s];
-                const f4 kk = load4<T>(xk + s * C::LDX + e);
-                store4<T>(dK + (size_t)(t0 + s) * D + e, v - kk * rsum);
+                if (ok) store4<T>(dK + (size_t)(t0 + s) * D + e, v - xk.get4(s, e) * reduce_col<C>(red, s));
             });
         } else {
 #pragma unroll
@@ -436,32 +429,26 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdkv_kernel(ChunkAr
 #pragma unroll
                 for (int sb = 0; sb < NTB; ++sb) {
                     const int s = sb * 16 + lc;
-                    const f4 x = frag_to_f4<T>(lds_frag<T>(xk, C::LDX, sb * 16, w * MW + fb * 16));
+                    const f4 x = frag_to_f4<T>(xk.frag_c(sb * 16, w * MW + fb * 16));
                     f4 v;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) v[j] = dk[fb][sb][j] * elu1_grad(x[j]);
                     if (s < nv) store4<T>(dK + (size_t)(t0 + s) * D + w * MW + fb * 16 + 4 * g, v);
                 }
         }
-        // gradient state: dR += dNum^T g(Q), dS += sum dden g(Q) (after use)
+        // gradient state (after use): [dR; dS] += [dNum | dden]^T g(Q)
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb) {
 #pragma unroll
-            for (int eb = 0; eb < NEB; ++eb) {
-                mma_range<T>(dr[eb][fb], 0, NTB, [&](int tb) { return lds_frag<T>(dnt, C::LDT, eb * 16, tb * 16); },
-                             [&](int tb) { return fqS[tb][fb]; });
-                mma_range<T>(drt[fb][eb], 0, NTB, [&](int tb) { return fqS[tb][fb]; },
-                             [&](int tb) { return lds_frag<T>(dnt, C::LDT, eb * 16, tb * 16); });
-            }
-            float s = 0.f;
+            for (int eb = 0; eb < NEA; ++eb)
+                mma_range<T>(dr[eb][fb], 0, NTB, [&](int tb) { return DN.fr(eb, tb * 16); },
+                             [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); });
+            if constexpr (!DR_LDS) {
 #pragma unroll
-            for (int tb = 0; tb < NTB; ++tb) {
-                const f4 q4 = frag_to_f4<T>(fqS[tb][fb]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s += q4[j] * ddl[tb * 16 + 4 * g + j];
+                for (int eb = 0; eb < NEB; ++eb)
+                    mma_range<T>(drt[fb][eb], 0, NTB, [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); },
+                                 [&](int tb) { return DN.fr(eb, tb * 16); });
             }
-            s = sum_groups(s);
-            if (g == 0) dSl[w * MW + fb * 16 + lc] += s;
         }
         __syncthreads();
     }
