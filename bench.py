@@ -28,7 +28,6 @@ sys.path.insert(0, ROOT)
 METRIC = "causal linear-attn fwd+bwd tokens/s & % roofline; peak HBM, L=16K d=64 M=256"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA peaks
 PEAK_HBM_GBS = 8000.0
-TILE = {("f32", 128): 16}                       # rows per tile of the kernels (else 32)
 
 
 def parse():
@@ -122,8 +121,8 @@ def main():
         return
 
     w = WORKLOADS[args.workload or HEADLINE]
-    tile = TILE.get((w.dtype, w.d), 32)
     q, k, v, W, dy = make_inputs(w, torch, synth)
+    tile = int(_lib.lib().slim_tile_rows(__import__("ctypes").byref(A.make_desc(q, w.M, w.feat, w.chunks))))
     torch.cuda.synchronize()
 
     def step():

@@ -12,6 +12,7 @@ struct KernelTable {
     void (*state)(dim3, hipStream_t, const ChunkArgs &);
     void (*fwd)(dim3, hipStream_t, const ChunkArgs &);
     void (*stats)(dim3, hipStream_t, const ChunkArgs &);
+    void (*gstate)(dim3, hipStream_t, const ChunkArgs &);
     void (*bwdq)(dim3, hipStream_t, const ChunkArgs &);
     void (*bwdkv)(dim3, hipStream_t, const ChunkArgs &);
 };

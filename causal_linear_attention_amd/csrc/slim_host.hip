@@ -7,9 +7,9 @@
 //       state -> forward prefix scan (carry = running final state) -> fwd
 //   backward (Subsection 3.3): for each window in reverse order:
 //       state -> reverse scan (entry states by subtraction from the carry,
-//       update (19)) -> stats (recompute forward, per-row statistics, the
-//       slice's gradient w.r.t. its entry state) -> gradient suffix scan
-//       (update (20)) -> dQ -> dK, dV
+//       update (19)) -> stats (recompute forward, per-row statistics) -> dQ
+//       -> gstate (the slice's gradient w.r.t. its entry state) -> gradient
+//       suffix scan (update (20)) -> dK, dV
 // Only the carries (d x M + M per head) live across windows, so the workspace
 // is bounded by the window, not by L.
 #include <hip/hip_runtime.h>
@@ -275,6 +275,12 @@ int64_t slim_window_chunks(const slim_desc *d)
     return plan(d, SLIM_PASS_FWD).P;
 }
 
+int64_t slim_tile_rows(const slim_desc *d)
+{
+    if (slim_validate(d, SLIM_PASS_FWD) != SLIM_OK) return 0;
+    return find(d)->tt;
+}
+
 slim_status slim_featmap(const slim_desc *d, const void *X, const void *W, float *phi, float *row_offset,
                          void *stream)
 {
@@ -376,8 +382,9 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
         SLIM_TIMED("state", s, kt->state(dim3(np, BH), s, a));
         scan(1, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
         SLIM_TIMED("stats", s, kt->stats(dim3(np, BH), s, a));
-        scan(2, a.gslots, gR, gS, D, M, (int)p.P, np, BH, s);
         SLIM_TIMED("bwdq", s, kt->bwdq(dim3(np, BH), s, a));
+        SLIM_TIMED("gstate", s, kt->gstate(dim3(np, BH), s, a));
+        scan(2, a.gslots, gR, gS, D, M, (int)p.P, np, BH, s);
         SLIM_TIMED("bwdkv", s, kt->bwdkv(dim3(np, BH), s, a));
     }
     if (dR_in) {

@@ -17,7 +17,10 @@
 // workgroup split the M features: wave w owns features [w*MW, (w+1)*MW), holds
 // its slice of every feature-indexed matrix (g(Q), g(K), R, S and their
 // gradients) in MFMA accumulator layout, and reduces the feature-contracted
-// outputs (numerators, dQ, dK, dV) across waves through LDS.
+// outputs (numerators, dQ, dK, dV) across waves through LDS.  Waves are kept to
+// 4 per workgroup where the state fits (64 features per wave), and a kernel whose
+// LDS fits twice in a compute unit is compiled for 2 waves per SIMD, so two
+// workgroups share each compute unit and hide each other's barrier waits.
 //
 // Augmented value index.  V, the state R, dNum and dR carry one extra 16-wide
 // block of the value index e whose first column is 1 (V), S (R), dden (dNum) or
@@ -35,9 +38,10 @@
 //                    (forward prefix, reverse subtraction, gradient suffix sum).
 //   fwd_kernel     : Y for a chunk from its entry state.
 //   stats_kernel   : backward pass 1: recompute the chunk forward, emit per-row
-//                    1/den and dden = -(dY.Y)/den, and the chunk's gradient
-//                    contribution to its entry state: dG_n = sum dNum g(Q)^T.
+//                    1/den and dden = -(dY.Y)/den.
 //   bwdq_kernel    : dQ (forward tile order, entry state R).
+//   gstate_kernel  : the chunk's gradient contribution to its entry state,
+//                    dG_n = sum dNum g(Q)^T (and dden g(Q)).
 //   bwdkv_kernel   : dK, dV (reverse tile order, gradient state dR).
 #pragma once
 #include "slim_device.h"
@@ -58,10 +62,13 @@ struct ChunkArgs {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
-template <typename T_, int D_, int M_, int FEAT_, int TT_, int MW_ = 32> struct KCfg {
+// MW_ = features per wave (0: 64 for bf16 with d <= 64, else 32 -- what keeps a
+// wave's fp32 state blocks and fragments within 256 registers).
+template <typename T_, int D_, int M_, int FEAT_, int TT_, int MW_ = 0> struct KCfg {
     typedef T_ T;
     static constexpr int D = D_, M = M_, FEAT = FEAT_, TT = TT_;
-    static constexpr int MW = M >= MW_ ? MW_ : M;  // features per wave
+    static constexpr int MWA = MW_ ? MW_ : ((sizeof(T_) == 2 && D_ <= 64) ? 64 : 32);
+    static constexpr int MW = M >= MWA ? MWA : M;  // features per wave
     static constexpr int NW = M / MW;              // waves per workgroup
     static constexpr int NT = NW * 64;
     static constexpr int NFB = MW / 16;
@@ -78,6 +85,11 @@ template <typename T_, int D_, int M_, int FEAT_, int TT_, int MW_ = 32> struct 
     static_assert(FEAT == FEAT_FAVOR || D == M, "elu+1 needs M == d");
     static_assert(MW % 16 == 0 && D % 16 == 0 && TT % 16 == 0, "block sizes");
 };
+
+// Waves per SIMD a kernel is compiled for (its register budget): 2 when two of
+// its workgroups fit a compute unit's 160 KB of LDS and 4 SIMDs, so that one
+// workgroup's barriers and memory waits overlap the other's work; else 1.
+constexpr int waves_per_simd(size_t lds_bytes, int nw) { return (nw <= 4 && 2 * lds_bytes <= 160 * 1024) ? 2 : 1; }
 
 // A value-indexed tile (V or dNum) with its auxiliary block.
 template <class C> struct AugTile {
@@ -144,6 +156,20 @@ __device__ __forceinline__ void load_wtfrag(Frag<typename C::T> (&wt)[NE][C::NFB
                                      : (T)(lcol() == 0 ? 1.f : 0.f);
             wt[eb][fb] = f;
         }
+}
+
+// One value block eb of the W^T fragments above.
+template <class C>
+__device__ __forceinline__ void load_wtfrag_block(Frag<typename C::T> (&wt)[C::NFB], const void *Wv, int eb)
+{
+    typedef typename C::T T;
+    const T *W = (const T *)Wv;
+    const int w = wave_id();
+#pragma unroll
+    for (int fb = 0; fb < C::NFB; ++fb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            wt[fb].v[j] = W[(size_t)(w * C::MW + fb * 16 + 4 * lgrp() + j) * C::D + eb * 16 + lcol()];
 }
 
 // Feature blocks in "transposed" orientation: ph[fb][tb] has rows m = w*MW + fb*16 + 4g + j
@@ -467,16 +493,22 @@ template <class C> __device__ __forceinline__ void store_state_T(float *slot, co
 }
 
 // state_kernel: slot[n+1] = (dR_n, dS_n) of chunk n (R part stored [e][m]).
-template <class C> __global__ __launch_bounds__(C::NT) void state_kernel(ChunkArgs a)
+template <class C> struct StateSmem {
+    typedef typename C::T T;
+    __align__(16) T xk[C::XMat::SIZE];
+    __align__(16) T xv[C::XMat::SIZE];
+    __align__(16) T xva[C::AuxMat::SIZE];
+    float kn2[C::TT];
+};
+template <class C>
+__global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StateSmem<C>), C::NW)) void state_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
     constexpr int NFB = C::NFB, NEA = C::NEA, NTB = C::NTB, TT = C::TT;
-    __shared__ __align__(16) T xk_[C::XMat::SIZE];
-    __shared__ __align__(16) T xv_[C::XMat::SIZE];
-    __shared__ __align__(16) T xva_[C::AuxMat::SIZE];
-    __shared__ float kn2[TT];
-    const typename C::XMat xk(xk_);
-    const AugTile<C> V(xv_, xva_);
+    __shared__ StateSmem<C> sm;
+    float *kn2 = sm.kn2;
+    const typename C::XMat xk(sm.xk);
+    const AugTile<C> V(sm.xv, sm.xva);
     const ChunkGeom G = chunk_geom<C>(a);
     const T *Kp = (const T *)a.K + G.hb, *Vp = (const T *)a.V + G.hb;
     Frag<T> wf[NFB][C::NEB];
@@ -554,15 +586,16 @@ __global__ __launch_bounds__(256) void scan_kernel(float *slots, float *carryR, 
     *reinterpret_cast<f4 *>(cp) = cur;
 }
 
-// LDS of the chunk kernels that evaluate a chunk's forward.
-template <class C> struct FwdSmem {
+// LDS of the chunk kernels that evaluate a chunk's forward.  RED: per-wave fp32
+// rows for the cross-wave sum of the numerators (else two floats per row and wave).
+template <class C, bool RED = true> struct FwdSmem {
     typedef typename C::T T;
     __align__(16) T xq[C::XMat::SIZE];
     __align__(16) T xk[C::XMat::SIZE];
     __align__(16) T xv[C::XMat::SIZE];
     __align__(16) T xva[C::AuxMat::SIZE];
     __align__(16) T fk[C::NW * C::FMat::SIZE];
-    __align__(16) float red[C::NW * C::TT * C::LDR];
+    __align__(16) float red[RED ? C::NW * C::TT * C::LDR : 2 * C::NW * C::TT];
     float qmax[C::NW * C::TT];
     float kn2[C::TT];
 };
@@ -578,7 +611,7 @@ template <class C> struct FwdRegs {
         k.load(K + (size_t)t0 * C::D, nv);
         v.load(V + (size_t)t0 * C::D, nv);
     }
-    __device__ __forceinline__ void store(FwdSmem<C> &sm, int nv)
+    template <class SM> __device__ __forceinline__ void store(SM &sm, int nv)
     {
         q.store(typename C::XMat(sm.xq), false, nullptr);
         store_k_tile<C>(k, typename C::XMat(sm.xk), sm.kn2, nv);
@@ -586,13 +619,14 @@ template <class C> struct FwdRegs {
     }
 };
 
-// One tile of the chunk forward, shared by fwd_kernel and stats_kernel: writes
-// this wave's partial numerator^T (and denominator, column D) into red and
-// syncs; leaves g(Q) of this wave's features (rows m, cols t) in pq and g(K) in
-// the wave's feature buffer (rows t, cols m).
-template <class C>
-__device__ __forceinline__ void fwd_tile(FwdSmem<C> &sm, const Frag<typename C::T> (&wf)[C::NFB][C::NEB],
-                                         const f4 (&rt)[C::NFB][C::NEA], f4 (&pq)[C::NFB][C::NTB])
+// One tile of the chunk forward, shared by fwd_kernel and stats_kernel: hands
+// this wave's partial numerator^T blocks (rows e, cols t; the auxiliary block's
+// first row is the denominator) to emit(eb, tb, acc); leaves g(Q) of this wave's
+// features (rows m, cols t) in pq and g(K) in the wave's feature buffer (rows t,
+// cols m).
+template <class C, class SM, class EMIT>
+__device__ __forceinline__ void fwd_tile(SM &sm, const Frag<typename C::T> (&wf)[C::NFB][C::NEB],
+                                         const f4 (&rt)[C::NFB][C::NEA], f4 (&pq)[C::NFB][C::NTB], EMIT emit)
 {
     typedef typename C::T T;
     constexpr int NFB = C::NFB, NEA = C::NEA, NTB = C::NTB;
@@ -633,13 +667,12 @@ __device__ __forceinline__ void fwd_tile(FwdSmem<C> &sm, const Frag<typename C::
             f4 acc = f4zero();
             mma_range<T>(acc, 0, tb + 1, [&](int sb) { return V.fr(eb, sb * 16); }, [&](int sb) { return pt[sb][tb]; });
             mma_range<T>(acc, 0, NFB, [&](int fb) { return cfrag<T>(rt[fb][eb]); }, [&](int fb) { return fq[fb][tb]; });
-            put_red<C>(sm.red, eb, tb, acc);
+            emit(eb, tb, acc);
         }
-    __syncthreads();
 }
 
 // State update after a tile: [R^T | S] += g(K)^T [V | 1] over this wave's features.
-template <class C> __device__ __forceinline__ void state_update_T(FwdSmem<C> &sm, f4 (&rt)[C::NFB][C::NEA])
+template <class C, class SM> __device__ __forceinline__ void state_update_T(SM &sm, f4 (&rt)[C::NFB][C::NEA])
 {
     typedef typename C::T T;
     const AugTile<C> V(sm.xv, sm.xva);
@@ -653,7 +686,8 @@ template <class C> __device__ __forceinline__ void state_update_T(FwdSmem<C> &sm
 }
 
 // fwd_kernel: Y of one chunk from its entry state slot[n].
-template <class C> __global__ __launch_bounds__(C::NT) void fwd_kernel(ChunkArgs a)
+template <class C>
+__global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(FwdSmem<C>), C::NW)) void fwd_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
     constexpr int NFB = C::NFB, NEA = C::NEA, NTB = C::NTB, TT = C::TT;
@@ -673,7 +707,8 @@ template <class C> __global__ __launch_bounds__(C::NT) void fwd_kernel(ChunkArgs
         __syncthreads();
         if (t0 + TT < G.len) rg.load(Q, K, V, t0 + TT, G.len);
         f4 pq[NFB][NTB];
-        fwd_tile<C>(sm, wf, rt, pq);
+        fwd_tile<C>(sm, wf, rt, pq, [&](int eb, int tb, f4 acc) { put_red<C>(sm.red, eb, tb, acc); });
+        __syncthreads();
         reduce_rows<C>(sm.red, nv, [&](int t, int e, f4 s, bool ok) {
             if (ok) store4<T>(Y + (size_t)(t0 + t) * C::D + e, s * (1.f / reduce_col<C>(sm.red, t)));
         });

@@ -20,65 +20,139 @@
 
 namespace slim {
 
-// stats_kernel: recompute the chunk forward from slot[n]; write per-row
-// (1/den, dden) to stats and gslot[n+1] = (dG_n, dGs_n) = sum over the chunk of
-// (dNum_t g(Q_t)^T, dden_t g(Q_t)) -- the chunk's gradient w.r.t. its entry state.
-template <class C> __global__ __launch_bounds__(C::NT) void stats_kernel(ChunkArgs a)
+// stats_kernel: recompute the chunk forward from slot[n] and write per row
+// (1/den, dden) to stats.  dden = -(dY . Y) / den = -(dY . Num) / den^2 needs only
+// two numbers per row from each wave -- its partial denominator and its partial
+// dY . Num -- so the numerators themselves are never summed across waves.
+template <class C> struct StatsSmem {
+    FwdSmem<C, false> f;
+    __align__(16) typename C::T xdy[C::XMat::SIZE];
+};
+template <class C>
+__global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StatsSmem<C>), C::NW)) void stats_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
-    constexpr int NFB = C::NFB, NEA = C::NEA, NTB = C::NTB, TT = C::TT, D = C::D;
-    __shared__ FwdSmem<C> sm;
-    __shared__ __align__(16) T dn_[C::XMat::SIZE];
-    __shared__ __align__(16) T dna_[C::AuxMat::SIZE];
-    __shared__ __align__(16) T fq_[C::NW * C::FMat::SIZE];
-    const AugTile<C> DN(dn_, dna_);  // holds dY until the row statistics turn it into dNum
-    const typename C::FMat Fq(fq_ + wave_id() * C::FMat::SIZE);
+    constexpr int NFB = C::NFB, NEB = C::NEB, NEA = C::NEA, NTB = C::NTB, TT = C::TT, D = C::D, NW = C::NW;
+    __shared__ StatsSmem<C> sm;
+    const typename C::XMat xdy(sm.xdy);
     const ChunkGeom G = chunk_geom<C>(a);
+    const int w = wave_id(), g = lgrp(), lc = lcol();
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     const T *dY = (const T *)a.dY + G.hb;
     float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * 2;
-    Frag<T> wf[NFB][C::NEB];
+    Frag<T> wf[NFB][NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
-    f4 rt[NFB][NEA], dg[NFB][NEA];
+    f4 rt[NFB][NEA];
     load_state_T<C>(rt, slot_ptr<C>(a.slots, a, G.bh, G.nl));
-#pragma unroll
-    for (int fb = 0; fb < NFB; ++fb)
-#pragma unroll
-        for (int eb = 0; eb < NEA; ++eb) dg[fb][eb] = f4zero();
     FwdRegs<C> rg;
     typename C::Tile rdy;
     rg.load(Q, K, V, 0, G.len);
     rdy.load(dY, min(TT, G.len));
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        rg.store(sm, nv);
-        rdy.store(DN.x, false, nullptr);
+        rg.store(sm.f, nv);
+        rdy.store(xdy, false, nullptr);
         __syncthreads();
         if (t0 + TT < G.len) {
             rg.load(Q, K, V, t0 + TT, G.len);
             rdy.load(dY + (size_t)(t0 + TT) * D, min(TT, G.len - t0 - TT));
         }
         f4 pq[NFB][NTB];
-        fwd_tile<C>(sm, wf, rt, pq);
-        put_features<C>(Fq, pq);
-        reduce_rows<C>(sm.red, nv, [&](int t, int e, f4 s, bool ok) {
-            const float inv = ok ? 1.f / reduce_col<C>(sm.red, t) : 0.f;
-            const f4 y = s * inv;
-            const f4 dy = DN.x.get4(t, e);
-            float p = dy[0] * y[0] + dy[1] * y[1] + dy[2] * y[2] + dy[3] * y[3];
+        float dot[NTB], den[NTB];
 #pragma unroll
-            for (int o = 1; o < D / 4; o <<= 1) p += __shfl_xor(p, o, 64);
-            DN.x.put4(t, e, dy * inv);
-            if (e == 0) {
-                const float dd = ok ? -p * inv : 0.f;
-                DN.set_aux(t, dd);
-                if (ok) {
-                    st[(size_t)(t0 + t) * 2] = inv;
-                    st[(size_t)(t0 + t) * 2 + 1] = dd;
-                }
+        for (int tb = 0; tb < NTB; ++tb) dot[tb] = den[tb] = 0.f;
+        fwd_tile<C>(sm.f, wf, rt, pq, [&](int eb, int tb, f4 acc) {
+            if (eb < NEB) {
+                const f4 dy = xdy.get4(tb * 16 + lc, eb * 16 + 4 * g);
+                dot[tb] += acc[0] * dy[0] + acc[1] * dy[1] + acc[2] * dy[2] + acc[3] * dy[3];
+            } else {
+                den[tb] = acc[0];  // row D of the numerators; zero in lanes with g > 0
             }
         });
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            float p = dot[tb];
+            p += __shfl_xor(p, 16, 64);
+            p += __shfl_xor(p, 32, 64);
+            if (g == 0) {
+                sm.f.red[((w * TT) + tb * 16 + lc) * 2] = den[tb];
+                sm.f.red[((w * TT) + tb * 16 + lc) * 2 + 1] = p;
+            }
+        }
         __syncthreads();
+        if (threadIdx.x < nv) {
+            const int t = threadIdx.x;
+            float dn = 0.f, dt = 0.f;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                dn += sm.f.red[(v * TT + t) * 2];
+                dt += sm.f.red[(v * TT + t) * 2 + 1];
+            }
+            const float inv = 1.f / dn;
+            st[(size_t)(t0 + t) * 2] = inv;
+            st[(size_t)(t0 + t) * 2 + 1] = -dt * inv * inv;
+        }
+        state_update_T<C>(sm.f, rt);
+        __syncthreads();
+    }
+}
+
+// gstate_kernel: gslot[n+1] = (dG_n, dGs_n) = sum over chunk n of
+// (g(Q_t) dNum_t^T, dden_t g(Q_t)), the chunk's gradient w.r.t. its entry state
+// (stored like a state slot), from Q, dY and the per-row statistics.
+template <class C> struct GstateSmem {
+    typedef typename C::T T;
+    __align__(16) T xq[C::XMat::SIZE];
+    __align__(16) T dn[C::XMat::SIZE];
+    __align__(16) T dna[C::AuxMat::SIZE];
+    __align__(16) T fq[C::NW * C::FMat::SIZE];
+    float qmax[C::NW * C::TT];
+};
+template <class C>
+__global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(GstateSmem<C>), C::NW)) void gstate_kernel(ChunkArgs a)
+{
+    typedef typename C::T T;
+    constexpr int NFB = C::NFB, NEB = C::NEB, NEA = C::NEA, NTB = C::NTB, TT = C::TT, D = C::D;
+    __shared__ GstateSmem<C> sm;
+    const typename C::XMat xq(sm.xq);
+    const AugTile<C> DN(sm.dn, sm.dna);
+    const typename C::FMat Fq(sm.fq + wave_id() * C::FMat::SIZE);
+    const ChunkGeom G = chunk_geom<C>(a);
+    const T *Q = (const T *)a.Q + G.hb, *dY = (const T *)a.dY + G.hb;
+    const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * 2;
+    Frag<T> wf[NFB][NEB];
+    if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
+    f4 dg[NFB][NEA];
+#pragma unroll
+    for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+        for (int eb = 0; eb < NEA; ++eb) dg[fb][eb] = f4zero();
+    typename C::Tile rq, rdy;
+    RowStatRegs<TT> rs;
+    {
+        const int n = min(TT, G.len);
+        rq.load(Q, n);
+        rdy.load(dY, n, st);
+        rs.load(st, n);
+    }
+    for (int t0 = 0; t0 < G.len; t0 += TT) {
+        rq.store(xq, false, nullptr);
+        rdy.store(DN.x, true, nullptr);
+        if (threadIdx.x < TT) DN.set_aux(threadIdx.x, rs.dd);
+        __syncthreads();
+        if (t0 + TT < G.len) {
+            const int n = min(TT, G.len - t0 - TT);
+            rq.load(Q + (size_t)(t0 + TT) * D, n);
+            rdy.load(dY + (size_t)(t0 + TT) * D, n, st + (size_t)(t0 + TT) * 2);
+            rs.load(st + (size_t)(t0 + TT) * 2, n);
+        }
+        f4 pq[NFB][NTB];
+        feat_T<C>(pq, xq, wf);
+        if constexpr (C::FAVOR) q_partial_max<C>(pq, sm.qmax);
+        __syncthreads();
+        q_finish_T<C>(pq, sm.qmax);
+        put_features<C>(Fq, pq);
+        wave_lds_fence();  // Fq written by this wave above
         // [dG | dGs] += g(Q)^T [dNum | dden] over this wave's features
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
@@ -86,7 +160,6 @@ template <class C> __global__ __launch_bounds__(C::NT) void stats_kernel(ChunkAr
             for (int eb = 0; eb < NEA; ++eb)
                 mma_range<T>(dg[fb][eb], 0, NTB, [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); },
                              [&](int tb) { return DN.fr(eb, tb * 16); });
-        state_update_T<C>(sm, rt);
         __syncthreads();
     }
     store_state_T<C>(slot_ptr<C>(a.gslots, a, G.bh, G.nl + 1), dg);
@@ -136,33 +209,36 @@ template <class C> struct BwdRegs {
 
 // bwdq_kernel: dQ of one chunk.  Tiles in forward order, carrying the entry
 // state [R; S] (rows e, cols m) from slot[n].
-template <class C> __global__ __launch_bounds__(C::NT) void bwdq_kernel(ChunkArgs a)
+template <class C> struct BwdqSmem {
+    typedef typename C::T T;
+    __align__(16) T xq[C::XMat::SIZE];
+    __align__(16) T xk[C::XMat::SIZE];
+    __align__(16) T xv[C::XMat::SIZE];
+    __align__(16) T xva[C::AuxMat::SIZE];
+    __align__(16) T dn[C::XMat::SIZE];
+    __align__(16) T dna[C::AuxMat::SIZE];
+    __align__(16) T fk[C::NW * C::FMat::SIZE];
+    __align__(16) float red[C::FAVOR ? C::NW * C::TT * C::LDR : 4];
+    float kn2[C::TT], qmax[C::NW * C::TT];
+};
+template <class C>
+__global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) void bwdq_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
     constexpr int NFB = C::NFB, NEB = C::NEB, NEA = C::NEA, NTB = C::NTB, TT = C::TT, D = C::D, MW = C::MW;
-    __shared__ __align__(16) T xq_[C::XMat::SIZE];
-    __shared__ __align__(16) T xk_[C::XMat::SIZE];
-    __shared__ __align__(16) T xv_[C::XMat::SIZE];
-    __shared__ __align__(16) T xva_[C::AuxMat::SIZE];
-    __shared__ __align__(16) T dn_[C::XMat::SIZE];
-    __shared__ __align__(16) T dna_[C::AuxMat::SIZE];
-    __shared__ __align__(16) T fk_[C::NW * C::FMat::SIZE];
-    __shared__ __align__(16) float red[C::FAVOR ? C::NW * TT * C::LDR : 4];
-    __shared__ float kn2[TT], qmax[C::NW * TT];
-    const typename C::XMat xq(xq_), xk(xk_);
-    const AugTile<C> Vt(xv_, xva_), DN(dn_, dna_);
-    const typename C::FMat Fk(fk_ + wave_id() * C::FMat::SIZE);
+    __shared__ BwdqSmem<C> sm;
+    float *red = sm.red, *kn2 = sm.kn2, *qmax = sm.qmax;
+    const typename C::XMat xq(sm.xq), xk(sm.xk);
+    const AugTile<C> Vt(sm.xv, sm.xva), DN(sm.dn, sm.dna);
+    const typename C::FMat Fk(sm.fk + wave_id() * C::FMat::SIZE);
     const ChunkGeom G = chunk_geom<C>(a);
     const int w = wave_id(), g = lgrp(), lc = lcol();
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     const T *dY = (const T *)a.dY + G.hb;
     T *dQ = (T *)a.out0 + G.hb;
     const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * 2;
-    Frag<T> wf[NFB][NEB], wt[NEB][NFB];
-    if constexpr (C::FAVOR) {
-        load_wfrag<C>(wf, a.W);
-        load_wtfrag<C, NEB>(wt, a.W);
-    }
+    Frag<T> wf[NFB][NEB];
+    if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
     f4 r[NEA][NFB];
     load_state_E<C>(r, slot_ptr<C>(a.slots, a, G.bh, G.nl));
     BwdRegs<C> rg;
@@ -213,20 +289,24 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdq_kernel(ChunkArg
                 dq[fb][tb] = acc;
             }
         if constexpr (C::FAVOR) {
-            // dQ^T (rows e, cols t) = W^T (dg(Q) . g(Q))^T over own features, reduced across waves
+            // dQ^T (rows e, cols t) = W^T (dg(Q) . g(Q))^T over own features, reduced across
+            // waves; the W^T fragments are read (from cache) per value block here.
             Frag<T> gq[NFB][NTB];
 #pragma unroll
             for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
                 for (int tb = 0; tb < NTB; ++tb) gq[fb][tb] = cfrag<T>(dq[fb][tb] * pq[fb][tb]);
 #pragma unroll
-            for (int eb = 0; eb < NEB; ++eb)
+            for (int eb = 0; eb < NEB; ++eb) {
+                Frag<T> wt[NFB];
+                load_wtfrag_block<C>(wt, a.W, eb);
 #pragma unroll
                 for (int tb = 0; tb < NTB; ++tb) {
                     f4 acc = f4zero();
-                    mma_range<T>(acc, 0, NFB, [&](int fb) { return wt[eb][fb]; }, [&](int fb) { return gq[fb][tb]; });
+                    mma_range<T>(acc, 0, NFB, [&](int fb) { return wt[fb]; }, [&](int fb) { return gq[fb][tb]; });
                     put_red<C>(red, eb, tb, acc);
                 }
+            }
             __syncthreads();
             reduce_rows<C>(red, nv, [&](int t, int e, f4 s, bool ok) {
                 if (ok) store4<T>(dQ + (size_t)(t0 + t) * D + e, s);
@@ -261,27 +341,35 @@ template <class C> __global__ __launch_bounds__(C::NT) void bwdq_kernel(ChunkArg
 // contraction index: a copy of this wave's dR block goes to LDS each tile and is
 // read back transposed (if the copies of all waves fit in 64 KB of LDS;
 // otherwise a second fp32 orientation is carried in registers).
-template <class C> __global__ __launch_bounds__(C::NT) void bwdkv_kernel(ChunkArgs a)
+template <class C> struct BwdkvSmem {
+    typedef typename C::T T;
+    typedef LMat<T, C::MW, C::D> DrMat;  // rows m, cols e
+    static constexpr bool DR_LDS = (size_t)C::NW * DrMat::SIZE * sizeof(T) <= 64 * 1024;
+    __align__(16) T xq[C::XMat::SIZE];
+    __align__(16) T xk[C::XMat::SIZE];
+    __align__(16) T xv[C::XMat::SIZE];
+    __align__(16) T xva[C::AuxMat::SIZE];
+    __align__(16) T dn[C::XMat::SIZE];
+    __align__(16) T dna[C::AuxMat::SIZE];
+    __align__(16) T fq[C::NW * C::FMat::SIZE];
+    __align__(16) T dr[DR_LDS ? C::NW * DrMat::SIZE : 8];
+    __align__(16) float red[C::NW * C::TT * C::LDR];
+    float kn2[C::TT], qmax[C::NW * C::TT];
+};
+template <class C>
+__global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW)) void bwdkv_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
     constexpr int NFB = C::NFB, NEB = C::NEB, NEA = C::NEA, NTB = C::NTB, TT = C::TT, D = C::D, MW = C::MW;
-    typedef LMat<T, MW, D> DrMat;  // rows m, cols e
-    constexpr bool DR_LDS = (size_t)C::NW * DrMat::SIZE * sizeof(T) <= 64 * 1024;
+    typedef typename BwdkvSmem<C>::DrMat DrMat;
+    constexpr bool DR_LDS = BwdkvSmem<C>::DR_LDS;
     constexpr int NEW = C::FAVOR ? NEA : 1;  // W^T blocks (the auxiliary one gives the row sum)
-    __shared__ __align__(16) T xq_[C::XMat::SIZE];
-    __shared__ __align__(16) T xk_[C::XMat::SIZE];
-    __shared__ __align__(16) T xv_[C::XMat::SIZE];
-    __shared__ __align__(16) T xva_[C::AuxMat::SIZE];
-    __shared__ __align__(16) T dn_[C::XMat::SIZE];
-    __shared__ __align__(16) T dna_[C::AuxMat::SIZE];
-    __shared__ __align__(16) T fq_[C::NW * C::FMat::SIZE];
-    __shared__ __align__(16) T dr_[DR_LDS ? C::NW * DrMat::SIZE : 8];
-    __shared__ __align__(16) float red[C::NW * TT * C::LDR];
-    __shared__ float kn2[TT], qmax[C::NW * TT];
-    const typename C::XMat xq(xq_), xk(xk_);
-    const AugTile<C> Vt(xv_, xva_), DN(dn_, dna_);
-    const typename C::FMat Fq(fq_ + wave_id() * C::FMat::SIZE);
-    const DrMat Dr(dr_ + (DR_LDS ? wave_id() * DrMat::SIZE : 0));
+    __shared__ BwdkvSmem<C> sm;
+    float *red = sm.red, *kn2 = sm.kn2, *qmax = sm.qmax;
+    const typename C::XMat xq(sm.xq), xk(sm.xk);
+    const AugTile<C> Vt(sm.xv, sm.xva), DN(sm.dn, sm.dna);
+    const typename C::FMat Fq(sm.fq + wave_id() * C::FMat::SIZE);
+    const DrMat Dr(sm.dr + (DR_LDS ? wave_id() * DrMat::SIZE : 0));
     const ChunkGeom G = chunk_geom<C>(a);
     const int w = wave_id(), g = lgrp(), lc = lcol();
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;

@@ -79,7 +79,7 @@ def kernel_flops(w: Workload, tile: int) -> dict:
     d x M state, so the intra-tile causal products cost about (tile+1) M and
     (tile+1) d per row, and every state-sized product (a d x M contraction per
     row) costs 2 d M.  A FAVOR+ feature-map projection is one more 2 d M per row
-    and orientation computed (elu+1 needs none).  Zero padding, masked-out
+    and input it is applied to (elu+1 needs none).  Zero padding, masked-out
     upper triangles and elementwise work are not counted."""
     d, M = w.d, w.M
     favor = w.feat == "favor"
@@ -89,12 +89,13 @@ def kernel_flops(w: Workload, tile: int) -> dict:
     td = (tile + 1) * d                  # causal tile x tile x d product, per row
     vjp = dm if favor else 0             # FAVOR+ chain rule through W
     return {
-        "state": P + dm,                                   # g(K); dR = V^T g(K)
-        "fwd": 3 * P + tm + td + 2 * dm,                   # g(Q)^T, g(K)^T, g(K); P^T; V^T P^T; R g(Q); state
-        "stats": 4 * P + tm + td + 3 * dm,                 # fwd + g(Q) rows-major + dG
-        "bwdq": 2 * P + tm + td + 2 * dm + vjp,            # g(Q)^T, g(K); A^T; A g(K); dNum R; W chain; R
-        "bwdkv": 3 * P + 2 * tm + 2 * td + 4 * dm + vjp,   # g(Q)^T, g(Q), g(K)^T; P; A; A^T g(Q); dR V; chain;
-                                                            # P^T dNum; g(K) dR^T; dR, dR^T updates
+        "state": P + dm,                                   # g(K); [R | S] += g(K)^T [V | 1]
+        "fwd": 2 * P + tm + td + 2 * dm,                   # g(Q), g(K); P^T; [V | 1]^T P^T; R g(Q); state
+        "stats": 2 * P + tm + td + 2 * dm,                 # the fwd tile (numerators dotted with dY); state
+        "bwdq": 2 * P + tm + td + 2 * dm + vjp,            # g(Q), g(K); A^T; g(K)^T A^T; R^T dNum; W chain; R
+        "gstate": P + dm,                                  # g(Q); dG += g(Q)^T [dNum | dden]
+        "bwdkv": 2 * P + 2 * tm + 2 * td + 3 * dm + vjp,   # g(Q), g(K); P; dNum^T P; dR g(K)^T; A;
+                                                            # g(Q)^T A; dR^T V; W chain; dR update
     }
 
 

@@ -92,6 +92,11 @@ size_t slim_workspace_bytes(const slim_desc *desc, int pass);
 /* Slices whose states one window holds (the resolved window_chunks). */
 int64_t slim_window_chunks(const slim_desc *desc);
 
+/* Rows per tile with which the chunk kernels walk a slice for this
+ * descriptor's (dtype, feat, d, M): 32, or 16 where 32-row tiles would not fit
+ * a compute unit's LDS.  0 if the descriptor is invalid.  Host-only. */
+int64_t slim_tile_rows(const slim_desc *desc);
+
 /* Feature map (Subsection 2.1): phi[r][m] = g(X_r)_m in fp32 for the
  * B*H*L rows of X ([B][H][L][d], desc dtype).  FAVOR+: if row_offset is
  * non-NULL, row r is scaled by exp(-row_offset[r]) with

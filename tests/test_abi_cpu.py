@@ -119,3 +119,15 @@ def test_auto_window(lib):
     assert lib.slim_window_chunks(ctypes.byref(d)) == 32
     d = d_(B=1, H=8, L=1 << 20, d=64, M=64, num_chunks=2048)
     assert lib.slim_window_chunks(ctypes.byref(d)) == 512
+
+
+def test_tile_rows(lib):
+    def tr(**kw):
+        return lib.slim_tile_rows(ctypes.byref(d_(**kw)))
+    assert tr(d=64, M=256) == 32                                   # bf16 FAVOR+ d=64 M=256
+    assert tr(d=128, M=128, feat=_lib.SLIM_FEAT_ELU1) == 32
+    assert tr(d=64, M=256, dtype=_lib.SLIM_F32) == 32
+    assert tr(d=128, M=256) == 16                                  # 8 waves of d+4 fp32 reduction rows
+    assert tr(d=128, M=256, dtype=_lib.SLIM_F32) == 16
+    assert tr(d=16, M=16, dtype=_lib.SLIM_F32) == 32
+    assert tr(d=48) == 0                                           # invalid descriptor
