@@ -115,6 +115,27 @@ static void copy_or_zero(float *dst, const float *src, long long n, hipStream_t 
     hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, src, n);
 }
 
+// Fragment-packed W^T: for value block eb and feature block mb, lane i of a
+// wave reads 4 consecutive elements W[mb*16 + 4(i/16) + j][eb*16 + i%16] at
+// Wp[((eb*(M/16) + mb)*64 + i)*4 + j]  (elements of 2 or 4 bytes moved as integers).
+template <typename U> __global__ __launch_bounds__(256) void pack_wt_kernel(const U *W, U *Wp, int M, int D)
+{
+    const int o = blockIdx.x * 256 + threadIdx.x;
+    if (o >= M * D) return;
+    const int j = o & 3, i = (o >> 2) & 63, blk = o >> 8;
+    const int mb = blk % (M / 16), eb = blk / (M / 16);
+    Wp[o] = W[(size_t)(mb * 16 + 4 * (i / 16) + j) * D + eb * 16 + i % 16];
+}
+
+static void pack_wt(const void *W, void *Wp, int M, int D, bool bf16, hipStream_t s)
+{
+    const dim3 grid((unsigned)((M * D + 255) / 256));
+    if (bf16)
+        hipLaunchKernelGGL(pack_wt_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t *)W, (uint16_t *)Wp, M, D);
+    else
+        hipLaunchKernelGGL(pack_wt_kernel<uint32_t>, grid, dim3(256), 0, s, (const uint32_t *)W, (uint32_t *)Wp, M, D);
+}
+
 // scan_kernel lives in slim_kernels.h (instantiated here once).
 static void scan(int mode, float *slots, float *cR, float *cS, int D, int M, int P, int np, int BH, hipStream_t s)
 {
@@ -139,7 +160,7 @@ static const KernelTable *find(const slim_desc *d)
 
 struct Plan {
     long long BH, c, nchunks, P, SZ;
-    size_t slots_off, gslots_off, stats_off, cR_off, cS_off, gR_off, gS_off, total;
+    size_t slots_off, gslots_off, stats_off, cR_off, cS_off, gR_off, gS_off, wt_off, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -183,6 +204,10 @@ static Plan plan(const slim_desc *d, int pass)
         off = align256(off + (size_t)p.BH * d->d * d->M * 4);
         p.gS_off = off;
         off = align256(off + (size_t)p.BH * d->M * 4);
+        if (d->feat == SLIM_FEAT_FAVOR) {  // fragment-packed W^T (coalesced fragment loads)
+            p.wt_off = off;
+            off = align256(off + (size_t)d->d * d->M * (d->dtype == SLIM_BF16 ? 2 : 4));
+        }
     }
     p.total = pass == SLIM_PASS_FEATMAP ? 0 : off;
     return p;
@@ -370,6 +395,10 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
     a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
     float *cR = (float *)(base + p.cR_off), *cS = (float *)(base + p.cS_off);
     float *gR = (float *)(base + p.gR_off), *gS = (float *)(base + p.gS_off);
+    if (d->feat == SLIM_FEAT_FAVOR) {
+        a.Wt = base + p.wt_off;
+        pack_wt(W, base + p.wt_off, M, D, d->dtype == SLIM_BF16, s);
+    }
     copy_or_zero(cR, R_out, p.BH * D * M, s);
     copy_or_zero(cS, S_out, p.BH * M, s);
     copy_or_zero(gR, dR_out, p.BH * D * M, s);

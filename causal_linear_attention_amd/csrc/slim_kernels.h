@@ -50,6 +50,7 @@ namespace slim {
 
 struct ChunkArgs {
     const void *Q, *K, *V, *W, *dY;
+    const void *Wt;            // W^T fragments, packed (backward, FAVOR+)
     void *out0, *out1, *out2;  // fwd: Y | bwdq: dQ | bwdkv: dK, dV
     float *slots;              // [BH][P+1][(D+1)*M]  state slots (R rows, then S)
     float *gslots;             // [BH][P+1][(D+1)*M]  gradient-state slots
@@ -158,18 +159,19 @@ __device__ __forceinline__ void load_wtfrag(Frag<typename C::T> (&wt)[NE][C::NFB
         }
 }
 
-// One value block eb of the W^T fragments above.
+// One value block eb (< NEB) of the W^T fragments above, from the fragment-packed
+// copy Wp of W: for feature block mb (16 features) and value block eb, the 64
+// lanes' fragments lie in one contiguous 512-byte run, lane i holding
+// W[mb*16 + 4(i/16) + j][eb*16 + i%16], j = 0..3.
 template <class C>
-__device__ __forceinline__ void load_wtfrag_block(Frag<typename C::T> (&wt)[C::NFB], const void *Wv, int eb)
+__device__ __forceinline__ void load_wtfrag_block(Frag<typename C::T> (&wt)[C::NFB], const void *Wpv, int eb)
 {
     typedef typename C::T T;
-    const T *W = (const T *)Wv;
-    const int w = wave_id();
+    const T *Wp = (const T *)Wpv;
+    const int mb0 = wave_id() * (C::MW / 16);
 #pragma unroll
     for (int fb = 0; fb < C::NFB; ++fb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            wt[fb].v[j] = W[(size_t)(w * C::MW + fb * 16 + 4 * lgrp() + j) * C::D + eb * 16 + lcol()];
+        wt[fb] = *reinterpret_cast<const Frag<T> *>(Wp + (((size_t)eb * (C::M / 16) + mb0 + fb) * 64 + threadIdx.x % 64) * 4);
 }
 
 // Feature blocks in "transposed" orientation: ph[fb][tb] has rows m = w*MW + fb*16 + 4g + j

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
 #pragma unroll
             for (int eb = 0; eb < NEB; ++eb) {
                 Frag<T> wt[NFB];
-                load_wtfrag_block<C>(wt, a.W, eb);
+                load_wtfrag_block<C>(wt, a.Wt, eb);
 #pragma unroll
                 for (int tb = 0; tb < NTB; ++tb) {
                     f4 acc = f4zero();
