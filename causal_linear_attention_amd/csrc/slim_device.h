@@ -154,32 +154,33 @@ __device__ __forceinline__ void store16(__bf16 *p, bf8 x)
     reinterpret_cast<bf4 *>(p)[1] = bf4{x[4], x[5], x[6], x[7]};
 }
 
-// Row-major matrix in LDS, ROWS x COLS of the operand type T (COLS a multiple of 16).
+// Matrix in LDS, ROWS x COLS of the operand type T (COLS a multiple of 16).
 // Operand fragments can contract over either index:
 //   frag_c(n0, k0): free index = row n0 + i%16, contraction = columns k0 + 4g..+3;
 //   frag_r(n0, k0): free index = column n0 + i%16, contraction = rows k0 + 4g..+3.
-// bf16: rows are packed and the 8-byte chunk q of row r is stored at chunk
-// q ^ swz(r), swz(r) = ((r&3)<<2 | (r>>2)&3) mod (COLS/4), which keeps both read
-// patterns free of bank conflicts; frag_r is one ds_read_b64_tr_b16 (within each
-// 16-lane group, lane i receives element i%4 of the chunks addressed by lanes
-// i/4, 4+i/4, 8+i/4, 12+i/4, so lane L points at row k0+4g+L/4, column
-// n0+4(L%4)).  fp32: rows padded by 4 elements, frag_r is four 4-byte reads.
+// bf16: column-blocked -- each 16-column block is its own ROWS x 16 array (32-byte
+// rows), and within a row the 8-byte chunk q (0..3) is stored at q ^ ((r>>2)&3).
+// Both read patterns (16 lanes over 16 rows of one chunk; 16 lanes over 4 rows x
+// 4 chunks) then touch every bank once, and the address of a block at row or
+// column offset n0, k0 (multiples of 16) is a fixed offset from the lane's base
+// address, so one address register serves every block.  frag_r is one
+// ds_read_b64_tr_b16 (within each 16-lane group, lane i receives element i%4 of
+// the chunks addressed by lanes i/4, 4+i/4, 8+i/4, 12+i/4, so lane L points at
+// row k0+4g+L/4, column n0+4(L%4)).  fp32: row-major with rows padded by 4
+// elements, frag_r is four 4-byte reads.
 template <typename T, int ROWS, int COLS> struct LMat {
     static constexpr bool BF = sizeof(T) == 2;
     static constexpr int LD = BF ? COLS : COLS + 4;
-    static constexpr int NCH = COLS / 4;
     static constexpr int SIZE = ROWS * LD;
-    static_assert(COLS % 16 == 0 && (NCH & (NCH - 1)) == 0, "columns: power-of-two multiple of 16");
+    static_assert(COLS % 16 == 0, "columns: a multiple of 16");
     T *p;
     __device__ __forceinline__ explicit LMat(T *base) : p(base) {}
     __device__ static __forceinline__ int off(int r, int c)  // c % 4 == 0
     {
-        if constexpr (BF) {
-            const int f = (((r & 3) << 2) | ((r >> 2) & 3)) & (NCH - 1);
-            return r * COLS + ((((c >> 2) ^ f)) << 2);
-        } else {
+        if constexpr (BF)
+            return (c >> 4) * (ROWS * 16) + r * 16 + ((((c >> 2) & 3) ^ ((r >> 2) & 3)) << 2);
+        else
             return r * LD + c;
-        }
     }
     // four consecutive columns c..c+3 of row r
     __device__ __forceinline__ void put4(int r, int c, f4 v) const

@@ -338,13 +338,14 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
 // bwdkv_kernel: dK and dV of one chunk.  Tiles in reverse order, carrying the
 // gradient w.r.t. the state after the tile, [dR; dS] (rows e, cols m), which
 // starts from gslot[n+1].  The dV product also needs dR with the features as the
-// contraction index: a copy of this wave's dR block goes to LDS each tile and is
-// read back transposed (if the copies of all waves fit in 64 KB of LDS;
-// otherwise a second fp32 orientation is carried in registers).
+// contraction index: each tile a bf16 copy of this wave's dR block goes to the
+// wave's own fp32 reduction rows (idle until the dV partials are written, which
+// happens only after the last read of the copy) and is read back transposed; if
+// it does not fit there, a second fp32 orientation is carried in registers.
 template <class C> struct BwdkvSmem {
     typedef typename C::T T;
     typedef LMat<T, C::MW, C::D> DrMat;  // rows m, cols e
-    static constexpr bool DR_LDS = (size_t)C::NW * DrMat::SIZE * sizeof(T) <= 64 * 1024;
+    static constexpr bool DR_IN_RED = DrMat::SIZE * sizeof(T) <= (size_t)C::TT * C::LDR * sizeof(float);
     __align__(16) T xq[C::XMat::SIZE];
     __align__(16) T xk[C::XMat::SIZE];
     __align__(16) T xv[C::XMat::SIZE];
@@ -352,7 +353,6 @@ template <class C> struct BwdkvSmem {
     __align__(16) T dn[C::XMat::SIZE];
     __align__(16) T dna[C::AuxMat::SIZE];
     __align__(16) T fq[C::NW * C::FMat::SIZE];
-    __align__(16) T dr[DR_LDS ? C::NW * DrMat::SIZE : 8];
     __align__(16) float red[C::NW * C::TT * C::LDR];
     float kn2[C::TT], qmax[C::NW * C::TT];
 };
@@ -362,30 +362,24 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
     typedef typename C::T T;
     constexpr int NFB = C::NFB, NEB = C::NEB, NEA = C::NEA, NTB = C::NTB, TT = C::TT, D = C::D, MW = C::MW;
     typedef typename BwdkvSmem<C>::DrMat DrMat;
-    constexpr bool DR_LDS = BwdkvSmem<C>::DR_LDS;
-    constexpr int NEW = C::FAVOR ? NEA : 1;  // W^T blocks (the auxiliary one gives the row sum)
+    constexpr bool DRL = BwdkvSmem<C>::DR_IN_RED;
     __shared__ BwdkvSmem<C> sm;
     float *red = sm.red, *kn2 = sm.kn2, *qmax = sm.qmax;
     const typename C::XMat xq(sm.xq), xk(sm.xk);
     const AugTile<C> Vt(sm.xv, sm.xva), DN(sm.dn, sm.dna);
     const typename C::FMat Fq(sm.fq + wave_id() * C::FMat::SIZE);
-    const DrMat Dr(sm.dr + (DR_LDS ? wave_id() * DrMat::SIZE : 0));
+    const DrMat Dr(reinterpret_cast<T *>(red + (size_t)wave_id() * TT * C::LDR));
     const ChunkGeom G = chunk_geom<C>(a);
     const int w = wave_id(), g = lgrp(), lc = lcol();
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     const T *dY = (const T *)a.dY + G.hb;
     T *dK = (T *)a.out1 + G.hb, *dV = (T *)a.out2 + G.hb;
     const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * 2;
-    Frag<T> wf[NFB][NEB], wt[NEW][NFB];
-    if constexpr (C::FAVOR) {
-        load_wfrag<C>(wf, a.W);
-        load_wtfrag<C, NEW>(wt, a.W);
-    }
     const float *gsl = slot_ptr<C>(a.gslots, a, G.bh, G.nl + 1);
-    f4 dr[NEA][NFB];                             // [dR; dS], rows e, cols m
-    f4 drt[DR_LDS ? 1 : NFB][DR_LDS ? 1 : NEB];  // dR^T (rows m, cols e) when not staged in LDS
+    f4 dr[NEA][NFB];                       // [dR; dS], rows e, cols m
+    f4 drt[DRL ? 1 : NFB][DRL ? 1 : NEB];  // dR^T (rows m, cols e) when not copied through LDS
     load_state_E<C>(dr, gsl);
-    if constexpr (!DR_LDS) {
+    if constexpr (!DRL) {
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
@@ -401,9 +395,11 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
         const int nv = min(TT, G.len - t0);
         rg.store(xq, xk, Vt, DN, kn2, nv);
         __syncthreads();
-        if (t0 > 0) rg.load(Q, K, V, dY, st, t0 - TT, G.len);
         Frag<T> fq[NFB][NTB], fkT[NFB][NTB];
         {
+            // W fragments are re-read (from cache) every tile rather than held over the loop
+            Frag<T> wf[NFB][NEB];
+            if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
             f4 pq[NFB][NTB];
             feat_T<C>(pq, xq, wf);
             if constexpr (C::FAVOR) q_partial_max<C>(pq, qmax);
@@ -411,18 +407,22 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
             q_finish_T<C>(pq, qmax);
             put_features<C>(Fq, pq);
             to_frags<C>(fq, pq);
-        }
-        {
             f4 pkT[NFB][NTB];
             feat_T<C>(pkT, xk, wf);
             k_finish_T<C>(pkT, kn2);
             to_frags<C>(fkT, pkT);
         }
-        if constexpr (DR_LDS) {
+        if constexpr (DRL) {
 #pragma unroll
             for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
                 for (int fb = 0; fb < NFB; ++fb) Dr.put_frag(fb * 16 + lc, eb * 16 + 4 * g, cfrag<T>(dr[eb][fb]));
+            // keep the compiler from holding these bf16 copies in registers until the dK
+            // products below (it would otherwise reuse them there)
+#pragma unroll
+            for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+                for (int fb = 0; fb < NFB; ++fb) asm volatile("" : "+v"(dr[eb][fb]));
         }
         // dV^T blocks (rows e, cols s): dNum^T P + dR g(K)^T, reduced across waves.
         {
@@ -439,7 +439,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                             if (lc > 4 * g + j) acc[j] = 0.f;
                     fp[tb][sb] = cfrag<T>(acc);
                 }
-            if constexpr (DR_LDS) wave_lds_fence();  // Dr written by this wave above
+            if constexpr (DRL) wave_lds_fence();  // Dr written by this wave above
+            f4 dv[NEB][NTB];
 #pragma unroll
             for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
@@ -447,14 +448,20 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                     f4 acc = f4zero();
                     mma_range<T>(acc, sb, NTB, [&](int tb) { return DN.fr(eb, tb * 16); },
                                  [&](int tb) { return fp[tb][sb]; });
-                    if constexpr (DR_LDS)
+                    if constexpr (DRL)
                         mma_range<T>(acc, 0, NFB, [&](int fb) { return Dr.frag_r(eb * 16, fb * 16); },
                                      [&](int fb) { return fkT[fb][sb]; });
                     else
                         mma_range<T>(acc, 0, NFB, [&](int fb) { return cfrag<T>(drt[fb][eb]); },
                                      [&](int fb) { return fkT[fb][sb]; });
-                    put_red<C>(red, eb, sb, acc);
+                    dv[eb][sb] = acc;
                 }
+            // the partials overwrite this wave's dR copy: all its reads (of another type) first
+            if constexpr (DRL) wave_lds_fence();
+#pragma unroll
+            for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+                for (int sb = 0; sb < NTB; ++sb) put_red<C>(red, eb, sb, dv[eb][sb]);
         }
         __syncthreads();
         reduce_rows<C>(red, nv, [&](int s, int e, f4 v, bool ok) {
@@ -492,21 +499,33 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                 }
         }
         if constexpr (C::FAVOR) {
-            // [dK^T | rowsum] = [W | 1]^T (dg(K) . g(K))^T, reduced across waves;
-            // dK = (dg(K) . g(K)) W - K * rowsum.
+            // dK^T = W^T (dg(K) . g(K))^T and the row sums of dg(K) . g(K), reduced across
+            // waves (the sums in column D of the reduction rows); dK = that - K * rowsum.
             Frag<T> gk[NFB][NTB];
 #pragma unroll
-            for (int fb = 0; fb < NFB; ++fb)
+            for (int sb = 0; sb < NTB; ++sb) {
+                float rsum = 0.f;
 #pragma unroll
-                for (int sb = 0; sb < NTB; ++sb) gk[fb][sb] = cfrag<T>(dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]));
-#pragma unroll
-            for (int eb = 0; eb < NEA; ++eb)
+                for (int fb = 0; fb < NFB; ++fb) {
+                    const f4 v = dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]);
+                    rsum += (v[0] + v[1]) + (v[2] + v[3]);
+                    gk[fb][sb] = cfrag<T>(v);
+                }
+                rsum += __shfl_xor(rsum, 16, 64);
+                rsum += __shfl_xor(rsum, 32, 64);
+                if (g == 0) red[(w * TT + sb * 16 + lc) * C::LDR + D] = rsum;
+            }
+#pragma unroll 1
+            for (int eb = 0; eb < NEB; ++eb) {  // one W^T block at a time
+                Frag<T> wt[NFB];
+                load_wtfrag_block<C>(wt, a.Wt, eb);
 #pragma unroll
                 for (int sb = 0; sb < NTB; ++sb) {
                     f4 acc = f4zero();
-                    mma_range<T>(acc, 0, NFB, [&](int fb) { return wt[eb][fb]; }, [&](int fb) { return gk[fb][sb]; });
+                    mma_range<T>(acc, 0, NFB, [&](int fb) { return wt[fb]; }, [&](int fb) { return gk[fb][sb]; });
                     put_red<C>(red, eb, sb, acc);
                 }
+            }
             __syncthreads();
             reduce_rows<C>(red, nv, [&](int s, int e, f4 v, bool ok) {
                 if (ok) store4<T>(dK + (size_t)(t0 + s) * D + e, v - xk.get4(s, e) * reduce_col<C>(red, s));
@@ -524,6 +543,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                     if (s < nv) store4<T>(dK + (size_t)(t0 + s) * D + w * MW + fb * 16 + 4 * g, v);
                 }
         }
+        // next tile's inputs, fetched during the state update and the barriers
+        if (t0 > 0) rg.load(Q, K, V, dY, st, t0 - TT, G.len);
         // gradient state (after use): [dR; dS] += [dNum | dden]^T g(Q)
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb) {
@@ -531,7 +552,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
             for (int eb = 0; eb < NEA; ++eb)
                 mma_range<T>(dr[eb][fb], 0, NTB, [&](int tb) { return DN.fr(eb, tb * 16); },
                              [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); });
-            if constexpr (!DR_LDS) {
+            if constexpr (!DRL) {
 #pragma unroll
                 for (int eb = 0; eb < NEB; ++eb)
                     mma_range<T>(drt[fb][eb], 0, NTB, [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); },
