@@ -13,12 +13,22 @@ and the fp64 CPU oracle timed on a bounded sample of the same workload.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
   python bench.py --profile-run     # a few steps, for rocprofv3 runs
   python bench.py --copy-calib      # one plain copy kernel of known size (PMC calibration)
+  python bench.py --pmc-summary DIR # (host only) HBM traffic per kernel from rocprofv3 counter CSVs
+
+roofline.traffic: HBM bytes per launch of the dominant kernel, FETCH_SIZE and
+WRITE_SIZE scaled by what the same counters read for a plain copy of known
+size; taken from profiles/traffic_<workload>.md when that summary was made
+from the kernel sources as they are now (hash match), else null.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -40,7 +50,79 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU oracle sample (0 = H)")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--pmc-summary", default=None, metavar="DIR",
+                    help="DIR holds rocprofv3 counter runs F, W (FETCH_SIZE, WRITE_SIZE of --profile-run) "
+                         "and CF, CW (the same of --copy-calib); writes profiles/traffic_<workload>.md")
     return ap.parse_args()
+
+
+def kernel_source_hash():
+    """sha256 of the kernel sources and the C-ABI header (what the traffic figures depend on)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "causal_linear_attention_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "slim.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_kernel(name):
+    m = re.match(r"void slim::scan_kernel<(\d)>", name)
+    if m:
+        return ("scan_prefix", "scan_reverse", "scan_grad")[int(m.group(1))]
+    m = re.match(r"void slim::(\w+?)_kernel<", name) or re.match(r"_ZN4slim\d+(\w+?)_kernel", name)
+    if m:
+        return m.group(1)
+    if "copyBuffer" in name:
+        return "copy"
+    return None
+
+
+def read_counter(path, counter):
+    """Per short kernel name: list of per-dispatch values of `counter` (KiB)."""
+    out = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            k = short_kernel(r["Kernel_Name"])
+            if k:
+                out.setdefault(k, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def pmc_summary(d, w, bytes_of_copy):
+    fetch = read_counter(glob.glob(os.path.join(d, "F", "*counter_collection.csv"))[0], "FETCH_SIZE")
+    write = read_counter(glob.glob(os.path.join(d, "W", "*counter_collection.csv"))[0], "WRITE_SIZE")
+    cf = read_counter(glob.glob(os.path.join(d, "CF", "*counter_collection.csv"))[0], "FETCH_SIZE")["copy"]
+    cw = read_counter(glob.glob(os.path.join(d, "CW", "*counter_collection.csv"))[0], "WRITE_SIZE")["copy"]
+    # the calibration copy reads and writes bytes_of_copy per launch
+    f_fac = bytes_of_copy / (sum(cf) / len(cf) * 1024)
+    w_fac = bytes_of_copy / (sum(cw) / len(cw) * 1024)
+    rows = {}
+    for k in sorted(set(fetch) & set(write)):
+        fb = sum(fetch[k]) / len(fetch[k]) * 1024 * f_fac
+        wb = sum(write[k]) / len(write[k]) * 1024 * w_fac
+        rows[k] = {"dispatches": len(fetch[k]), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                   "traffic_bytes": round(fb + wb)}
+    return {"workload": w.name, "source_hash": kernel_source_hash(), "fetch_factor": round(f_fac, 4),
+            "write_factor": round(w_fac, 4), "kernels": rows}
+
+
+def load_traffic(w, kernel):
+    """HBM bytes per launch of `kernel` from the committed summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_hash") != kernel_source_hash() or kernel not in rec.get("kernels", {}):
+        return None
+    return rec["kernels"][kernel]["traffic_bytes"]
 
 
 def make_inputs(w, torch, synth):
@@ -94,6 +176,47 @@ def cpu_baseline(w, synth, heads):
             "seconds": dt}
 
 
+def kernel_records(w, prof, steps, tile):
+    """Per-kernel records from the library's hipEvent timings {name: (ms total, launches)}
+    over `steps` steps, and the roofline record of the dominant kernel."""
+    from causal_linear_attention_amd.workloads import kernel_bytes, kernel_flops
+    fl = kernel_flops(w, tile)
+    by = kernel_bytes(w)
+    passes = {"state": 2 if w.backward else 1}
+    peak_t = PEAK_TFLOPS[w.dtype]
+    kernels = {}
+    for name, (ms, n) in prof.items():
+        rec = {"ms_total": round(ms, 4), "launches": n, "ms_avg": round(ms / n, 5),
+               "ms_per_step": round(ms / steps, 5)}
+        units = w.head_tokens * passes.get(name, 1) * steps / n  # token-heads per launch
+        if name in fl:
+            rec["flop_per_launch"] = fl[name] * units
+            rec["tflops"] = round(rec["flop_per_launch"] / (rec["ms_avg"] * 1e-3) / 1e12, 2)
+        if name in by:
+            rec["bytes_per_launch"] = by[name] * units
+            rec["gbs"] = round(rec["bytes_per_launch"] / (rec["ms_avg"] * 1e-3) / 1e9, 1)
+        kernels[name] = rec
+    # dominant kernel: most time in the timed region; its roof is whichever of the MFMA
+    # peak (its flops) and the HBM peak (its algorithmic bytes) takes longer
+    dom = max(kernels, key=lambda k2: kernels[k2]["ms_total"])
+    d = kernels[dom]
+    t_mfma = d.get("flop_per_launch", 0.0) / (peak_t * 1e12)
+    t_hbm = d.get("bytes_per_launch", 0.0) / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        achieved = d["flop_per_launch"] / (d["ms_avg"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_t, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak_t, 4)}
+    else:
+        achieved = d["bytes_per_launch"] / (d["ms_avg"] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roofline.update({"traffic": load_traffic(w, dom), "kernel": dom, "ms_avg": d["ms_avg"],
+                     "flop_per_launch": d.get("flop_per_launch"), "bytes_per_launch": d.get("bytes_per_launch"),
+                     "mfma_frac": round(t_mfma / (d["ms_avg"] * 1e-3), 4),
+                     "hbm_frac": round(t_hbm / (d["ms_avg"] * 1e-3), 4)})
+    return kernels, roofline
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -106,7 +229,7 @@ def main():
     from causal_linear_attention_amd import _lib
     from causal_linear_attention_amd import attention as A
     from causal_linear_attention_amd import synth
-    from causal_linear_attention_amd.workloads import HEADLINE, WORKLOADS, kernel_flops, survey_flops
+    from causal_linear_attention_amd.workloads import HEADLINE, WORKLOADS, kernel_bytes, kernel_flops, survey_flops
 
     if args.copy_calib:
         # plain device-to-device copy of 1 GiB (reads 1 GiB, writes 1 GiB): the
@@ -121,6 +244,10 @@ def main():
         return
 
     w = WORKLOADS[args.workload or HEADLINE]
+    if args.pmc_summary:
+        rec = pmc_summary(args.pmc_summary, w, 1 << 30)
+        print(json.dumps(rec))
+        return
     q, k, v, W, dy = make_inputs(w, torch, synth)
     tile = int(_lib.lib().slim_tile_rows(__import__("ctypes").byref(A.make_desc(q, w.M, w.feat, w.chunks))))
     torch.cuda.synchronize()
@@ -163,25 +290,9 @@ def main():
 
     ms_step = 1e3 * elapsed / args.steps
     tokens_per_s = w.tokens * args.steps / elapsed
+    kernels, roofline = kernel_records(w, prof, args.steps, tile)
     fl = kernel_flops(w, tile)
     passes = {"state": 2 if w.backward else 1}
-    kernels = {}
-    for name, (ms, n) in prof.items():
-        rec = {"ms_total": round(ms, 4), "launches": n, "ms_avg": round(ms / n, 5),
-               "ms_per_step": round(ms / args.steps, 5)}
-        if name in fl:
-            flop = fl[name] * w.head_tokens * passes.get(name, 1) * args.steps
-            rec["tflops"] = round(flop / (ms * 1e-3) / 1e12, 2)
-            rec["flop_per_launch"] = flop / n
-        kernels[name] = rec
-    mfma = {k2: v2 for k2, v2 in kernels.items() if "tflops" in v2}
-    dom = max(mfma, key=lambda k2: mfma[k2]["ms_total"])
-    d = kernels[dom]
-    achieved = d["flop_per_launch"] / (d["ms_avg"] * 1e-3) / 1e12
-    peak_t = PEAK_TFLOPS[w.dtype]
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak_t,
-                "unit": "TFLOP/s", "frac": round(achieved / peak_t, 4), "traffic": None,
-                "flop_per_launch": d["flop_per_launch"], "ms_avg": d["ms_avg"]}
     isz = 2 if w.dtype == "bf16" else 4
     # minimum HBM traffic of a step: read Q K V (fwd) and Q K V dY (bwd), write Y dQ dK dV
     io = w.head_tokens * w.d * isz * (11 if w.backward else 4)
