@@ -255,7 +255,7 @@ def main():
     def step():
         Y, R, S = A.attn_fwd(q, k, v, W, w.feat, w.chunks)
         if w.backward:
-            A.attn_bwd(q, k, v, W, dy, R, S, w.feat, w.chunks)
+            A.attn_bwd(q, k, v, W, dy, w.feat, w.chunks)
         return Y
 
     if args.profile_run:

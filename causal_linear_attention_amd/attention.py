@@ -97,16 +97,18 @@ def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, 
     return Y, R, S
 
 
-def attn_bwd(q, k, v, W, dY, R_out, S_out, feat="favor", num_chunks=1, dR_out=None, dS_out=None,
+def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, dR_out=None, dS_out=None,
              want_state_grad=False, window_chunks=0):
-    """Backward.  Returns (dQ, dK, dV, dR_in, dS_in); the last two are None
-    unless want_state_grad."""
+    """Backward of attn_fwd(q, k, v, W, feat, num_chunks, R_in, S_in) for the
+    loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out>.  Returns (dQ, dK, dV,
+    dR_in, dS_in); the last two are None unless want_state_grad."""
     B, H, L, d = q.shape
     M = _feat_M(W, feat, d)
     for n, t in (("q", q), ("k", k), ("v", v), ("dY", dY)):
         _check_io(n, t, q.dtype, q.shape)
-    _check_io("R_out", R_out, torch.float32, (B, H, d, M))
-    _check_io("S_out", S_out, torch.float32, (B, H, M))
+    if R_in is not None:
+        _check_io("R_in", R_in, torch.float32, (B, H, d, M))
+        _check_io("S_in", S_in, torch.float32, (B, H, M))
     if dR_out is not None:
         _check_io("dR_out", dR_out, torch.float32, (B, H, d, M))
         _check_io("dS_out", dS_out, torch.float32, (B, H, M))
@@ -118,7 +120,7 @@ def attn_bwd(q, k, v, W, dY, R_out, S_out, feat="favor", num_chunks=1, dR_out=No
         dR = torch.empty((B, H, d, M), dtype=torch.float32, device=q.device)
         dS = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
     _lib.check(_lib.lib().slim_attn_bwd(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(dY),
-                                        _ptr(R_out), _ptr(S_out), _ptr(dR_out), _ptr(dS_out), _ptr(dQ), _ptr(dK),
+                                        _ptr(R_in), _ptr(S_in), _ptr(dR_out), _ptr(dS_out), _ptr(dQ), _ptr(dK),
                                         _ptr(dV), _ptr(dR), _ptr(dS), _ptr(ws), ws.numel(), _stream()),
                "slim_attn_bwd")
     return dQ, dK, dV, dR, dS
@@ -127,17 +129,17 @@ def attn_bwd(q, k, v, W, dY, R_out, S_out, feat="favor", num_chunks=1, dR_out=No
 class _SlimAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, W, feat, num_chunks, window_chunks):
-        Y, R, S = attn_fwd(q, k, v, W, feat, num_chunks, window_chunks=window_chunks)
-        # Only the inputs and the final state are kept for the backward (the
-        # reverse walk recovers every slice's entry state from R, S).
-        ctx.save_for_backward(q, k, v, W if W is not None else torch.empty(0), R, S)
+        Y, _, _ = attn_fwd(q, k, v, W, feat, num_chunks, window_chunks=window_chunks)
+        # Only the inputs are kept for the backward, which recomputes every
+        # slice's forward (no per-slice state is stored).
+        ctx.save_for_backward(q, k, v, W if W is not None else torch.empty(0))
         ctx.feat, ctx.num_chunks, ctx.window_chunks, ctx.has_w = feat, num_chunks, window_chunks, W is not None
         return Y
 
     @staticmethod
     def backward(ctx, dY):
-        q, k, v, W, R, S = ctx.saved_tensors
-        dQ, dK, dV, _, _ = attn_bwd(q, k, v, W if ctx.has_w else None, dY.contiguous(), R, S, ctx.feat,
+        q, k, v, W = ctx.saved_tensors
+        dQ, dK, dV, _, _ = attn_bwd(q, k, v, W if ctx.has_w else None, dY.contiguous(), ctx.feat,
                                     ctx.num_chunks, window_chunks=ctx.window_chunks)
         return dQ, dK, dV, None, None, None, None
 

@@ -6,10 +6,14 @@
 //   forward  (Subsection 3.2): for each window of P slices in order:
 //       state -> forward prefix scan (carry = running final state) -> fwd
 //   backward (Subsection 3.3): for each window in reverse order:
-//       state -> reverse scan (entry states by subtraction from the carry,
-//       update (19)) -> stats (recompute forward, per-row statistics) -> dQ
+//       state -> entry states (one window: forward prefix from the initial
+//       state; several: the window's start state recovered from the state
+//       after it by subtraction, update (19) at window granularity, then a
+//       forward prefix) -> stats (recompute forward, per-row statistics) -> dQ
 //       -> gstate (the slice's gradient w.r.t. its entry state) -> gradient
-//       suffix scan (update (20)) -> dK, dV
+//       suffix scan (update (20)) -> dK, dV.  With several windows, a forward
+//       sweep over all chunk contributions first rebuilds the final state.
+// All carries are fp64.
 // Only the carries (d x M + M per head) live across windows, so the workspace
 // is bounded by the window, not by L.
 #include <hip/hip_runtime.h>
@@ -115,6 +119,26 @@ static void copy_or_zero(float *dst, const float *src, long long n, hipStream_t 
     hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, src, n);
 }
 
+// fp64 carries: loaded from an fp32 state (or zero), stored back rounded to fp32.
+__global__ __launch_bounds__(256) void widen_kernel(double *dst, const float *src, long long n)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] = src ? (double)src[i] : 0.0;
+}
+__global__ __launch_bounds__(256) void narrow_kernel(float *dst, const double *src, long long n)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] = (float)src[i];
+}
+static void widen(double *dst, const float *src, long long n, hipStream_t s)
+{
+    if (n > 0) hipLaunchKernelGGL(widen_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, src, n);
+}
+static void narrow(float *dst, const double *src, long long n, hipStream_t s)
+{
+    if (n > 0) hipLaunchKernelGGL(narrow_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, src, n);
+}
+
 // Fragment-packed W^T: for value block eb and feature block mb, lane i of a
 // wave reads 4 consecutive elements W[mb*16 + 4(i/16) + j][eb*16 + i%16] at
 // Wp[((eb*(M/16) + mb)*64 + i)*4 + j]  (elements of 2 or 4 bytes moved as integers).
@@ -137,17 +161,20 @@ static void pack_wt(const void *W, void *Wp, int M, int D, bool bf16, hipStream_
 }
 
 // scan_kernel lives in slim_kernels.h (instantiated here once).
-static void scan(int mode, float *slots, float *cR, float *cS, int D, int M, int P, int np, int BH, hipStream_t s)
+static void scan(int mode, float *slots, double *cR, double *cS, int D, int M, int P, int np, int BH, hipStream_t s)
 {
     const int SZ = (D + 1) * M;
     dim3 grid((unsigned)((SZ / 4 + 255) / 256), (unsigned)BH);
-    prof::Scope ps(mode == 0 ? "scan_prefix" : mode == 1 ? "scan_reverse" : "scan_grad", s);
+    static const char *names[4] = {"scan_prefix", "scan_window", "scan_grad", "scan_sum"};
+    prof::Scope ps(names[mode], s);
     if (mode == 0)
         hipLaunchKernelGGL(scan_kernel<0>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np);
     else if (mode == 1)
         hipLaunchKernelGGL(scan_kernel<1>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np);
-    else
+    else if (mode == 2)
         hipLaunchKernelGGL(scan_kernel<2>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np);
+    else
+        hipLaunchKernelGGL(scan_kernel<3>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np);
 }
 
 static const KernelTable *find(const slim_desc *d)
@@ -191,19 +218,20 @@ static Plan plan(const slim_desc *d, int pass)
     size_t off = 0;
     p.slots_off = off;
     off = align256(off + slots);
+    // fp64 carries of the state (both passes) and of its gradient (backward)
+    p.cR_off = off;
+    off = align256(off + (size_t)p.BH * d->d * d->M * 8);
+    p.cS_off = off;
+    off = align256(off + (size_t)p.BH * d->M * 8);
     if (pass == SLIM_PASS_BWD) {
         p.gslots_off = off;
         off = align256(off + slots);
         p.stats_off = off;
         off = align256(off + (size_t)p.BH * p.P * p.c * 2 * 4);
-        p.cR_off = off;
-        off = align256(off + (size_t)p.BH * d->d * d->M * 4);
-        p.cS_off = off;
-        off = align256(off + (size_t)p.BH * d->M * 4);
         p.gR_off = off;
-        off = align256(off + (size_t)p.BH * d->d * d->M * 4);
+        off = align256(off + (size_t)p.BH * d->d * d->M * 8);
         p.gS_off = off;
-        off = align256(off + (size_t)p.BH * d->M * 4);
+        off = align256(off + (size_t)p.BH * d->M * 8);
         if (d->feat == SLIM_FEAT_FAVOR) {  // fragment-packed W^T (coalesced fragment loads)
             p.wt_off = off;
             off = align256(off + (size_t)d->d * d->M * (d->dtype == SLIM_BF16 ? 2 : 4));
@@ -350,32 +378,36 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
     a.Q = Q; a.K = K; a.V = V; a.W = W; a.out0 = Y;
     a.slots = (float *)(base + p.slots_off);
     a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
-    copy_or_zero(R_out, R_in, p.BH * D * M, s);
-    copy_or_zero(S_out, S_in, p.BH * M, s);
+    double *cR = (double *)(base + p.cR_off), *cS = (double *)(base + p.cS_off);
+    widen(cR, R_in, p.BH * D * M, s);
+    widen(cS, S_in, p.BH * M, s);
     for (long long n0 = 0; n0 < p.nchunks; n0 += p.P) {
         const int np = (int)(p.nchunks - n0 < p.P ? p.nchunks - n0 : p.P);
         a.n0 = (int)n0;
         SLIM_TIMED("state", s, kt->state(dim3(np, BH), s, a));
-        scan(0, a.slots, R_out, S_out, D, M, (int)p.P, np, BH, s);
+        scan(0, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
         SLIM_TIMED("fwd", s, kt->fwd(dim3(np, BH), s, a));
     }
+    narrow(R_out, cR, p.BH * D * M, s);
+    narrow(S_out, cS, p.BH * M, s);
     return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
 
 slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
-                          const void *dY, const float *R_out, const float *S_out, const float *dR_out,
+                          const void *dY, const float *R_in, const float *S_in, const float *dR_out,
                           const float *dS_out, void *dQ, void *dK, void *dV, float *dR_in, float *dS_in, void *ws,
                           size_t ws_bytes, void *stream)
 {
     slim_status st = slim_validate(d, SLIM_PASS_BWD);
     if (st != SLIM_OK) return st;
-    if (!Q || !K || !V || !dY || !R_out || !S_out || !dQ || !dK || !dV || !ws) return SLIM_ERR_NULL;
+    if (!Q || !K || !V || !dY || !dQ || !dK || !dV || !ws) return SLIM_ERR_NULL;
     if (d->feat == SLIM_FEAT_FAVOR && !W) return SLIM_ERR_NULL;
     if (d->feat == SLIM_FEAT_ELU1 && W) return SLIM_ERR_SHAPE;
+    if ((R_in == nullptr) != (S_in == nullptr)) return SLIM_ERR_NULL;
     if ((dR_out == nullptr) != (dS_out == nullptr)) return SLIM_ERR_NULL;
     if ((dR_in == nullptr) != (dS_in == nullptr)) return SLIM_ERR_NULL;
     if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(W, 16) || misaligned(dY, 16) ||
-        misaligned(R_out, 16) || misaligned(S_out, 16) || misaligned(dR_out, 16) || misaligned(dS_out, 16) ||
+        misaligned(R_in, 16) || misaligned(S_in, 16) || misaligned(dR_out, 16) || misaligned(dS_out, 16) ||
         misaligned(dQ, 16) || misaligned(dK, 16) || misaligned(dV, 16) || misaligned(dR_in, 16) ||
         misaligned(dS_in, 16) || misaligned(ws, 256))
         return SLIM_ERR_ALIGN;
@@ -393,23 +425,42 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
     a.gslots = (float *)(base + p.gslots_off);
     a.stats = (float *)(base + p.stats_off);
     a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
-    float *cR = (float *)(base + p.cR_off), *cS = (float *)(base + p.cS_off);
-    float *gR = (float *)(base + p.gR_off), *gS = (float *)(base + p.gS_off);
+    double *cR = (double *)(base + p.cR_off), *cS = (double *)(base + p.cS_off);
+    double *gR = (double *)(base + p.gR_off), *gS = (double *)(base + p.gS_off);
     if (d->feat == SLIM_FEAT_FAVOR) {
         a.Wt = base + p.wt_off;
         pack_wt(W, base + p.wt_off, M, D, d->dtype == SLIM_BF16, s);
     }
-    copy_or_zero(cR, R_out, p.BH * D * M, s);
-    copy_or_zero(cS, S_out, p.BH * M, s);
-    copy_or_zero(gR, dR_out, p.BH * D * M, s);
-    copy_or_zero(gS, dS_out, p.BH * M, s);
+    widen(cR, R_in, p.BH * D * M, s);
+    widen(cS, S_in, p.BH * M, s);
+    widen(gR, dR_out, p.BH * D * M, s);
+    widen(gS, dS_out, p.BH * M, s);
     const long long nwin = (p.nchunks + p.P - 1) / p.P;
-    for (long long wi = nwin - 1; wi >= 0; --wi) {
+    auto window = [&](long long wi) {
         const long long n0 = wi * p.P;
-        const int np = (int)(p.nchunks - n0 < p.P ? p.nchunks - n0 : p.P);
         a.n0 = (int)n0;
-        SLIM_TIMED("state", s, kt->state(dim3(np, BH), s, a));
-        scan(1, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
+        return (int)(p.nchunks - n0 < p.P ? p.nchunks - n0 : p.P);
+    };
+    if (nwin > 1) {
+        // Several windows: the reverse walk needs the state after the last one.  It is
+        // rebuilt here, in fp64, from the initial state and every chunk's contribution
+        // (the fp32 final state of the forward would carry its rounding into every
+        // entry state recovered from it by subtraction).
+        for (long long wi = 0; wi < nwin; ++wi) {
+            const int np = window(wi);
+            SLIM_TIMED("state", s, kt->state(dim3(np, BH), s, a));
+            scan(3, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
+        }
+    }
+    for (long long wi = nwin - 1; wi >= 0; --wi) {
+        const int np = window(wi);
+        if (nwin == 1) {  // entry states forward from the initial state
+            SLIM_TIMED("state", s, kt->state(dim3(np, BH), s, a));
+            scan(0, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
+        } else {  // window start = state after it minus its chunks; entry states forward from there
+            if (wi != nwin - 1) SLIM_TIMED("state", s, kt->state(dim3(np, BH), s, a));
+            scan(1, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
+        }
         SLIM_TIMED("stats", s, kt->stats(dim3(np, BH), s, a));
         SLIM_TIMED("bwdq", s, kt->bwdq(dim3(np, BH), s, a));
         SLIM_TIMED("gstate", s, kt->gstate(dim3(np, BH), s, a));
@@ -417,8 +468,8 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
         SLIM_TIMED("bwdkv", s, kt->bwdkv(dim3(np, BH), s, a));
     }
     if (dR_in) {
-        copy_or_zero(dR_in, gR, p.BH * D * M, s);
-        copy_or_zero(dS_in, gS, p.BH * M, s);
+        narrow(dR_in, gR, p.BH * D * M, s);
+        narrow(dS_in, gS, p.BH * M, s);
     }
     return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }

@@ -34,8 +34,9 @@
 // Kernels (all launched on a grid (chunks in window, B*H)):
 //   featmap_kernel : standalone g(X), optional per-row max offset.
 //   state_kernel   : dR_n = sum_{rows of chunk n} V g(K)^T, dS_n = sum g(K).
-//   scan_kernel    : per-head sequential sweep over the window's chunk states
-//                    (forward prefix, reverse subtraction, gradient suffix sum).
+//   scan_kernel    : per-head sequential sweep over the window's chunk states with
+//                    an fp64 carry (forward prefix, window start by subtraction,
+//                    gradient suffix sum, plain accumulation).
 //   fwd_kernel     : Y for a chunk from its entry state.
 //   stats_kernel   : backward pass 1: recompute the chunk forward, emit per-row
 //                    1/den and dden = -(dY.Y)/den.
@@ -549,17 +550,20 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StateSmem<C>), C::NW))
     store_state_T<C>(slot_ptr<C>(a.slots, a, G.bh, G.nl + 1), rt);
 }
 
-// scan_kernel: sweep the window's chunk slots of one head.  Each thread owns 4
-// consecutive floats of the (D+1)*M state.  carryR [BH][D*M], carryS [BH][M].
-//   MODE 0 (forward prefix):  slot[0] = carry; slot[n+1] = slot[n] + dR_n; carry = slot[np].
-//   MODE 1 (reverse subtract): carry holds the state after the window;
-//                              slot[n+1] = state after chunk n, slot[0] = carry = state
-//                              before the window (update (19) of the page).
-//   MODE 2 (gradient suffix):  carry holds the gradient after the window; slot[n+1] =
-//                              gradient w.r.t. the state after chunk n; slot[0] = carry =
-//                              gradient w.r.t. the state before the window.
+// scan_kernel: per-head sweep over the window's chunk slots (4 floats of the
+// (d+1) x M state per thread; carryR [BH][d*M], carryS [BH][M]), with the
+// running state ("carry") kept in fp64 so that no precision is lost across many
+// chunks or windows.  slot[0] = state entering the window's first chunk; slot[n+1]
+// holds chunk n's contribution on entry and, for modes 0-2, leaves with:
+//   MODE 0  forward prefix:   slot[n+1] = carry + sum_{n' <= n} contribution; carry = the last
+//   MODE 1  backward window:  start = carry - sum of the window's contributions (the
+//                             reversal of Subsection 3.3 at window granularity), then as
+//                             MODE 0 from start; carry = start
+//   MODE 2  gradient suffix:  slot[n+1] = carry + sum_{n' > n} contribution, slot[0] = all;
+//                             carry = slot[0]
+//   MODE 3  accumulate:       carry += sum of the window's contributions (slots untouched)
 template <int MODE>
-__global__ __launch_bounds__(256) void scan_kernel(float *slots, float *carryR, float *carryS, int DM, int M, int P,
+__global__ __launch_bounds__(256) void scan_kernel(float *slots, double *carryR, double *carryS, int DM, int M, int P,
                                                    int np)
 {
     const int SZ = DM + M;
@@ -567,25 +571,43 @@ __global__ __launch_bounds__(256) void scan_kernel(float *slots, float *carryR, 
     if (k >= SZ) return;
     const int bh = blockIdx.y;
     float *base = slots + (size_t)bh * (P + 1) * SZ + k;
-    float *cp = k < DM ? carryR + (size_t)bh * DM + k : carryS + (size_t)bh * M + (k - DM);
-    f4 cur = *reinterpret_cast<f4 *>(cp);
-    if (MODE == 0) {
-        *reinterpret_cast<f4 *>(base) = cur;
+    double *cp = k < DM ? carryR + (size_t)bh * DM + k : carryS + (size_t)bh * M + (k - DM);
+    double cur[4] = {cp[0], cp[1], cp[2], cp[3]};
+    auto slot = [&](int i) { return reinterpret_cast<f4 *>(base + (size_t)i * SZ); };
+    auto put = [&](int i, const double *v) { *slot(i) = f4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; };
+    if (MODE == 1 || MODE == 3) {
+        double tot[4] = {0.0, 0.0, 0.0, 0.0};
         for (int n = 0; n < np; ++n) {
-            f4 *p = reinterpret_cast<f4 *>(base + (size_t)(n + 1) * SZ);
-            cur += *p;
-            *p = cur;
+            const f4 dl = *slot(n + 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) tot[j] += (double)dl[j];
         }
-    } else {
-        for (int n = np - 1; n >= 0; --n) {
-            f4 *p = reinterpret_cast<f4 *>(base + (size_t)(n + 1) * SZ);
-            const f4 dlt = *p;
-            *p = cur;
-            if (MODE == 1) cur -= dlt; else cur += dlt;
-        }
-        *reinterpret_cast<f4 *>(base) = cur;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cur[j] = MODE == 1 ? cur[j] - tot[j] : cur[j] + tot[j];
     }
-    *reinterpret_cast<f4 *>(cp) = cur;
+    if (MODE == 0 || MODE == 1) {
+        double run[4] = {cur[0], cur[1], cur[2], cur[3]};
+        put(0, run);
+        for (int n = 0; n < np; ++n) {
+            const f4 dl = *slot(n + 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) run[j] += (double)dl[j];
+            put(n + 1, run);
+        }
+        if (MODE == 0)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cur[j] = run[j];
+    } else if (MODE == 2) {
+        for (int n = np - 1; n >= 0; --n) {
+            const f4 dl = *slot(n + 1);
+            put(n + 1, cur);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cur[j] += (double)dl[j];
+        }
+        put(0, cur);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cp[j] = cur[j];
 }
 
 // LDS of the chunk kernels that evaluate a chunk's forward.  RED: per-wave fp32

@@ -9,6 +9,11 @@ Every per-head block of a [B, H, L, d] tensor comes from its own stream,
 ``PCG64(SeedSequence([seed, tensor_id, b, h]))``, so any single head can be
 regenerated without drawing the rest (needed for the 1M-token workload).
 
+For inputs too large to draw on the host in reasonable time (the 1M-token
+workload), ``device_normal`` draws a whole [B, H, rows, cols] tensor from torch's
+seeded device generator; the tests then copy the sampled heads of that very
+tensor back for the oracle.
+
 The FAVOR+ projection W ([M, d], one row per random feature) is also drawn
 here: the feature map consumes it as an input.  Two draws are offered:
   * "gaussian":   iid N(0, 1) entries;
@@ -45,6 +50,19 @@ def normal(seed: int, tid: int, B: int, H: int, rows: int, cols: int, scale: flo
         for h in range(H):
             out[b, h] = head_normal(seed, tid, b, h, rows, cols, scale)
     return out
+
+
+def device_normal(seed: int, tid: int, shape, scale: float, device="cuda"):
+    """N(0, scale^2) float32 torch tensor of `shape` on `device`, from torch's
+    generator seeded with (seed, tid)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000003 + int(tid))
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    if scale != 1.0:
+        x.mul_(scale)
+    return x
 
 
 def positive(seed: int, tid: int, B: int, H: int, rows: int, cols: int, scale: float) -> np.ndarray:

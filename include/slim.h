@@ -109,23 +109,31 @@ slim_status slim_featmap(const slim_desc *desc, const void *X, const void *W, fl
 /* Forward (eq. (2) evaluated slice by slice, Subsection 3.2).
  * In : Q, K, V, W (NULL for elu+1); R_in, S_in = initial state (both NULL =
  *      zero, or both given).
- * Out: Y; R_out, S_out = final state R_L, S_L (required: the backward starts
- *      from it).  R_out/S_out may not alias R_in/S_in.
+ * Out: Y; R_out, S_out = final state R_L, S_L (required; R_out/S_out may not
+ *      alias R_in/S_in).
  * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_FWD). */
 slim_status slim_attn_fwd(const slim_desc *desc, const void *Q, const void *K, const void *V, const void *W,
                           const float *R_in, const float *S_in, void *Y, float *R_out, float *S_out, void *ws,
                           size_t ws_bytes, void *stream);
 
-/* Backward of the loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out>
- * (Subsection 3.3: reverse walk over slices, entry states recovered from the
- * final state R_out/S_out of the forward by subtraction).
- * In : Q, K, V, W as in the forward; dY; R_out, S_out from the forward;
+/* Backward of the loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out> of the
+ * forward above (Subsection 3.3: a reverse walk over the slices that recomputes
+ * each slice's forward and carries the gradient of the state).  Every slice's
+ * entry state is rebuilt from the initial state with fp64 carries: within a
+ * window by a forward prefix from the window's start state, which for a later
+ * window is the state after it minus its slices' contributions (update (19));
+ * when the sequence spans several windows, one extra sweep over all slices
+ * first rebuilds the final state.  The forward's fp32 final state is not used
+ * for this, since recovering small entry states from it by subtraction would
+ * carry its rounding into every one of them.
+ * In : Q, K, V, W as in the forward; dY; R_in, S_in = the forward's initial
+ *      state (both NULL = zero, or both given);
  *      dR_out, dS_out = incoming gradient of the final state (both NULL = zero).
  * Out: dQ, dK, dV; dR_in, dS_in = gradient w.r.t. the initial state (both NULL
  *      = not wanted, or both given).  dW is not computed.
  * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_BWD). */
 slim_status slim_attn_bwd(const slim_desc *desc, const void *Q, const void *K, const void *V, const void *W,
-                          const void *dY, const float *R_out, const float *S_out, const float *dR_out,
+                          const void *dY, const float *R_in, const float *S_in, const float *dR_out,
                           const float *dS_out, void *dQ, void *dK, void *dV, float *dR_in, float *dS_in, void *ws,
                           size_t ws_bytes, void *stream);
 
@@ -137,7 +145,8 @@ const char *slim_status_string(slim_status s);
  * slim_prof_enable(0) stops.  slim_prof_count() and slim_prof_entry() first
  * wait for the recorded events to complete (they synchronise with those
  * events), then report per kernel name ("state", "scan_prefix", "fwd",
- * "scan_reverse", "stats", "scan_grad", "bwdq", "bwdkv", "featmap") the summed
+ * "scan_window", "scan_sum", "stats", "bwdq", "gstate", "scan_grad", "bwdkv",
+ * "featmap") the summed
  * GPU time in milliseconds and the number of launches.  The name pointer stays
  * valid until the next slim_prof_enable(1).  Guarded by a process-wide mutex;
  * the timings are global to the process, not per stream. */

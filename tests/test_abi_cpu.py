@@ -86,6 +86,8 @@ def test_entry_points_reject_before_any_launch(lib):
                            p, 1 << 40, None) == 2
     # only one of the paired initial-state pointers
     assert lib.slim_attn_fwd(ctypes.byref(d), p, p, p, p, p, None, p, p, p, p, 1 << 40, None) == 1
+    assert lib.slim_attn_bwd(ctypes.byref(d), p, p, p, p, p, p, None, None, None, p, p, p, None, None,
+                           p, 1 << 40, None) == 1
     # elu+1 takes no W
     de = d_(feat=_lib.SLIM_FEAT_ELU1, M=64)
     assert lib.slim_attn_fwd(ctypes.byref(de), p, p, p, p, None, None, p, p, p, p, 1 << 40, None) == 2
