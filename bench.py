@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU oracle sample (0 = H)")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--mem-sweep", action="store_true",
+                    help="peak HBM of one fwd+bwd step vs L at the 1M-token workload's shape (one JSON line)")
     ap.add_argument("--pmc-summary", default=None, metavar="DIR",
                     help="DIR holds rocprofv3 counter runs F, W (FETCH_SIZE, WRITE_SIZE of --profile-run) "
                          "and CF, CW (the same of --copy-calib); writes profiles/traffic_<workload>.md")
@@ -176,6 +178,43 @@ def cpu_baseline(w, synth, heads):
             "seconds": dt}
 
 
+def mem_sweep(torch, A, synth, w):
+    """Peak HBM of one fwd+bwd step for L = 2^16 .. 2^20 at the shape of workload w
+    (B, H, d, M, slice length 512, automatic window).  Inputs (Q, K, V, dY, W) are
+    resident before the step; the step allocates the outputs Y, dQ, dK, dV (4 L d
+    bf16 per head), the workspaces and the final state.  'beyond_io' = peak step
+    allocation minus those outputs: what the sliced method itself needs."""
+    import ctypes
+    from causal_linear_attention_amd import _lib
+    rows = []
+    for lg in range(16, 21):
+        L = 1 << lg
+        shp = (w.B, w.H, L, w.d)
+        q = synth.device_normal(w.seed, synth.TID_Q, shp, w.qkv_scale).to(torch.bfloat16)
+        k = synth.device_normal(w.seed, synth.TID_K, shp, w.qkv_scale).to(torch.bfloat16)
+        v = synth.device_normal(w.seed, synth.TID_V, shp, 1.0).to(torch.bfloat16)
+        dy = synth.device_normal(w.seed, synth.TID_DY, shp, 1.0).to(torch.bfloat16)
+        W = torch.from_numpy(synth.projection(w.seed, w.M, w.d, w.w_kind)).to(torch.bfloat16).cuda()
+        chunks = L // 512
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        Y, R, S = A.attn_fwd(q, k, v, W, w.feat, chunks)
+        g = A.attn_bwd(q, k, v, W, dy, w.feat, chunks)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        dsc = A.make_desc(q, w.M, w.feat, chunks)
+        outs = 4 * q.numel() * 2
+        rows.append({"L": L, "chunks": chunks, "window_chunks": int(_lib.lib().slim_window_chunks(ctypes.byref(dsc))),
+                     "inputs_bytes": 4 * q.numel() * 2, "step_peak_bytes": peak, "outputs_bytes": outs,
+                     "beyond_io_bytes": peak - outs,
+                     "ws_fwd_bytes": int(A.workspace_bytes(dsc, _lib.SLIM_PASS_FWD)),
+                     "ws_bwd_bytes": int(A.workspace_bytes(dsc, _lib.SLIM_PASS_BWD))})
+        del q, k, v, dy, W, Y, R, S, g
+        torch.cuda.empty_cache()
+    return {"mem_sweep": w.name, "B": w.B, "H": w.H, "d": w.d, "M": w.M, "chunk_len": 512, "rows": rows}
+
+
 def kernel_records(w, prof, steps, tile):
     """Per-kernel records from the library's hipEvent timings {name: (ms total, launches)}
     over `steps` steps, and the roofline record of the dominant kernel."""
@@ -243,6 +282,9 @@ def main():
         print(json.dumps({"copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4, "launches": 3}))
         return
 
+    if args.mem_sweep:
+        print(json.dumps(mem_sweep(torch, A, synth, WORKLOADS["favor_bf16_L1048576_d64_M64"])))
+        return
     w = WORKLOADS[args.workload or HEADLINE]
     if args.pmc_summary:
         rec = pmc_summary(args.pmc_summary, w, 1 << 30)
