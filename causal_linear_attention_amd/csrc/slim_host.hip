@@ -164,17 +164,23 @@ static void pack_wt(const void *W, void *Wp, int M, int D, bool bf16, hipStream_
 static void scan(int mode, float *slots, double *cR, double *cS, int D, int M, int P, int np, int BH, hipStream_t s)
 {
     const int SZ = (D + 1) * M;
-    dim3 grid((unsigned)((SZ / 4 + 255) / 256), (unsigned)BH);
+    const long long elems = (long long)(SZ / 4) * BH;
+    // segments of the chunk range: enough workgroups to fill the chip (about 1024),
+    // at least 4 chunks per segment, at most 32 segments
+    int G = 1;
+    while (G < 32 && elems * G < 1024LL * 256 && np >= 8 * G) G *= 2;
+    const int E = 256 / G;
+    dim3 grid((unsigned)((SZ / 4 + E - 1) / E), (unsigned)BH);
     static const char *names[4] = {"scan_prefix", "scan_window", "scan_grad", "scan_sum"};
     prof::Scope ps(names[mode], s);
     if (mode == 0)
-        hipLaunchKernelGGL(scan_kernel<0>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np);
+        hipLaunchKernelGGL(scan_kernel<0>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np, G);
     else if (mode == 1)
-        hipLaunchKernelGGL(scan_kernel<1>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np);
+        hipLaunchKernelGGL(scan_kernel<1>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np, G);
     else if (mode == 2)
-        hipLaunchKernelGGL(scan_kernel<2>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np);
+        hipLaunchKernelGGL(scan_kernel<2>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np, G);
     else
-        hipLaunchKernelGGL(scan_kernel<3>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np);
+        hipLaunchKernelGGL(scan_kernel<3>, grid, dim3(256), 0, s, slots, cR, cS, D * M, M, P, np, G);
 }
 
 static const KernelTable *find(const slim_desc *d)

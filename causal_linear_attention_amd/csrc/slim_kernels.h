@@ -551,7 +551,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StateSmem<C>), C::NW))
 }
 
 // scan_kernel: per-head sweep over the window's chunk slots (4 floats of the
-// (d+1) x M state per thread; carryR [BH][d*M], carryS [BH][M]), with the
+// (d+1) x M state per element; carryR [BH][d*M], carryS [BH][M]), with the
 // running state ("carry") kept in fp64 so that no precision is lost across many
 // chunks or windows.  slot[0] = state entering the window's first chunk; slot[n+1]
 // holds chunk n's contribution on entry and, for modes 0-2, leaves with:
@@ -562,52 +562,94 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StateSmem<C>), C::NW))
 //   MODE 2  gradient suffix:  slot[n+1] = carry + sum_{n' > n} contribution, slot[0] = all;
 //                             carry = slot[0]
 //   MODE 3  accumulate:       carry += sum of the window's contributions (slots untouched)
+// The np chunks are cut into G segments (G a power of two <= 32, chosen by the host
+// for parallelism): a workgroup holds G segments x 256/G elements; each thread sums its
+// segment, the segment totals are exchanged through LDS, and each thread then sweeps
+// its segment starting from the carry plus the totals of the segments before it
+// (after it, for the suffix).
 template <int MODE>
 __global__ __launch_bounds__(256) void scan_kernel(float *slots, double *carryR, double *carryS, int DM, int M, int P,
-                                                   int np)
+                                                   int np, int G)
 {
+    __shared__ double tot[256][4];
     const int SZ = DM + M;
-    const int k = (blockIdx.x * 256 + threadIdx.x) * 4;
-    if (k >= SZ) return;
+    const int E = 256 / G;                     // elements per workgroup
+    const int g = threadIdx.x / E, el = threadIdx.x % E;
+    const int k = (blockIdx.x * E + el) * 4;   // first float of this thread's element
+    const bool active = k < SZ;
     const int bh = blockIdx.y;
-    float *base = slots + (size_t)bh * (P + 1) * SZ + k;
-    double *cp = k < DM ? carryR + (size_t)bh * DM + k : carryS + (size_t)bh * M + (k - DM);
-    double cur[4] = {cp[0], cp[1], cp[2], cp[3]};
+    const int sl = (np + G - 1) / G;
+    const int na = min(np, g * sl), nb = min(np, na + sl);
+    float *base = slots + (size_t)bh * (P + 1) * SZ + (active ? k : 0);
+    double *cp = !active ? nullptr : k < DM ? carryR + (size_t)bh * DM + k : carryS + (size_t)bh * M + (k - DM);
     auto slot = [&](int i) { return reinterpret_cast<f4 *>(base + (size_t)i * SZ); };
     auto put = [&](int i, const double *v) { *slot(i) = f4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; };
-    if (MODE == 1 || MODE == 3) {
-        double tot[4] = {0.0, 0.0, 0.0, 0.0};
-        for (int n = 0; n < np; ++n) {
+    // segment totals: needed by the window-start and accumulate modes, and by every
+    // mode when the chunks are split over several segments
+    const bool totals = MODE == 1 || MODE == 3 || G > 1;
+    double cur[4] = {0.0, 0.0, 0.0, 0.0}, seg[4] = {0.0, 0.0, 0.0, 0.0};
+    if (active) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cur[j] = cp[j];
+        for (int n = na; totals && n < nb; ++n) {
             const f4 dl = *slot(n + 1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) tot[j] += (double)dl[j];
+            for (int j = 0; j < 4; ++j) seg[j] += (double)dl[j];
         }
+    }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) cur[j] = MODE == 1 ? cur[j] - tot[j] : cur[j] + tot[j];
+    for (int j = 0; j < 4; ++j) tot[threadIdx.x][j] = seg[j];
+    __syncthreads();
+    // totals of the segments before (and after) this one, and of all of them
+    double before[4] = {0.0, 0.0, 0.0, 0.0}, all[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const double t = tot[h * E + el][j];
+            all[j] += t;
+            if (h < g) before[j] += t;
+        }
+    if (!active) return;
+    const bool last = g == G - 1;
+    if (MODE == 3) {
+        if (last)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cp[j] = cur[j] + all[j];
+        return;
     }
     if (MODE == 0 || MODE == 1) {
-        double run[4] = {cur[0], cur[1], cur[2], cur[3]};
-        put(0, run);
-        for (int n = 0; n < np; ++n) {
+        double start[4], run[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            start[j] = MODE == 1 ? cur[j] - all[j] : cur[j];
+            run[j] = start[j] + before[j];
+        }
+        if (g == 0) put(0, start);
+        for (int n = na; n < nb; ++n) {
             const f4 dl = *slot(n + 1);
 #pragma unroll
             for (int j = 0; j < 4; ++j) run[j] += (double)dl[j];
             put(n + 1, run);
         }
-        if (MODE == 0)
+        if (last)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cur[j] = run[j];
-    } else if (MODE == 2) {
-        for (int n = np - 1; n >= 0; --n) {
+            for (int j = 0; j < 4; ++j) cp[j] = MODE == 0 ? run[j] : start[j];
+    } else {  // MODE 2
+        double run[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) run[j] = cur[j] + (all[j] - before[j] - seg[j]);
+        for (int n = nb - 1; n >= na; --n) {
             const f4 dl = *slot(n + 1);
-            put(n + 1, cur);
+            put(n + 1, run);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cur[j] += (double)dl[j];
+            for (int j = 0; j < 4; ++j) run[j] += (double)dl[j];
         }
-        put(0, cur);
-    }
+        if (g == 0) {
+            put(0, run);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cp[j] = cur[j];
+            for (int j = 0; j < 4; ++j) cp[j] = run[j];
+        }
+    }
 }
 
 // LDS of the chunk kernels that evaluate a chunk's forward.  RED: per-wave fp32
