@@ -64,12 +64,14 @@ struct ChunkArgs {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
-// MW_ = features per wave (0: 64 for bf16 with d <= 64, else 32 -- what keeps a
-// wave's fp32 state blocks and fragments within 256 registers).
+// MW_ = features per wave (0: 64 for bf16 with d <= 64 when that still leaves 4
+// waves, else 32 -- 64 keeps a wave's fp32 state blocks and fragments within 256
+// registers only at d <= 64, and workgroups of fewer than 4 waves leave too little
+// work in flight per compute unit: one-wave workgroups at M = 64 ran 2.2x slower).
 template <typename T_, int D_, int M_, int FEAT_, int TT_, int MW_ = 0> struct KCfg {
     typedef T_ T;
     static constexpr int D = D_, M = M_, FEAT = FEAT_, TT = TT_;
-    static constexpr int MWA = MW_ ? MW_ : ((sizeof(T_) == 2 && D_ <= 64) ? 64 : 32);
+    static constexpr int MWA = MW_ ? MW_ : ((sizeof(T_) == 2 && D_ <= 64 && M_ >= 256) ? 64 : 32);
     static constexpr int MW = M >= MWA ? MWA : M;  // features per wave
     static constexpr int NW = M / MW;              // waves per workgroup
     static constexpr int NT = NW * 64;
