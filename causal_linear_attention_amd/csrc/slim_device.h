@@ -245,6 +245,10 @@ __device__ __forceinline__ void wave_lds_fence()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Floats per row of the backward's row statistics: 1/den, dden, the query
+// feature offset (exp2 domain) and one unused.
+constexpr int ROWSTAT = 4;
+
 // A [TT][D] tile of a row-major tensor held in registers: thread i owns the
 // 16-byte vectors i, i+NT, ... (row t = idx / VPR, columns c..c+EPV-1).  load()
 // issues the global reads (rows >= nvalid read as zero) and returns at once, so a
@@ -268,7 +272,7 @@ template <typename T, int D, int TT, int NT> struct TileRegs {
             const int t = idx / VPR, c = (idx % VPR) * EPV;
             const bool ok = idx < NV && t < nvalid;
             v[i] = ok ? *reinterpret_cast<const V *>(src + (size_t)t * D + c) : zero16<T>();
-            if (stats) s[i] = ok ? stats[(size_t)t * 2] : 0.f;
+            if (stats) s[i] = ok ? stats[(size_t)t * ROWSTAT] : 0.f;
         }
     }
     // Move the tile into an LDS matrix (rows t, columns e); scaled: multiply row t
@@ -313,20 +317,14 @@ template <typename T, int D, int TT, int NT> struct TileRegs {
 
 // Per-row statistics of a tile held in registers by threads 0..TT-1.
 template <int TT> struct RowStatRegs {
-    float inv, dd;
+    float inv, dd, qoff;
     __device__ __forceinline__ void load(const float *st, int nvalid)
     {
         const int t = threadIdx.x;
         const bool ok = t < TT && t < nvalid;
-        inv = ok ? st[(size_t)t * 2] : 0.f;
-        dd = ok ? st[(size_t)t * 2 + 1] : 0.f;
-    }
-    __device__ __forceinline__ void store(float *invl, float *ddl) const
-    {
-        if (threadIdx.x < TT) {
-            invl[threadIdx.x] = inv;
-            ddl[threadIdx.x] = dd;
-        }
+        inv = ok ? st[(size_t)t * ROWSTAT] : 0.f;
+        dd = ok ? st[(size_t)t * ROWSTAT + 1] : 0.f;
+        qoff = ok ? st[(size_t)t * ROWSTAT + 2] : 0.f;
     }
 };
 

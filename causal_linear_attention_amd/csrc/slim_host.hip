@@ -233,7 +233,7 @@ static Plan plan(const slim_desc *d, int pass)
         p.gslots_off = off;
         off = align256(off + slots);
         p.stats_off = off;
-        off = align256(off + (size_t)p.BH * p.P * p.c * 2 * 4);
+        off = align256(off + (size_t)p.BH * p.P * p.c * ROWSTAT * 4);
         p.gR_off = off;
         off = align256(off + (size_t)p.BH * d->d * d->M * 8);
         p.gS_off = off;

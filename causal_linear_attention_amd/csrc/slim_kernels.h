@@ -55,7 +55,7 @@ struct ChunkArgs {
     void *out0, *out1, *out2;  // fwd: Y | bwdq: dQ | bwdkv: dK, dV
     float *slots;              // [BH][P+1][(D+1)*M]  state slots (R rows, then S)
     float *gslots;             // [BH][P+1][(D+1)*M]  gradient-state slots
-    float *stats;              // [BH][P][c][2]       per-row (1/den, dden)
+    float *stats;              // [BH][P][c][ROWSTAT] per-row (1/den, dden, query offset, -)
     long long L;
     int c;   // chunk length
     int n0;  // first chunk of the window
@@ -261,6 +261,22 @@ template <class C> __device__ __forceinline__ void q_finish_T(f4 (&ph)[C::NFB][C
 // g(K) exactly: exp(w_m.k_t - |k_t|^2/2) / sqrt(M) = 2^(log2e w_m.k_t - kn2[t]) with
 // kn2[t] = log2e (|k_t|^2/2 + ln(M)/2), +inf for rows beyond the chunk (g = 0 there).
 // elu+1 rows beyond the chunk were staged as -inf, so g = 0 there too.
+// As q_finish_T with the per-row offset (exp2 domain, -rowmax * log2 e) already
+// known: qoff[t] for tile row t (the backward reads it from the row statistics the
+// stats pass wrote, so it needs no cross-wave maximum).  elu+1: nothing to do.
+template <class C> __device__ __forceinline__ void q_finish_off(f4 (&ph)[C::NFB][C::NTB], const float *qoff)
+{
+    if constexpr (C::FAVOR) {
+#pragma unroll
+        for (int tb = 0; tb < C::NTB; ++tb) {
+            const float off = qoff[tb * 16 + lcol()];
+#pragma unroll
+            for (int fb = 0; fb < C::NFB; ++fb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ph[fb][tb][j] = __builtin_amdgcn_exp2f(fmaf(ph[fb][tb][j], LOG2E, off));
+        }
+    }
+}
 template <class C> __device__ __forceinline__ void k_finish_T(f4 (&ph)[C::NFB][C::NTB], const float *kn2)
 {
     if constexpr (C::FAVOR) {

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StatsSmem<C>), C::NW))
     const int w = wave_id(), g = lgrp(), lc = lcol();
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     const T *dY = (const T *)a.dY + G.hb;
-    float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * 2;
+    float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
     Frag<T> wf[NFB][NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
     f4 rt[NFB][NEA];
@@ -89,8 +89,17 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StatsSmem<C>), C::NW))
                 dt += sm.f.red[(v * TT + t) * 2 + 1];
             }
             const float inv = 1.f / dn;
-            st[(size_t)(t0 + t) * 2] = inv;
-            st[(size_t)(t0 + t) * 2 + 1] = -dt * inv * inv;
+            st[(size_t)(t0 + t) * ROWSTAT] = inv;
+            st[(size_t)(t0 + t) * ROWSTAT + 1] = -dt * inv * inv;
+            // the query offset this pass used (the later passes reuse it)
+            float m = 0.f;
+            if constexpr (C::FAVOR) {
+                m = sm.f.qmax[t];
+#pragma unroll
+                for (int v = 1; v < NW; ++v) m = fmaxf(m, sm.f.qmax[v * TT + t]);
+            }
+            st[(size_t)(t0 + t) * ROWSTAT + 2] = -m * LOG2E;
+            st[(size_t)(t0 + t) * ROWSTAT + 3] = 0.f;
         }
         state_update_T<C>(sm.f, rt);
         __syncthreads();
@@ -106,7 +115,7 @@ template <class C> struct GstateSmem {
     __align__(16) T dn[C::XMat::SIZE];
     __align__(16) T dna[C::AuxMat::SIZE];
     __align__(16) T fq[C::NW * C::FMat::SIZE];
-    float qmax[C::NW * C::TT];
+    float qoff[C::TT];
 };
 template <class C>
 __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(GstateSmem<C>), C::NW)) void gstate_kernel(ChunkArgs a)
@@ -119,7 +128,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(GstateSmem<C>), C::NW)
     const typename C::FMat Fq(sm.fq + wave_id() * C::FMat::SIZE);
     const ChunkGeom G = chunk_geom<C>(a);
     const T *Q = (const T *)a.Q + G.hb, *dY = (const T *)a.dY + G.hb;
-    const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * 2;
+    const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
     Frag<T> wf[NFB][NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
     f4 dg[NFB][NEA];
@@ -138,19 +147,20 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(GstateSmem<C>), C::NW)
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         rq.store(xq, false, nullptr);
         rdy.store(DN.x, true, nullptr);
-        if (threadIdx.x < TT) DN.set_aux(threadIdx.x, rs.dd);
+        if (threadIdx.x < TT) {
+            DN.set_aux(threadIdx.x, rs.dd);
+            sm.qoff[threadIdx.x] = rs.qoff;
+        }
         __syncthreads();
         if (t0 + TT < G.len) {
             const int n = min(TT, G.len - t0 - TT);
             rq.load(Q + (size_t)(t0 + TT) * D, n);
-            rdy.load(dY + (size_t)(t0 + TT) * D, n, st + (size_t)(t0 + TT) * 2);
-            rs.load(st + (size_t)(t0 + TT) * 2, n);
+            rdy.load(dY + (size_t)(t0 + TT) * D, n, st + (size_t)(t0 + TT) * ROWSTAT);
+            rs.load(st + (size_t)(t0 + TT) * ROWSTAT, n);
         }
         f4 pq[NFB][NTB];
         feat_T<C>(pq, xq, wf);
-        if constexpr (C::FAVOR) q_partial_max<C>(pq, sm.qmax);
-        __syncthreads();
-        q_finish_T<C>(pq, sm.qmax);
+        q_finish_off<C>(pq, sm.qoff);
         put_features<C>(Fq, pq);
         wave_lds_fence();  // Fq written by this wave above
         // [dG | dGs] += g(Q)^T [dNum | dden] over this wave's features
@@ -193,17 +203,20 @@ template <class C> struct BwdRegs {
         q.load(Q + (size_t)t0 * C::D, n);
         k.load(K + (size_t)t0 * C::D, n);
         v.load(V + (size_t)t0 * C::D, n);
-        dy.load(dY + (size_t)t0 * C::D, n, st + (size_t)t0 * 2);
-        rs.load(st + (size_t)t0 * 2, n);
+        dy.load(dY + (size_t)t0 * C::D, n, st + (size_t)t0 * ROWSTAT);
+        rs.load(st + (size_t)t0 * ROWSTAT, n);
     }
     __device__ __forceinline__ void store(const typename C::XMat &xq, const typename C::XMat &xk,
-                                          const AugTile<C> &Vt, const AugTile<C> &DN, float *kn2, int nv)
+                                          const AugTile<C> &Vt, const AugTile<C> &DN, float *kn2, float *qoff, int nv)
     {
         q.store(xq, false, nullptr);
         store_k_tile<C>(k, xk, kn2, nv);
         store_v_tile<C>(v, Vt, nv);
         dy.store(DN.x, true, nullptr);
-        if (threadIdx.x < C::TT) DN.set_aux(threadIdx.x, rs.dd);
+        if (threadIdx.x < C::TT) {
+            DN.set_aux(threadIdx.x, rs.dd);
+            qoff[threadIdx.x] = rs.qoff;
+        }
     }
 };
 
@@ -219,7 +232,7 @@ template <class C> struct BwdqSmem {
     __align__(16) T dna[C::AuxMat::SIZE];
     __align__(16) T fk[C::NW * C::FMat::SIZE];
     __align__(16) float red[C::FAVOR ? C::NW * C::TT * C::LDR : 4];
-    float kn2[C::TT], qmax[C::NW * C::TT];
+    float kn2[C::TT], qoff[C::TT];
 };
 template <class C>
 __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) void bwdq_kernel(ChunkArgs a)
@@ -227,7 +240,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
     typedef typename C::T T;
     constexpr int NFB = C::NFB, NEB = C::NEB, NEA = C::NEA, NTB = C::NTB, TT = C::TT, D = C::D, MW = C::MW;
     __shared__ BwdqSmem<C> sm;
-    float *red = sm.red, *kn2 = sm.kn2, *qmax = sm.qmax;
+    float *red = sm.red, *kn2 = sm.kn2, *qoff = sm.qoff;
     const typename C::XMat xq(sm.xq), xk(sm.xk);
     const AugTile<C> Vt(sm.xv, sm.xva), DN(sm.dn, sm.dna);
     const typename C::FMat Fk(sm.fk + wave_id() * C::FMat::SIZE);
@@ -236,7 +249,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     const T *dY = (const T *)a.dY + G.hb;
     T *dQ = (T *)a.out0 + G.hb;
-    const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * 2;
+    const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
     Frag<T> wf[NFB][NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
     f4 r[NEA][NFB];
@@ -245,14 +258,12 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
     rg.load(Q, K, V, dY, st, 0, G.len);
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        rg.store(xq, xk, Vt, DN, kn2, nv);
+        rg.store(xq, xk, Vt, DN, kn2, qoff, nv);
         __syncthreads();
         if (t0 + TT < G.len) rg.load(Q, K, V, dY, st, t0 + TT, G.len);
         f4 pq[NFB][NTB];
         feat_T<C>(pq, xq, wf);
-        if constexpr (C::FAVOR) q_partial_max<C>(pq, qmax);
-        __syncthreads();
-        q_finish_T<C>(pq, qmax);
+        q_finish_off<C>(pq, qoff);
         {
             f4 pkT[NFB][NTB];
             feat_T<C>(pkT, xk, wf);
@@ -354,7 +365,7 @@ template <class C> struct BwdkvSmem {
     __align__(16) T dna[C::AuxMat::SIZE];
     __align__(16) T fq[C::NW * C::FMat::SIZE];
     __align__(16) float red[C::NW * C::TT * C::LDR];
-    float kn2[C::TT], qmax[C::NW * C::TT];
+    float kn2[C::TT], qoff[C::TT];
 };
 template <class C>
 __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW)) void bwdkv_kernel(ChunkArgs a)
@@ -364,7 +375,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
     typedef typename BwdkvSmem<C>::DrMat DrMat;
     constexpr bool DRL = BwdkvSmem<C>::DR_IN_RED;
     __shared__ BwdkvSmem<C> sm;
-    float *red = sm.red, *kn2 = sm.kn2, *qmax = sm.qmax;
+    float *red = sm.red, *kn2 = sm.kn2, *qoff = sm.qoff;
     const typename C::XMat xq(sm.xq), xk(sm.xk);
     const AugTile<C> Vt(sm.xv, sm.xva), DN(sm.dn, sm.dna);
     const typename C::FMat Fq(sm.fq + wave_id() * C::FMat::SIZE);
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     const T *dY = (const T *)a.dY + G.hb;
     T *dK = (T *)a.out1 + G.hb, *dV = (T *)a.out2 + G.hb;
-    const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * 2;
+    const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
     const float *gsl = slot_ptr<C>(a.gslots, a, G.bh, G.nl + 1);
     f4 dr[NEA][NFB];                       // [dR; dS], rows e, cols m
     f4 drt[DRL ? 1 : NFB][DRL ? 1 : NEB];  // dR^T (rows m, cols e) when not copied through LDS
@@ -393,7 +404,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
     rg.load(Q, K, V, dY, st, last, G.len);
     for (int t0 = last; t0 >= 0; t0 -= TT) {
         const int nv = min(TT, G.len - t0);
-        rg.store(xq, xk, Vt, DN, kn2, nv);
+        rg.store(xq, xk, Vt, DN, kn2, qoff, nv);
         __syncthreads();
         Frag<T> fq[NFB][NTB], fkT[NFB][NTB];
         {
@@ -402,9 +413,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
             if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
             f4 pq[NFB][NTB];
             feat_T<C>(pq, xq, wf);
-            if constexpr (C::FAVOR) q_partial_max<C>(pq, qmax);
-            __syncthreads();
-            q_finish_T<C>(pq, qmax);
+            q_finish_off<C>(pq, qoff);
             put_features<C>(Fq, pq);
             to_frags<C>(fq, pq);
             f4 pkT[NFB][NTB];
