@@ -238,17 +238,27 @@ template <class C> __device__ __forceinline__ void q_partial_max(const f4 (&ph)[
     }
 }
 
-// g(Q) up to a per-row positive factor: exp(w_m.q_t - max_m' w_m'.q_t).  The factor
-// cancels in Y and in dQ (Y is homogeneous of degree 0 in each g(Q_l)).
-template <class C> __device__ __forceinline__ void q_finish_T(f4 (&ph)[C::NFB][C::NTB], const float *qmax)
+// g(K) exactly: exp(w_m.k_t - |k_t|^2/2) / sqrt(M) = 2^(log2e w_m.k_t - kn2[t]) with
+// kn2[t] = log2e (|k_t|^2/2 + ln(M)/2), +inf for rows beyond the chunk (g = 0 there).
+// elu+1 rows beyond the chunk were staged as -inf, so g = 0 there too.
+// g(Q) is evaluated up to a positive per-row factor, which cancels in Y and in dQ
+// (Y is homogeneous of degree 0 in each g(Q_l)).
+// Queries with this wave's own row maximum as offset: g'(Q_t) = g(Q_t) * exp(-m_w(t))
+// with m_w(t) = max over the wave's features of w_m . q_t, recorded in qmax[w][t] for
+// the cross-wave sums, which rescale each wave's partials to the common maximum
+// (no barrier is needed here).  elu+1: nothing to do.
+template <class C> __device__ __forceinline__ void q_wave_finish(f4 (&ph)[C::NFB][C::NTB], float *qmax)
 {
     if constexpr (C::FAVOR) {
 #pragma unroll
         for (int tb = 0; tb < C::NTB; ++tb) {
-            const int t = tb * 16 + lcol();
-            float m = qmax[t];
+            float m = -3.0e38f;
 #pragma unroll
-            for (int w = 1; w < C::NW; ++w) m = fmaxf(m, qmax[w * C::TT + t]);
+            for (int fb = 0; fb < C::NFB; ++fb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m = fmaxf(m, ph[fb][tb][j]);
+            m = max_groups(m);
+            if (lgrp() == 0) qmax[wave_id() * C::TT + tb * 16 + lcol()] = m;
             const float off = -m * LOG2E;
 #pragma unroll
             for (int fb = 0; fb < C::NFB; ++fb)
@@ -257,12 +267,26 @@ template <class C> __device__ __forceinline__ void q_finish_T(f4 (&ph)[C::NFB][C
         }
     }
 }
+// Per-wave scale factors of tile row t: sc[w] = exp(m_w(t) - max_w' m_w'(t)) (all 1 for
+// elu+1); *moff = the common offset -max * log2 e (0 for elu+1).
+template <class C> __device__ __forceinline__ void wave_scales(const float *qmax, int t, float (&sc)[C::NW], float *moff)
+{
+    if constexpr (C::FAVOR) {
+        float m = qmax[t];
+#pragma unroll
+        for (int w = 1; w < C::NW; ++w) m = fmaxf(m, qmax[w * C::TT + t]);
+#pragma unroll
+        for (int w = 0; w < C::NW; ++w) sc[w] = __builtin_amdgcn_exp2f((qmax[w * C::TT + t] - m) * LOG2E);
+        *moff = -m * LOG2E;
+    } else {
+#pragma unroll
+        for (int w = 0; w < C::NW; ++w) sc[w] = 1.f;
+        *moff = 0.f;
+    }
+}
 
-// g(K) exactly: exp(w_m.k_t - |k_t|^2/2) / sqrt(M) = 2^(log2e w_m.k_t - kn2[t]) with
-// kn2[t] = log2e (|k_t|^2/2 + ln(M)/2), +inf for rows beyond the chunk (g = 0 there).
-// elu+1 rows beyond the chunk were staged as -inf, so g = 0 there too.
-// As q_finish_T with the per-row offset (exp2 domain, -rowmax * log2 e) already
-// known: qoff[t] for tile row t (the backward reads it from the row statistics the
+// Queries with a known per-row offset (exp2 domain, -rowmax * log2 e): qoff[t] for
+// tile row t (the backward reads it from the row statistics the
 // stats pass wrote, so it needs no cross-wave maximum).  elu+1: nothing to do.
 template <class C> __device__ __forceinline__ void q_finish_off(f4 (&ph)[C::NFB][C::NTB], const float *qoff)
 {
@@ -355,6 +379,26 @@ template <class C> __device__ __forceinline__ float reduce_col(const float *red,
 #pragma unroll
     for (int w = 1; w < C::NW; ++w) s += red[(w * C::TT + t) * C::LDR + C::D];
     return s;
+}
+// As reduce_rows, with each wave's partial rescaled by its factor (wave_scales) and
+// the rescaled sum of column D (denominator) handed over too: emit(t, e, s, den, ok).
+template <class C, typename F>
+__device__ __forceinline__ void reduce_rows_scaled(const float *red, const float *qmax, int nv, F emit)
+{
+    constexpr int Q4 = C::D / 4;
+    for (int v = threadIdx.x; v < C::TT * Q4; v += C::NT) {
+        const int t = v / Q4, e = (v % Q4) * 4;
+        float sc[C::NW], moff;
+        wave_scales<C>(qmax, t, sc, &moff);
+        f4 s = f4zero();
+        float den = 0.f;
+#pragma unroll
+        for (int w = 0; w < C::NW; ++w) {
+            s += *reinterpret_cast<const f4 *>(red + (w * C::TT + t) * C::LDR + e) * sc[w];
+            den += red[(w * C::TT + t) * C::LDR + C::D] * sc[w];
+        }
+        emit(t, e, s, den, t < nv);
+    }
 }
 // Write a value-indexed block acc (rows e = eb*16 + 4g + j, cols t = tb*16 + i%16) of
 // this wave's partial to red; the auxiliary block contributes only column D.
@@ -705,9 +749,9 @@ template <class C> struct FwdRegs {
 
 // One tile of the chunk forward, shared by fwd_kernel and stats_kernel: hands
 // this wave's partial numerator^T blocks (rows e, cols t; the auxiliary block's
-// first row is the denominator) to emit(eb, tb, acc); leaves g(Q) of this wave's
-// features (rows m, cols t) in pq and g(K) in the wave's feature buffer (rows t,
-// cols m).
+// first row is the denominator), scaled by the wave's own query offset (recorded in
+// sm.qmax), to emit(eb, tb, acc); leaves g(Q) of this wave's features (rows m,
+// cols t) in pq and g(K) in the wave's feature buffer (rows t, cols m).
 template <class C, class SM, class EMIT>
 __device__ __forceinline__ void fwd_tile(SM &sm, const Frag<typename C::T> (&wf)[C::NFB][C::NEB],
                                          const f4 (&rt)[C::NFB][C::NEA], f4 (&pq)[C::NFB][C::NTB], EMIT emit)
@@ -721,9 +765,7 @@ __device__ __forceinline__ void fwd_tile(SM &sm, const Frag<typename C::T> (&wf)
     f4 pkT[NFB][NTB];
     feat_T<C>(pq, xq, wf);
     feat_T<C>(pkT, xk, wf);
-    if constexpr (C::FAVOR) q_partial_max<C>(pq, sm.qmax);
-    __syncthreads();
-    q_finish_T<C>(pq, sm.qmax);
+    q_wave_finish<C>(pq, sm.qmax);
     k_finish_T<C>(pkT, sm.kn2);
     put_features<C>(Fk, pkT);
     Frag<T> fq[NFB][NTB], fkT[NFB][NTB];
@@ -793,8 +835,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(FwdSmem<C>), C::NW)) v
         f4 pq[NFB][NTB];
         fwd_tile<C>(sm, wf, rt, pq, [&](int eb, int tb, f4 acc) { put_red<C>(sm.red, eb, tb, acc); });
         __syncthreads();
-        reduce_rows<C>(sm.red, nv, [&](int t, int e, f4 s, bool ok) {
-            if (ok) store4<T>(Y + (size_t)(t0 + t) * C::D + e, s * (1.f / reduce_col<C>(sm.red, t)));
+        reduce_rows_scaled<C>(sm.red, sm.qmax, nv, [&](int t, int e, f4 s, float den, bool ok) {
+            if (ok) store4<T>(Y + (size_t)(t0 + t) * C::D + e, s * (1.f / den));
         });
         state_update_T<C>(sm, rt);
         __syncthreads();

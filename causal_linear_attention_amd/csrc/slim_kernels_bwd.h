@@ -81,24 +81,21 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StatsSmem<C>), C::NW))
         }
         __syncthreads();
         if (threadIdx.x < nv) {
+            // the waves' partials rescaled to the common query offset, which the later
+            // passes reuse
             const int t = threadIdx.x;
+            float sc[NW], moff;
+            wave_scales<C>(sm.f.qmax, t, sc, &moff);
             float dn = 0.f, dt = 0.f;
 #pragma unroll
             for (int v = 0; v < NW; ++v) {
-                dn += sm.f.red[(v * TT + t) * 2];
-                dt += sm.f.red[(v * TT + t) * 2 + 1];
+                dn += sm.f.red[(v * TT + t) * 2] * sc[v];
+                dt += sm.f.red[(v * TT + t) * 2 + 1] * sc[v];
             }
             const float inv = 1.f / dn;
             st[(size_t)(t0 + t) * ROWSTAT] = inv;
             st[(size_t)(t0 + t) * ROWSTAT + 1] = -dt * inv * inv;
-            // the query offset this pass used (the later passes reuse it)
-            float m = 0.f;
-            if constexpr (C::FAVOR) {
-                m = sm.f.qmax[t];
-#pragma unroll
-                for (int v = 1; v < NW; ++v) m = fmaxf(m, sm.f.qmax[v * TT + t]);
-            }
-            st[(size_t)(t0 + t) * ROWSTAT + 2] = -m * LOG2E;
+            st[(size_t)(t0 + t) * ROWSTAT + 2] = moff;
             st[(size_t)(t0 + t) * ROWSTAT + 3] = 0.f;
         }
         state_update_T<C>(sm.f, rt);
