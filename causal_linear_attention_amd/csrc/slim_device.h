@@ -167,18 +167,22 @@ __device__ __forceinline__ void store16(__bf16 *p, bf8 x)
 // ds_read_b64_tr_b16 (within each 16-lane group, lane i receives element i%4 of
 // the chunks addressed by lanes i/4, 4+i/4, 8+i/4, 12+i/4, so lane L points at
 // row k0+4g+L/4, column n0+4(L%4)).  fp32: row-major with rows padded by 4
-// elements, frag_r is four 4-byte reads.
-template <typename T, int ROWS, int COLS> struct LMat {
+// elements, frag_r is four 4-byte reads.  PAD (bf16) spaces the column blocks by
+// PAD extra elements: a matrix written row-wise across blocks (the staged input
+// tiles: each thread stores 8 consecutive columns) would otherwise put the same
+// row of different blocks on the same banks.
+template <typename T, int ROWS, int COLS, int PAD = 0> struct LMat {
     static constexpr bool BF = sizeof(T) == 2;
     static constexpr int LD = BF ? COLS : COLS + 4;
-    static constexpr int SIZE = ROWS * LD;
+    static constexpr int BSTRIDE = ROWS * 16 + PAD;  // bf16: elements per 16-column block
+    static constexpr int SIZE = BF ? (COLS / 16) * BSTRIDE : ROWS * LD;
     static_assert(COLS % 16 == 0, "columns: a multiple of 16");
     T *p;
     __device__ __forceinline__ explicit LMat(T *base) : p(base) {}
     __device__ static __forceinline__ int off(int r, int c)  // c % 4 == 0
     {
         if constexpr (BF)
-            return (c >> 4) * (ROWS * 16) + r * 16 + ((((c >> 2) & 3) ^ ((r >> 2) & 3)) << 2);
+            return (c >> 4) * BSTRIDE + r * 16 + ((((c >> 2) & 3) ^ ((r >> 2) & 3)) << 2);
         else
             return r * LD + c;
     }

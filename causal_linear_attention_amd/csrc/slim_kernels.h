@@ -68,7 +68,8 @@ constexpr float LOG2E = 1.4426950408889634f;
 // waves, else 32 -- 64 keeps a wave's fp32 state blocks and fragments within 256
 // registers only at d <= 64, and workgroups of fewer than 4 waves leave too little
 // work in flight per compute unit: one-wave workgroups at M = 64 ran 2.2x slower).
-template <typename T_, int D_, int M_, int FEAT_, int TT_, int MW_ = 0> struct KCfg {
+// PADX_ = bf16 elements between the 16-column blocks of the staged input tiles (see LMat).
+template <typename T_, int D_, int M_, int FEAT_, int TT_, int MW_ = 0, int PADX_ = 32> struct KCfg {
     typedef T_ T;
     static constexpr int D = D_, M = M_, FEAT = FEAT_, TT = TT_;
     static constexpr int MWA = MW_ ? MW_ : ((sizeof(T_) == 2 && D_ <= 64 && M_ >= 256) ? 64 : 32);
@@ -83,7 +84,7 @@ template <typename T_, int D_, int M_, int FEAT_, int TT_, int MW_ = 0> struct K
     static constexpr int SZ = (D + 1) * M;
     static constexpr bool FAVOR = FEAT == FEAT_FAVOR;
     typedef TileRegs<T, D, TT, NT> Tile;
-    typedef LMat<T, TT, D> XMat;     // [TT][D] input tile
+    typedef LMat<T, TT, D, PADX_> XMat;  // [TT][D] input tile
     typedef LMat<T, TT, 16> AuxMat;  // auxiliary value block of a tile (column 0 used)
     typedef LMat<T, TT, MW> FMat;    // one wave's features of a tile: rows t, columns m
     static_assert(FEAT == FEAT_FAVOR || D == M, "elu+1 needs M == d");

@@ -354,6 +354,7 @@ template <class C> struct BwdkvSmem {
     typedef typename C::T T;
     typedef LMat<T, C::MW, C::D> DrMat;  // rows m, cols e
     static constexpr bool DR_IN_RED = DrMat::SIZE * sizeof(T) <= (size_t)C::TT * C::LDR * sizeof(float);
+    __align__(16) float red[C::NW * C::TT * C::LDR];
     __align__(16) T xq[C::XMat::SIZE];
     __align__(16) T xk[C::XMat::SIZE];
     __align__(16) T xv[C::XMat::SIZE];
@@ -361,7 +362,6 @@ template <class C> struct BwdkvSmem {
     __align__(16) T dn[C::XMat::SIZE];
     __align__(16) T dna[C::AuxMat::SIZE];
     __align__(16) T fq[C::NW * C::FMat::SIZE];
-    __align__(16) float red[C::NW * C::TT * C::LDR];
     float kn2[C::TT], qoff[C::TT];
 };
 template <class C>
