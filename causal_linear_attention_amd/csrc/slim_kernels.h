@@ -350,6 +350,17 @@ __device__ __forceinline__ void put_features(const typename C::FMat &F, const f4
         for (int tb = 0; tb < C::NTB; ++tb) F.put4(tb * 16 + lcol(), fb * 16 + 4 * lgrp(), ph[fb][tb]);
 }
 
+// Same, from the blocks already converted to operand fragments (no second conversion).
+template <class C>
+__device__ __forceinline__ void put_feature_frags(const typename C::FMat &F,
+                                                  const Frag<typename C::T> (&f)[C::NFB][C::NTB])
+{
+#pragma unroll
+    for (int fb = 0; fb < C::NFB; ++fb)
+#pragma unroll
+        for (int tb = 0; tb < C::NTB; ++tb) F.put_frag(tb * 16 + lcol(), fb * 16 + 4 * lgrp(), f[fb][tb]);
+}
+
 template <class C, int A, int B>
 __device__ __forceinline__ void to_frags(Frag<typename C::T> (&f)[A][B], const f4 (&c)[A][B])
 {
@@ -768,10 +779,10 @@ __device__ __forceinline__ void fwd_tile(SM &sm, const Frag<typename C::T> (&wf)
     feat_T<C>(pkT, xk, wf);
     q_wave_finish<C>(pq, sm.qmax);
     k_finish_T<C>(pkT, sm.kn2);
-    put_features<C>(Fk, pkT);
     Frag<T> fq[NFB][NTB], fkT[NFB][NTB];
     to_frags<C>(fq, pq);
     to_frags<C>(fkT, pkT);
+    put_feature_frags<C>(Fk, fkT);
     // P^T blocks (rows s, cols t), s-block <= t-block, over this wave's features.
     Frag<T> pt[NTB][NTB];
 #pragma unroll

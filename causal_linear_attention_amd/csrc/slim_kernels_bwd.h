@@ -411,8 +411,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
             f4 pq[NFB][NTB];
             feat_T<C>(pq, xq, wf);
             q_finish_off<C>(pq, qoff);
-            put_features<C>(Fq, pq);
             to_frags<C>(fq, pq);
+            put_feature_frags<C>(Fq, fq);
             f4 pkT[NFB][NTB];
             feat_T<C>(pkT, xk, wf);
             k_finish_T<C>(pkT, kn2);
