@@ -102,12 +102,13 @@ def kernel_flops(w: Workload, tile: int) -> dict:
 def kernel_bytes(w: Workload) -> dict:
     """Algorithmic HBM bytes per (token, head) of each chunk kernel and scan: every
     input tensor row read once, every output row written once, one (d+1) x M fp32
-    state slot read or written per chunk (so per row: slot / c), 8 bytes of row
-    statistics (1/den, dden) per row where used.  No re-reads, no caches."""
+    state slot read or written per chunk (so per row: slot / c), 16 bytes of row
+    statistics (1/den, dden, query offset, one unused float) per row where used.  No
+    re-reads, no caches."""
     s = 2 if w.dtype == "bf16" else 4
     row = w.d * s                                   # one Q/K/V/Y/dY/dQ/dK/dV row
     slot = (w.d + 1) * w.M * 4 / w.chunk_len        # one chunk state, per row of the chunk
-    st = 8
+    st = 16
     return {
         "state": 2 * row + slot,                    # K, V -> chunk state
         "scan_prefix": 2 * slot, "scan_reverse": 2 * slot, "scan_grad": 2 * slot,  # slots in place
