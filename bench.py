@@ -14,6 +14,7 @@ and the fp64 CPU oracle timed on a bounded sample of the same workload.
   python bench.py --profile-run     # a few steps, for rocprofv3 runs
   python bench.py --copy-calib      # one plain copy kernel of known size (PMC calibration)
   python bench.py --pmc-summary DIR # (host only) HBM traffic per kernel from rocprofv3 counter CSVs
+  python bench.py --decode [...]    # the recurrent decode step instead (one JSON line of its own)
 
 roofline.traffic: HBM bytes per launch of the dominant kernel, FETCH_SIZE and
 WRITE_SIZE scaled by what the same counters read for a plain copy of known
@@ -52,6 +53,8 @@ def parse():
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--mem-sweep", action="store_true",
                     help="peak HBM of one fwd+bwd step vs L at the 1M-token workload's shape (one JSON line)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the recurrent decode step (one token per sequence per step) instead")
     ap.add_argument("--pmc-summary", default=None, metavar="DIR",
                     help="DIR holds rocprofv3 counter runs F, W (FETCH_SIZE, WRITE_SIZE of --profile-run) "
                          "and CF, CW (the same of --copy-calib); writes profiles/traffic_<workload>.md")
@@ -215,6 +218,98 @@ def mem_sweep(torch, A, synth, w):
     return {"mem_sweep": w.name, "B": w.B, "H": w.H, "d": w.d, "M": w.M, "chunk_len": 512, "rows": rows}
 
 
+DECODE_METRIC = "causal linear-attn decode tokens/s (one new token per sequence per step, state in place)"
+
+
+def decode_cpu_baseline(w, synth, seqs, budget_s=10.0):
+    """The fp64 oracle's decode step (its prefix form over one position) on
+    `seqs` sequences x H heads, stepped until about budget_s seconds pass."""
+    import numpy as np
+
+    import oracle
+    W = synth.projection(w.seed, w.M, w.d, w.w_kind).astype(np.float64) if w.feat == "favor" else None
+    rng = np.random.default_rng(w.seed)
+    R = np.zeros((seqs, w.H, w.d, w.M))
+    S = np.zeros((seqs, w.H, w.M))
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        q, k = (rng.standard_normal((seqs, w.H, w.d)) * w.qkv_scale for _ in range(2))
+        v = rng.standard_normal((seqs, w.H, w.d))
+        _, R, S = oracle.decode_step(q, k, v, W, w.feat, R, S)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or steps >= 10000:
+            break
+    threads = min(seqs * w.H, 32, os.cpu_count() or 1)
+    return {"value": seqs * steps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle decode step (prefix form over one position), {seqs} of {w.B} sequences "
+                      f"x {w.H} heads, {steps} steps ({dt:.1f} s), one thread per head"}
+
+
+def decode_main(args, torch, _lib, A, synth):
+    from causal_linear_attention_amd.workloads import DECODE_HEADLINE, DECODE_WORKLOADS, decode_bytes_per_head
+    w = DECODE_WORKLOADS[args.workload or DECODE_HEADLINE]
+    if args.pmc_summary:
+        print(json.dumps(pmc_summary(args.pmc_summary, w, 1 << 30)))
+        return
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    W = None
+    if w.feat == "favor":
+        W = torch.from_numpy(synth.projection(w.seed, w.M, w.d, w.w_kind)).cuda().to(dt).contiguous()
+
+    def draw(tid, L, scale):
+        return synth.device_normal(w.seed, tid, (w.B, w.H, L, w.d), scale).to(dt).contiguous()
+
+    # the state after a prompt of w.prefix tokens (chunked forward), then one token per step
+    _, R, S = A.attn_fwd(draw(synth.TID_Q, w.prefix, w.qkv_scale), draw(synth.TID_K, w.prefix, w.qkv_scale),
+                         draw(synth.TID_V, w.prefix, 1.0), W, w.feat, 1)
+    tok = [draw(tid, 1, sc)[:, :, 0].contiguous()
+           for tid, sc in ((synth.TID_Q, w.qkv_scale), (synth.TID_K, w.qkv_scale), (synth.TID_V, 1.0))]
+    torch.cuda.synchronize()
+
+    def step():
+        return A.decode_step(*tok, W, w.feat, R, S, inplace=True)[0]
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    if args.profile_run:
+        for _ in range(max(1, args.steps)):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": w.name, "steps": args.steps}))
+        return
+    _lib.prof_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _lib.prof_enable(False)
+    ms, n = _lib.prof_read()["decode"]
+    isz = 2 if w.dtype == "bf16" else 4
+    by = w.heads * decode_bytes_per_head(w) + (w.M * w.d * isz if W is not None else 0)
+    avg = ms / n
+    achieved = by / (avg * 1e-3) / 1e9
+    rec = {
+        "metric": DECODE_METRIC, "value": round(w.B * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * elapsed / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "M": w.M, "feat": w.feat, "W": w.w_kind,
+                   "prompt": w.prefix, "state_bytes": w.heads * (w.d + 1) * w.M * 4,
+                   "global_batch": w.B, "seq_len": 1, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(w, "decode"),
+                     "kernel": "decode", "ms_avg": round(avg, 5), "bytes_per_launch": by},
+        "kernels": {"decode": {"ms_total": round(ms, 4), "launches": n, "ms_avg": round(avg, 5)}},
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = decode_cpu_baseline(w, synth, min(w.B, 8))
+    print(json.dumps(rec))
+
+
 def kernel_records(w, prof, steps, tile):
     """Per-kernel records from the library's hipEvent timings {name: (ms total, launches)}
     over `steps` steps, and the roofline record of the dominant kernel."""
@@ -280,6 +375,10 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4, "launches": 3}))
+        return
+
+    if args.decode:
+        decode_main(args, torch, _lib, A, synth)
         return
 
     if args.mem_sweep:

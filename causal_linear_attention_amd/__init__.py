@@ -7,7 +7,7 @@ the library has not been built.
 """
 from . import _lib  # noqa: F401
 
-__all__ = ["featmap", "attn_fwd", "attn_bwd", "slim_attention"]
+__all__ = ["featmap", "attn_fwd", "attn_bwd", "slim_attention", "decode_step"]
 
 
 def __getattr__(name):

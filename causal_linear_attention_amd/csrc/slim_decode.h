@@ -1,0 +1,140 @@
+// slim_decode.h -- the recurrent decode step: one new token per (batch, head)
+// advances the attention state and emits its output.  This is the iterative
+// prefix-sum evaluation of page "Sub-Linear Memory: How to Make Performers
+// SLiM", Subsection 2.1 (eq. (3)-(4)), taken one position at a time:
+//
+//     R' = R + v g(k)^T,   S' = S + g(k),   y = R' g(q) / (S' . g(q)).
+//
+// It is bound by streaming the (d+1) x M fp32 state [R; S] in and out once, so
+// it is laid out for that and not for the matrix cores: one 256-thread
+// workgroup per head; each thread owns four consecutive features of every
+// (1024/M)-th state row, so rows move as contiguous 16-byte accesses.  The
+// state loads are issued first and overlap the feature computation; g(k) and
+// the query projection are computed once per workgroup (one feature per
+// thread) and shared through LDS.  The numerators and the denominator are
+// reduced over the M/4 threads of a row with lane shuffles.
+#pragma once
+#include "slim_kernels.h"
+
+namespace slim {
+
+struct DecodeArgs {
+    const void *q, *k, *v, *W;  // [BH][d] io dtype; W [M][d] (FAVOR+) or NULL
+    const float *Rin, *Sin;     // state before the token, NULL = zero
+    void *y;                    // [BH][d] io dtype
+    float *Rout, *Sout;         // state after the token (may equal Rin, Sin)
+};
+
+constexpr int DECODE_NT = 256;
+
+template <class C> __global__ __launch_bounds__(DECODE_NT) void decode_kernel(DecodeArgs a)
+{
+    typedef typename C::T T;
+    constexpr int D = C::D, M = C::M;
+    constexpr int TPR = M / 4;                       // threads per state row
+    constexpr int RPP = DECODE_NT / TPR;             // rows per pass of the workgroup
+    constexpr int NP = (D + 1 + RPP - 1) / RPP;      // passes over the D + 1 rows
+    constexpr int NWF = (M + 63) / 64;               // waves that compute features
+    static_assert(M % 16 == 0 && M <= DECODE_NT, "decode feature count");
+    __shared__ float x[3][D];                        // q, k, v
+    __shared__ float fk[M], pq[M];                   // g(k); w_m.q (FAVOR+) or g(q) (elu+1)
+    __shared__ float wmax[NWF];
+    __shared__ float red[D + 1];                     // numerators, then the denominator
+    const long long bh = blockIdx.x;
+    const int tid = threadIdx.x, cg = tid % TPR, rs = tid / TPR;
+    const float *rin = a.Rin ? a.Rin + (size_t)bh * D * M : nullptr;
+    const float *sin_ = a.Sin ? a.Sin + (size_t)bh * M : nullptr;
+    float *rout = a.Rout + (size_t)bh * D * M;
+    float *sout = a.Sout + (size_t)bh * M;
+
+    f4 st[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int row = rs + p * RPP;
+        st[p] = f4zero();
+        if (rin && row <= D)
+            st[p] = *reinterpret_cast<const f4 *>((row < D ? rin + (size_t)row * M : sin_) + 4 * cg);
+    }
+    for (int i = tid; i < 3 * D; i += DECODE_NT) {
+        const T *src = (const T *)(i < D ? a.q : i < 2 * D ? a.k : a.v);
+        x[i / D][i % D] = (float)src[bh * D + i % D];
+    }
+    __syncthreads();
+
+    if constexpr (C::FAVOR) {
+        float qm = -__builtin_inff();
+        if (tid < M) {
+            typedef typename Vec16<T>::type VT;
+            constexpr int VN = Vec16<T>::N;
+            const VT *w = reinterpret_cast<const VT *>((const T *)a.W + (size_t)tid * D);
+            float sk = 0.f, sq = 0.f, kk = 0.f;
+#pragma unroll 4
+            for (int e0 = 0; e0 < D; e0 += VN) {
+                const VT wv = w[e0 / VN];
+#pragma unroll
+                for (int j = 0; j < VN; ++j) {
+                    const float we = (float)wv[j], ke = x[1][e0 + j];
+                    sk = fmaf(we, ke, sk);
+                    sq = fmaf(we, x[0][e0 + j], sq);
+                    kk = fmaf(ke, ke, kk);
+                }
+            }
+            // g(k)_m = exp(w_m.k - |k|^2/2) / sqrt(M), exactly (no offset: it would not cancel)
+            const float kn2 = (0.5f * kk + 0.5f * __logf((float)M)) * LOG2E;
+            fk[tid] = __builtin_amdgcn_exp2f(fmaf(sk, LOG2E, -kn2));
+            pq[tid] = sq;
+            qm = sq;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) qm = fmaxf(qm, __shfl_xor(qm, o, 64));
+        if (tid < M && lane_id() == 0) wmax[wave_id()] = qm;
+    } else {
+        if (tid < M) {
+            fk[tid] = elu1(x[1][tid]);
+            pq[tid] = elu1(x[0][tid]);
+        }
+    }
+    __syncthreads();
+
+    // g(q) of this thread's four features.  FAVOR+: scaled by exp(-(max_m w_m.q)) and
+    // without the |q|^2/2 and sqrt(M) factors: y is invariant to any positive factor
+    // on g(q), and the largest feature becomes 1.
+    float gk[4], gq[4];
+    float qoff = 0.f;
+    if constexpr (C::FAVOR) {
+        qoff = wmax[0];
+#pragma unroll
+        for (int w = 1; w < NWF; ++w) qoff = fmaxf(qoff, wmax[w]);
+        qoff *= -LOG2E;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        gk[j] = fk[4 * cg + j];
+        gq[j] = C::FAVOR ? __builtin_amdgcn_exp2f(fmaf(pq[4 * cg + j], LOG2E, qoff)) : pq[4 * cg + j];
+    }
+
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int row = rs + p * RPP;
+        float part = 0.f;
+        if (row <= D) {
+            const float c = row < D ? x[2][row] : 1.f;
+            f4 r = st[p];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r[j] = fmaf(c, gk[j], r[j]);
+            *reinterpret_cast<f4 *>((row < D ? rout + (size_t)row * M : sout) + 4 * cg) = r;
+            part = r[0] * gq[0];
+#pragma unroll
+            for (int j = 1; j < 4; ++j) part = fmaf(r[j], gq[j], part);
+        }
+        // every lane of a row's group takes the same branch above; the shuffles stay
+        // outside it so that the whole wave executes them
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) part += __shfl_xor(part, o, 64);
+        if (row <= D && cg == 0) red[row] = part;
+    }
+    __syncthreads();
+    if (tid < D) ((T *)a.y)[bh * D + tid] = (T)(red[tid] / red[D]);
+}
+
+}  // namespace slim

@@ -1,7 +1,7 @@
 // slim_dispatch.h -- per-shape kernel tables (internal to libslim).
 #pragma once
 #include <hip/hip_runtime.h>
-#include "slim_kernels.h"
+#include "slim_decode.h"
 
 namespace slim {
 
@@ -15,6 +15,7 @@ struct KernelTable {
     void (*gstate)(dim3, hipStream_t, const ChunkArgs &);
     void (*bwdq)(dim3, hipStream_t, const ChunkArgs &);
     void (*bwdkv)(dim3, hipStream_t, const ChunkArgs &);
+    void (*decode)(dim3, hipStream_t, const DecodeArgs &);
 };
 
 // One lookup per (dtype, feature map) translation unit; NULL if the shape is not compiled.

@@ -14,6 +14,8 @@
 //       suffix scan (update (20)) -> dK, dV.  With several windows, a forward
 //       sweep over all chunk contributions first rebuilds the final state.
 // All carries are fp64.
+// The decode step (one token per head, Subsection 2.1's iterative evaluation) is
+// a single kernel with no workspace.
 // Only the carries (d x M + M per head) live across windows, so the workspace
 // is bounded by the window, not by L.
 #include <hip/hip_runtime.h>
@@ -243,11 +245,18 @@ static Plan plan(const slim_desc *d, int pass)
             off = align256(off + (size_t)d->d * d->M * (d->dtype == SLIM_BF16 ? 2 : 4));
         }
     }
-    p.total = pass == SLIM_PASS_FEATMAP ? 0 : off;
+    p.total = (pass == SLIM_PASS_FEATMAP || pass == SLIM_PASS_DECODE) ? 0 : off;
     return p;
 }
 
 static bool misaligned(const void *p, uintptr_t a) { return p && ((uintptr_t)p % a) != 0; }
+
+// Two fp32 ranges of n elements that overlap without being the same range.
+static bool overlaps_partly(const float *x, const float *y, long long n)
+{
+    if (!x || !y || x == y) return false;
+    return x < y + n && y < x + n;
+}
 
 }  // namespace slim
 
@@ -255,7 +264,7 @@ using namespace slim;
 
 extern "C" {
 
-int slim_version(void) { return (1 << 16) | 1; }
+int slim_version(void) { return (1 << 16) | 2; }
 
 slim_status slim_prof_enable(int enable)
 {
@@ -309,14 +318,16 @@ slim_status slim_validate(const slim_desc *d, int pass)
     if (!d) return SLIM_ERR_NULL;
     if (d->dtype != SLIM_F32 && d->dtype != SLIM_BF16) return SLIM_ERR_DTYPE;
     if (d->feat != SLIM_FEAT_FAVOR && d->feat != SLIM_FEAT_ELU1) return SLIM_ERR_DTYPE;
-    if (pass < SLIM_PASS_FEATMAP || pass > SLIM_PASS_BWD) return SLIM_ERR_SHAPE;
+    if (pass < SLIM_PASS_FEATMAP || pass > SLIM_PASS_DECODE) return SLIM_ERR_SHAPE;
     if (d->B < 1 || d->H < 1 || d->L < 1 || d->d < 1 || d->M < 1) return SLIM_ERR_SHAPE;
     if (d->L >= (1LL << 31) || d->B > (1LL << 31) || d->H > (1LL << 31)) return SLIM_ERR_SHAPE;
     if (pass != SLIM_PASS_FEATMAP && (d->num_chunks < 1 || d->num_chunks > d->L)) return SLIM_ERR_SHAPE;
     if (d->window_chunks < 0) return SLIM_ERR_SHAPE;
     if (d->feat == SLIM_FEAT_ELU1 && d->M != d->d) return SLIM_ERR_SHAPE;
+    if (pass == SLIM_PASS_DECODE && d->L != 1) return SLIM_ERR_SHAPE;
     const long long BH = d->B * d->H;
-    if (BH > 65535 && pass != SLIM_PASS_FEATMAP) return SLIM_ERR_UNSUPPORTED;
+    if (pass == SLIM_PASS_DECODE ? BH > (1LL << 24) : (BH > 65535 && pass != SLIM_PASS_FEATMAP))
+        return SLIM_ERR_UNSUPPORTED;
     if ((double)BH * (double)d->L * (double)(d->d > d->M ? d->d : d->M) > 4.0e18) return SLIM_ERR_SHAPE;
     if (!find(d)) return SLIM_ERR_UNSUPPORTED;
     return SLIM_OK;
@@ -477,6 +488,32 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
         narrow(dR_in, gR, p.BH * D * M, s);
         narrow(dS_in, gS, p.BH * M, s);
     }
+    return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
+}
+
+slim_status slim_decode_step(const slim_desc *d, const void *q, const void *k, const void *v, const void *W,
+                             const float *R_in, const float *S_in, void *y, float *R_out, float *S_out,
+                             void *stream)
+{
+    slim_status st = slim_validate(d, SLIM_PASS_DECODE);
+    if (st != SLIM_OK) return st;
+    if (!q || !k || !v || !y || !R_out || !S_out) return SLIM_ERR_NULL;
+    if (d->feat == SLIM_FEAT_FAVOR && !W) return SLIM_ERR_NULL;
+    if (d->feat == SLIM_FEAT_ELU1 && W) return SLIM_ERR_SHAPE;
+    if ((R_in == nullptr) != (S_in == nullptr)) return SLIM_ERR_NULL;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(W, 16) || misaligned(y, 16) ||
+        misaligned(R_in, 16) || misaligned(S_in, 16) || misaligned(R_out, 16) || misaligned(S_out, 16))
+        return SLIM_ERR_ALIGN;
+    // the state may be updated in place, but not through partly overlapping ranges
+    const long long BH = d->B * d->H;
+    if (overlaps_partly(R_in, R_out, BH * d->d * d->M) || overlaps_partly(S_in, S_out, BH * d->M))
+        return SLIM_ERR_SHAPE;
+    const KernelTable *kt = find(d);
+    hipStream_t s = (hipStream_t)stream;
+    DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.W = W;
+    a.Rin = R_in; a.Sin = S_in; a.y = y; a.Rout = R_out; a.Sout = S_out;
+    SLIM_TIMED("decode", s, kt->decode(dim3((unsigned)(d->B * d->H)), s, a));
     return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
 

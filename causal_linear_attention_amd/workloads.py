@@ -65,6 +65,51 @@ WORKLOADS = {
 HEADLINE = "favor_bf16_L16384_d64_M256"
 
 
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """Recurrent decoding: every step feeds one new token to each of B sequences
+    (all H heads) and updates their (d+1) x M fp32 states in place.  The state
+    of each head starts as the state after a `prefix`-token prompt."""
+    name: str
+    B: int
+    H: int
+    d: int
+    M: int
+    dtype: str
+    feat: str
+    w_kind: str
+    qkv_scale: float
+    seed: int
+    prefix: int = 64
+
+    @property
+    def heads(self) -> int:
+        return self.B * self.H
+
+
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        # the headline head shape, 512 sequences: 545 MB of state, more than the on-chip caches hold
+        DecodeWorkload("decode_favor_bf16_B512_H16_d64_M256", 512, 16, 64, 256, "bf16", "favor", "gaussian",
+                       64 ** -0.25, 6),
+        # 32 sequences: 34 MB of state, small enough to stay in the last-level cache between steps
+        DecodeWorkload("decode_favor_bf16_B32_H16_d64_M256", 32, 16, 64, 256, "bf16", "favor", "gaussian",
+                       64 ** -0.25, 6),
+    ]
+}
+
+DECODE_HEADLINE = "decode_favor_bf16_B512_H16_d64_M256"
+
+
+def decode_bytes_per_head(w: DecodeWorkload) -> int:
+    """Algorithmic HBM bytes of one decode step per head: the fp32 state [R; S]
+    read and written once, q, k, v read and y written once (W, shared by all
+    heads, is counted once per launch, not here)."""
+    s = 2 if w.dtype == "bf16" else 4
+    return 2 * (w.d + 1) * w.M * 4 + 4 * w.d * s
+
+
 def io_bytes_per_head_token(w: Workload, backward: bool = True) -> float:
     """Minimum HBM traffic per (token, head): read Q, K, V (+ dY) and write Y
     (+ dQ, dK, dV) once, in the I/O dtype."""

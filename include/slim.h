@@ -71,7 +71,7 @@ typedef enum slim_status {
 
 typedef enum slim_dtype { SLIM_F32 = 0, SLIM_BF16 = 1 } slim_dtype;
 typedef enum slim_feat { SLIM_FEAT_FAVOR = 0, SLIM_FEAT_ELU1 = 1 } slim_feat;
-typedef enum slim_pass { SLIM_PASS_FEATMAP = 0, SLIM_PASS_FWD = 1, SLIM_PASS_BWD = 2 } slim_pass;
+typedef enum slim_pass { SLIM_PASS_FEATMAP = 0, SLIM_PASS_FWD = 1, SLIM_PASS_BWD = 2, SLIM_PASS_DECODE = 3 } slim_pass;
 
 typedef struct slim_desc {
     int64_t B, H, L;       /* batch, heads, sequence length */
@@ -82,10 +82,11 @@ typedef struct slim_desc {
     int32_t feat;          /* slim_feat */
 } slim_desc;
 
-/* Host-only check of a descriptor for a pass; touches no GPU. */
+/* Host-only check of a descriptor for a pass; touches no GPU.  SLIM_PASS_DECODE
+ * requires L == 1 (one token per head) and allows B*H up to 2^24. */
 slim_status slim_validate(const slim_desc *desc, int pass);
 
-/* Workspace bytes the pass needs (0 for SLIM_PASS_FEATMAP); 0 if the
+/* Workspace bytes the pass needs (0 for SLIM_PASS_FEATMAP and SLIM_PASS_DECODE); 0 if the
  * descriptor is invalid.  Host-only. */
 size_t slim_workspace_bytes(const slim_desc *desc, int pass);
 
@@ -137,6 +138,26 @@ slim_status slim_attn_bwd(const slim_desc *desc, const void *Q, const void *K, c
                           const float *dS_out, void *dQ, void *dK, void *dV, float *dR_in, float *dS_in, void *ws,
                           size_t ws_bytes, void *stream);
 
+/* Recurrent decode step: the iterative prefix-sum evaluation of Subsection
+ * 2.1 (eq. (3)-(4)) advanced by one position.  For every b, h and the one new
+ * token (q, k, v):
+ *     R' = R + v g(k)^T,   S' = S + g(k),   y = R' g(q) / (S' . g(q)).
+ * This is what slim_attn_fwd computes for its first row, and a run of decode
+ * steps gives the same outputs and state as one slim_attn_fwd over the same
+ * tokens (up to fp32 rounding order).
+ * desc: L must be 1 (num_chunks therefore 1); window_chunks is ignored.
+ * In : q, k, v [B][H][d] (desc dtype); W as in the forward (NULL for elu+1);
+ *      R_in [B][H][d][M], S_in [B][H][M] fp32 = the state before the token
+ *      (both NULL = zero, i.e. the first token, or both given).
+ * Out: y [B][H][d]; R_out, S_out = the state after the token (required).
+ *      R_out may be the same pointer as R_in and S_out as S_in (update in
+ *      place); no other overlap of inputs and outputs is allowed.
+ * No workspace.  Two calls that update the same state must be ordered (same
+ * stream or synchronised). */
+slim_status slim_decode_step(const slim_desc *desc, const void *q, const void *k, const void *v, const void *W,
+                             const float *R_in, const float *S_in, void *y, float *R_out, float *S_out,
+                             void *stream);
+
 const char *slim_status_string(slim_status s);
 
 /* Kernel timing, for measurement tools.  slim_prof_enable(1) clears the
@@ -146,7 +167,7 @@ const char *slim_status_string(slim_status s);
  * wait for the recorded events to complete (they synchronise with those
  * events), then report per kernel name ("state", "scan_prefix", "fwd",
  * "scan_window", "scan_sum", "stats", "bwdq", "gstate", "scan_grad", "bwdkv",
- * "featmap") the summed
+ * "featmap", "decode") the summed
  * GPU time in milliseconds and the number of launches.  The name pointer stays
  * valid until the next slim_prof_enable(1).  Guarded by a process-wide mutex;
  * the timings are global to the process, not per stream. */

@@ -208,6 +208,17 @@ def attn_fwd_rows(Q, K, V, W, rows, feat="favor", R0=None, S0=None):
     return Yr, dr
 
 
+def decode_step(q, k, v, W=None, feat="favor", R0=None, S0=None):
+    """One position of the iterative prefix-sum evaluation (eq. (3)-(4) of
+    Subsection 2.1, walked one token at a time): q, k, v [B, H, d], state
+    R0 [B, H, d, M], S0 [B, H, M] (None = zero).  Returns (y [B, H, d], R, S),
+    the output for the new token and the state after it.  It is the prefix
+    form run over a sequence of length one from the given state."""
+    q, k, v = (_f64(t)[:, :, None, :] for t in (q, k, v))
+    Y, _, R, S = attn_fwd(q, k, v, W, feat, R0, S0, form="prefix")
+    return Y[:, :, 0, :], R, S
+
+
 def softmax_fwd(Q, K, V, threads=None):
     """Causal exponential attention (no temperature); [B, H, L, d] -> Y."""
     lib = load()

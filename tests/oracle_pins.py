@@ -219,6 +219,45 @@ def pin_rows_match_full():
     assert _relerr(Yr, Y[0, 1, rows]) < 1e-14
 
 
+def pin_decode_golden():
+    # The hand-worked rows again, now fed one token at a time through the decode
+    # step (eq. (3)-(4) advanced by one position), starting from the zero state.
+    for c in json.load(open(GOLDEN))["cases"]:
+        if "Y" not in c:
+            continue
+        W = np.array(c["W"]) if "W" in c else None
+        want = np.array([_ev(e) for e in c["Y"]])
+        R = S = None
+        for l, w in enumerate(want):
+            tok = [np.asarray(c[n][l], dtype=np.float64)[None, None] for n in ("Q", "K", "V")]
+            y, R, S = oracle.decode_step(*tok, W, c["feat"], R, S)
+            assert abs(y[0, 0, 0] - w) <= 1e-13 * abs(w), (c["name"], l, y, w)
+
+
+def pin_decode_steps_equal_quadratic():
+    # A run of decode steps from an initial state reproduces every row of the
+    # masked definition and its final state.
+    for feat, d, M in (("favor", 3, 7), ("elu1", 4, 4)):
+        Q, K, V, W = _qkv(21, 10, d, M)
+        R = _rand(22, 1, 2, d, M)
+        S = np.abs(_rand(23, 1, 2, M)) + 0.5
+        Yq, _, Rq, Sq = oracle.attn_fwd(Q, K, V, W, feat, R0=R, S0=S, form="quadratic")
+        for l in range(Q.shape[2]):
+            y, R, S = oracle.decode_step(Q[:, :, l], K[:, :, l], V[:, :, l], W, feat, R, S)
+            assert _relerr(y, Yq[:, :, l]) < 1e-13, (feat, l)
+        assert _relerr(R, Rq) < 1e-13 and _relerr(S, Sq) < 1e-13, feat
+
+
+def pin_decode_first_token_is_value():
+    # From the zero state the only weight is on the token itself: y = v.
+    Q, K, V, W = _qkv(24, 1, 5, 9)
+    y, R, S = oracle.decode_step(Q[:, :, 0], K[:, :, 0], V[:, :, 0], W, "favor")
+    assert np.allclose(y, V[:, :, 0], rtol=1e-14)
+    phik = oracle.featmap(K[:, :, 0], W, "favor")
+    assert np.allclose(S, phik, rtol=1e-15)
+    assert np.allclose(R, V[:, :, 0, :, None] * phik[:, :, None, :], rtol=1e-15)
+
+
 def pin_softmax_special_cases():
     Q, K, V, _ = _qkv(21, 10, 3, 1)
     # Q = 0 => all scores equal => running mean
@@ -327,7 +366,8 @@ ALL_PINS = [
     pin_featmap_golden, pin_featmap_zero_input, pin_elu1_values, pin_favor_unbiased,
     pin_featmap_vjp_fd, pin_fwd_golden, pin_single_row_is_value, pin_identical_keys_give_running_mean,
     pin_constant_values, pin_causality, pin_convex_hull, pin_quadratic_equals_prefix,
-    pin_initial_state_is_a_prefix, pin_rows_match_full, pin_softmax_special_cases,
+    pin_initial_state_is_a_prefix, pin_rows_match_full, pin_decode_golden, pin_decode_steps_equal_quadratic,
+    pin_decode_first_token_is_value, pin_softmax_special_cases,
     pin_favor_converges_to_softmax, pin_bwd_finite_differences, pin_bwd_special_cases,
     pin_bwd_quadratic_equals_prefix,
 ]

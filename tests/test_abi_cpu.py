@@ -133,3 +133,31 @@ def test_tile_rows(lib):
     assert tr(d=128, M=256, dtype=_lib.SLIM_F32) == 16
     assert tr(d=16, M=16, dtype=_lib.SLIM_F32) == 32
     assert tr(d=48) == 0                                           # invalid descriptor
+
+
+def test_decode_validation(lib):
+    assert validate(lib, _lib.SLIM_PASS_DECODE, L=1, num_chunks=1) == 0
+    assert validate(lib, _lib.SLIM_PASS_DECODE, L=2, num_chunks=1) == 2       # one token per head
+    assert validate(lib, _lib.SLIM_PASS_DECODE, L=1, num_chunks=1, B=1 << 12, H=1 << 12) == 0
+    assert validate(lib, _lib.SLIM_PASS_DECODE, L=1, num_chunks=1, B=1 << 12, H=(1 << 12) + 1) == 4
+    assert validate(lib, 4) == 2                                              # unknown pass
+    assert ws(lib, _lib.SLIM_PASS_DECODE, L=1, num_chunks=1) == 0
+
+
+def test_decode_rejects_before_any_launch(lib):
+    d = d_(L=1, num_chunks=1)
+    p = ctypes.c_void_p(1 << 20)  # never dereferenced: every case fails on the host
+    assert lib.slim_decode_step(ctypes.byref(d), None, p, p, p, None, None, p, p, p, None) == 1
+    assert lib.slim_decode_step(ctypes.byref(d), p, p, p, None, None, None, p, p, p, None) == 1   # FAVOR+ W
+    assert lib.slim_decode_step(ctypes.byref(d), p, p, p, p, p, None, p, p, p, None) == 1         # lone R_in
+    assert lib.slim_decode_step(ctypes.byref(d), p, p, p, p, None, None, p, None, p, None) == 1   # R_out
+    assert lib.slim_decode_step(ctypes.byref(d_(L=2, num_chunks=1)), p, p, p, p, None, None, p, p, p, None) == 2
+    bad = ctypes.c_void_p((1 << 20) + 8)
+    assert lib.slim_decode_step(ctypes.byref(d), p, p, p, p, None, None, bad, p, p, None) == 6
+    # in place is allowed; a partly overlapping state is not
+    r_in = ctypes.c_void_p(1 << 24)
+    r_out = ctypes.c_void_p((1 << 24) + 256)
+    s_ = ctypes.c_void_p(1 << 28)
+    assert lib.slim_decode_step(ctypes.byref(d), p, p, p, p, r_in, s_, p, r_out, s_, None) == 2
+    de = d_(L=1, num_chunks=1, feat=_lib.SLIM_FEAT_ELU1, M=64)
+    assert lib.slim_decode_step(ctypes.byref(de), p, p, p, p, None, None, p, p, p, None) == 2    # elu+1: no W

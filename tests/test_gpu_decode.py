@@ -1,0 +1,147 @@
+"""Parity of the recurrent decode step (slim_decode_step) with the fp64 oracle.
+
+The oracle's decode step is its prefix-sum recurrence run over one position
+(page "Sub-Linear Memory: How to Make Performers SLiM", Subsection 2.1,
+eq. (3)-(4)); it receives exactly the values the GPU received (io-dtype
+inputs, the fp32 state).  Outputs y are compared normwise per head at the
+io dtype's tolerance; the fp32 states at 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DT, TOL, host64, inputs, relerr_heads, to_dev
+from causal_linear_attention_amd import attention as A
+
+pytestmark = pytest.mark.gpu
+
+TOL_STATE = 1e-5
+
+# (B, H, d, M, dtype, feat)
+CASES = [
+    (3, 5, 64, 256, "bf16", "favor"),
+    (2, 3, 16, 16, "f32", "favor"),
+    (1, 7, 32, 64, "f32", "favor"),
+    (2, 2, 128, 256, "bf16", "favor"),
+    (2, 4, 64, 64, "bf16", "favor"),
+    (1, 3, 16, 256, "f32", "favor"),
+    (3, 2, 128, 128, "bf16", "elu1"),
+    (2, 2, 16, 16, "f32", "elu1"),
+]
+
+
+def _ids(c):
+    return "B%d_H%d_d%d_M%d_%s_%s" % c
+
+
+def _token(B, H, d, M, dt, feat, seed, scale=None):
+    t = inputs(B, H, 1, d, M, DT[dt], feat, seed=seed, scale=scale, dy=False)
+    q, k, v = (t[n][:, :, 0, :].contiguous() for n in ("q", "k", "v"))
+    return q, k, v, t["W"]
+
+
+def _state(B, H, d, M, dt, feat, seed, W, L=12):
+    """A state reached by a real prefix of L tokens (fp32 on the device)."""
+    t = inputs(B, H, L, d, M, DT[dt], feat, seed=seed, dy=False)
+    _, _, R, S = oracle.attn_fwd(t["q"], t["k"], t["v"], W, feat, form="prefix")
+    return (torch.from_numpy(R).float().cuda().contiguous(), torch.from_numpy(S).float().cuda().contiguous())
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_decode_step_matches_oracle(case):
+    B, H, d, M, dt, feat = case
+    print("decode", case, flush=True)
+    q, k, v, W = _token(B, H, d, M, dt, feat, seed=31)
+    R, S = _state(B, H, d, M, dt, feat, 32, W)
+    y, R2, S2 = A.decode_step(q, k, v, W, feat, R, S)
+    torch.cuda.synchronize()
+    yo, Ro, So = oracle.decode_step(q, k, v, W, feat, host64(R), host64(S))
+    assert relerr_heads(host64(y), yo) < TOL[DT[dt]]
+    assert relerr_heads(host64(R2), Ro) < TOL_STATE
+    assert relerr_heads(host64(S2), So) < TOL_STATE
+    # inputs untouched (not in place)
+    assert torch.equal(R, _state(B, H, d, M, dt, feat, 32, W)[0])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("feat", ["favor", "elu1"])
+def test_first_token_gives_its_value(dt, feat):
+    B, H, d = 2, 3, 64
+    M = 128 if feat == "favor" else d
+    q, k, v, W = _token(B, H, d, M, dt, feat, seed=33)
+    y, R, S = A.decode_step(q, k, v, W, feat)
+    torch.cuda.synchronize()
+    if dt == "bf16":  # v (1 + O(1e-7)) rounds back to v
+        assert torch.equal(y, v)
+    else:
+        assert relerr_heads(host64(y), host64(v)) < 1e-6
+    _, Ro, So = oracle.decode_step(q, k, v, W, feat)
+    assert relerr_heads(host64(R), Ro) < TOL_STATE
+    assert relerr_heads(host64(S), So) < TOL_STATE
+
+
+@pytest.mark.parametrize("dt,feat,d,M", [("bf16", "favor", 64, 256), ("f32", "favor", 32, 64),
+                                         ("bf16", "elu1", 128, 128)])
+def test_decode_run_equals_chunked_forward_and_oracle(dt, feat, d, M):
+    # T decode steps in place == one chunked forward over the T tokens == the definition
+    B, H, T = 2, 3, 40
+    print("decode run", dt, feat, d, M, flush=True)
+    t = inputs(B, H, T, d, M, DT[dt], feat, seed=34, dy=False)
+    R0, S0 = _state(B, H, d, M, dt, feat, 35, t["W"])
+    R, S = R0.clone(), S0.clone()
+    ys = []
+    for l in range(T):
+        tok = [t[n][:, :, l, :].contiguous() for n in ("q", "k", "v")]
+        y, R_, S_ = A.decode_step(*tok, t["W"], feat, R, S, inplace=True)
+        assert R_ is R and S_ is S
+        ys.append(y)
+    Yd = torch.stack(ys, dim=2)
+    Yc, Rc, Sc = A.attn_fwd(t["q"], t["k"], t["v"], t["W"], feat, num_chunks=3, R_in=R0, S_in=S0)
+    torch.cuda.synchronize()
+    Yo, _, Ro, So = oracle.attn_fwd(t["q"], t["k"], t["v"], t["W"], feat, R0=host64(R0), S0=host64(S0))
+    tol = TOL[DT[dt]]
+    assert relerr_heads(host64(Yd), Yo) < tol
+    assert relerr_heads(host64(Yc), Yo) < tol
+    assert relerr_heads(host64(R), Ro) < TOL_STATE and relerr_heads(host64(S), So) < TOL_STATE
+    # the chunked forward multiplies bf16 copies of the features on the matrix cores, so
+    # its state carries bf16 rounding; the decode step keeps them in fp32
+    assert relerr_heads(host64(R), host64(Rc)) < tol
+
+
+def test_in_place_equals_out_of_place():
+    B, H, d, M = 2, 4, 64, 256
+    q, k, v, W = _token(B, H, d, M, "bf16", "favor", seed=36)
+    R, S = _state(B, H, d, M, "bf16", "favor", 37, W)
+    y1, R1, S1 = A.decode_step(q, k, v, W, "favor", R, S)
+    y2, R2, S2 = A.decode_step(q, k, v, W, "favor", R.clone(), S.clone(), inplace=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(R1, R2) and torch.equal(S1, S2)
+
+
+def test_wide_query_range():
+    # large query projections: the per-token query offset keeps g(q) finite
+    B, H, d, M = 1, 4, 64, 256
+    q, k, v, W = _token(B, H, d, M, "f32", "favor", seed=38)
+    q = (q * 12.0).contiguous()
+    R, S = _state(B, H, d, M, "f32", "favor", 39, W)
+    y, R2, S2 = A.decode_step(q, k, v, W, "favor", R, S)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    yo, _, _ = oracle.decode_step(q, k, v, W, "favor", host64(R), host64(S))
+    assert relerr_heads(host64(y), yo) < 1e-4
+
+
+def test_many_heads():
+    # more heads than one grid dimension of the chunked path allows (65535)
+    B, H, d, M = 300, 256, 16, 16
+    q, k, v, W = _token(B, H, d, M, "bf16", "favor", seed=40)
+    R = torch.rand((B, H, d, M), device="cuda") - 0.5
+    S = torch.rand((B, H, M), device="cuda") + 0.5
+    y, R2, S2 = A.decode_step(q, k, v, W, "favor", R, S)
+    torch.cuda.synchronize()
+    idx = np.random.default_rng(0).choice(B * H, 64, replace=False)
+    sel = lambda x: host64(x).reshape((B * H,) + tuple(x.shape[2:]))[idx][:, None]  # noqa: E731
+    yo, Ro, So = oracle.decode_step(sel(q), sel(k), sel(v), W, "favor", sel(R), sel(S))
+    assert relerr_heads(sel(y), yo) < TOL[torch.bfloat16]
+    assert relerr_heads(sel(R2), Ro) < TOL_STATE and relerr_heads(sel(S2), So) < TOL_STATE
