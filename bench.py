@@ -56,8 +56,8 @@ def parse():
     ap.add_argument("--decode", action="store_true",
                     help="time the recurrent decode step (one token per sequence per step) instead")
     ap.add_argument("--pmc-summary", default=None, metavar="DIR",
-                    help="DIR holds rocprofv3 counter runs F, W (FETCH_SIZE, WRITE_SIZE of --profile-run) "
-                         "and CF, CW (the same of --copy-calib); writes profiles/traffic_<workload>.md")
+                    help="DIR holds rocprofv3 counter runs F, W (FETCH_SIZE, WRITE_SIZE of --profile-run; "
+                         "DF, DW with --decode) and CF, CW (the same of --copy-calib); prints the summary")
     return ap.parse_args()
 
 
@@ -98,9 +98,11 @@ def read_counter(path, counter):
     return out
 
 
-def pmc_summary(d, w, bytes_of_copy):
-    fetch = read_counter(glob.glob(os.path.join(d, "F", "*counter_collection.csv"))[0], "FETCH_SIZE")
-    write = read_counter(glob.glob(os.path.join(d, "W", "*counter_collection.csv"))[0], "WRITE_SIZE")
+def pmc_summary(d, w, bytes_of_copy, runs=("F", "W")):
+    """HBM bytes per dispatch and kernel from counter runs in d: runs[0] (FETCH_SIZE) and
+    runs[1] (WRITE_SIZE) of the workload, CF and CW of the calibration copy."""
+    fetch = read_counter(glob.glob(os.path.join(d, runs[0], "*counter_collection.csv"))[0], "FETCH_SIZE")
+    write = read_counter(glob.glob(os.path.join(d, runs[1], "*counter_collection.csv"))[0], "WRITE_SIZE")
     cf = read_counter(glob.glob(os.path.join(d, "CF", "*counter_collection.csv"))[0], "FETCH_SIZE")["copy"]
     cw = read_counter(glob.glob(os.path.join(d, "CW", "*counter_collection.csv"))[0], "WRITE_SIZE")["copy"]
     # the calibration copy reads and writes bytes_of_copy per launch
@@ -251,7 +253,7 @@ def decode_main(args, torch, _lib, A, synth):
     from causal_linear_attention_amd.workloads import DECODE_HEADLINE, DECODE_WORKLOADS, decode_bytes_per_head
     w = DECODE_WORKLOADS[args.workload or DECODE_HEADLINE]
     if args.pmc_summary:
-        print(json.dumps(pmc_summary(args.pmc_summary, w, 1 << 30)))
+        print(json.dumps(pmc_summary(args.pmc_summary, w, 1 << 30, runs=("DF", "DW"))))
         return
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     W = None
