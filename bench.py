@@ -15,6 +15,7 @@ and the fp64 CPU oracle timed on a bounded sample of the same workload.
   python bench.py --copy-calib      # one plain copy kernel of known size (PMC calibration)
   python bench.py --pmc-summary DIR # (host only) HBM traffic per kernel from rocprofv3 counter CSVs
   python bench.py --decode [...]    # the recurrent decode step instead (one JSON line of its own)
+  python bench.py --chunk-sweep     # time, peak HBM and gradient discrepancy vs slice length (one JSON line)
 
 roofline.traffic: HBM bytes per launch of the dominant kernel, FETCH_SIZE and
 WRITE_SIZE scaled by what the same counters read for a plain copy of known
@@ -53,6 +54,12 @@ def parse():
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--mem-sweep", action="store_true",
                     help="peak HBM of one fwd+bwd step vs L at the 1M-token workload's shape (one JSON line)")
+    ap.add_argument("--chunk-sweep", action="store_true",
+                    help="fwd+bwd time, peak HBM and gradient discrepancy against one unsliced run for slice "
+                         "lengths 1, 2, 4, ..., L at the headline head shape (one JSON line)")
+    ap.add_argument("--sweep-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--sweep-window", type=int, default=0, help="window_chunks of the swept runs (0 = auto)")
+    ap.add_argument("--sweep-cmax", type=int, default=0, help="largest slice length swept (0 = L)")
     ap.add_argument("--decode", action="store_true",
                     help="time the recurrent decode step (one token per sequence per step) instead")
     ap.add_argument("--pmc-summary", default=None, metavar="DIR",
@@ -312,6 +319,65 @@ def decode_main(args, torch, _lib, A, synth):
     print(json.dumps(rec))
 
 
+def chunk_sweep(torch, A, synth, w, dtype, window, cmax):
+    """The page's time / memory / precision trade-off at op level (its Figure 2 study,
+    for this one operation): for slice lengths c = 1, 2, 4, ..., cmax, one fwd+bwd step's
+    time and peak HBM, and the relative discrepancy ||grad_c - grad_L|| / ||grad_L|| of
+    (dQ, dK, dV) against the unsliced run; beside each, the time and peak HBM of the
+    unsliced computation on an input of length c alone.  `window` = slices whose states
+    are held at once (0 = automatic, about 4096 workgroups per launch; 1 = the page's
+    order, one slice after another).  Peak HBM is max_memory_allocated over one step
+    minus what was allocated before it (inputs resident; outputs and workspaces count)."""
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    shp = (w.B, w.H, w.L, w.d)
+    q = synth.device_normal(w.seed, synth.TID_Q, shp, w.qkv_scale).to(dt)
+    k = synth.device_normal(w.seed, synth.TID_K, shp, w.qkv_scale).to(dt)
+    v = synth.device_normal(w.seed, synth.TID_V, shp, 1.0).to(dt)
+    dy = synth.device_normal(w.seed, synth.TID_DY, shp, 1.0).to(dt)
+    W = torch.from_numpy(synth.projection(w.seed, w.M, w.d, w.w_kind)).cuda().to(dt).contiguous()
+
+    def step(qq, kk, vv, dd, chunks, win):
+        A.attn_fwd(qq, kk, vv, W, w.feat, chunks, window_chunks=win)
+        return A.attn_bwd(qq, kk, vv, W, dd, w.feat, chunks, window_chunks=win)[:3]
+
+    def measure(qq, kk, vv, dd, chunks, win, reps):
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        g = step(qq, kk, vv, dd, chunks, win)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            step(qq, kk, vv, dd, chunks, win)
+        torch.cuda.synchronize()
+        return g, 1e3 * (time.perf_counter() - t0) / reps, peak
+
+    full, full_ms, full_peak = measure(q, k, v, dy, 1, 0, 3)
+    fnorm = sum(float(x.double().pow(2).sum()) for x in full) ** 0.5
+    rows = []
+    c = 1
+    while c <= min(cmax or w.L, w.L):
+        chunks = -(-w.L // c)
+        reps = 1 if chunks > 4096 else 2 if c < 64 else 5
+        g, ms, peak = measure(q, k, v, dy, chunks, window, reps)
+        disc = sum(float((a.double() - b.double()).pow(2).sum()) for a, b in zip(g, full)) ** 0.5 / fnorm
+        del g
+        sl = [x[:, :, :c].contiguous() for x in (q, k, v, dy)]
+        g, ms_c, peak_c = measure(*sl, 1, 0, 5)
+        del sl, g
+        rows.append({"c": c, "chunks": chunks, "ms_per_step": round(ms, 4), "step_peak_bytes": peak,
+                     "grad_discrepancy": disc, "full_on_c_ms": round(ms_c, 4), "full_on_c_peak_bytes": peak_c})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        c *= 2
+    # the explicit prefix-sum evaluation (eq. (4) materialised) would hold L d M fp32 per head
+    return {"chunk_sweep": w.name, "dtype": dtype, "window_chunks": window, "B": w.B, "H": w.H, "L": w.L,
+            "d": w.d, "M": w.M, "unsliced_ms": round(full_ms, 4), "unsliced_peak_bytes": full_peak,
+            "io_bytes": 4 * q.numel() * q.element_size(),
+            "explicit_prefix_state_bytes": w.B * w.H * w.L * w.d * w.M * 4, "rows": rows}
+
+
 def kernel_records(w, prof, steps, tile):
     """Per-kernel records from the library's hipEvent timings {name: (ms total, launches)}
     over `steps` steps, and the roofline record of the dominant kernel."""
@@ -381,6 +447,11 @@ def main():
 
     if args.decode:
         decode_main(args, torch, _lib, A, synth)
+        return
+
+    if args.chunk_sweep:
+        print(json.dumps(chunk_sweep(torch, A, synth, WORKLOADS[args.workload or HEADLINE], args.sweep_dtype,
+                                     args.sweep_window, args.sweep_cmax)))
         return
 
     if args.mem_sweep:
