@@ -258,6 +258,23 @@ constexpr int ROWSTAT = 4;
 // issues the global reads (rows >= nvalid read as zero) and returns at once, so a
 // tile can be fetched while the previous one is being computed; store() moves it
 // into LDS once the data is needed.
+// The same pointer, moved to scalar registers (it must be uniform across the wave).
+// Tile loads then address base + 32-bit lane offset, so the compiler keeps one small
+// offset per lane instead of a 64-bit pointer per tensor and lane across the tile loop.
+template <typename T> __device__ __forceinline__ const T *uniform_ptr(const T *p)
+{
+    const unsigned long long a = (unsigned long long)p;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+    return (const T *)(((unsigned long long)hi << 32) | lo);
+}
+// Load through a global-memory pointer (a pointer rebuilt from integers is generic,
+// which would make the compiler emit flat loads).
+template <typename U> __device__ __forceinline__ U gload(const void *p)
+{
+    return *(const __attribute__((address_space(1))) U *)p;
+}
+
 template <typename T, int D, int TT, int NT> struct TileRegs {
     typedef typename Vec16<T>::type V;
     static constexpr int EPV = Vec16<T>::N;
@@ -270,13 +287,15 @@ template <typename T, int D, int TT, int NT> struct TileRegs {
     // stats (optional): per-row (scale, unused) pairs; row t's scale goes with its vectors.
     __device__ __forceinline__ void load(const T *__restrict__ src, int nvalid, const float *stats = nullptr)
     {
+        const T *base = uniform_ptr(src);
+        const float *sbase = stats ? uniform_ptr(stats) : nullptr;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int idx = threadIdx.x + i * NT;
             const int t = idx / VPR, c = (idx % VPR) * EPV;
             const bool ok = idx < NV && t < nvalid;
-            v[i] = ok ? *reinterpret_cast<const V *>(src + (size_t)t * D + c) : zero16<T>();
-            if (stats) s[i] = ok ? stats[(size_t)t * ROWSTAT] : 0.f;
+            v[i] = ok ? gload<V>(base + (unsigned)(t * D + c)) : zero16<T>();
+            if (stats) s[i] = ok ? gload<float>(sbase + (unsigned)(t * ROWSTAT)) : 0.f;
         }
     }
     // Move the tile into an LDS matrix (rows t, columns e); scaled: multiply row t
@@ -326,9 +345,10 @@ template <int TT> struct RowStatRegs {
     {
         const int t = threadIdx.x;
         const bool ok = t < TT && t < nvalid;
-        inv = ok ? st[(size_t)t * ROWSTAT] : 0.f;
-        dd = ok ? st[(size_t)t * ROWSTAT + 1] : 0.f;
-        qoff = ok ? st[(size_t)t * ROWSTAT + 2] : 0.f;
+        const float *sb = uniform_ptr(st) + (unsigned)(t * ROWSTAT);
+        inv = ok ? gload<float>(sb) : 0.f;
+        dd = ok ? gload<float>(sb + 1) : 0.f;
+        qoff = ok ? gload<float>(sb + 2) : 0.f;
     }
 };
 
