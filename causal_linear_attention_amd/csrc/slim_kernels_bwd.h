@@ -253,6 +253,12 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
     load_state_E<C>(r, slot_ptr<C>(a.slots, a, G.bh, G.nl));
     BwdRegs<C> rg;
     rg.load(Q, K, V, dY, st, 0, G.len);
+    // W^T fragments of this wave's features, held over the tile loop (reloading them per
+    // tile put their cache latency on the dQ chain)
+    Frag<T> wt[C::FAVOR ? NEB : 1][NFB];
+    if constexpr (C::FAVOR)
+#pragma unroll
+        for (int eb = 0; eb < NEB; ++eb) load_wtfrag_block<C>(wt[eb], a.Wt, eb);
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
         rg.store(xq, xk, Vt, DN, kn2, qoff, nv);
@@ -298,7 +304,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
             }
         if constexpr (C::FAVOR) {
             // dQ^T (rows e, cols t) = W^T (dg(Q) . g(Q))^T over own features, reduced across
-            // waves; the W^T fragments are read (from cache) per value block here.
+            // waves.
             Frag<T> gq[NFB][NTB];
 #pragma unroll
             for (int fb = 0; fb < NFB; ++fb)
@@ -306,12 +312,10 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
                 for (int tb = 0; tb < NTB; ++tb) gq[fb][tb] = cfrag<T>(dq[fb][tb] * pq[fb][tb]);
 #pragma unroll
             for (int eb = 0; eb < NEB; ++eb) {
-                Frag<T> wt[NFB];
-                load_wtfrag_block<C>(wt, a.Wt, eb);
 #pragma unroll
                 for (int tb = 0; tb < NTB; ++tb) {
                     f4 acc = f4zero();
-                    mma_range<T>(acc, 0, NFB, [&](int fb) { return wt[fb]; }, [&](int fb) { return gq[fb][tb]; });
+                    mma_range<T>(acc, 0, NFB, [&](int fb) { return wt[eb][fb]; }, [&](int fb) { return gq[fb][tb]; });
                     put_red<C>(red, eb, tb, acc);
                 }
             }
@@ -401,13 +405,14 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
     rg.load(Q, K, V, dY, st, last, G.len);
     for (int t0 = last; t0 >= 0; t0 -= TT) {
         const int nv = min(TT, G.len - t0);
+        // W fragments are re-read (from cache) every tile rather than held over the loop;
+        // issued before the tile's staging and barrier, which cover their latency
+        Frag<T> wf[NFB][NEB];
+        if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
         rg.store(xq, xk, Vt, DN, kn2, qoff, nv);
         __syncthreads();
         Frag<T> fq[NFB][NTB], fkT[NFB][NTB];
         {
-            // W fragments are re-read (from cache) every tile rather than held over the loop
-            Frag<T> wf[NFB][NEB];
-            if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
             f4 pq[NFB][NTB];
             feat_T<C>(pq, xq, wf);
             q_finish_off<C>(pq, qoff);
