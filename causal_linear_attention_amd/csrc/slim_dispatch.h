@@ -12,7 +12,7 @@ struct KernelTable {
     void (*state)(dim3, hipStream_t, const ChunkArgs &);
     void (*fwd)(dim3, hipStream_t, const ChunkArgs &);
     void (*stats)(dim3, hipStream_t, const ChunkArgs &);
-    void (*gstate)(dim3, hipStream_t, const ChunkArgs &);
+    void (*gstate)(dim3, hipStream_t, const ChunkArgs &);  // NULL: the dQ kernel does its work
     void (*bwdq)(dim3, hipStream_t, const ChunkArgs &);
     void (*bwdkv)(dim3, hipStream_t, const ChunkArgs &);
     void (*decode)(dim3, hipStream_t, const DecodeArgs &);

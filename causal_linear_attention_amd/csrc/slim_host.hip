@@ -10,8 +10,9 @@
 //       state; several: the window's start state recovered from the state
 //       after it by subtraction, update (19) at window granularity, then a
 //       forward prefix) -> stats (recompute forward, per-row statistics) -> dQ
-//       -> gstate (the slice's gradient w.r.t. its entry state) -> gradient
-//       suffix scan (update (20)) -> dK, dV.  With several windows, a forward
+//       -> gstate (the slice's gradient w.r.t. its entry state; folded into the
+//       dQ kernel where its registers allow) -> gradient suffix scan (update
+//       (20)) -> dK, dV.  With several windows, a forward
 //       sweep over all chunk contributions first rebuilds the final state.
 // All carries are fp64.
 // The decode step (one token per head, Subsection 2.1's iterative evaluation) is
@@ -479,8 +480,12 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
             scan(1, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
         }
         SLIM_TIMED("stats", s, kt->stats(dim3(np, BH), s, a));
-        SLIM_TIMED("bwdq", s, kt->bwdq(dim3(np, BH), s, a));
-        SLIM_TIMED("gstate", s, kt->gstate(dim3(np, BH), s, a));
+        if (kt->gstate) {
+            SLIM_TIMED("bwdq", s, kt->bwdq(dim3(np, BH), s, a));
+            SLIM_TIMED("gstate", s, kt->gstate(dim3(np, BH), s, a));
+        } else {
+            SLIM_TIMED("bwdq_gstate", s, kt->bwdq(dim3(np, BH), s, a));
+        }
         scan(2, a.gslots, gR, gS, D, M, (int)p.P, np, BH, s);
         SLIM_TIMED("bwdkv", s, kt->bwdkv(dim3(np, BH), s, a));
     }

@@ -40,8 +40,8 @@
 //   fwd_kernel     : Y for a chunk from its entry state.
 //   stats_kernel   : backward pass 1: recompute the chunk forward, emit per-row
 //                    1/den and dden = -(dY.Y)/den.
-//   bwdq_kernel    : dQ (forward tile order, entry state R).
-//   gstate_kernel  : the chunk's gradient contribution to its entry state,
+//   bwdq_kernel    : dQ (forward tile order, entry state R), and the chunk's
+//                    gradient contribution to its entry state,
 //                    dG_n = sum dNum g(Q)^T (and dden g(Q)).
 //   bwdkv_kernel   : dK, dV (reverse tile order, gradient state dR).
 #pragma once

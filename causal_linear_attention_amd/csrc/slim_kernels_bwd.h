@@ -217,8 +217,14 @@ template <class C> struct BwdRegs {
     }
 };
 
-// bwdq_kernel: dQ of one chunk.  Tiles in forward order, carrying the entry
-// state [R; S] (rows e, cols m) from slot[n].
+// bwdq_kernel: dQ of one chunk.  Tiles in forward order, carrying the entry state
+// [R; S] (rows e, cols m) from slot[n].  Where its registers allow (bf16 with d <= 32,
+// or d = 64 with M >= 128; fp32 with d <= 32), it also accumulates the gstate_kernel's
+// result from the g(Q) it already has, and the gstate_kernel is not launched.
+template <class C> constexpr bool bwdq_fuses_gstate()
+{
+    return C::D <= 32 || (sizeof(typename C::T) == 2 && C::D <= 64 && C::M >= 128);
+}
 template <class C> struct BwdqSmem {
     typedef typename C::T T;
     __align__(16) T xq[C::XMat::SIZE];
@@ -228,6 +234,7 @@ template <class C> struct BwdqSmem {
     __align__(16) T dn[C::XMat::SIZE];
     __align__(16) T dna[C::AuxMat::SIZE];
     __align__(16) T fk[C::NW * C::FMat::SIZE];
+    __align__(16) T fq[bwdq_fuses_gstate<C>() ? C::NW * C::FMat::SIZE : 8];
     __align__(16) float red[C::FAVOR ? C::NW * C::TT * C::LDR : 4];
     float kn2[C::TT], qoff[C::TT];
 };
@@ -241,11 +248,19 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
     const typename C::XMat xq(sm.xq), xk(sm.xk);
     const AugTile<C> Vt(sm.xv, sm.xva), DN(sm.dn, sm.dna);
     const typename C::FMat Fk(sm.fk + wave_id() * C::FMat::SIZE);
+    const typename C::FMat Fq(sm.fq + wave_id() * C::FMat::SIZE);
     const ChunkGeom G = chunk_geom<C>(a);
     const int w = wave_id(), g = lgrp(), lc = lcol();
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     const T *dY = (const T *)a.dY + G.hb;
     T *dQ = (T *)a.out0 + G.hb;
+    constexpr bool FG = bwdq_fuses_gstate<C>();
+    f4 dg[FG ? NFB : 1][FG ? NEA : 1];  // the chunk's gradient w.r.t. its entry state, own features
+    if constexpr (FG)
+#pragma unroll
+        for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+            for (int eb = 0; eb < NEA; ++eb) dg[fb][eb] = f4zero();
     const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
     Frag<T> wf[NFB][NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
@@ -267,6 +282,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
         f4 pq[NFB][NTB];
         feat_T<C>(pq, xq, wf);
         q_finish_off<C>(pq, qoff);
+        if constexpr (FG) put_features<C>(Fq, pq);
         {
             f4 pkT[NFB][NTB];
             feat_T<C>(pkT, xk, wf);
@@ -288,7 +304,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
                         if (4 * g + j > lc) acc[j] = 0.f;
                 at[sb][tb] = cfrag<T>(acc);
             }
-        wave_lds_fence();  // Fk written by this wave above
+        wave_lds_fence();  // Fk, Fq written by this wave above
         // dg(Q)^T blocks (rows m, cols t) = g(K)^T A^T + [R; S]^T [dNum | dden]^T
         f4 dq[NFB][NTB];
 #pragma unroll
@@ -336,15 +352,20 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
                     if (t < nv) store4<T>(dQ + (size_t)(t0 + t) * D + w * MW + fb * 16 + 4 * g, v);
                 }
         }
-        // [R; S] += [V | 1]^T g(K)
+        // [R; S] += [V | 1]^T g(K);  fused: [dG | dGs] += g(Q)^T [dNum | dden]
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-            for (int eb = 0; eb < NEA; ++eb)
+            for (int eb = 0; eb < NEA; ++eb) {
                 mma_range<T>(r[eb][fb], 0, NTB, [&](int tb) { return Vt.fr(eb, tb * 16); },
                              [&](int tb) { return Fk.frag_r(fb * 16, tb * 16); });
+                if constexpr (FG)
+                    mma_range<T>(dg[fb][eb], 0, NTB, [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); },
+                                 [&](int tb) { return DN.fr(eb, tb * 16); });
+            }
         __syncthreads();
     }
+    if constexpr (FG) store_state_T<C>(slot_ptr<C>(a.gslots, a, G.bh, G.nl + 1), dg);
 }
 
 // bwdkv_kernel: dK and dV of one chunk.  Tiles in reverse order, carrying the

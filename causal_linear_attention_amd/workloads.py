@@ -139,6 +139,7 @@ def kernel_flops(w: Workload, tile: int) -> dict:
         "stats": 2 * P + tm + td + 2 * dm,                 # the fwd tile (numerators dotted with dY); state
         "bwdq": 2 * P + tm + td + 2 * dm + vjp,            # g(Q), g(K); A^T; g(K)^T A^T; R^T dNum; W chain; R
         "gstate": P + dm,                                  # g(Q); dG += g(Q)^T [dNum | dden]
+        "bwdq_gstate": 2 * P + tm + td + 3 * dm + vjp,     # bwdq, and dG += g(Q)^T [dNum | dden]
         "bwdkv": 2 * P + 2 * tm + 2 * td + 3 * dm + vjp,   # g(Q), g(K); P; dNum^T P; dR g(K)^T; A;
                                                             # g(Q)^T A; dR^T V; W chain; dR update
     }
@@ -161,6 +162,7 @@ def kernel_bytes(w: Workload) -> dict:
         "stats": 4 * row + slot + st,               # Q, K, V, dY, entry state -> row statistics
         "bwdq": 4 * row + slot + st + row,          # Q, K, V, dY, entry state, statistics -> dQ
         "gstate": 2 * row + st + slot,              # Q, dY, statistics -> gradient slot
+        "bwdq_gstate": 4 * row + 2 * slot + st + row,  # Q, K, V, dY, entry state, statistics -> dQ, gradient slot
         "bwdkv": 4 * row + st + slot + 2 * row,     # Q, K, V, dY, statistics, gradient slot -> dK, dV
     }
 

@@ -166,9 +166,10 @@ const char *slim_status_string(slim_status s);
  * slim_prof_enable(0) stops.  slim_prof_count() and slim_prof_entry() first
  * wait for the recorded events to complete (they synchronise with those
  * events), then report per kernel name ("state", "scan_prefix", "fwd",
- * "scan_window", "scan_sum", "stats", "bwdq", "gstate", "scan_grad", "bwdkv",
- * "featmap", "decode") the summed
- * GPU time in milliseconds and the number of launches.  The name pointer stays
+ * "scan_window", "scan_sum", "stats", "bwdq", "gstate", "bwdq_gstate" (the dQ
+ * kernel with the gradient state folded in, for shapes where it fits),
+ * "scan_grad", "bwdkv", "featmap", "decode") the summed GPU time in
+ * milliseconds and the number of launches.  The name pointer stays
  * valid until the next slim_prof_enable(1).  Guarded by a process-wide mutex;
  * the timings are global to the process, not per stream. */
 slim_status slim_prof_enable(int enable);
