@@ -121,6 +121,8 @@ def pmc_summary(d, w, bytes_of_copy, runs=("F", "W")):
         wb = sum(write[k]) / len(write[k]) * 1024 * w_fac
         rows[k] = {"dispatches": len(fetch[k]), "fetch_bytes": round(fb), "write_bytes": round(wb),
                    "traffic_bytes": round(fb + wb)}
+    if "bwdq" in rows and "gstate" not in rows and "bwdkv" in rows:
+        rows["bwdq_gstate"] = rows.pop("bwdq")  # the dQ kernel with the gradient state folded in
     return {"workload": w.name, "source_hash": kernel_source_hash(), "fetch_factor": round(f_fac, 4),
             "write_factor": round(w_fac, 4), "kernels": rows}
 

@@ -595,31 +595,42 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StateSmem<C>), C::NW))
     for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
         for (int eb = 0; eb < NEA; ++eb) rt[fb][eb] = f4zero();
-    typename C::Tile rk, rv;
-    rk.load(Kp, min(TT, G.len));
-    rv.load(Vp, min(TT, G.len));
-    for (int t0 = 0; t0 < G.len; t0 += TT) {
-        const int nv = min(TT, G.len - t0);
-        store_k_tile<C>(rk, xk, kn2, nv);
-        store_v_tile<C>(rv, V, nv);
-        __syncthreads();
-        if (t0 + TT < G.len) {  // prefetch the next tile while this one is computed
-            const int nv1 = min(TT, G.len - t0 - TT);
-            rk.load(Kp + (size_t)(t0 + TT) * C::D, nv1);
-            rv.load(Vp + (size_t)(t0 + TT) * C::D, nv1);
+    // two tiles in flight: this kernel's per-tile work is short, so one tile of
+    // prefetch left part of the load latency exposed
+    typename C::Tile rk[2], rv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        if (i * TT < G.len) {
+            rk[i].load(Kp + (size_t)(i * TT) * C::D, min(TT, G.len - i * TT));
+            rv[i].load(Vp + (size_t)(i * TT) * C::D, min(TT, G.len - i * TT));
         }
-        f4 pk[NTB][NFB];
-        feat_S<C>(pk, xk, wf);
-        k_finish_S<C>(pk, kn2);
-        Frag<T> fk[NTB][NFB];
-        to_frags<C>(fk, pk);
+    for (int t00 = 0; t00 < G.len; t00 += 2 * TT) {
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb)
+        for (int i = 0; i < 2; ++i) {
+            const int t0 = t00 + i * TT;
+            if (t0 >= G.len) break;
+            const int nv = min(TT, G.len - t0);
+            store_k_tile<C>(rk[i], xk, kn2, nv);
+            store_v_tile<C>(rv[i], V, nv);
+            __syncthreads();
+            if (t0 + 2 * TT < G.len) {  // prefetch two tiles ahead
+                const int nv2 = min(TT, G.len - t0 - 2 * TT);
+                rk[i].load(Kp + (size_t)(t0 + 2 * TT) * C::D, nv2);
+                rv[i].load(Vp + (size_t)(t0 + 2 * TT) * C::D, nv2);
+            }
+            f4 pk[NTB][NFB];
+            feat_S<C>(pk, xk, wf);
+            k_finish_S<C>(pk, kn2);
+            Frag<T> fk[NTB][NFB];
+            to_frags<C>(fk, pk);
 #pragma unroll
-            for (int eb = 0; eb < NEA; ++eb)
-                mma_range<T>(rt[fb][eb], 0, NTB, [&](int tb) { return fk[tb][fb]; },
-                             [&](int tb) { return V.fr(eb, tb * 16); });
-        __syncthreads();
+            for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+                for (int eb = 0; eb < NEA; ++eb)
+                    mma_range<T>(rt[fb][eb], 0, NTB, [&](int tb) { return fk[tb][fb]; },
+                                 [&](int tb) { return V.fr(eb, tb * 16); });
+            __syncthreads();
+        }
     }
     store_state_T<C>(slot_ptr<C>(a.slots, a, G.bh, G.nl + 1), rt);
 }
