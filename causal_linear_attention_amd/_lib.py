@@ -11,7 +11,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libslim.so")
 
-SLIM_F32, SLIM_BF16 = 0, 1
+SLIM_F32, SLIM_BF16, SLIM_F64 = 0, 1, 2
 SLIM_FEAT_FAVOR, SLIM_FEAT_ELU1 = 0, 1
 SLIM_PASS_FEATMAP, SLIM_PASS_FWD, SLIM_PASS_BWD, SLIM_PASS_DECODE = 0, 1, 2, 3
 STATUS = {0: "SLIM_OK", 1: "SLIM_ERR_NULL", 2: "SLIM_ERR_SHAPE", 3: "SLIM_ERR_DTYPE",
@@ -26,7 +26,7 @@ EXPORTS = ["slim_validate", "slim_workspace_bytes", "slim_window_chunks", "slim_
 class SlimDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("L", ctypes.c_int64), ("d", ctypes.c_int64),
                 ("M", ctypes.c_int64), ("num_chunks", ctypes.c_int64), ("window_chunks", ctypes.c_int64),
-                ("dtype", ctypes.c_int32), ("feat", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("feat", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
 
 
 class SlimError(RuntimeError):
@@ -94,9 +94,10 @@ def check(code: int, where: str):
         raise SlimError(code, where)
 
 
-def desc(B, H, L, d, M, num_chunks=1, window_chunks=0, dtype=SLIM_F32, feat=SLIM_FEAT_FAVOR) -> SlimDesc:
+def desc(B, H, L, d, M, num_chunks=1, window_chunks=0, dtype=SLIM_F32, feat=SLIM_FEAT_FAVOR,
+         state_dtype=SLIM_F32) -> SlimDesc:
     return SlimDesc(int(B), int(H), int(L), int(d), int(M), int(num_chunks), int(window_chunks), int(dtype),
-                    int(feat))
+                    int(feat), int(state_dtype))
 
 
 def prof_enable(on: bool):

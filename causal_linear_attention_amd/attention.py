@@ -14,6 +14,7 @@ import torch
 from . import _lib
 
 _DT = {torch.float32: _lib.SLIM_F32, torch.bfloat16: _lib.SLIM_BF16}
+_SDT = {torch.float32: _lib.SLIM_F32, torch.float64: _lib.SLIM_F64}  # state element types
 _FEAT = {"favor": _lib.SLIM_FEAT_FAVOR, "elu1": _lib.SLIM_FEAT_ELU1}
 
 
@@ -36,11 +37,13 @@ def _check_io(name, t, dtype, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def make_desc(q, M, feat, num_chunks, window_chunks=0):
+def make_desc(q, M, feat, num_chunks, window_chunks=0, state_dtype=torch.float32):
     B, H, L, d = q.shape
     if q.dtype not in _DT:
         raise ValueError(f"unsupported dtype {q.dtype}")
-    return _lib.desc(B, H, L, d, M, num_chunks, window_chunks, _DT[q.dtype], _FEAT[feat])
+    if state_dtype not in _SDT:
+        raise ValueError(f"unsupported state dtype {state_dtype}")
+    return _lib.desc(B, H, L, d, M, num_chunks, window_chunks, _DT[q.dtype], _FEAT[feat], _SDT[state_dtype])
 
 
 def _feat_M(W, feat, d):
@@ -75,22 +78,25 @@ def featmap(x, W=None, feat="favor", row_offset=False):
     return (phi, off) if row_offset else phi
 
 
-def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, window_chunks=0):
-    """Forward.  Returns (Y, R_out [B,H,d,M] fp32, S_out [B,H,M] fp32)."""
+def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, window_chunks=0,
+             state_dtype=None):
+    """Forward.  Returns (Y, R_out [B,H,d,M], S_out [B,H,M]).  States are fp32, or
+    fp64 when R_in is fp64 or state_dtype=torch.float64."""
     B, H, L, d = q.shape
     M = _feat_M(W, feat, d)
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check_io(n, t, q.dtype, q.shape)
     if W is not None:
         _check_io("W", W, q.dtype, (M, d))
+    sd = R_in.dtype if R_in is not None else (state_dtype or torch.float32)
     if R_in is not None:
-        _check_io("R_in", R_in, torch.float32, (B, H, d, M))
-        _check_io("S_in", S_in, torch.float32, (B, H, M))
-    dsc = make_desc(q, M, feat, num_chunks, window_chunks)
+        _check_io("R_in", R_in, sd, (B, H, d, M))
+        _check_io("S_in", S_in, sd, (B, H, M))
+    dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd)
     ws = torch.empty(max(1, workspace_bytes(dsc, _lib.SLIM_PASS_FWD)), dtype=torch.uint8, device=q.device)
     Y = torch.empty_like(q)
-    R = torch.empty((B, H, d, M), dtype=torch.float32, device=q.device)
-    S = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    R = torch.empty((B, H, d, M), dtype=sd, device=q.device)
+    S = torch.empty((B, H, M), dtype=sd, device=q.device)
     _lib.check(_lib.lib().slim_attn_fwd(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(R_in),
                                         _ptr(S_in), _ptr(Y), _ptr(R), _ptr(S), _ptr(ws), ws.numel(), _stream()),
                "slim_attn_fwd")
@@ -98,27 +104,30 @@ def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, 
 
 
 def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, dR_out=None, dS_out=None,
-             want_state_grad=False, window_chunks=0):
+             want_state_grad=False, window_chunks=0, state_dtype=None):
     """Backward of attn_fwd(q, k, v, W, feat, num_chunks, R_in, S_in) for the
     loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out>.  Returns (dQ, dK, dV,
-    dR_in, dS_in); the last two are None unless want_state_grad."""
+    dR_in, dS_in); the last two are None unless want_state_grad.  The state
+    tensors share one dtype (fp32, or fp64), taken from those given."""
     B, H, L, d = q.shape
     M = _feat_M(W, feat, d)
     for n, t in (("q", q), ("k", k), ("v", v), ("dY", dY)):
         _check_io(n, t, q.dtype, q.shape)
+    given = [t for t in (R_in, dR_out) if t is not None]
+    sd = given[0].dtype if given else (state_dtype or torch.float32)
     if R_in is not None:
-        _check_io("R_in", R_in, torch.float32, (B, H, d, M))
-        _check_io("S_in", S_in, torch.float32, (B, H, M))
+        _check_io("R_in", R_in, sd, (B, H, d, M))
+        _check_io("S_in", S_in, sd, (B, H, M))
     if dR_out is not None:
-        _check_io("dR_out", dR_out, torch.float32, (B, H, d, M))
-        _check_io("dS_out", dS_out, torch.float32, (B, H, M))
-    dsc = make_desc(q, M, feat, num_chunks, window_chunks)
+        _check_io("dR_out", dR_out, sd, (B, H, d, M))
+        _check_io("dS_out", dS_out, sd, (B, H, M))
+    dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd)
     ws = torch.empty(max(1, workspace_bytes(dsc, _lib.SLIM_PASS_BWD)), dtype=torch.uint8, device=q.device)
     dQ, dK, dV = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dR = dS = None
     if want_state_grad:
-        dR = torch.empty((B, H, d, M), dtype=torch.float32, device=q.device)
-        dS = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+        dR = torch.empty((B, H, d, M), dtype=sd, device=q.device)
+        dS = torch.empty((B, H, M), dtype=sd, device=q.device)
     _lib.check(_lib.lib().slim_attn_bwd(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(dY),
                                         _ptr(R_in), _ptr(S_in), _ptr(dR_out), _ptr(dS_out), _ptr(dQ), _ptr(dK),
                                         _ptr(dV), _ptr(dR), _ptr(dS), _ptr(ws), ws.numel(), _stream()),

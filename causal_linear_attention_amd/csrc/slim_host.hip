@@ -122,24 +122,35 @@ static void copy_or_zero(float *dst, const float *src, long long n, hipStream_t 
     hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, src, n);
 }
 
-// fp64 carries: loaded from an fp32 state (or zero), stored back rounded to fp32.
-__global__ __launch_bounds__(256) void widen_kernel(double *dst, const float *src, long long n)
+// fp64 carries: loaded from a state of the caller's type (or zero), stored back in
+// that type (rounded when it is fp32).
+template <typename S> __global__ __launch_bounds__(256) void widen_kernel(double *dst, const S *src, long long n)
 {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i < n) dst[i] = src ? (double)src[i] : 0.0;
 }
-__global__ __launch_bounds__(256) void narrow_kernel(float *dst, const double *src, long long n)
+template <typename S> __global__ __launch_bounds__(256) void narrow_kernel(S *dst, const double *src, long long n)
 {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) dst[i] = (float)src[i];
+    if (i < n) dst[i] = (S)src[i];
 }
-static void widen(double *dst, const float *src, long long n, hipStream_t s)
+static void widen(double *dst, const void *src, long long n, bool f64, hipStream_t s)
 {
-    if (n > 0) hipLaunchKernelGGL(widen_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, src, n);
+    if (n <= 0) return;
+    const dim3 g((unsigned)((n + 255) / 256));
+    if (f64)
+        hipLaunchKernelGGL(widen_kernel<double>, g, dim3(256), 0, s, dst, (const double *)src, n);
+    else
+        hipLaunchKernelGGL(widen_kernel<float>, g, dim3(256), 0, s, dst, (const float *)src, n);
 }
-static void narrow(float *dst, const double *src, long long n, hipStream_t s)
+static void narrow(void *dst, const double *src, long long n, bool f64, hipStream_t s)
 {
-    if (n > 0) hipLaunchKernelGGL(narrow_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, src, n);
+    if (n <= 0) return;
+    const dim3 g((unsigned)((n + 255) / 256));
+    if (f64)
+        hipLaunchKernelGGL(narrow_kernel<double>, g, dim3(256), 0, s, (double *)dst, src, n);
+    else
+        hipLaunchKernelGGL(narrow_kernel<float>, g, dim3(256), 0, s, (float *)dst, src, n);
 }
 
 // Fragment-packed W^T: for value block eb and feature block mb, lane i of a
@@ -265,7 +276,7 @@ using namespace slim;
 
 extern "C" {
 
-int slim_version(void) { return (1 << 16) | 2; }
+int slim_version(void) { return (1 << 16) | 3; }
 
 slim_status slim_prof_enable(int enable)
 {
@@ -325,7 +336,9 @@ slim_status slim_validate(const slim_desc *d, int pass)
     if (pass != SLIM_PASS_FEATMAP && (d->num_chunks < 1 || d->num_chunks > d->L)) return SLIM_ERR_SHAPE;
     if (d->window_chunks < 0) return SLIM_ERR_SHAPE;
     if (d->feat == SLIM_FEAT_ELU1 && d->M != d->d) return SLIM_ERR_SHAPE;
+    if (d->state_dtype != SLIM_F32 && d->state_dtype != SLIM_F64) return SLIM_ERR_DTYPE;
     if (pass == SLIM_PASS_DECODE && d->L != 1) return SLIM_ERR_SHAPE;
+    if (pass == SLIM_PASS_DECODE && d->state_dtype != SLIM_F32) return SLIM_ERR_UNSUPPORTED;
     const long long BH = d->B * d->H;
     if (pass == SLIM_PASS_DECODE ? BH > (1LL << 24) : (BH > 65535 && pass != SLIM_PASS_FEATMAP))
         return SLIM_ERR_UNSUPPORTED;
@@ -372,7 +385,7 @@ slim_status slim_featmap(const slim_desc *d, const void *X, const void *W, float
 }
 
 slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
-                          const float *R_in, const float *S_in, void *Y, float *R_out, float *S_out, void *ws,
+                          const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, void *ws,
                           size_t ws_bytes, void *stream)
 {
     slim_status st = slim_validate(d, SLIM_PASS_FWD);
@@ -397,8 +410,9 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
     a.slots = (float *)(base + p.slots_off);
     a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
     double *cR = (double *)(base + p.cR_off), *cS = (double *)(base + p.cS_off);
-    widen(cR, R_in, p.BH * D * M, s);
-    widen(cS, S_in, p.BH * M, s);
+    const bool f64 = d->state_dtype == SLIM_F64;
+    widen(cR, R_in, p.BH * D * M, f64, s);
+    widen(cS, S_in, p.BH * M, f64, s);
     for (long long n0 = 0; n0 < p.nchunks; n0 += p.P) {
         const int np = (int)(p.nchunks - n0 < p.P ? p.nchunks - n0 : p.P);
         a.n0 = (int)n0;
@@ -406,14 +420,14 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
         scan(0, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
         SLIM_TIMED("fwd", s, kt->fwd(dim3(np, BH), s, a));
     }
-    narrow(R_out, cR, p.BH * D * M, s);
-    narrow(S_out, cS, p.BH * M, s);
+    narrow(R_out, cR, p.BH * D * M, f64, s);
+    narrow(S_out, cS, p.BH * M, f64, s);
     return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
 
 slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
-                          const void *dY, const float *R_in, const float *S_in, const float *dR_out,
-                          const float *dS_out, void *dQ, void *dK, void *dV, float *dR_in, float *dS_in, void *ws,
+                          const void *dY, const void *R_in, const void *S_in, const void *dR_out,
+                          const void *dS_out, void *dQ, void *dK, void *dV, void *dR_in, void *dS_in, void *ws,
                           size_t ws_bytes, void *stream)
 {
     slim_status st = slim_validate(d, SLIM_PASS_BWD);
@@ -449,10 +463,11 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
         a.Wt = base + p.wt_off;
         pack_wt(W, base + p.wt_off, M, D, d->dtype == SLIM_BF16, s);
     }
-    widen(cR, R_in, p.BH * D * M, s);
-    widen(cS, S_in, p.BH * M, s);
-    widen(gR, dR_out, p.BH * D * M, s);
-    widen(gS, dS_out, p.BH * M, s);
+    const bool f64 = d->state_dtype == SLIM_F64;
+    widen(cR, R_in, p.BH * D * M, f64, s);
+    widen(cS, S_in, p.BH * M, f64, s);
+    widen(gR, dR_out, p.BH * D * M, f64, s);
+    widen(gS, dS_out, p.BH * M, f64, s);
     const long long nwin = (p.nchunks + p.P - 1) / p.P;
     auto window = [&](long long wi) {
         const long long n0 = wi * p.P;
@@ -490,8 +505,8 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
         SLIM_TIMED("bwdkv", s, kt->bwdkv(dim3(np, BH), s, a));
     }
     if (dR_in) {
-        narrow(dR_in, gR, p.BH * D * M, s);
-        narrow(dS_in, gS, p.BH * M, s);
+        narrow(dR_in, gR, p.BH * D * M, f64, s);
+        narrow(dS_in, gS, p.BH * M, f64, s);
     }
     return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }

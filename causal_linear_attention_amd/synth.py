@@ -87,3 +87,48 @@ def projection(seed: int, M: int, d: int, kind: str = "gaussian") -> np.ndarray:
     Wo = np.concatenate(blocks, axis=0)[:M]
     norms = np.linalg.norm(g.standard_normal((M, d)), axis=1)
     return np.ascontiguousarray((Wo * norms[:, None]).astype(np.float32))
+
+
+# ---------------------------------------------------------------- model stack ---
+# Randomly initialised parameters and random token strings for the multi-layer
+# Performer stack (the page's experiments feed random strings to randomly
+# initialised models).  Drawn here, in float32, so that the GPU path and the
+# fp64 CPU reference receive the very same values.
+
+TID_MODEL = 100
+
+
+def performer_params(seed: int, vocab: int, d_model: int, heads: int, layers: int, M: int, d_ff: int) -> dict:
+    """Parameters {name: float32 array} of an s-layer stack; layer r's names carry
+    the suffix `.r`.  Matrices ~ N(0, 1/fan_in) (the query and key projections
+    additionally times d^-1/4 with d = d_model / heads, which keeps g's arguments
+    of order one), biases 0, layer-norm gains 1; `wf.r` [M, d] is layer r's fixed
+    FAVOR+ projection, N(0, 1)."""
+    d = d_model // heads
+    g = _rng(seed, TID_MODEL)
+
+    def mat(rows, cols, scale=1.0):
+        return (g.standard_normal((rows, cols)) * (scale / np.sqrt(rows))).astype(np.float32)
+
+    p = {"emb": (g.standard_normal((vocab, d_model)) * 0.5).astype(np.float32)}
+    for r in range(layers):
+        p[f"ln1_g.{r}"] = np.ones(d_model, np.float32)
+        p[f"ln1_b.{r}"] = np.zeros(d_model, np.float32)
+        p[f"wq.{r}"] = mat(d_model, d_model, d ** -0.25)
+        p[f"wk.{r}"] = mat(d_model, d_model, d ** -0.25)
+        p[f"wv.{r}"] = mat(d_model, d_model)
+        p[f"ln2_g.{r}"] = np.ones(d_model, np.float32)
+        p[f"ln2_b.{r}"] = np.zeros(d_model, np.float32)
+        p[f"w1.{r}"] = mat(d_model, d_ff)
+        p[f"b1.{r}"] = np.zeros(d_ff, np.float32)
+        p[f"w2.{r}"] = mat(d_ff, d_model)
+        p[f"b2.{r}"] = np.zeros(d_model, np.float32)
+        p[f"wf.{r}"] = g.standard_normal((M, d)).astype(np.float32)
+    p["wout"] = mat(d_model, vocab)
+    p["bout"] = np.zeros(vocab, np.float32)
+    return p
+
+
+def random_tokens(seed: int, B: int, L: int, vocab: int) -> np.ndarray:
+    """[B, L] int64 tokens drawn uniformly from the alphabet."""
+    return _rng(seed, TID_MODEL + 1).integers(0, vocab, size=(B, L), dtype=np.int64)

@@ -29,8 +29,8 @@
  *
  * Conventions for every entry point:
  *   - Layout: Q, K, V, Y, dY, dQ, dK, dV are contiguous row-major
- *     [B][H][L][d]; W is [M][d]; states R are [B][H][d][M] fp32, S [B][H][M]
- *     fp32; phi is [B][H][L][M] fp32.
+ *     [B][H][L][d]; W is [M][d]; states R are [B][H][d][M], S [B][H][M], in
+ *     desc.state_dtype (fp32 or fp64); phi is [B][H][L][M] fp32.
  *   - dtype: SLIM_F32 or SLIM_BF16 is the element type of Q, K, V, W, Y, dY,
  *     dQ, dK, dV.  States, statistics and all accumulation are fp32.
  *   - All pointers are device pointers (HIP).  The caller owns every buffer;
@@ -69,7 +69,7 @@ typedef enum slim_status {
     SLIM_ERR_HIP = 7          /* a HIP launch failed */
 } slim_status;
 
-typedef enum slim_dtype { SLIM_F32 = 0, SLIM_BF16 = 1 } slim_dtype;
+typedef enum slim_dtype { SLIM_F32 = 0, SLIM_BF16 = 1, SLIM_F64 = 2 } slim_dtype;
 typedef enum slim_feat { SLIM_FEAT_FAVOR = 0, SLIM_FEAT_ELU1 = 1 } slim_feat;
 typedef enum slim_pass { SLIM_PASS_FEATMAP = 0, SLIM_PASS_FWD = 1, SLIM_PASS_BWD = 2, SLIM_PASS_DECODE = 3 } slim_pass;
 
@@ -78,12 +78,18 @@ typedef struct slim_desc {
     int64_t d, M;          /* head dim, number of features */
     int64_t num_chunks;    /* N slices; slice length c = ceil(L / N) */
     int64_t window_chunks; /* slices whose states are held at once; 0 = auto */
-    int32_t dtype;         /* slim_dtype */
+    int32_t dtype;         /* slim_dtype of Q, K, V, W, Y, dY, dQ, dK, dV: SLIM_F32 or SLIM_BF16 */
     int32_t feat;          /* slim_feat */
+    int32_t state_dtype;   /* element type of the states and their gradients (R_in, S_in,
+                              R_out, S_out, dR_out, dS_out, dR_in, dS_in): SLIM_F32, or
+                              SLIM_F64 for slim_attn_fwd / slim_attn_bwd (states passed
+                              between calls then keep the precision of the internal
+                              fp64 carries) */
 } slim_desc;
 
 /* Host-only check of a descriptor for a pass; touches no GPU.  SLIM_PASS_DECODE
- * requires L == 1 (one token per head) and allows B*H up to 2^24. */
+ * requires L == 1 (one token per head) and fp32 states, and allows B*H up to
+ * 2^24. */
 slim_status slim_validate(const slim_desc *desc, int pass);
 
 /* Workspace bytes the pass needs (0 for SLIM_PASS_FEATMAP and SLIM_PASS_DECODE); 0 if the
@@ -114,7 +120,7 @@ slim_status slim_featmap(const slim_desc *desc, const void *X, const void *W, fl
  *      alias R_in/S_in).
  * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_FWD). */
 slim_status slim_attn_fwd(const slim_desc *desc, const void *Q, const void *K, const void *V, const void *W,
-                          const float *R_in, const float *S_in, void *Y, float *R_out, float *S_out, void *ws,
+                          const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, void *ws,
                           size_t ws_bytes, void *stream);
 
 /* Backward of the loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out> of the
@@ -134,8 +140,8 @@ slim_status slim_attn_fwd(const slim_desc *desc, const void *Q, const void *K, c
  *      = not wanted, or both given).  dW is not computed.
  * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_BWD). */
 slim_status slim_attn_bwd(const slim_desc *desc, const void *Q, const void *K, const void *V, const void *W,
-                          const void *dY, const float *R_in, const float *S_in, const float *dR_out,
-                          const float *dS_out, void *dQ, void *dK, void *dV, float *dR_in, float *dS_in, void *ws,
+                          const void *dY, const void *R_in, const void *S_in, const void *dR_out,
+                          const void *dS_out, void *dQ, void *dK, void *dV, void *dR_in, void *dS_in, void *ws,
                           size_t ws_bytes, void *stream);
 
 /* Recurrent decode step: the iterative prefix-sum evaluation of Subsection
@@ -145,7 +151,8 @@ slim_status slim_attn_bwd(const slim_desc *desc, const void *Q, const void *K, c
  * This is what slim_attn_fwd computes for its first row, and a run of decode
  * steps gives the same outputs and state as one slim_attn_fwd over the same
  * tokens (up to fp32 rounding order).
- * desc: L must be 1 (num_chunks therefore 1); window_chunks is ignored.
+ * desc: L must be 1 (num_chunks therefore 1); window_chunks is ignored;
+ *       state_dtype must be SLIM_F32.
  * In : q, k, v [B][H][d] (desc dtype); W as in the forward (NULL for elu+1);
  *      R_in [B][H][d][M], S_in [B][H][M] fp32 = the state before the token
  *      (both NULL = zero, i.e. the first token, or both given).

@@ -258,6 +258,44 @@ def pin_decode_first_token_is_value():
     assert np.allclose(R, V[:, :, 0, :, None] * phik[:, :, None, :], rtol=1e-15)
 
 
+def _tiny_performer():
+    from causal_linear_attention_amd import synth
+    params = synth.performer_params(3, 8, 8, 2, 2, 4, 16)
+    tokens = synth.random_tokens(3, 1, 6, 8)
+    return params, tokens
+
+
+def pin_performer_ref_finite_differences():
+    # The fp64 multi-layer reference: autograd gradients (through the oracle's
+    # attention backward) against central differences of the loss, on a tiny model.
+    from oracle import performer_ref
+    params, tokens = _tiny_performer()
+    params = {n: a.astype(np.float64) for n, a in params.items()}
+    _, grads = performer_ref.loss_and_grads(params, tokens, heads=2, layers=2)
+    rng = np.random.default_rng(5)
+    h = 1e-6
+    for name in ("emb", "wq.0", "wk.1", "wv.0", "w1.1", "b2.0", "ln1_g.1", "wout", "bout"):
+        a = params[name]
+        for _ in range(2):
+            i = tuple(int(rng.integers(0, s)) for s in a.shape)
+            plus = {n: v.copy() for n, v in params.items()}
+            minus = {n: v.copy() for n, v in params.items()}
+            plus[name][i] += h
+            minus[name][i] -= h
+            fd = (performer_ref.loss_and_grads(plus, tokens, 2, 2)[0] -
+                  performer_ref.loss_and_grads(minus, tokens, 2, 2)[0]) / (2 * h)
+            g = grads[name][i]
+            assert abs(fd - g) <= 1e-6 * max(1.0, abs(g)), (name, i, fd, g)
+
+
+def pin_performer_ref_no_target():
+    # A one-token sequence has no next token: its loss and gradients are zero.
+    from oracle import performer_ref
+    params, tokens = _tiny_performer()
+    loss, grads = performer_ref.loss_and_grads(params, tokens[:, :1], heads=2, layers=2)
+    assert loss == 0.0 and all(np.all(g == 0) for g in grads.values())
+
+
 def pin_softmax_special_cases():
     Q, K, V, _ = _qkv(21, 10, 3, 1)
     # Q = 0 => all scores equal => running mean
@@ -367,7 +405,8 @@ ALL_PINS = [
     pin_featmap_vjp_fd, pin_fwd_golden, pin_single_row_is_value, pin_identical_keys_give_running_mean,
     pin_constant_values, pin_causality, pin_convex_hull, pin_quadratic_equals_prefix,
     pin_initial_state_is_a_prefix, pin_rows_match_full, pin_decode_golden, pin_decode_steps_equal_quadratic,
-    pin_decode_first_token_is_value, pin_softmax_special_cases,
+    pin_decode_first_token_is_value, pin_performer_ref_finite_differences, pin_performer_ref_no_target,
+    pin_softmax_special_cases,
     pin_favor_converges_to_softmax, pin_bwd_finite_differences, pin_bwd_special_cases,
     pin_bwd_quadratic_equals_prefix,
 ]

@@ -44,7 +44,7 @@ def test_version_and_status_strings(lib):
 
 def d_(**kw):
     base = dict(B=2, H=3, L=1000, d=64, M=128, num_chunks=8, window_chunks=0, dtype=_lib.SLIM_BF16,
-                feat=_lib.SLIM_FEAT_FAVOR)
+                feat=_lib.SLIM_FEAT_FAVOR, state_dtype=_lib.SLIM_F32)
     base.update(kw)
     return _lib.desc(**base)
 
@@ -161,3 +161,13 @@ def test_decode_rejects_before_any_launch(lib):
     assert lib.slim_decode_step(ctypes.byref(d), p, p, p, p, r_in, s_, p, r_out, s_, None) == 2
     de = d_(L=1, num_chunks=1, feat=_lib.SLIM_FEAT_ELU1, M=64)
     assert lib.slim_decode_step(ctypes.byref(de), p, p, p, p, None, None, p, p, p, None) == 2    # elu+1: no W
+
+
+def test_state_dtype_validation(lib):
+    assert validate(lib, _lib.SLIM_PASS_FWD, state_dtype=_lib.SLIM_F64) == 0
+    assert validate(lib, _lib.SLIM_PASS_BWD, state_dtype=_lib.SLIM_F64) == 0
+    assert validate(lib, _lib.SLIM_PASS_FWD, state_dtype=_lib.SLIM_BF16) == 3     # states are fp32 or fp64
+    assert validate(lib, _lib.SLIM_PASS_FWD, state_dtype=7) == 3
+    assert validate(lib, _lib.SLIM_PASS_DECODE, L=1, num_chunks=1, state_dtype=_lib.SLIM_F64) == 4
+    # the workspace does not depend on the state type (the carries are fp64 either way)
+    assert ws(lib, 2, state_dtype=_lib.SLIM_F64) == ws(lib, 2)

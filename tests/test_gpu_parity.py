@@ -125,6 +125,49 @@ def test_initial_state_and_state_gradients():
         assert e < 1e-4, (name, e)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_fp64_states(dt):
+    # States passed between calls in fp64 (desc.state_dtype = SLIM_F64): streaming a
+    # sequence in three pieces gives the one-call result to within the internal
+    # rounding (no fp32 rounding of the states between calls), and every state and
+    # state gradient matches the oracle.
+    B, H, L, d, M = 1, 2, 192, 64, 128
+    x = inputs(B, H, L, d, M, DT[dt], "favor", seed=15)
+    q, k, v, W, dy = x["q"], x["k"], x["v"], x["W"], x["dy"]
+    Yf, Rf, Sf = A.attn_fwd(q, k, v, W, "favor", 3, state_dtype=torch.float64)
+    assert Rf.dtype == torch.float64 and Sf.dtype == torch.float64
+    R = S = None
+    ys = []
+    for a, b in ((0, 48), (48, 112), (112, 192)):
+        sl = [t[:, :, a:b].contiguous() for t in (q, k, v)]
+        y, R, S = A.attn_fwd(*sl, W, "favor", 1, R_in=R, S_in=S, state_dtype=torch.float64)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert relerr_heads(host64(R), host64(Rf)) < 1e-12 + 1e-6
+    assert relerr_heads(host64(torch.cat(ys, 2)), host64(Yf)) < (1e-5 if dt == "f32" else 1e-2)
+    Yo, _, Ro, So = oracle.attn_fwd(host64(q), host64(k), host64(v), host64(W), "favor", form="prefix")
+    assert relerr_heads(host64(Rf), Ro) < (1e-5 if dt == "f32" else 2e-2)
+    assert relerr_heads(host64(Sf), So) < (1e-5 if dt == "f32" else 2e-2)
+    # backward of the last piece from its fp64 entry state, with an fp64 incoming state gradient
+    rng = np.random.default_rng(6)
+    dRo = torch.from_numpy(rng.standard_normal((B, H, d, M)) * 1e-3).cuda()
+    dSo = torch.from_numpy(rng.standard_normal((B, H, M)) * 1e-3).cuda()
+    _, Rp, Sp = A.attn_fwd(q[:, :, :112].contiguous(), k[:, :, :112].contiguous(), v[:, :, :112].contiguous(), W,
+                           "favor", 2, state_dtype=torch.float64)
+    qs, ks, vs, dys = (t[:, :, 112:].contiguous() for t in (q, k, v, dy))
+    dQ, dK, dV, dR0, dS0 = A.attn_bwd(qs, ks, vs, W, dys, "favor", 2, R_in=Rp, S_in=Sp, dR_out=dRo,
+                                      dS_out=dSo, want_state_grad=True)
+    torch.cuda.synchronize()
+    assert dR0.dtype == torch.float64
+    g = oracle.attn_bwd(host64(qs), host64(ks), host64(vs), host64(W), host64(dys), "favor", R0=host64(Rp),
+                        S0=host64(Sp), dRout=host64(dRo), dSout=host64(dSo))
+    tol = TOL[DT[dt]]
+    for name, got, ref in (("dQ", dQ, g[0]), ("dK", dK, g[1]), ("dV", dV, g[2]), ("dR0", dR0, g[3]),
+                           ("dS0", dS0, g[4])):
+        e = relerr_heads(host64(got), ref)
+        assert e < tol, (name, e)
+
+
 @pytest.mark.parametrize("window", [0, 4])
 def test_backward_wide_dynamic_range(window):
     # fp32 keys scaled up so that g(K) spans many orders of magnitude: the final
