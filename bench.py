@@ -16,6 +16,7 @@ and the fp64 CPU oracle timed on a bounded sample of the same workload.
   python bench.py --pmc-summary DIR # (host only) HBM traffic per kernel from rocprofv3 counter CSVs
   python bench.py --decode [...]    # the recurrent decode step instead (one JSON line of its own)
   python bench.py --chunk-sweep     # time, peak HBM and gradient discrepancy vs slice length (one JSON line)
+  python bench.py --algorithm1      # the same for the page's Algorithm 1 on a multi-layer Performer
 
 roofline.traffic: HBM bytes per launch of the dominant kernel, FETCH_SIZE and
 WRITE_SIZE scaled by what the same counters read for a plain copy of known
@@ -60,6 +61,9 @@ def parse():
     ap.add_argument("--sweep-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--sweep-window", type=int, default=0, help="window_chunks of the swept runs (0 = auto)")
     ap.add_argument("--sweep-cmax", type=int, default=0, help="largest slice length swept (0 = L)")
+    ap.add_argument("--algorithm1", action="store_true",
+                    help="time, peak HBM and gradient discrepancy of Algorithm 1 on a 4-layer Performer vs the "
+                         "slice length C (one JSON line)")
     ap.add_argument("--decode", action="store_true",
                     help="time the recurrent decode step (one token per sequence per step) instead")
     ap.add_argument("--pmc-summary", default=None, metavar="DIR",
@@ -380,6 +384,56 @@ def chunk_sweep(torch, A, synth, w, dtype, window, cmax):
             "explicit_prefix_state_bytes": w.B * w.H * w.L * w.d * w.M * 4, "rows": rows}
 
 
+def algorithm1_sweep(torch, synth):
+    """The page's Figure-2 study on a randomly initialised Performer (4 layers,
+    d_model 256 = 4 heads x 64, M = 64 FAVOR+ features, d_ff 1024, alphabet 256)
+    over one random string of L = 16384 tokens: one gradient evaluation by
+    Algorithm 1 per slice length C (time, peak HBM, relative gradient discrepancy
+    against the whole sequence in one pass), beside the whole-sequence pass and
+    the whole-sequence pass on C tokens alone."""
+    from causal_linear_attention_amd.performer import Performer
+    cfg = dict(vocab=256, d_model=256, heads=4, layers=4, M=64, d_ff=1024)
+    L = 16384
+    tok = torch.from_numpy(synth.random_tokens(9, 1, L, cfg["vocab"])).cuda()
+    model = Performer(**cfg, seed=9)
+
+    def grads():
+        return {n: t.grad.detach().clone() for n, t in model.parameters().items()}
+
+    def measure(fn):
+        model.zero_grad()
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        t0 = time.perf_counter()
+        loss = fn()
+        torch.cuda.synchronize()
+        return loss, 1e3 * (time.perf_counter() - t0), torch.cuda.max_memory_allocated() - base
+
+    def full(t):
+        loss = model.loss_full(t)
+        loss.backward()
+        return float(loss)
+
+    measure(lambda: full(tok))  # warm-up
+    lf, ms_f, mem_f = measure(lambda: full(tok))
+    gf = grads()
+    fnorm = sum(float(g.double().pow(2).sum()) for g in gf.values()) ** 0.5
+    rows = []
+    for C in (4096, 1024, 256, 64):
+        lc, ms, mem = measure(lambda: model.algorithm1(tok, C))
+        gc = grads()
+        disc = sum(float((gc[n].double() - gf[n].double()).pow(2).sum()) for n in gf) ** 0.5 / fnorm
+        _, ms_c, mem_c = measure(lambda: full(tok[:, :C]))
+        rows.append({"C": C, "ms": round(ms, 1), "peak_bytes": mem, "grad_discrepancy": disc,
+                     "loss_rel_diff": abs(lc - lf) / abs(lf), "full_on_C_ms": round(ms_c, 2),
+                     "full_on_C_peak_bytes": mem_c})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    n_param = sum(t.numel() for t in model.parameters().values())
+    return {"algorithm1": "performer_4x256_M64_L16384", "config": dict(cfg, L=L, B=1, params=n_param),
+            "full_ms": round(ms_f, 1), "full_peak_bytes": mem_f, "rows": rows}
+
+
 def kernel_records(w, prof, steps, tile):
     """Per-kernel records from the library's hipEvent timings {name: (ms total, launches)}
     over `steps` steps, and the roofline record of the dominant kernel."""
@@ -449,6 +503,10 @@ def main():
 
     if args.decode:
         decode_main(args, torch, _lib, A, synth)
+        return
+
+    if args.algorithm1:
+        print(json.dumps(algorithm1_sweep(torch, synth)))
         return
 
     if args.chunk_sweep:
