@@ -221,6 +221,26 @@ template <class C> struct BwdRegs {
 // [R; S] (rows e, cols m) from slot[n].  Where its registers allow (bf16 with d <= 32,
 // or d = 64 with M >= 128; fp32 with d <= 32), it also accumulates the gstate_kernel's
 // result from the g(Q) it already has, and the gstate_kernel is not launched.
+// dQ's W^T product: with bf16 inputs, d <= 64 and a whole number of value blocks per
+// wave count, the waves share dg(Q).g(Q) through LDS and each finishes whole output
+// blocks from W^T fragments it holds (no partial sums); elsewhere (where the held
+// fragments would cost spills) each wave reduces its own features' partial sums
+// across waves through LDS.
+template <class C> struct DqShared {
+    static constexpr bool value = C::FAVOR && sizeof(typename C::T) == 2 && C::D <= 64 && C::NW % C::NEB == 0;
+};
+// W^T fragments of value block eb over all M features (free index e, contraction m),
+// from the packed W^T.
+template <class C>
+__device__ __forceinline__ void load_wt_col(Frag<typename C::T> (&wt)[C::M / 16], const void *Wpv, int eb)
+{
+    typedef typename C::T T;
+    const T *Wp = (const T *)Wpv;
+#pragma unroll
+    for (int mb = 0; mb < C::M / 16; ++mb)
+        wt[mb] = *reinterpret_cast<const Frag<T> *>(Wp + (((size_t)eb * (C::M / 16) + mb) * 64 + threadIdx.x % 64) * 4);
+}
+
 template <class C> constexpr bool bwdq_fuses_gstate()
 {
     return C::D <= 32 || (sizeof(typename C::T) == 2 && C::D <= 64 && C::M >= 128);
@@ -235,7 +255,10 @@ template <class C> struct BwdqSmem {
     __align__(16) T dna[C::AuxMat::SIZE];
     __align__(16) T fk[C::NW * C::FMat::SIZE];
     __align__(16) T fq[bwdq_fuses_gstate<C>() ? C::NW * C::FMat::SIZE : 8];
-    __align__(16) float red[C::FAVOR ? C::NW * C::TT * C::LDR : 4];
+    // dg(Q) . g(Q) of the tile over all features (rows t, cols m), or the waves'
+    // partial dQ sums (see DqShared)
+    __align__(16) T gqm[DqShared<C>::value ? LMat<T, C::TT, C::M>::SIZE : 8];
+    __align__(16) float red[C::FAVOR && !DqShared<C>::value ? C::NW * C::TT * C::LDR : 4];
     float kn2[C::TT], qoff[C::TT];
 };
 template <class C>
@@ -268,12 +291,21 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
     load_state_E<C>(r, slot_ptr<C>(a.slots, a, G.bh, G.nl));
     BwdRegs<C> rg;
     rg.load(Q, K, V, dY, st, 0, G.len);
-    // W^T fragments of this wave's features, held over the tile loop (reloading them per
-    // tile put their cache latency on the dQ chain)
-    Frag<T> wt[C::FAVOR ? NEB : 1][NFB];
-    if constexpr (C::FAVOR)
+    // W^T fragments held over the tile loop (reloading them per tile put their cache
+    // latency on the dQ chain).  Shared dg(Q).g(Q): a wave finishes the dQ^T blocks
+    // (16 value columns x 16 rows) of value block w % NEB, over all features.
+    // Otherwise: its own features, all value blocks.
+    constexpr bool SH = DqShared<C>::value;
+    constexpr int NB = NTB * NEB, MB = C::M / 16;
+    const LMat<T, TT, C::M> Gq(sm.gqm);
+    Frag<T> wt[C::FAVOR ? (SH ? MB : NEB * NFB) : 1];
+    if constexpr (C::FAVOR) {
+        if constexpr (SH)
+            load_wt_col<C>(wt, a.Wt, w % NEB);
+        else
 #pragma unroll
-        for (int eb = 0; eb < NEB; ++eb) load_wtfrag_block<C>(wt[eb], a.Wt, eb);
+            for (int eb = 0; eb < NEB; ++eb) load_wtfrag_block<C>(*reinterpret_cast<Frag<T>(*)[NFB]>(wt + eb * NFB), a.Wt, eb);
+    }
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
         rg.store(xq, xk, Vt, DN, kn2, qoff, nv);
@@ -319,26 +351,43 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
                 dq[fb][tb] = acc;
             }
         if constexpr (C::FAVOR) {
-            // dQ^T (rows e, cols t) = W^T (dg(Q) . g(Q))^T over own features, reduced across
-            // waves.
-            Frag<T> gq[NFB][NTB];
+            // dQ^T (rows e, cols t) = W^T (dg(Q) . g(Q))^T
+            if constexpr (SH) {
 #pragma unroll
-            for (int fb = 0; fb < NFB; ++fb)
+                for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-                for (int tb = 0; tb < NTB; ++tb) gq[fb][tb] = cfrag<T>(dq[fb][tb] * pq[fb][tb]);
-#pragma unroll
-            for (int eb = 0; eb < NEB; ++eb) {
-#pragma unroll
-                for (int tb = 0; tb < NTB; ++tb) {
+                    for (int tb = 0; tb < NTB; ++tb)
+                        Gq.put_frag(tb * 16 + lc, w * MW + fb * 16 + 4 * g, cfrag<T>(dq[fb][tb] * pq[fb][tb]));
+                __syncthreads();
+                for (int blk = w; blk < NB; blk += C::NW) {
+                    const int tb = blk / NEB, eb = blk % NEB;
                     f4 acc = f4zero();
-                    mma_range<T>(acc, 0, NFB, [&](int fb) { return wt[eb][fb]; }, [&](int fb) { return gq[fb][tb]; });
-                    put_red<C>(red, eb, tb, acc);
+                    mma_range<T>(acc, 0, MB, [&](int mb) { return wt[mb]; },
+                                 [&](int mb) { return Gq.frag_c(tb * 16, mb * 16); });
+                    const int t = tb * 16 + lc;
+                    if (t < nv) store4<T>(dQ + (size_t)(t0 + t) * D + eb * 16 + 4 * g, acc);
                 }
+            } else {
+                Frag<T> gq[NFB][NTB];
+#pragma unroll
+                for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+                    for (int tb = 0; tb < NTB; ++tb) gq[fb][tb] = cfrag<T>(dq[fb][tb] * pq[fb][tb]);
+#pragma unroll
+                for (int eb = 0; eb < NEB; ++eb) {
+#pragma unroll
+                    for (int tb = 0; tb < NTB; ++tb) {
+                        f4 acc = f4zero();
+                        mma_range<T>(acc, 0, NFB, [&](int fb) { return wt[eb * NFB + fb]; },
+                                     [&](int fb) { return gq[fb][tb]; });
+                        put_red<C>(red, eb, tb, acc);
+                    }
+                }
+                __syncthreads();
+                reduce_rows<C>(red, nv, [&](int t, int e, f4 s, bool ok) {
+                    if (ok) store4<T>(dQ + (size_t)(t0 + t) * D + e, s);
+                });
             }
-            __syncthreads();
-            reduce_rows<C>(red, nv, [&](int t, int e, f4 s, bool ok) {
-                if (ok) store4<T>(dQ + (size_t)(t0 + t) * D + e, s);
-            });
         } else {
 #pragma unroll
             for (int fb = 0; fb < NFB; ++fb)
