@@ -269,10 +269,11 @@ template <typename T> __device__ __forceinline__ const T *uniform_ptr(const T *p
     return (const T *)(((unsigned long long)hi << 32) | lo);
 }
 // Load through a global-memory pointer (a pointer rebuilt from integers is generic,
-// which would make the compiler emit flat loads).
+// which would make the compiler emit flat loads), marked non-temporal: the tiles are
+// read once, and streaming them keeps the caches for what is reused (W, W^T).
 template <typename U> __device__ __forceinline__ U gload(const void *p)
 {
-    return *(const __attribute__((address_space(1))) U *)p;
+    return __builtin_nontemporal_load((const __attribute__((address_space(1))) U *)p);
 }
 
 template <typename T, int D, int TT, int NT> struct TileRegs {
