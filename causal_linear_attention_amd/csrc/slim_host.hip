@@ -124,33 +124,55 @@ static void copy_or_zero(float *dst, const float *src, long long n, hipStream_t 
 
 // fp64 carries: loaded from a state of the caller's type (or zero), stored back in
 // that type (rounded when it is fp32).
-template <typename S> __global__ __launch_bounds__(256) void widen_kernel(double *dst, const S *src, long long n)
+// Two carries stored back in one launch (in the caller's state type).
+template <typename S>
+__global__ __launch_bounds__(256) void narrow2_kernel(S *d0, const double *s0, long long n0, S *d1, const double *s1,
+                                                      long long n1)
 {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) dst[i] = src ? (double)src[i] : 0.0;
+    if (i < n0)
+        d0[i] = (S)s0[i];
+    else if (i - n0 < n1)
+        d1[i - n0] = (S)s1[i - n0];
 }
-template <typename S> __global__ __launch_bounds__(256) void narrow_kernel(S *dst, const double *src, long long n)
+// Up to four carries loaded in one launch (each from its source, or zero).
+struct WidenSet {
+    double *dst[4];
+    const void *src[4];
+    long long n[4];
+};
+template <typename S> __global__ __launch_bounds__(256) void widen_set_kernel(WidenSet w)
 {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) dst[i] = (S)src[i];
+    long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (i < w.n[k]) {
+            w.dst[k][i] = w.src[k] ? (double)((const S *)w.src[k])[i] : 0.0;
+            return;
+        }
+        i -= w.n[k];
+    }
 }
-static void widen(double *dst, const void *src, long long n, bool f64, hipStream_t s)
+static void widen(const WidenSet &w, bool f64, hipStream_t s)
 {
+    const long long n = w.n[0] + w.n[1] + w.n[2] + w.n[3];
     if (n <= 0) return;
     const dim3 g((unsigned)((n + 255) / 256));
     if (f64)
-        hipLaunchKernelGGL(widen_kernel<double>, g, dim3(256), 0, s, dst, (const double *)src, n);
+        hipLaunchKernelGGL(widen_set_kernel<double>, g, dim3(256), 0, s, w);
     else
-        hipLaunchKernelGGL(widen_kernel<float>, g, dim3(256), 0, s, dst, (const float *)src, n);
+        hipLaunchKernelGGL(widen_set_kernel<float>, g, dim3(256), 0, s, w);
 }
-static void narrow(void *dst, const double *src, long long n, bool f64, hipStream_t s)
+static void narrow2(void *d0, const double *s0, long long n0, void *d1, const double *s1, long long n1, bool f64,
+                    hipStream_t s)
 {
+    const long long n = n0 + n1;
     if (n <= 0) return;
     const dim3 g((unsigned)((n + 255) / 256));
     if (f64)
-        hipLaunchKernelGGL(narrow_kernel<double>, g, dim3(256), 0, s, (double *)dst, src, n);
+        hipLaunchKernelGGL(narrow2_kernel<double>, g, dim3(256), 0, s, (double *)d0, s0, n0, (double *)d1, s1, n1);
     else
-        hipLaunchKernelGGL(narrow_kernel<float>, g, dim3(256), 0, s, (float *)dst, src, n);
+        hipLaunchKernelGGL(narrow2_kernel<float>, g, dim3(256), 0, s, (float *)d0, s0, n0, (float *)d1, s1, n1);
 }
 
 // Fragment-packed W^T: for value block eb and feature block mb, lane i of a
@@ -411,8 +433,8 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
     a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
     double *cR = (double *)(base + p.cR_off), *cS = (double *)(base + p.cS_off);
     const bool f64 = d->state_dtype == SLIM_F64;
-    widen(cR, R_in, p.BH * D * M, f64, s);
-    widen(cS, S_in, p.BH * M, f64, s);
+    widen(WidenSet{{cR, cS, nullptr, nullptr}, {R_in, S_in, nullptr, nullptr}, {p.BH * D * M, p.BH * M, 0, 0}},
+          f64, s);
     for (long long n0 = 0; n0 < p.nchunks; n0 += p.P) {
         const int np = (int)(p.nchunks - n0 < p.P ? p.nchunks - n0 : p.P);
         a.n0 = (int)n0;
@@ -420,8 +442,7 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
         scan(0, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
         SLIM_TIMED("fwd", s, kt->fwd(dim3(np, BH), s, a));
     }
-    narrow(R_out, cR, p.BH * D * M, f64, s);
-    narrow(S_out, cS, p.BH * M, f64, s);
+    narrow2(R_out, cR, p.BH * D * M, S_out, cS, p.BH * M, f64, s);
     return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
 
@@ -464,10 +485,8 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
         pack_wt(W, base + p.wt_off, M, D, d->dtype == SLIM_BF16, s);
     }
     const bool f64 = d->state_dtype == SLIM_F64;
-    widen(cR, R_in, p.BH * D * M, f64, s);
-    widen(cS, S_in, p.BH * M, f64, s);
-    widen(gR, dR_out, p.BH * D * M, f64, s);
-    widen(gS, dS_out, p.BH * M, f64, s);
+    widen(WidenSet{{cR, cS, gR, gS}, {R_in, S_in, dR_out, dS_out}, {p.BH * D * M, p.BH * M, p.BH * D * M, p.BH * M}},
+          f64, s);
     const long long nwin = (p.nchunks + p.P - 1) / p.P;
     auto window = [&](long long wi) {
         const long long n0 = wi * p.P;
@@ -505,8 +524,7 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
         SLIM_TIMED("bwdkv", s, kt->bwdkv(dim3(np, BH), s, a));
     }
     if (dR_in) {
-        narrow(dR_in, gR, p.BH * D * M, f64, s);
-        narrow(dS_in, gS, p.BH * M, f64, s);
+        narrow2(dR_in, gR, p.BH * D * M, dS_in, gS, p.BH * M, f64, s);
     }
     return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
