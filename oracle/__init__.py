@@ -64,9 +64,10 @@ def _bind(lib):
         "oracle_featmap": [i, l, i, i, _D, _D, _D],
         "oracle_featmap_vjp": [i, l, i, i, _D, _D, _D, _D],
         "oracle_fwd_quadratic": [i, l, i, i, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D],
-        "oracle_bwd_quadratic": [i, l, i, i, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D],
+        "oracle_featmap_wgrad": [l, i, i, _D, _D, _D, _D],
+        "oracle_bwd_quadratic": [i, l, i, i, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D],
         "oracle_fwd_prefix": [i, l, i, i, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D],
-        "oracle_bwd_prefix": [i, l, i, i, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D],
+        "oracle_bwd_prefix": [i, l, i, i, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D],
         "oracle_fwd_rows": [i, l, i, i, _D, _D, _D, _D, _D, _D, l, _Lp, _D, _D],
         "oracle_softmax_fwd": [l, i, _D, _D, _D, _D],
     }
@@ -126,6 +127,19 @@ def featmap_vjp(X, W, dPhi, feat="favor"):
     return out
 
 
+def featmap_wgrad(X, W, dPhi):
+    """FAVOR+ projection gradient of feature rows: sum over rows r of
+    J_W(g(X_r))^T dPhi_r, i.e. dW[m] = sum_r dPhi[r, m] g(X_r)_m X_r  ([M, d])."""
+    lib = load()
+    X, W, dPhi = _f64(X), _f64(W), _f64(dPhi)
+    d = X.shape[-1]
+    M = W.shape[0]
+    rows = int(np.prod(X.shape[:-1]))
+    out = np.zeros((M, d))
+    lib.oracle_featmap_wgrad(rows, d, M, _p(X), _p(W), _p(dPhi), _p(out))
+    return out
+
+
 def _heads(Q):
     B, H = Q.shape[0], Q.shape[1]
     return [(b, h) for b in range(B) for h in range(H)]
@@ -160,10 +174,12 @@ def attn_fwd(Q, K, V, W=None, feat="favor", R0=None, S0=None, form="quadratic", 
 
 
 def attn_bwd(Q, K, V, W, dY, feat="favor", R0=None, S0=None, dRout=None, dSout=None,
-             form="quadratic", threads=None):
+             form="quadratic", threads=None, want_dw=False):
     """Gradients of <dY,Y> + <dRout,Rout> + <dSout,Sout>.
 
-    Returns (dQ, dK, dV, dR0, dS0)."""
+    Returns (dQ, dK, dV, dR0, dS0), and with want_dw (FAVOR+) also dW [M, d],
+    the gradient w.r.t. the projection W shared by every batch row and head
+    (the heads' contributions summed in (b, h) order)."""
     lib = load()
     Q, K, V, dY, R0, S0, dRout, dSout = map(_f64, (Q, K, V, dY, R0, S0, dRout, dSout))
     kind = _kind(feat)
@@ -173,6 +189,9 @@ def attn_bwd(Q, K, V, W, dY, feat="favor", R0=None, S0=None, dRout=None, dSout=N
     dQ, dK, dV = (np.empty((B, H, L, d)) for _ in range(3))
     dR0 = np.empty((B, H, d, M))
     dS0 = np.empty((B, H, M))
+    if want_dw and kind != FEAT_FAVOR:
+        raise ValueError("dW exists only for the FAVOR+ feature map")
+    dWh = np.zeros((B, H, M, d)) if want_dw else None
     fn = lib.oracle_bwd_quadratic if form == "quadratic" else lib.oracle_bwd_prefix
 
     def sel(a, b, h):
@@ -183,11 +202,17 @@ def attn_bwd(Q, K, V, W, dY, feat="favor", R0=None, S0=None, dRout=None, dSout=N
         fn(kind, L, d, M, _p(Q[b, h]), _p(K[b, h]), _p(V[b, h]), _p(W),
            _p(sel(R0, b, h)), _p(sel(S0, b, h)), _p(dY[b, h]),
            _p(sel(dRout, b, h)), _p(sel(dSout, b, h)),
-           _p(dQ[b, h]), _p(dK[b, h]), _p(dV[b, h]), _p(dR0[b, h]), _p(dS0[b, h]))
+           _p(dQ[b, h]), _p(dK[b, h]), _p(dV[b, h]), _p(dR0[b, h]), _p(dS0[b, h]),
+           _p(sel(dWh, b, h)))
 
     with ThreadPoolExecutor(_threads(threads)) as ex:
         list(ex.map(run, _heads(Q)))
-    return dQ, dK, dV, dR0, dS0
+    if not want_dw:
+        return dQ, dK, dV, dR0, dS0
+    dW = np.zeros((M, d))
+    for b, h in _heads(Q):
+        dW += dWh[b, h]
+    return dQ, dK, dV, dR0, dS0, dW
 
 
 def attn_fwd_rows(Q, K, V, W, rows, feat="favor", R0=None, S0=None):

@@ -74,6 +74,17 @@ static void feat_vjp_row(int kind, int d, int M, const double *x, const double *
     }
 }
 
+/* Gradient of one FAVOR+ feature row with respect to the projection W,
+ * accumulated: g_m(x) depends on W only through w_m, with d g_m/d w_m = g_m x,
+ * so dW[m] += dphi_m g_m x.  (elu+1 has no parameters.) */
+static void feat_wgrad_row(int d, int M, const double *x, const double *phi, const double *dphi, double *dW)
+{
+    for (int m = 0; m < M; ++m) {
+        const double gm = dphi[m] * phi[m];
+        for (int e = 0; e < d; ++e) dW[(size_t)m * d + e] += gm * x[e];
+    }
+}
+
 static double dot(const double *a, const double *b, int n)
 {
     double s = 0.0;
@@ -95,6 +106,19 @@ void oracle_featmap_vjp(int kind, long rows, int d, int M, const double *X, cons
     for (long r = 0; r < rows; ++r) {
         feat_row(kind, d, M, X + (size_t)r * d, W, phi);
         feat_vjp_row(kind, d, M, X + (size_t)r * d, W, phi, dPhi + (size_t)r * M, dX + (size_t)r * d);
+    }
+    free(phi);
+}
+
+/* W-gradient of `rows` FAVOR+ rows, accumulated into dW [M][d]:
+ * dW += sum_r J_W(g(X[r]))^T dPhi[r]. */
+void oracle_featmap_wgrad(long rows, int d, int M, const double *X, const double *W, const double *dPhi,
+                          double *dW)
+{
+    double *phi = (double *)malloc(sizeof(double) * M);
+    for (long r = 0; r < rows; ++r) {
+        feat_row(FEAT_FAVOR, d, M, X + (size_t)r * d, W, phi);
+        feat_wgrad_row(d, M, X + (size_t)r * d, phi, dPhi + (size_t)r * M, dW);
     }
     free(phi);
 }
@@ -164,11 +188,13 @@ void oracle_fwd_quadratic(int kind, long L, int d, int M, const double *Q, const
  *   dg(K_i) = sum_{l>=i} c_{l,i} g(Q_l) + dRout^T V_i + dSout
  *   dV_i    = sum_{l>=i} a_{l,i} G_l + dRout g(K_i)
  *   dR0     = sum_l G_l g(Q_l)^T + dRout,   dS0 = sum_l E_l g(Q_l) + dSout
- * then dQ, dK through the feature-map VJP.  dR0, dS0 may be NULL. */
+ * then dQ, dK through the feature-map VJP, and (FAVOR+, dW not NULL) the
+ * gradient of the projection, dW = sum over the Q and K rows of J_W^T dg.
+ * dR0, dS0, dW may be NULL. */
 void oracle_bwd_quadratic(int kind, long L, int d, int M, const double *Q, const double *K,
                           const double *V, const double *W, const double *R0, const double *S0,
                           const double *dY, const double *dRout, const double *dSout,
-                          double *dQ, double *dK, double *dV, double *dR0, double *dS0)
+                          double *dQ, double *dK, double *dV, double *dR0, double *dS0, double *dW)
 {
     double *Fq = feats(kind, L, d, M, Q, W);
     double *Fk = feats(kind, L, d, M, K, W);
@@ -231,6 +257,11 @@ void oracle_bwd_quadratic(int kind, long L, int d, int M, const double *Q, const
         }
     oracle_featmap_vjp(kind, L, d, M, Q, W, dFq, dQ);
     oracle_featmap_vjp(kind, L, d, M, K, W, dFk, dK);
+    if (dW && kind == FEAT_FAVOR) {
+        memset(dW, 0, sizeof(double) * (size_t)M * d);
+        oracle_featmap_wgrad(L, d, M, Q, W, dFq, dW);
+        oracle_featmap_wgrad(L, d, M, K, W, dFk, dW);
+    }
 
     free(Fq); free(Fk); free(Y); free(den); free(G); free(E); free(dFq); free(dFk);
 }
@@ -274,11 +305,13 @@ void oracle_fwd_prefix(int kind, long L, int d, int M, const double *Q, const do
  * with G_l = dY_l/den_l, E_l = -(dY_l.Y_l)/den_l.  Per row:
  *   dg(Q_l) = R_l^T G_l + E_l S_l,  dg(K_l) = GR_l^T V_l + GS_l,  dV_l = GR_l g(K_l),
  * and R_{l-1} = R_l - V_l g(K_l)^T is recovered by subtraction from the final
- * state (the reversal the page uses for its slice states).  dR0 = GR_1, dS0 = GS_1. */
+ * state (the reversal the page uses for its slice states).  dR0 = GR_1, dS0 = GS_1.
+ * dW (FAVOR+, may be NULL) accumulates the projection gradient of every row's
+ * two feature vectors as the walk passes them. */
 void oracle_bwd_prefix(int kind, long L, int d, int M, const double *Q, const double *K,
                        const double *V, const double *W, const double *R0, const double *S0,
                        const double *dY, const double *dRout, const double *dSout,
-                       double *dQ, double *dK, double *dV, double *dR0, double *dS0)
+                       double *dQ, double *dK, double *dV, double *dR0, double *dS0, double *dW)
 {
     size_t DM = (size_t)d * M;
     double *Y = (double *)malloc(sizeof(double) * (size_t)L * d);
@@ -296,6 +329,7 @@ void oracle_bwd_prefix(int kind, long L, int d, int M, const double *Q, const do
     oracle_fwd_prefix(kind, L, d, M, Q, K, V, W, R0, S0, Y, den, R, S);
     for (size_t t = 0; t < DM; ++t) GR[t] = dRout ? dRout[t] : 0.0;
     for (int m = 0; m < M; ++m) GS[m] = dSout ? dSout[m] : 0.0;
+    if (dW && kind == FEAT_FAVOR) memset(dW, 0, sizeof(double) * (size_t)M * d);
 
     for (long l = L - 1; l >= 0; --l) {
         const double *x = Q + (size_t)l * d, *k = K + (size_t)l * d, *v = V + (size_t)l * d;
@@ -320,6 +354,10 @@ void oracle_bwd_prefix(int kind, long L, int d, int M, const double *Q, const do
         for (int e = 0; e < d; ++e) dV[(size_t)l * d + e] = dot(GR + (size_t)e * M, fk, M);
         feat_vjp_row(kind, d, M, x, W, fq, dfq, dQ + (size_t)l * d);
         feat_vjp_row(kind, d, M, k, W, fk, dfk, dK + (size_t)l * d);
+        if (dW && kind == FEAT_FAVOR) {
+            feat_wgrad_row(d, M, x, fq, dfq, dW);
+            feat_wgrad_row(d, M, k, fk, dfk, dW);
+        }
         for (int e = 0; e < d; ++e)
             for (int m = 0; m < M; ++m) R[(size_t)e * M + m] -= v[e] * fk[m];
         for (int m = 0; m < M; ++m) S[m] -= fk[m];

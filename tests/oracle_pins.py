@@ -11,7 +11,9 @@ Every function raises AssertionError when the oracle disagrees with:
   * FAVOR+ unbiasedness for exp(q.k) (Subsection 2.1 cites it as an unbiased
     approximation of exponential attention) and the M^{-1/2} convergence of
     FAVOR+ attention to exact softmax attention,
-  * central finite differences of every gradient.
+  * central finite differences of every gradient,
+  * the rotation invariance of FAVOR+ (W, Q, K rotated together), which ties
+    the projection gradient dW to dQ and dK.
 
 The functions are shared by tests/test_oracle_pins.py and by the mutation
 check (tests/test_oracle_mutants.py), which plants mistakes in copies of
@@ -113,6 +115,24 @@ def pin_featmap_vjp_fd():
                 Xm[r, e] -= h
                 fd[r, e] = np.sum(dPhi * (oracle.featmap(Xp, W, feat) - oracle.featmap(Xm, W, feat))) / (2 * h)
         assert _relerr(got, fd) < 1e-7, (feat, got, fd)
+
+
+def pin_featmap_wgrad_fd():
+    # the projection gradient of g against central differences in W
+    rng = np.random.default_rng(4)
+    d, M = 4, 6
+    X = rng.standard_normal((5, d)) * 0.7
+    W = rng.standard_normal((M, d))
+    dPhi = rng.standard_normal((5, M))
+    got = oracle.featmap_wgrad(X, W, dPhi)
+    h = 1e-6
+    fd = np.zeros_like(W)
+    for idx in np.ndindex(W.shape):
+        Wp, Wm = W.copy(), W.copy()
+        Wp[idx] += h
+        Wm[idx] -= h
+        fd[idx] = np.sum(dPhi * (oracle.featmap(X, Wp, "favor") - oracle.featmap(X, Wm, "favor"))) / (2 * h)
+    assert _relerr(got, fd) < 1e-7, (got, fd)
 
 
 # --------------------------------------------------------------- forward ---
@@ -369,21 +389,71 @@ def pin_bwd_finite_differences():
                 assert _relerr(g, fd) < 1e-6, (feat, form, g, fd)
 
 
+def pin_bwd_dw_finite_differences():
+    # dW (the projection shared by all heads) against central differences of the
+    # loss in W, two heads, with an initial state and incoming state gradients
+    rng = np.random.default_rng(41)
+    B, H, L, d, M = 1, 2, 6, 3, 5
+    Q = rng.standard_normal((B, H, L, d)) * 0.6
+    K = rng.standard_normal((B, H, L, d)) * 0.6
+    V = rng.standard_normal((B, H, L, d))
+    W = rng.standard_normal((M, d))
+    R0 = rng.standard_normal((B, H, d, M)) * 0.5
+    S0 = np.abs(rng.standard_normal((B, H, M))) + 0.5
+    dY = rng.standard_normal((B, H, L, d))
+    dR = rng.standard_normal((B, H, d, M))
+    dS = rng.standard_normal((B, H, M))
+    h = 1e-6
+    fd = np.zeros_like(W)
+    for idx in np.ndindex(W.shape):
+        keep = W[idx]
+        W[idx] = keep + h
+        fp = _loss(Q, K, V, W, "favor", R0, S0, dY, dR, dS, "quadratic")
+        W[idx] = keep - h
+        fm = _loss(Q, K, V, W, "favor", R0, S0, dY, dR, dS, "quadratic")
+        W[idx] = keep
+        fd[idx] = (fp - fm) / (2 * h)
+    for form in ("quadratic", "prefix"):
+        dW = oracle.attn_bwd(Q, K, V, W, dY, "favor", R0, S0, dR, dS, form=form, want_dw=True)[5]
+        assert _relerr(dW, fd) < 1e-6, (form, dW, fd)
+
+
+def pin_dw_rotation_symmetry():
+    # g depends on W and x only through w_m.x and |x|^2, so the loss is unchanged when
+    # W, Q and K are rotated together (x -> U x, w_m -> U w_m, U orthogonal).  Its
+    # derivative along any rotation generator vanishes, which makes
+    # W^T dW + sum_rows (Q^T dQ + K^T dK)  (d x d) a symmetric matrix.
+    Q, K, V, W = _qkv(42, 24, 5, 7)
+    dY = _rand(43, 1, 2, 24, 5)
+    R0 = _rand(44, 1, 2, 5, 7) * 0.3
+    S0 = np.abs(_rand(45, 1, 2, 7)) + 0.5
+    for form in ("quadratic", "prefix"):
+        dQ, dK, _, _, _, dW = oracle.attn_bwd(Q, K, V, W, dY, "favor", R0, S0, form=form, want_dw=True)
+        T = W.T @ dW
+        for b in range(Q.shape[0]):
+            for hh in range(Q.shape[1]):
+                T = T + Q[b, hh].T @ dQ[b, hh] + K[b, hh].T @ dK[b, hh]
+        assert np.abs(T - T.T).max() < 1e-12 * np.abs(T).max(), (form, T - T.T)
+        assert np.abs(T - T.T).max() < 1e-3 * np.abs(W.T @ dW).max()  # not vacuous: dW matters
+
+
 def pin_bwd_special_cases():
     Q, K, V, W = _qkv(24, 1, 3, 4)
     dY = _rand(25, 1, 2, 1, 3)
     for form in ("quadratic", "prefix"):
         # L = 1: Y = V, so dQ = dK = 0 and dV = dY.
-        dQ, dK, dV, _, _ = oracle.attn_bwd(Q, K, V, W, dY, "favor", form=form)
+        dQ, dK, dV, _, _, dW = oracle.attn_bwd(Q, K, V, W, dY, "favor", form=form, want_dw=True)
         assert np.allclose(dQ, 0, atol=1e-14) and np.allclose(dK, 0, atol=1e-14)
         assert np.allclose(dV, dY, rtol=1e-14)
+        assert np.allclose(dW, 0, atol=1e-14)
     # constant V: Y = V whatever Q, K are, so dQ = dK = 0.
     Q, K, V, W = _qkv(26, 9, 3, 4)
     V[:] = np.array([0.5, -1.0, 2.0])
     dY = _rand(27, 1, 2, 9, 3)
     for form in ("quadratic", "prefix"):
-        dQ, dK, dV, _, _ = oracle.attn_bwd(Q, K, V, W, dY, "favor", form=form)
+        dQ, dK, dV, _, _, dW = oracle.attn_bwd(Q, K, V, W, dY, "favor", form=form, want_dw=True)
         assert np.allclose(dQ, 0, atol=1e-12) and np.allclose(dK, 0, atol=1e-12), form
+        assert np.allclose(dW, 0, atol=1e-12), form
 
 
 def pin_bwd_quadratic_equals_prefix():
@@ -394,21 +464,23 @@ def pin_bwd_quadratic_equals_prefix():
         dS = _rand(31, 1, 2, M)
         R0 = _rand(32, 1, 2, d, M)
         S0 = np.abs(_rand(33, 1, 2, M)) + 0.5
-        a = oracle.attn_bwd(Q, K, V, W, dY, feat, R0, S0, dR, dS, form="quadratic")
-        b = oracle.attn_bwd(Q, K, V, W, dY, feat, R0, S0, dR, dS, form="prefix")
+        dw = feat == "favor"
+        a = oracle.attn_bwd(Q, K, V, W, dY, feat, R0, S0, dR, dS, form="quadratic", want_dw=dw)
+        b = oracle.attn_bwd(Q, K, V, W, dY, feat, R0, S0, dR, dS, form="prefix", want_dw=dw)
+        assert len(a) == (6 if dw else 5)
         for x, y in zip(a, b):
             assert _relerr(x, y) < 1e-11, feat
 
 
 ALL_PINS = [
     pin_featmap_golden, pin_featmap_zero_input, pin_elu1_values, pin_favor_unbiased,
-    pin_featmap_vjp_fd, pin_fwd_golden, pin_single_row_is_value, pin_identical_keys_give_running_mean,
+    pin_featmap_vjp_fd, pin_featmap_wgrad_fd, pin_fwd_golden, pin_single_row_is_value, pin_identical_keys_give_running_mean,
     pin_constant_values, pin_causality, pin_convex_hull, pin_quadratic_equals_prefix,
     pin_initial_state_is_a_prefix, pin_rows_match_full, pin_decode_golden, pin_decode_steps_equal_quadratic,
     pin_decode_first_token_is_value, pin_performer_ref_finite_differences, pin_performer_ref_no_target,
     pin_softmax_special_cases,
-    pin_favor_converges_to_softmax, pin_bwd_finite_differences, pin_bwd_special_cases,
-    pin_bwd_quadratic_equals_prefix,
+    pin_favor_converges_to_softmax, pin_bwd_finite_differences, pin_bwd_dw_finite_differences,
+    pin_dw_rotation_symmetry, pin_bwd_special_cases, pin_bwd_quadratic_equals_prefix,
 ]
 
 

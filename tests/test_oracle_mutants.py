@@ -39,6 +39,12 @@ MUTANTS = [
      "GR[(size_t)e * M + m] += g[e] * fk[m];"),
     ("prefix_bwd_no_state_reversal", "R[(size_t)e * M + m] -= v[e] * fk[m];", "R[(size_t)e * M + m] -= 0.0;"),
     ("prefix_bwd_drops_dS", "double s = GS[m];", "double s = 0.0;"),
+    ("wgrad_wrong_input_index", "dW[(size_t)m * d + e] += gm * x[e];",
+     "dW[(size_t)m * d + e] += gm * x[(e + 1) % d];"),
+    ("wgrad_drops_feature_factor", "const double gm = dphi[m] * phi[m];", "const double gm = dphi[m];"),
+    ("quadratic_wgrad_keys_take_query_grad", "oracle_featmap_wgrad(L, d, M, K, W, dFk, dW);",
+     "oracle_featmap_wgrad(L, d, M, K, W, dFq, dW);"),
+    ("prefix_wgrad_skips_keys", "feat_wgrad_row(d, M, k, fk, dfk, dW);", "(void)0;"),
     ("softmax_half_temperature", "double p = exp(s[i] - mx);", "double p = exp(0.5 * (s[i] - mx));"),
     ("rows_mask_excludes_diagonal",
      "for (long i = 0; i <= l; ++i) {\n            feat_row(kind, d, M, K",
