@@ -104,11 +104,13 @@ def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, 
 
 
 def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, dR_out=None, dS_out=None,
-             want_state_grad=False, window_chunks=0, state_dtype=None):
+             want_state_grad=False, window_chunks=0, state_dtype=None, want_dw=False):
     """Backward of attn_fwd(q, k, v, W, feat, num_chunks, R_in, S_in) for the
     loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out>.  Returns (dQ, dK, dV,
-    dR_in, dS_in); the last two are None unless want_state_grad.  The state
-    tensors share one dtype (fp32, or fp64), taken from those given."""
+    dR_in, dS_in); the last two are None unless want_state_grad.  With want_dw
+    (FAVOR+) a sixth value follows: dW [M, d] fp32, the gradient w.r.t. the
+    projection W.  The state tensors share one dtype (fp32, or fp64), taken
+    from those given."""
     B, H, L, d = q.shape
     M = _feat_M(W, feat, d)
     for n, t in (("q", q), ("k", k), ("v", v), ("dY", dY)):
@@ -121,17 +123,23 @@ def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, d
     if dR_out is not None:
         _check_io("dR_out", dR_out, sd, (B, H, d, M))
         _check_io("dS_out", dS_out, sd, (B, H, M))
+    if want_dw and feat != "favor":
+        raise ValueError("dW exists only for the FAVOR+ feature map")
     dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd)
-    ws = torch.empty(max(1, workspace_bytes(dsc, _lib.SLIM_PASS_BWD)), dtype=torch.uint8, device=q.device)
+    ps = _lib.SLIM_PASS_BWD_DW if want_dw else _lib.SLIM_PASS_BWD
+    ws = torch.empty(max(1, workspace_bytes(dsc, ps)), dtype=torch.uint8, device=q.device)
     dQ, dK, dV = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dW = torch.empty((M, d), dtype=torch.float32, device=q.device) if want_dw else None
     dR = dS = None
     if want_state_grad:
         dR = torch.empty((B, H, d, M), dtype=sd, device=q.device)
         dS = torch.empty((B, H, M), dtype=sd, device=q.device)
     _lib.check(_lib.lib().slim_attn_bwd(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(dY),
                                         _ptr(R_in), _ptr(S_in), _ptr(dR_out), _ptr(dS_out), _ptr(dQ), _ptr(dK),
-                                        _ptr(dV), _ptr(dR), _ptr(dS), _ptr(ws), ws.numel(), _stream()),
+                                        _ptr(dV), _ptr(dR), _ptr(dS), _ptr(dW), _ptr(ws), ws.numel(), _stream()),
                "slim_attn_bwd")
+    if want_dw:
+        return dQ, dK, dV, dR, dS, dW
     return dQ, dK, dV, dR, dS
 
 
@@ -185,12 +193,15 @@ class _SlimAttention(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dY):
         q, k, v, W = ctx.saved_tensors
-        dQ, dK, dV, _, _ = attn_bwd(q, k, v, W if ctx.has_w else None, dY.contiguous(), ctx.feat,
-                                    ctx.num_chunks, window_chunks=ctx.window_chunks)
-        return dQ, dK, dV, None, None, None, None
+        want_dw = ctx.has_w and ctx.needs_input_grad[3]
+        g = attn_bwd(q, k, v, W if ctx.has_w else None, dY.contiguous(), ctx.feat, ctx.num_chunks,
+                     window_chunks=ctx.window_chunks, want_dw=want_dw)
+        dW = g[5].to(W.dtype) if want_dw else None
+        return g[0], g[1], g[2], dW, None, None, None
 
 
 def slim_attention(q, k, v, W=None, feat="favor", num_chunks=1, window_chunks=0):
-    """Causal linear attention with autograd (gradients for q, k, v; W is a
-    fixed random projection and gets none)."""
+    """Causal linear attention with autograd: gradients for q, k, v, and for
+    the FAVOR+ projection W when it requires one (the page keeps W a fixed
+    random projection; a caller may train it)."""
     return _SlimAttention.apply(q, k, v, W, feat, num_chunks, window_chunks)

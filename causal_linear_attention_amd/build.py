@@ -19,8 +19,8 @@ LIB = os.path.join(PKG, "libslim.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["slim_host.hip", "slim_f32_favor.hip", "slim_bf16_favor.hip", "slim_f32_elu1.hip",
-           "slim_bf16_elu1.hip"]
+SOURCES = ["slim_bf16_favor.hip", "slim_f32_favor.hip", "slim_bf16_favor_dw.hip", "slim_f32_favor_dw.hip",
+           "slim_f32_elu1.hip", "slim_bf16_elu1.hip", "slim_host.hip"]
 
 CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include "slim_decode.h"
+#include "slim_dw.h"
 
 namespace slim {
 
@@ -18,10 +19,20 @@ struct KernelTable {
     void (*decode)(dim3, hipStream_t, const DecodeArgs &);
 };
 
+// The dW pass (FAVOR+): dQ and dK/dV kernels that also store dg(X) . g(X), and the
+// row contraction that turns it into partial sums of dW.
+struct DwTable {
+    void (*bwdq)(dim3, hipStream_t, const ChunkArgs &);
+    void (*bwdkv)(dim3, hipStream_t, const ChunkArgs &);
+    void (*dw)(dim3, hipStream_t, const DwArgs &);
+};
+
 // One lookup per (dtype, feature map) translation unit; NULL if the shape is not compiled.
 const KernelTable *table_f32_favor(int D, int M);
 const KernelTable *table_bf16_favor(int D, int M);
 const KernelTable *table_f32_elu1(int D, int M);
 const KernelTable *table_bf16_elu1(int D, int M);
+const DwTable *table_f32_favor_dw(int D, int M);
+const DwTable *table_bf16_favor_dw(int D, int M);
 
 }  // namespace slim

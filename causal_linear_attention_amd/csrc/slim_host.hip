@@ -14,6 +14,9 @@
 //       dQ kernel where its registers allow) -> gradient suffix scan (update
 //       (20)) -> dK, dV.  With several windows, a forward
 //       sweep over all chunk contributions first rebuilds the final state.
+//       dW pass: the dQ and dK/dV kernels also store dg(X) . g(X) for the
+//       window's rows; each window ends with their contraction with Q and K
+//       (dw) and the fixed-order sum of its partials into dW.
 // All carries are fp64.
 // The decode step (one token per head, Subsection 2.1's iterative evaluation) is
 // a single kernel with no workspace.
@@ -122,6 +125,21 @@ static void copy_or_zero(float *dst, const float *src, long long n, hipStream_t 
     hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, src, n);
 }
 
+// out[y][x] = (acc ? out[y][x] : 0) + sum of in[p][x] over rows p of block y
+// (p = y*per .. min(rows, (y+1)*per) - 1, in increasing order), x < n4, in f4
+// units: the fixed-order reduction of the dW partial sums.
+__global__ __launch_bounds__(256) void sum_rows_kernel(const f4 *in, int rows, int n4, int per, f4 *out, int acc)
+{
+    const int x = blockIdx.x * 256 + threadIdx.x;
+    if (x >= n4) return;
+    const int p0 = blockIdx.y * per, p1 = min(rows, p0 + per);
+    f4 *o = out + (size_t)blockIdx.y * n4 + x;
+    f4 sum = acc ? *o : f4zero();
+#pragma unroll 8
+    for (int p = p0; p < p1; ++p) sum += in[(size_t)p * n4 + x];
+    *o = sum;
+}
+
 // fp64 carries: loaded from a state of the caller's type (or zero), stored back in
 // that type (rounded when it is fp32).
 // Two carries stored back in one launch (in the caller's state type).
@@ -227,10 +245,38 @@ static const KernelTable *find(const slim_desc *d)
     return d->feat == SLIM_FEAT_FAVOR ? table_bf16_favor(D, M) : table_bf16_elu1(D, M);
 }
 
+static const DwTable *find_dw(const slim_desc *d)
+{
+    if (d->feat != SLIM_FEAT_FAVOR || d->d > 1024 || d->M > 1024) return nullptr;
+    const int D = (int)d->d, M = (int)d->M;
+    return d->dtype == SLIM_F32 ? table_f32_favor_dw(D, M) : table_bf16_favor_dw(D, M);
+}
+
 struct Plan {
     long long BH, c, nchunks, P, SZ;
-    size_t slots_off, gslots_off, stats_off, cR_off, cS_off, gR_off, gS_off, wt_off, total;
+    long long dw_parts;  // dW pass: partial sums per window (2 sides x BH x workgroups per head)
+    size_t slots_off, gslots_off, stats_off, cR_off, cS_off, gR_off, gS_off, wt_off;
+    size_t pq_off, pk_off, part_off, part2_off, total;
 };
+
+// dW pass: the row contraction runs about 1024 workgroups (at least 256 rows each).
+// dw_groups: the target workgroups per head and side for wl rows (non-decreasing in
+// wl); dw_split: the split actually used, S <= dw_groups workgroups of rows_per rows.
+static long long dw_groups(long long BH, long long wl)
+{
+    long long s = (1024 + 2 * BH - 1) / (2 * BH);
+    const long long smax = (wl + 255) / 256;
+    if (s > smax) s = smax;
+    return s < 1 ? 1 : s;
+}
+static void dw_split(long long BH, long long wl, int *S, int *rows_per)
+{
+    const long long s = dw_groups(BH, wl);
+    long long rp = (wl + s - 1) / s;
+    rp = (rp + DW_TT - 1) / DW_TT * DW_TT;
+    *rows_per = (int)rp;
+    *S = (int)((wl + rp - 1) / rp);
+}
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -265,7 +311,7 @@ static Plan plan(const slim_desc *d, int pass)
     off = align256(off + (size_t)p.BH * d->d * d->M * 8);
     p.cS_off = off;
     off = align256(off + (size_t)p.BH * d->M * 8);
-    if (pass == SLIM_PASS_BWD) {
+    if (pass == SLIM_PASS_BWD || pass == SLIM_PASS_BWD_DW) {
         p.gslots_off = off;
         off = align256(off + slots);
         p.stats_off = off;
@@ -278,6 +324,21 @@ static Plan plan(const slim_desc *d, int pass)
             p.wt_off = off;
             off = align256(off + (size_t)d->d * d->M * (d->dtype == SLIM_BF16 ? 2 : 4));
         }
+    }
+    if (pass == SLIM_PASS_BWD_DW) {
+        // dg(X) . g(X) of the window's rows for queries and keys, in the operand type
+        const size_t pbytes = (size_t)p.BH * p.P * p.c * d->M * (d->dtype == SLIM_BF16 ? 2 : 4);
+        p.pq_off = off;
+        off = align256(off + pbytes);
+        p.pk_off = off;
+        off = align256(off + pbytes);
+        // every window has at most min(P c, L) rows, so at most this many partials
+        p.dw_parts = 2 * p.BH * dw_groups(p.BH, p.P * p.c < d->L ? p.P * p.c : d->L);
+        const size_t pmd = (size_t)d->M * d->d * 4;
+        p.part_off = off;
+        off = align256(off + (size_t)p.dw_parts * pmd);
+        p.part2_off = off;
+        off = align256(off + (size_t)((p.dw_parts + 31) / 32) * pmd);
     }
     p.total = (pass == SLIM_PASS_FEATMAP || pass == SLIM_PASS_DECODE) ? 0 : off;
     return p;
@@ -298,7 +359,7 @@ using namespace slim;
 
 extern "C" {
 
-int slim_version(void) { return (1 << 16) | 3; }
+int slim_version(void) { return (2 << 16) | 0; }
 
 slim_status slim_prof_enable(int enable)
 {
@@ -352,7 +413,7 @@ slim_status slim_validate(const slim_desc *d, int pass)
     if (!d) return SLIM_ERR_NULL;
     if (d->dtype != SLIM_F32 && d->dtype != SLIM_BF16) return SLIM_ERR_DTYPE;
     if (d->feat != SLIM_FEAT_FAVOR && d->feat != SLIM_FEAT_ELU1) return SLIM_ERR_DTYPE;
-    if (pass < SLIM_PASS_FEATMAP || pass > SLIM_PASS_DECODE) return SLIM_ERR_SHAPE;
+    if (pass < SLIM_PASS_FEATMAP || pass > SLIM_PASS_BWD_DW) return SLIM_ERR_SHAPE;
     if (d->B < 1 || d->H < 1 || d->L < 1 || d->d < 1 || d->M < 1) return SLIM_ERR_SHAPE;
     if (d->L >= (1LL << 31) || d->B > (1LL << 31) || d->H > (1LL << 31)) return SLIM_ERR_SHAPE;
     if (pass != SLIM_PASS_FEATMAP && (d->num_chunks < 1 || d->num_chunks > d->L)) return SLIM_ERR_SHAPE;
@@ -366,6 +427,7 @@ slim_status slim_validate(const slim_desc *d, int pass)
         return SLIM_ERR_UNSUPPORTED;
     if ((double)BH * (double)d->L * (double)(d->d > d->M ? d->d : d->M) > 4.0e18) return SLIM_ERR_SHAPE;
     if (!find(d)) return SLIM_ERR_UNSUPPORTED;
+    if (pass == SLIM_PASS_BWD_DW && !find_dw(d)) return SLIM_ERR_UNSUPPORTED;  // FAVOR+ only
     return SLIM_OK;
 }
 
@@ -448,10 +510,11 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
 
 slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
                           const void *dY, const void *R_in, const void *S_in, const void *dR_out,
-                          const void *dS_out, void *dQ, void *dK, void *dV, void *dR_in, void *dS_in, void *ws,
-                          size_t ws_bytes, void *stream)
+                          const void *dS_out, void *dQ, void *dK, void *dV, void *dR_in, void *dS_in, float *dW,
+                          void *ws, size_t ws_bytes, void *stream)
 {
-    slim_status st = slim_validate(d, SLIM_PASS_BWD);
+    const int pass = dW ? SLIM_PASS_BWD_DW : SLIM_PASS_BWD;
+    slim_status st = slim_validate(d, pass);
     if (st != SLIM_OK) return st;
     if (!Q || !K || !V || !dY || !dQ || !dK || !dV || !ws) return SLIM_ERR_NULL;
     if (d->feat == SLIM_FEAT_FAVOR && !W) return SLIM_ERR_NULL;
@@ -462,11 +525,12 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
     if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(W, 16) || misaligned(dY, 16) ||
         misaligned(R_in, 16) || misaligned(S_in, 16) || misaligned(dR_out, 16) || misaligned(dS_out, 16) ||
         misaligned(dQ, 16) || misaligned(dK, 16) || misaligned(dV, 16) || misaligned(dR_in, 16) ||
-        misaligned(dS_in, 16) || misaligned(ws, 256))
+        misaligned(dS_in, 16) || misaligned(dW, 16) || misaligned(ws, 256))
         return SLIM_ERR_ALIGN;
-    const Plan p = plan(d, SLIM_PASS_BWD);
+    const Plan p = plan(d, pass);
     if (ws_bytes < p.total) return SLIM_ERR_WORKSPACE;
     const KernelTable *kt = find(d);
+    const DwTable *dt = dW ? find_dw(d) : nullptr;
     hipStream_t s = (hipStream_t)stream;
     const int D = (int)d->d, M = (int)d->M, BH = (int)p.BH;
     char *base = (char *)ws;
@@ -478,6 +542,10 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
     a.gslots = (float *)(base + p.gslots_off);
     a.stats = (float *)(base + p.stats_off);
     a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
+    if (dt) {
+        a.pq = base + p.pq_off;
+        a.pk = base + p.pk_off;
+    }
     double *cR = (double *)(base + p.cR_off), *cS = (double *)(base + p.cS_off);
     double *gR = (double *)(base + p.gR_off), *gS = (double *)(base + p.gS_off);
     if (d->feat == SLIM_FEAT_FAVOR) {
@@ -514,14 +582,51 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
             scan(1, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
         }
         SLIM_TIMED("stats", s, kt->stats(dim3(np, BH), s, a));
+        const dim3 cg(np, BH);
         if (kt->gstate) {
-            SLIM_TIMED("bwdq", s, kt->bwdq(dim3(np, BH), s, a));
-            SLIM_TIMED("gstate", s, kt->gstate(dim3(np, BH), s, a));
+            if (dt)
+                SLIM_TIMED("bwdq_dw", s, dt->bwdq(cg, s, a));
+            else
+                SLIM_TIMED("bwdq", s, kt->bwdq(cg, s, a));
+            SLIM_TIMED("gstate", s, kt->gstate(cg, s, a));
         } else {
-            SLIM_TIMED("bwdq_gstate", s, kt->bwdq(dim3(np, BH), s, a));
+            if (dt)
+                SLIM_TIMED("bwdq_gstate_dw", s, dt->bwdq(cg, s, a));
+            else
+                SLIM_TIMED("bwdq_gstate", s, kt->bwdq(cg, s, a));
         }
         scan(2, a.gslots, gR, gS, D, M, (int)p.P, np, BH, s);
-        SLIM_TIMED("bwdkv", s, kt->bwdkv(dim3(np, BH), s, a));
+        if (dt) {
+            SLIM_TIMED("bwdkv_dw", s, dt->bwdkv(cg, s, a));
+            // dW partials of this window's rows, then their fixed-order sum into dW
+            // (the first window processed, the last one, writes it; the others add)
+            DwArgs da;
+            da.P[0] = a.pq; da.P[1] = a.pk; da.X[0] = Q; da.X[1] = K;
+            da.part = (float *)(base + p.part_off);
+            da.L = d->L;
+            da.r0 = (long long)a.n0 * p.c;
+            da.prows = p.P * p.c;
+            const long long wl = d->L - da.r0 < (long long)np * p.c ? d->L - da.r0 : (long long)np * p.c;
+            da.wl = (int)wl;
+            dw_split(p.BH, wl, &da.S, &da.rps);
+            SLIM_TIMED("dw", s, dt->dw(dim3(da.S, BH, 2), s, da));
+            const int parts = 2 * BH * da.S, n4 = M * D / 4;
+            const f4 *src = (const f4 *)da.part;
+            int rows = parts;
+            prof::Scope ps("dw_sum", s);
+            if (rows > 32) {
+                f4 *mid = (f4 *)(base + p.part2_off);
+                const int r2 = (rows + 31) / 32;
+                hipLaunchKernelGGL(sum_rows_kernel, dim3((n4 + 255) / 256, r2), dim3(256), 0, s, src, rows, n4, 32,
+                                   mid, 0);
+                src = mid;
+                rows = r2;
+            }
+            hipLaunchKernelGGL(sum_rows_kernel, dim3((n4 + 255) / 256, 1), dim3(256), 0, s, src, rows, n4, rows,
+                               (f4 *)dW, wi != nwin - 1 ? 1 : 0);
+        } else {
+            SLIM_TIMED("bwdkv", s, kt->bwdkv(cg, s, a));
+        }
     }
     if (dR_in) {
         narrow2(dR_in, gR, p.BH * D * M, dS_in, gS, p.BH * M, f64, s);

@@ -56,6 +56,7 @@ struct ChunkArgs {
     float *slots;              // [BH][P+1][(D+1)*M]  state slots (R rows, then S)
     float *gslots;             // [BH][P+1][(D+1)*M]  gradient-state slots
     float *stats;              // [BH][P][c][ROWSTAT] per-row (1/den, dden, query offset, -)
+    void *pq, *pk;             // dW pass: dg(Q).g(Q), dg(K).g(K) [BH][P][c][M] (operand type)
     long long L;
     int c;   // chunk length
     int n0;  // first chunk of the window

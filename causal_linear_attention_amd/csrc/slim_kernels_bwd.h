@@ -241,6 +241,19 @@ __device__ __forceinline__ void load_wt_col(Frag<typename C::T> (&wt)[C::M / 16]
         wt[mb] = *reinterpret_cast<const Frag<T> *>(Wp + (((size_t)eb * (C::M / 16) + mb) * 64 + threadIdx.x % 64) * 4);
 }
 
+// dW pass: one operand fragment of dg(X) . g(X) (four consecutive features m..m+3
+// of tile row t) to the window's buffer; rows past the chunk's end are not stored.
+template <class C>
+__device__ __forceinline__ void store_pw(typename C::T *rows, int t, int nv, int m, Frag<typename C::T> v)
+{
+    if (t < nv) *reinterpret_cast<Frag<typename C::T> *>(rows + (size_t)t * C::M + m) = v;
+}
+// The chunk's first row in a dW buffer (see ChunkArgs::pq).
+template <class C> __device__ __forceinline__ typename C::T *pw_rows(void *buf, const ChunkArgs &a, const ChunkGeom &G)
+{
+    return (typename C::T *)buf + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * C::M;
+}
+
 template <class C> constexpr bool bwdq_fuses_gstate()
 {
     return C::D <= 32 || (sizeof(typename C::T) == 2 && C::D <= 64 && C::M >= 128);
@@ -261,7 +274,8 @@ template <class C> struct BwdqSmem {
     __align__(16) float red[C::FAVOR && !DqShared<C>::value ? C::NW * C::TT * C::LDR : 4];
     float kn2[C::TT], qoff[C::TT];
 };
-template <class C>
+// DW: also store dg(Q) . g(Q) for the projection gradient (slim_dw.h).
+template <class C, bool DW = false>
 __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) void bwdq_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
@@ -277,6 +291,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     const T *dY = (const T *)a.dY + G.hb;
     T *dQ = (T *)a.out0 + G.hb;
+    T *pw = DW ? pw_rows<C>(a.pq, a, G) : nullptr;
     constexpr bool FG = bwdq_fuses_gstate<C>();
     f4 dg[FG ? NFB : 1][FG ? NEA : 1];  // the chunk's gradient w.r.t. its entry state, own features
     if constexpr (FG)
@@ -356,8 +371,11 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
 #pragma unroll
                 for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-                    for (int tb = 0; tb < NTB; ++tb)
-                        Gq.put_frag(tb * 16 + lc, w * MW + fb * 16 + 4 * g, cfrag<T>(dq[fb][tb] * pq[fb][tb]));
+                    for (int tb = 0; tb < NTB; ++tb) {
+                        const Frag<T> v = cfrag<T>(dq[fb][tb] * pq[fb][tb]);
+                        Gq.put_frag(tb * 16 + lc, w * MW + fb * 16 + 4 * g, v);
+                        if constexpr (DW) store_pw<C>(pw + (size_t)t0 * C::M, tb * 16 + lc, nv, w * MW + fb * 16 + 4 * g, v);
+                    }
                 __syncthreads();
                 for (int blk = w; blk < NB; blk += C::NW) {
                     const int tb = blk / NEB, eb = blk % NEB;
@@ -372,7 +390,11 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
 #pragma unroll
                 for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-                    for (int tb = 0; tb < NTB; ++tb) gq[fb][tb] = cfrag<T>(dq[fb][tb] * pq[fb][tb]);
+                    for (int tb = 0; tb < NTB; ++tb) {
+                        gq[fb][tb] = cfrag<T>(dq[fb][tb] * pq[fb][tb]);
+                        if constexpr (DW)
+                            store_pw<C>(pw + (size_t)t0 * C::M, tb * 16 + lc, nv, w * MW + fb * 16 + 4 * g, gq[fb][tb]);
+                    }
 #pragma unroll
                 for (int eb = 0; eb < NEB; ++eb) {
 #pragma unroll
@@ -438,7 +460,8 @@ template <class C> struct BwdkvSmem {
     __align__(16) T fq[C::NW * C::FMat::SIZE];
     float kn2[C::TT], qoff[C::TT];
 };
-template <class C>
+// DW: also store dg(K) . g(K) for the projection gradient (slim_dw.h).
+template <class C, bool DW = false>
 __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW)) void bwdkv_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
@@ -456,6 +479,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     const T *dY = (const T *)a.dY + G.hb;
     T *dK = (T *)a.out1 + G.hb, *dV = (T *)a.out2 + G.hb;
+    T *pw = DW ? pw_rows<C>(a.pk, a, G) : nullptr;
     const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
     const float *gsl = slot_ptr<C>(a.gslots, a, G.bh, G.nl + 1);
     f4 dr[NEA][NFB];                       // [dR; dS], rows e, cols m
@@ -591,6 +615,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                     const f4 v = dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]);
                     rsum += (v[0] + v[1]) + (v[2] + v[3]);
                     gk[fb][sb] = cfrag<T>(v);
+                    if constexpr (DW)
+                        store_pw<C>(pw + (size_t)t0 * C::M, sb * 16 + lc, nv, w * MW + fb * 16 + 4 * g, gk[fb][sb]);
                 }
                 rsum += __shfl_xor(rsum, 16, 64);
                 rsum += __shfl_xor(rsum, 32, 64);

@@ -71,7 +71,15 @@ typedef enum slim_status {
 
 typedef enum slim_dtype { SLIM_F32 = 0, SLIM_BF16 = 1, SLIM_F64 = 2 } slim_dtype;
 typedef enum slim_feat { SLIM_FEAT_FAVOR = 0, SLIM_FEAT_ELU1 = 1 } slim_feat;
-typedef enum slim_pass { SLIM_PASS_FEATMAP = 0, SLIM_PASS_FWD = 1, SLIM_PASS_BWD = 2, SLIM_PASS_DECODE = 3 } slim_pass;
+/* SLIM_PASS_BWD_DW: the backward when it also computes dW (FAVOR+ only; a
+ * larger workspace). */
+typedef enum slim_pass {
+    SLIM_PASS_FEATMAP = 0,
+    SLIM_PASS_FWD = 1,
+    SLIM_PASS_BWD = 2,
+    SLIM_PASS_DECODE = 3,
+    SLIM_PASS_BWD_DW = 4
+} slim_pass;
 
 typedef struct slim_desc {
     int64_t B, H, L;       /* batch, heads, sequence length */
@@ -137,12 +145,21 @@ slim_status slim_attn_fwd(const slim_desc *desc, const void *Q, const void *K, c
  *      state (both NULL = zero, or both given);
  *      dR_out, dS_out = incoming gradient of the final state (both NULL = zero).
  * Out: dQ, dK, dV; dR_in, dS_in = gradient w.r.t. the initial state (both NULL
- *      = not wanted, or both given).  dW is not computed.
- * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_BWD). */
+ *      = not wanted, or both given);
+ *      dW = gradient w.r.t. the FAVOR+ projection, [M][d] fp32, summed over all
+ *      batch rows and heads (they share W), overwritten; NULL = not wanted.
+ *      g depends on W only through w_m, with d g(x)_m / d w_m = g(x)_m x, so
+ *      dW[m] = sum over the query and key rows x of (dL/dg(x)_m) g(x)_m x.
+ *      FAVOR+ only (SLIM_ERR_UNSUPPORTED for elu+1).  Deterministic: the
+ *      per-row products are summed in a fixed order.
+ * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_BWD),
+ *      or slim_workspace_bytes(desc, SLIM_PASS_BWD_DW) when dW is given (it
+ *      adds two [B*H][window rows][M] buffers of the io dtype and the partial
+ *      sums of dW). */
 slim_status slim_attn_bwd(const slim_desc *desc, const void *Q, const void *K, const void *V, const void *W,
                           const void *dY, const void *R_in, const void *S_in, const void *dR_out,
-                          const void *dS_out, void *dQ, void *dK, void *dV, void *dR_in, void *dS_in, void *ws,
-                          size_t ws_bytes, void *stream);
+                          const void *dS_out, void *dQ, void *dK, void *dV, void *dR_in, void *dS_in, float *dW,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /* Recurrent decode step: the iterative prefix-sum evaluation of Subsection
  * 2.1 (eq. (3)-(4)) advanced by one position.  For every b, h and the one new
@@ -175,7 +192,9 @@ const char *slim_status_string(slim_status s);
  * events), then report per kernel name ("state", "scan_prefix", "fwd",
  * "scan_window", "scan_sum", "stats", "bwdq", "gstate", "bwdq_gstate" (the dQ
  * kernel with the gradient state folded in, for shapes where it fits),
- * "scan_grad", "bwdkv", "featmap", "decode") the summed GPU time in
+ * "scan_grad", "bwdkv", "featmap", "decode"; with dW: "bwdq_dw" or
+ * "bwdq_gstate_dw", "bwdkv_dw", "dw" (the row contraction), "dw_sum" (the sum
+ * of its partials)) the summed GPU time in
  * milliseconds and the number of launches.  The name pointer stays
  * valid until the next slim_prof_enable(1).  Guarded by a process-wide mutex;
  * the timings are global to the process, not per stream. */

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.slim_version() >> 16 == 1
+    assert lib.slim_version() >> 16 == 2
     for code in range(8):
         assert lib.slim_status_string(code)
     assert lib.slim_status_string(0) == b"ok"
@@ -83,15 +83,50 @@ def test_entry_points_reject_before_any_launch(lib):
     bad = ctypes.c_void_p((1 << 20) + 4)
     assert lib.slim_attn_fwd(ctypes.byref(d), bad, p, p, p, None, None, p, p, p, p, 1 << 40, None) == 6
     assert lib.slim_attn_bwd(ctypes.byref(d_(num_chunks=0)), p, p, p, p, p, p, p, None, None, p, p, p, None, None,
-                           p, 1 << 40, None) == 2
+                           None, p, 1 << 40, None) == 2
     # only one of the paired initial-state pointers
     assert lib.slim_attn_fwd(ctypes.byref(d), p, p, p, p, p, None, p, p, p, p, 1 << 40, None) == 1
     assert lib.slim_attn_bwd(ctypes.byref(d), p, p, p, p, p, p, None, None, None, p, p, p, None, None,
-                           p, 1 << 40, None) == 1
+                           None, p, 1 << 40, None) == 1
     # elu+1 takes no W
     de = d_(feat=_lib.SLIM_FEAT_ELU1, M=64)
     assert lib.slim_attn_fwd(ctypes.byref(de), p, p, p, p, None, None, p, p, p, p, 1 << 40, None) == 2
     assert lib.slim_featmap(ctypes.byref(de), p, None, p, p, None) == 2
+
+
+def test_dw_pass_validation(lib):
+    # the projection gradient exists for FAVOR+ only, and needs the larger workspace
+    BWD, DW = _lib.SLIM_PASS_BWD, _lib.SLIM_PASS_BWD_DW
+    assert validate(lib, DW) == 0
+    assert validate(lib, DW, dtype=_lib.SLIM_F32, d=128, M=256) == 0
+    assert validate(lib, DW, feat=_lib.SLIM_FEAT_ELU1, M=64) == 4
+    assert validate(lib, 5) == 2
+    assert ws(lib, DW) > ws(lib, BWD) > 0
+    assert ws(lib, DW, feat=_lib.SLIM_FEAT_ELU1, M=64) == 0
+    # the extra space: two [B*H][window rows][M] buffers of the io dtype plus the partial sums
+    d = dict(B=2, H=3, L=4096, d=64, M=128, num_chunks=16, window_chunks=16)
+    extra = ws(lib, DW, **d) - ws(lib, BWD, **d)
+    assert extra >= 2 * 6 * 4096 * 128 * 2
+    # bounded by the window, not by L
+    big = [ws(lib, DW, B=1, H=8, L=n, d=64, M=64, num_chunks=n // 512, window_chunks=64) for n in (1 << 16, 1 << 20)]
+    assert big[0] == big[1]
+
+
+def test_dw_rejects_before_any_launch(lib):
+    p = ctypes.c_void_p(1 << 20)
+    dw = ctypes.c_void_p(1 << 21)
+    d = d_()
+    # workspace sized for the plain backward is too small once dW is asked for
+    wsb = lib.slim_workspace_bytes(ctypes.byref(d), _lib.SLIM_PASS_BWD)
+    assert lib.slim_attn_bwd(ctypes.byref(d), p, p, p, p, p, None, None, None, None, p, p, p, None, None,
+                           dw, p, wsb, None) == 5
+    # misaligned dW
+    assert lib.slim_attn_bwd(ctypes.byref(d), p, p, p, p, p, None, None, None, None, p, p, p, None, None,
+                           ctypes.c_void_p((1 << 21) + 4), p, 1 << 40, None) == 6
+    # elu+1 has no projection
+    de = d_(feat=_lib.SLIM_FEAT_ELU1, M=64)
+    assert lib.slim_attn_bwd(ctypes.byref(de), p, p, p, None, p, None, None, None, None, p, p, p, None, None,
+                           dw, p, 1 << 40, None) == 4
 
 
 def ws(lib, pass_, **kw):
@@ -140,7 +175,7 @@ def test_decode_validation(lib):
     assert validate(lib, _lib.SLIM_PASS_DECODE, L=2, num_chunks=1) == 2       # one token per head
     assert validate(lib, _lib.SLIM_PASS_DECODE, L=1, num_chunks=1, B=1 << 12, H=1 << 12) == 0
     assert validate(lib, _lib.SLIM_PASS_DECODE, L=1, num_chunks=1, B=1 << 12, H=(1 << 12) + 1) == 4
-    assert validate(lib, 4) == 2                                              # unknown pass
+    assert validate(lib, 5) == 2                                              # unknown pass
     assert ws(lib, _lib.SLIM_PASS_DECODE, L=1, num_chunks=1) == 0
 
 
