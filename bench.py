@@ -18,6 +18,7 @@ CPU oracle timed on a bounded sample of the same workload.
   python bench.py --decode [...]    # the recurrent decode step instead (one JSON line of its own)
   python bench.py --chunk-sweep     # time, peak HBM and gradient discrepancy vs slice length (one JSON line)
   python bench.py --algorithm1      # the same for the page's Algorithm 1 on a multi-layer Performer
+  python bench.py --dw              # the step with the backward also computing dW (FAVOR+ projection)
 
 roofline.traffic: HBM bytes per launch of the dominant kernel, FETCH_SIZE and
 WRITE_SIZE scaled by what the same counters read for a plain copy of known
@@ -67,9 +68,12 @@ def parse():
                          "slice length C (one JSON line)")
     ap.add_argument("--decode", action="store_true",
                     help="time the recurrent decode step (one token per sequence per step) instead")
+    ap.add_argument("--dw", action="store_true",
+                    help="the backward of every step also computes dW, the gradient of the FAVOR+ projection")
     ap.add_argument("--pmc-summary", default=None, metavar="DIR",
                     help="DIR holds rocprofv3 counter runs F, W (FETCH_SIZE, WRITE_SIZE of --profile-run; "
-                         "DF, DW with --decode) and CF, CW (the same of --copy-calib); prints the summary")
+                         "DF, DW with --decode; DWF, DWW with --dw) and CF, CW (the same of --copy-calib); prints "
+                      "the summary")
     return ap.parse_args()
 
 
@@ -110,9 +114,10 @@ def read_counter(path, counter):
     return out
 
 
-def pmc_summary(d, w, bytes_of_copy, runs=("F", "W")):
+def pmc_summary(d, w, bytes_of_copy, runs=("F", "W"), dw=False):
     """HBM bytes per dispatch and kernel from counter runs in d: runs[0] (FETCH_SIZE) and
-    runs[1] (WRITE_SIZE) of the workload, CF and CW of the calibration copy."""
+    runs[1] (WRITE_SIZE) of the workload, CF and CW of the calibration copy.  dw: the
+    runs are of the step with dW (its dQ and dK/dV kernels get the _dw names)."""
     fetch = read_counter(glob.glob(os.path.join(d, runs[0], "*counter_collection.csv"))[0], "FETCH_SIZE")
     write = read_counter(glob.glob(os.path.join(d, runs[1], "*counter_collection.csv"))[0], "WRITE_SIZE")
     cf = read_counter(glob.glob(os.path.join(d, "CF", "*counter_collection.csv"))[0], "FETCH_SIZE")["copy"]
@@ -128,22 +133,30 @@ def pmc_summary(d, w, bytes_of_copy, runs=("F", "W")):
                    "traffic_bytes": round(fb + wb)}
     if "bwdq" in rows and "gstate" not in rows and "bwdkv" in rows:
         rows["bwdq_gstate"] = rows.pop("bwdq")  # the dQ kernel with the gradient state folded in
+    if dw:
+        for k in ("bwdq", "bwdq_gstate", "bwdkv"):
+            if k in rows:
+                rows[k + "_dw"] = rows.pop(k)
+        if "sum_rows" in rows:
+            rows["dw_sum"] = rows.pop("sum_rows")
     return {"workload": w.name, "source_hash": kernel_source_hash(), "fetch_factor": round(f_fac, 4),
             "write_factor": round(w_fac, 4), "kernels": rows}
 
 
 def load_traffic(w, kernel):
-    """HBM bytes per launch of `kernel` from the committed summary, if it matches these sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.md")
-    if not os.path.exists(path):
-        return None
-    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
-    if not m:
-        return None
-    rec = json.loads(m.group(1))
-    if rec.get("source_hash") != kernel_source_hash() or kernel not in rec.get("kernels", {}):
-        return None
-    return rec["kernels"][kernel]["traffic_bytes"]
+    """HBM bytes per launch of `kernel` from the committed summaries of this workload (the
+    plain step's, or the dW step's), if one lists it and matches these sources."""
+    for fn in (f"traffic_{w.name}.md", f"traffic_dw_{w.name}.md"):
+        path = os.path.join(ROOT, "profiles", fn)
+        if not os.path.exists(path):
+            continue
+        m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec.get("source_hash") == kernel_source_hash() and kernel in rec.get("kernels", {}):
+            return rec["kernels"][kernel]["traffic_bytes"]
+    return None
 
 
 def make_inputs(w, torch, synth):
@@ -491,7 +504,7 @@ def main():
     from causal_linear_attention_amd import _lib
     from causal_linear_attention_amd import attention as A
     from causal_linear_attention_amd import synth
-    from causal_linear_attention_amd.workloads import HEADLINE, WORKLOADS, kernel_bytes, kernel_flops, survey_flops
+    from causal_linear_attention_amd.workloads import HEADLINE, WORKLOADS, survey_flops
 
     if args.copy_calib:
         # plain device-to-device copy of 1 GiB (reads 1 GiB, writes 1 GiB): the
@@ -523,17 +536,19 @@ def main():
         return
     w = WORKLOADS[args.workload or HEADLINE]
     if args.pmc_summary:
-        rec = pmc_summary(args.pmc_summary, w, 1 << 30)
+        rec = pmc_summary(args.pmc_summary, w, 1 << 30, ("DWF", "DWW") if args.dw else ("F", "W"), dw=args.dw)
         print(json.dumps(rec))
         return
     q, k, v, W, dy = make_inputs(w, torch, synth)
     tile = int(_lib.lib().slim_tile_rows(__import__("ctypes").byref(A.make_desc(q, w.M, w.feat, w.chunks))))
     torch.cuda.synchronize()
 
+    want_dw = bool(args.dw and w.backward and w.feat == "favor")
+
     def step():
         Y, R, S = A.attn_fwd(q, k, v, W, w.feat, w.chunks)
         if w.backward:
-            A.attn_bwd(q, k, v, W, dy, w.feat, w.chunks)
+            A.attn_bwd(q, k, v, W, dy, w.feat, w.chunks, want_dw=want_dw)
         return Y
 
     if args.profile_run:
@@ -574,13 +589,12 @@ def main():
     ms_step = 1e3 * elapsed / args.steps
     tokens_per_s = w.tokens * args.steps / elapsed
     kernels, roofline = kernel_records(w, prof, args.steps, tile)
-    fl = kernel_flops(w, tile)
-    passes = {"state": 2 if w.backward else 1}
     isz = 2 if w.dtype == "bf16" else 4
     # minimum HBM traffic of a step: read Q K V (fwd) and Q K V dY (bwd), write Y dQ dK dV
     io = w.head_tokens * w.d * isz * (11 if w.backward else 4)
     footprint = w.head_tokens * w.d * isz * (9 if w.backward else 4)  # Q K V dY Y dQ dK dV resident
-    step_flop = sum(fl[n] * (passes.get(n, 1)) for n in fl) * w.head_tokens
+    # the work of the kernels the step actually launched (per launch x launches per step)
+    step_flop = sum(r.get("flop_per_launch", 0.0) * r["launches"] for r in kernels.values()) / args.steps
     rec = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
@@ -589,7 +603,7 @@ def main():
                    "W": w.w_kind, "chunks": w.chunks, "chunk_len": w.chunk_len, "tile": tile,
                    "window_chunks": int(_lib.lib().slim_window_chunks(
                        __import__("ctypes").byref(A.make_desc(q, w.M, w.feat, w.chunks)))),
-                   "global_batch": w.B, "seq_len": w.L, "parallelism": "none (1 GPU)"},
+                   "dW": want_dw, "global_batch": w.B, "seq_len": w.L, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "step_tflops": round(step_flop / (ms_step * 1e-3) / 1e12, 2),
         "step_tflops_unsliced_accounting": round(survey_flops(w) * w.head_tokens / (ms_step * 1e-3) / 1e12, 2),

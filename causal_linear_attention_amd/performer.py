@@ -12,9 +12,10 @@ so the plainest GPT-2-like reading of the listed parameters is taken):
                     X  = X + GeLU(LN2(X) W1 + b1) W2 + b2
     X^(out) = X^(s) W_out + b_out;   loss = sum_{l < L} CE(X^(out)_l, p_{l+1})
 
-Att^lin is this package's causal linear attention (FAVOR+, one fixed random
-projection per layer) and runs in the HIP kernels; everything else is plain
-PyTorch (these layers are not the subject here).
+Att^lin is this package's causal linear attention (FAVOR+, one random
+projection per layer, fixed as on the page or, with train_features, trained
+through the backward's dW) and runs in the HIP kernels; everything else is
+plain PyTorch (these layers are not the subject here).
 
 Algorithm 1 (Subsection 3.2-3.3): the sequence is cut into N slices of length
 at most C; the forward pass walks the slices in order, layers inside, carrying
@@ -40,7 +41,7 @@ from . import synth
 class _StatefulAttention(torch.autograd.Function):
     """Att^lin of one slice from an entry state: (q, k, v, R_in, S_in) ->
     (Y, R_out, S_out), with the backward through all five inputs (slim_attn_bwd
-    with the incoming state gradient)."""
+    with the incoming state gradient) and through W when it requires one."""
 
     @staticmethod
     def forward(ctx, q, k, v, R_in, S_in, W, num_chunks, state_dtype):
@@ -62,10 +63,11 @@ class _StatefulAttention(torch.autograd.Function):
         if dS is None and dR is not None:
             dS = torch.zeros((q.shape[0], q.shape[1], W.shape[0]), dtype=sd, device=q.device)
         st = (R_in, S_in) if ctx.has_state else (None, None)
-        dq, dk, dv, dRi, dSi = A.attn_bwd(q, k, v, W, dY.contiguous(), "favor", ctx.num_chunks, R_in=st[0],
-                                          S_in=st[1], dR_out=dR, dS_out=dS, want_state_grad=ctx.has_state,
-                                          state_dtype=sd)
-        return dq, dk, dv, dRi, dSi, None, None, None
+        want_dw = ctx.needs_input_grad[5]
+        g = A.attn_bwd(q, k, v, W, dY.contiguous(), "favor", ctx.num_chunks, R_in=st[0], S_in=st[1], dR_out=dR,
+                       dS_out=dS, want_state_grad=ctx.has_state, state_dtype=sd, want_dw=want_dw)
+        dW = g[5].to(W.dtype) if want_dw else None
+        return g[0], g[1], g[2], g[3], g[4], dW, None, None
 
 
 def sinusoid(positions: torch.Tensor, d_model: int) -> torch.Tensor:
@@ -82,7 +84,7 @@ class Performer:
     """A randomly initialised s-layer Performer (parameters from synth.performer_params)."""
 
     def __init__(self, vocab=64, d_model=64, heads=2, layers=2, M=64, d_ff=None, seed=0, device="cuda",
-                 num_chunks=1, state_dtype=torch.float64):
+                 num_chunks=1, state_dtype=torch.float64, train_features=False):
         self.vocab, self.d_model, self.heads, self.layers, self.M = vocab, d_model, heads, layers, M
         self.d = d_model // heads
         self.d_ff = d_ff or 4 * d_model
@@ -94,7 +96,7 @@ class Performer:
         self.p = {}
         for n, a in raw.items():
             t = torch.from_numpy(a).to(device)
-            if not n.startswith("wf."):
+            if train_features or not n.startswith("wf."):  # wf.r: the layers' feature projections
                 t.requires_grad_(True)
             self.p[n] = t
 

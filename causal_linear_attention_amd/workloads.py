@@ -142,6 +142,12 @@ def kernel_flops(w: Workload, tile: int) -> dict:
         "bwdq_gstate": 2 * P + tm + td + 3 * dm + vjp,     # bwdq, and dG += g(Q)^T [dNum | dden]
         "bwdkv": 2 * P + 2 * tm + 2 * td + 3 * dm + vjp,   # g(Q), g(K); P; dNum^T P; dR g(K)^T; A;
                                                             # g(Q)^T A; dR^T V; W chain; dR update
+        # the dW pass: the same dQ and dK/dV work (they also store dg(X) . g(X)), and the
+        # row contraction dW += (dg(X) . g(X))^T X for X = Q and K
+        "bwdq_dw": 2 * P + tm + td + 2 * dm + vjp,
+        "bwdq_gstate_dw": 2 * P + tm + td + 3 * dm + vjp,
+        "bwdkv_dw": 2 * P + 2 * tm + 2 * td + 3 * dm + vjp,
+        "dw": 2 * dm if favor else 0,
     }
 
 
@@ -164,6 +170,12 @@ def kernel_bytes(w: Workload) -> dict:
         "gstate": 2 * row + st + slot,              # Q, dY, statistics -> gradient slot
         "bwdq_gstate": 4 * row + 2 * slot + st + row,  # Q, K, V, dY, entry state, statistics -> dQ, gradient slot
         "bwdkv": 4 * row + st + slot + 2 * row,     # Q, K, V, dY, statistics, gradient slot -> dK, dV
+        # the dW pass: each backward kernel also writes one row of dg(X) . g(X) (M operand-type
+        # values), which the row contraction reads back with X (query and key side)
+        "bwdq_dw": 4 * row + slot + st + row + w.M * s,
+        "bwdq_gstate_dw": 4 * row + 2 * slot + st + row + w.M * s,
+        "bwdkv_dw": 4 * row + st + slot + 2 * row + w.M * s,
+        "dw": 2 * (w.M * s + row),
     }
 
 

@@ -30,7 +30,8 @@ from . import attn_bwd, attn_fwd
 
 
 class _OracleAttention(torch.autograd.Function):
-    """Att^lin (FAVOR+) by the oracle's quadratic form, q, k, v [B, H, L, d] float64."""
+    """Att^lin (FAVOR+) by the oracle's quadratic form, q, k, v [B, H, L, d] float64;
+    the gradient of the projection W too when it requires one."""
 
     @staticmethod
     def forward(ctx, q, k, v, W):
@@ -42,9 +43,11 @@ class _OracleAttention(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dY):
         q, k, v, W = ctx.saved_tensors
-        dq, dk, dv, _, _ = attn_bwd(q.detach().numpy(), k.detach().numpy(), v.detach().numpy(),
-                                    W.detach().numpy(), dY.detach().contiguous().numpy(), "favor", form="quadratic")
-        return torch.from_numpy(dq), torch.from_numpy(dk), torch.from_numpy(dv), None
+        want_dw = ctx.needs_input_grad[3]
+        g = attn_bwd(q.detach().numpy(), k.detach().numpy(), v.detach().numpy(), W.detach().numpy(),
+                     dY.detach().contiguous().numpy(), "favor", form="quadratic", want_dw=want_dw)
+        dW = torch.from_numpy(g[5]) if want_dw else None
+        return torch.from_numpy(g[0]), torch.from_numpy(g[1]), torch.from_numpy(g[2]), dW
 
 
 def _positions(L: int, D: int) -> torch.Tensor:
@@ -67,10 +70,12 @@ def _gelu(x):
     return 0.5 * x * (1.0 + torch.erf(x / math.sqrt(2.0)))
 
 
-def loss_and_grads(params: dict, tokens: np.ndarray, heads: int, layers: int):
+def loss_and_grads(params: dict, tokens: np.ndarray, heads: int, layers: int, train_features: bool = False):
     """Loss (float) and {name: float64 gradient array} of every trainable
-    parameter (all but the fixed feature projections wf.r)."""
-    P = {n: torch.from_numpy(np.asarray(a, dtype=np.float64)).requires_grad_(not n.startswith("wf."))
+    parameter: all but the feature projections wf.r, which are fixed random
+    draws unless train_features."""
+    P = {n: torch.from_numpy(np.asarray(a, dtype=np.float64)).requires_grad_(train_features or
+                                                                             not n.startswith("wf."))
          for n, a in params.items()}
     tok = torch.from_numpy(np.asarray(tokens, dtype=np.int64))
     B, L = tok.shape

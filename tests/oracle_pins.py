@@ -308,6 +308,28 @@ def pin_performer_ref_finite_differences():
             assert abs(fd - g) <= 1e-6 * max(1.0, abs(g)), (name, i, fd, g)
 
 
+def pin_performer_ref_feature_gradients():
+    # with trainable feature projections: their gradients (the attention's dW)
+    # against central differences of the loss
+    from oracle import performer_ref
+    params, tokens = _tiny_performer()
+    params = {n: a.astype(np.float64) for n, a in params.items()}
+    _, grads = performer_ref.loss_and_grads(params, tokens, 2, 2, train_features=True)
+    h = 1e-6
+    for name in ("wf.0", "wf.1"):
+        a = params[name]
+        for i in np.ndindex(a.shape):
+            plus = {n: v.copy() for n, v in params.items()}
+            minus = {n: v.copy() for n, v in params.items()}
+            plus[name][i] += h
+            minus[name][i] -= h
+            fd = (performer_ref.loss_and_grads(plus, tokens, 2, 2)[0] -
+                  performer_ref.loss_and_grads(minus, tokens, 2, 2)[0]) / (2 * h)
+            g = grads[name][i]
+            assert abs(fd - g) <= 1e-6 * max(1.0, abs(g)), (name, i, fd, g)
+    assert max(float(np.abs(grads[n]).max()) for n in ("wf.0", "wf.1")) > 1e-3  # not vacuous
+
+
 def pin_performer_ref_no_target():
     # A one-token sequence has no next token: its loss and gradients are zero.
     from oracle import performer_ref
@@ -477,7 +499,8 @@ ALL_PINS = [
     pin_featmap_vjp_fd, pin_featmap_wgrad_fd, pin_fwd_golden, pin_single_row_is_value, pin_identical_keys_give_running_mean,
     pin_constant_values, pin_causality, pin_convex_hull, pin_quadratic_equals_prefix,
     pin_initial_state_is_a_prefix, pin_rows_match_full, pin_decode_golden, pin_decode_steps_equal_quadratic,
-    pin_decode_first_token_is_value, pin_performer_ref_finite_differences, pin_performer_ref_no_target,
+    pin_decode_first_token_is_value, pin_performer_ref_finite_differences, pin_performer_ref_feature_gradients,
+    pin_performer_ref_no_target,
     pin_softmax_special_cases,
     pin_favor_converges_to_softmax, pin_bwd_finite_differences, pin_bwd_dw_finite_differences,
     pin_dw_rotation_symmetry, pin_bwd_special_cases, pin_bwd_quadratic_equals_prefix,

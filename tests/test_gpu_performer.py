@@ -26,8 +26,8 @@ def _tokens():
     return synth.random_tokens(11, B, L, CFG["vocab"])
 
 
-def _model():
-    return Performer(**CFG, seed=SEED)
+def _model(train_features=False):
+    return Performer(**CFG, seed=SEED, train_features=train_features)
 
 
 def _grads(m):
@@ -48,12 +48,13 @@ def _worst(g, ref):
 _REF = {}
 
 
-def _reference():
-    if "r" not in _REF:
+def _reference(train_features=False):
+    if train_features not in _REF:
         params = synth.performer_params(SEED, CFG["vocab"], CFG["d_model"], CFG["heads"], CFG["layers"], CFG["M"],
                                         CFG["d_ff"])
-        _REF["r"] = performer_ref.loss_and_grads(params, _tokens(), CFG["heads"], CFG["layers"])
-    return _REF["r"]
+        _REF[train_features] = performer_ref.loss_and_grads(params, _tokens(), CFG["heads"], CFG["layers"],
+                                                            train_features=train_features)
+    return _REF[train_features]
 
 
 def test_full_pass_matches_fp64_reference():
@@ -103,3 +104,19 @@ def test_algorithm1_ragged_last_slice():
     gf = _grads(m)
     assert abs(loss_c - float(lf)) <= 1e-5 * abs(float(lf))
     assert _relerr(gc, gf) < 1e-5, _worst(gc, gf)
+
+
+@pytest.mark.parametrize("C", [256, 16])
+def test_algorithm1_with_trainable_features(C):
+    # the feature projections trained too: their gradients come from the backward's dW
+    print("algorithm 1 with trainable features, slice length", C, flush=True)
+    tok = torch.from_numpy(_tokens()).cuda()
+    m = _model(train_features=True)
+    m.algorithm1(tok, C)
+    gc = _grads(m)
+    assert "wf.0" in gc and "wf.1" in gc
+    ref_loss, ref = _reference(train_features=True)
+    print("discrepancy vs fp64 reference %.2e, features only %.2e" %
+          (_relerr(gc, ref), _relerr({n: gc[n] for n in ("wf.0", "wf.1")}, {n: ref[n] for n in ("wf.0", "wf.1")})))
+    assert _relerr(gc, ref) < 1e-5, _worst(gc, ref)
+    assert _relerr({n: gc[n] for n in ("wf.0", "wf.1")}, {n: ref[n] for n in ("wf.0", "wf.1")}) < 1e-5
