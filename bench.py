@@ -2,7 +2,9 @@
 
 One step = slim_attn_fwd + slim_attn_bwd over one batch of synthetic inputs
 already resident in HBM (every kernel of the path: feature maps, chunk states,
-scans, outputs, statistics, dQ, dK/dV).  Default workload: FAVOR+, bf16 I/O with
+scans, outputs, statistics, dQ, dK/dV); the forward keeps its output and per-row
+denominator statistics for the backward, as the autograd function does (the
+step with the backward recomputing them is timed too, ms_per_step_stats_recomputed).  Default workload: FAVOR+, bf16 I/O with
 fp32 state, B=4, H=16, L=16384, d=64, M=256, 32 slices of 512.
 
 Prints ONE JSON line (rank 0): throughput (tokens/s = B*L per step time, timed
@@ -545,10 +547,15 @@ def main():
 
     want_dw = bool(args.dw and w.backward and w.feat == "favor")
 
-    def step():
-        Y, R, S = A.attn_fwd(q, k, v, W, w.feat, w.chunks)
+    def step(keep_stats=True):
+        # the forward keeps its output and per-row denominator statistics for the
+        # backward (as autograd does); keep_stats=False: the backward recomputes them
+        keep = keep_stats and w.backward
+        out = A.attn_fwd(q, k, v, W, w.feat, w.chunks, want_row_stats=keep)
+        Y = out[0]
         if w.backward:
-            A.attn_bwd(q, k, v, W, dy, w.feat, w.chunks, want_dw=want_dw)
+            A.attn_bwd(q, k, v, W, dy, w.feat, w.chunks, want_dw=want_dw, Y=Y if keep else None,
+                       row_stats=out[3] if keep else None)
         return Y
 
     if args.profile_run:
@@ -578,6 +585,13 @@ def main():
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # the same steps with the backward recomputing the row statistics (no state kept
+    # from the forward but its inputs), for comparison
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step(keep_stats=False)
+    torch.cuda.synchronize()
+    elapsed_recompute = time.perf_counter() - t1
     # per-kernel times: the same number of steps again, each kernel bracketed by hipEvents
     _lib.prof_enable(True)
     for _ in range(args.steps):
@@ -598,6 +612,7 @@ def main():
     rec = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "ms_per_step_stats_recomputed": round(1e3 * elapsed_recompute / args.steps, 4),
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "M": w.M, "feat": w.feat,
                    "W": w.w_kind, "chunks": w.chunks, "chunk_len": w.chunk_len, "tile": tile,

@@ -79,9 +79,11 @@ def featmap(x, W=None, feat="favor", row_offset=False):
 
 
 def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, window_chunks=0,
-             state_dtype=None):
+             state_dtype=None, want_row_stats=False):
     """Forward.  Returns (Y, R_out [B,H,d,M], S_out [B,H,M]).  States are fp32, or
-    fp64 when R_in is fp64 or state_dtype=torch.float64."""
+    fp64 when R_in is fp64 or state_dtype=torch.float64.  want_row_stats: a fourth
+    value, the per-row statistics [B,H,L,2] fp32 that let attn_bwd skip recomputing
+    the denominators (pass it with Y)."""
     B, H, L, d = q.shape
     M = _feat_M(W, feat, d)
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -97,20 +99,26 @@ def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, 
     Y = torch.empty_like(q)
     R = torch.empty((B, H, d, M), dtype=sd, device=q.device)
     S = torch.empty((B, H, M), dtype=sd, device=q.device)
+    rs = torch.empty((B, H, L, 2), dtype=torch.float32, device=q.device) if want_row_stats else None
     _lib.check(_lib.lib().slim_attn_fwd(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(R_in),
-                                        _ptr(S_in), _ptr(Y), _ptr(R), _ptr(S), _ptr(ws), ws.numel(), _stream()),
+                                        _ptr(S_in), _ptr(Y), _ptr(R), _ptr(S), _ptr(rs), _ptr(ws), ws.numel(),
+                                        _stream()),
                "slim_attn_fwd")
+    if want_row_stats:
+        return Y, R, S, rs
     return Y, R, S
 
 
 def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, dR_out=None, dS_out=None,
-             want_state_grad=False, window_chunks=0, state_dtype=None, want_dw=False):
+             want_state_grad=False, window_chunks=0, state_dtype=None, want_dw=False, Y=None, row_stats=None):
     """Backward of attn_fwd(q, k, v, W, feat, num_chunks, R_in, S_in) for the
     loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out>.  Returns (dQ, dK, dV,
     dR_in, dS_in); the last two are None unless want_state_grad.  With want_dw
     (FAVOR+) a sixth value follows: dW [M, d] fp32, the gradient w.r.t. the
     projection W.  The state tensors share one dtype (fp32, or fp64), taken
-    from those given."""
+    from those given.  Y, row_stats: the output and row statistics of attn_fwd on
+    the same inputs (want_row_stats=True); given, the backward reuses the
+    forward's denominators instead of recomputing them."""
     B, H, L, d = q.shape
     M = _feat_M(W, feat, d)
     for n, t in (("q", q), ("k", k), ("v", v), ("dY", dY)):
@@ -125,6 +133,11 @@ def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, d
         _check_io("dS_out", dS_out, sd, (B, H, M))
     if want_dw and feat != "favor":
         raise ValueError("dW exists only for the FAVOR+ feature map")
+    if (Y is None) != (row_stats is None):
+        raise ValueError("give both Y and row_stats, or neither")
+    if Y is not None:
+        _check_io("Y", Y, q.dtype, q.shape)
+        _check_io("row_stats", row_stats, torch.float32, (B, H, L, 2))
     dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd)
     ps = _lib.SLIM_PASS_BWD_DW if want_dw else _lib.SLIM_PASS_BWD
     ws = torch.empty(max(1, workspace_bytes(dsc, ps)), dtype=torch.uint8, device=q.device)
@@ -135,8 +148,9 @@ def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, d
         dR = torch.empty((B, H, d, M), dtype=sd, device=q.device)
         dS = torch.empty((B, H, M), dtype=sd, device=q.device)
     _lib.check(_lib.lib().slim_attn_bwd(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(dY),
-                                        _ptr(R_in), _ptr(S_in), _ptr(dR_out), _ptr(dS_out), _ptr(dQ), _ptr(dK),
-                                        _ptr(dV), _ptr(dR), _ptr(dS), _ptr(dW), _ptr(ws), ws.numel(), _stream()),
+                                        _ptr(Y), _ptr(row_stats), _ptr(R_in), _ptr(S_in), _ptr(dR_out),
+                                        _ptr(dS_out), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dR), _ptr(dS), _ptr(dW),
+                                        _ptr(ws), ws.numel(), _stream()),
                "slim_attn_bwd")
     if want_dw:
         return dQ, dK, dV, dR, dS, dW
@@ -183,19 +197,20 @@ def decode_step(q, k, v, W=None, feat="favor", R=None, S=None, inplace=False):
 class _SlimAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, W, feat, num_chunks, window_chunks):
-        Y, _, _ = attn_fwd(q, k, v, W, feat, num_chunks, window_chunks=window_chunks)
-        # Only the inputs are kept for the backward, which recomputes every
-        # slice's forward (no per-slice state is stored).
-        ctx.save_for_backward(q, k, v, W if W is not None else torch.empty(0))
+        Y, _, _, rs = attn_fwd(q, k, v, W, feat, num_chunks, window_chunks=window_chunks, want_row_stats=True)
+        # Kept for the backward: the inputs, the output and 8 bytes per row of
+        # denominator statistics; the backward rebuilds every slice's entry state
+        # and recomputes the slice (no per-slice state is stored).
+        ctx.save_for_backward(q, k, v, W if W is not None else torch.empty(0), Y, rs)
         ctx.feat, ctx.num_chunks, ctx.window_chunks, ctx.has_w = feat, num_chunks, window_chunks, W is not None
         return Y
 
     @staticmethod
     def backward(ctx, dY):
-        q, k, v, W = ctx.saved_tensors
+        q, k, v, W, Y, rs = ctx.saved_tensors
         want_dw = ctx.has_w and ctx.needs_input_grad[3]
         g = attn_bwd(q, k, v, W if ctx.has_w else None, dY.contiguous(), ctx.feat, ctx.num_chunks,
-                     window_chunks=ctx.window_chunks, want_dw=want_dw)
+                     window_chunks=ctx.window_chunks, want_dw=want_dw, Y=Y, row_stats=rs)
         dW = g[5].to(W.dtype) if want_dw else None
         return g[0], g[1], g[2], dW, None, None, None
 

@@ -9,7 +9,8 @@
 //       state -> entry states (one window: forward prefix from the initial
 //       state; several: the window's start state recovered from the state
 //       after it by subtraction, update (19) at window granularity, then a
-//       forward prefix) -> stats (recompute forward, per-row statistics) -> dQ
+//       forward prefix) -> stats (recompute forward, per-row statistics; or, when
+//       the caller kept the forward's output and row statistics, rowstat) -> dQ
 //       -> gstate (the slice's gradient w.r.t. its entry state; folded into the
 //       dQ kernel where its registers allow) -> gradient suffix scan (update
 //       (20)) -> dK, dV.  With several windows, a forward
@@ -469,8 +470,8 @@ slim_status slim_featmap(const slim_desc *d, const void *X, const void *W, float
 }
 
 slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
-                          const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, void *ws,
-                          size_t ws_bytes, void *stream)
+                          const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, float *row_stats,
+                          void *ws, size_t ws_bytes, void *stream)
 {
     slim_status st = slim_validate(d, SLIM_PASS_FWD);
     if (st != SLIM_OK) return st;
@@ -480,7 +481,7 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
     if ((R_in == nullptr) != (S_in == nullptr)) return SLIM_ERR_NULL;
     if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(W, 16) || misaligned(Y, 16) ||
         misaligned(R_out, 16) || misaligned(S_out, 16) || misaligned(R_in, 16) || misaligned(S_in, 16) ||
-        misaligned(ws, 256))
+        misaligned(row_stats, 16) || misaligned(ws, 256))
         return SLIM_ERR_ALIGN;
     const Plan p = plan(d, SLIM_PASS_FWD);
     if (ws_bytes < p.total) return SLIM_ERR_WORKSPACE;
@@ -491,6 +492,7 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
     ChunkArgs a;
     memset(&a, 0, sizeof(a));
     a.Q = Q; a.K = K; a.V = V; a.W = W; a.out0 = Y;
+    a.rstat = row_stats;
     a.slots = (float *)(base + p.slots_off);
     a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
     double *cR = (double *)(base + p.cR_off), *cS = (double *)(base + p.cS_off);
@@ -509,9 +511,9 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
 }
 
 slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
-                          const void *dY, const void *R_in, const void *S_in, const void *dR_out,
-                          const void *dS_out, void *dQ, void *dK, void *dV, void *dR_in, void *dS_in, float *dW,
-                          void *ws, size_t ws_bytes, void *stream)
+                          const void *dY, const void *Y, const float *row_stats, const void *R_in, const void *S_in,
+                          const void *dR_out, const void *dS_out, void *dQ, void *dK, void *dV, void *dR_in,
+                          void *dS_in, float *dW, void *ws, size_t ws_bytes, void *stream)
 {
     const int pass = dW ? SLIM_PASS_BWD_DW : SLIM_PASS_BWD;
     slim_status st = slim_validate(d, pass);
@@ -522,6 +524,8 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
     if ((R_in == nullptr) != (S_in == nullptr)) return SLIM_ERR_NULL;
     if ((dR_out == nullptr) != (dS_out == nullptr)) return SLIM_ERR_NULL;
     if ((dR_in == nullptr) != (dS_in == nullptr)) return SLIM_ERR_NULL;
+    if ((Y == nullptr) != (row_stats == nullptr)) return SLIM_ERR_NULL;
+    if (misaligned(Y, 16) || misaligned(row_stats, 16)) return SLIM_ERR_ALIGN;
     if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(W, 16) || misaligned(dY, 16) ||
         misaligned(R_in, 16) || misaligned(S_in, 16) || misaligned(dR_out, 16) || misaligned(dS_out, 16) ||
         misaligned(dQ, 16) || misaligned(dK, 16) || misaligned(dV, 16) || misaligned(dR_in, 16) ||
@@ -537,6 +541,7 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
     ChunkArgs a;
     memset(&a, 0, sizeof(a));
     a.Q = Q; a.K = K; a.V = V; a.W = W; a.dY = dY;
+    a.Yin = Y; a.rstat = const_cast<float *>(row_stats);
     a.out0 = dQ; a.out1 = dK; a.out2 = dV;
     a.slots = (float *)(base + p.slots_off);
     a.gslots = (float *)(base + p.gslots_off);
@@ -581,8 +586,11 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
             if (wi != nwin - 1) SLIM_TIMED("state", s, kt->state(dim3(np, BH), s, a));
             scan(1, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
         }
-        SLIM_TIMED("stats", s, kt->stats(dim3(np, BH), s, a));
         const dim3 cg(np, BH);
+        if (Y)  // the forward's denominators and query offsets, and dden from its output
+            SLIM_TIMED("rowstat", s, kt->rowstat(cg, s, a));
+        else
+            SLIM_TIMED("stats", s, kt->stats(cg, s, a));
         if (kt->gstate) {
             if (dt)
                 SLIM_TIMED("bwdq_dw", s, dt->bwdq(cg, s, a));

@@ -57,6 +57,9 @@ struct ChunkArgs {
     float *gslots;             // [BH][P+1][(D+1)*M]  gradient-state slots
     float *stats;              // [BH][P][c][ROWSTAT] per-row (1/den, dden, query offset, -)
     void *pq, *pk;             // dW pass: dg(Q).g(Q), dg(K).g(K) [BH][P][c][M] (operand type)
+    float *rstat;              // [BH][L][2] per row (1/den, query offset): written by the forward,
+                               // read by the backward instead of recomputing them (or NULL)
+    const void *Yin;           // backward with the forward's row statistics: its output Y
     long long L;
     int c;   // chunk length
     int n0;  // first chunk of the window
@@ -394,7 +397,8 @@ template <class C> __device__ __forceinline__ float reduce_col(const float *red,
     return s;
 }
 // As reduce_rows, with each wave's partial rescaled by its factor (wave_scales) and
-// the rescaled sum of column D (denominator) handed over too: emit(t, e, s, den, ok).
+// the rescaled sum of column D (denominator) and the common query offset handed over
+// too: emit(t, e, s, den, moff, ok).
 template <class C, typename F>
 __device__ __forceinline__ void reduce_rows_scaled(const float *red, const float *qmax, int nv, F emit)
 {
@@ -410,7 +414,7 @@ __device__ __forceinline__ void reduce_rows_scaled(const float *red, const float
             s += *reinterpret_cast<const f4 *>(red + (w * C::TT + t) * C::LDR + e) * sc[w];
             den += red[(w * C::TT + t) * C::LDR + C::D] * sc[w];
         }
-        emit(t, e, s, den, t < nv);
+        emit(t, e, s, den, moff, t < nv);
     }
 }
 // Write a value-indexed block acc (rows e = eb*16 + 4g + j, cols t = tb*16 + i%16) of
@@ -845,6 +849,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(FwdSmem<C>), C::NW)) v
     const ChunkGeom G = chunk_geom<C>(a);
     const T *Q = (const T *)a.Q + G.hb, *K = (const T *)a.K + G.hb, *V = (const T *)a.V + G.hb;
     T *Y = (T *)a.out0 + G.hb;
+    // per-row statistics for the backward: 1/den at the common query offset, and that offset
+    float *rs = a.rstat ? a.rstat + ((size_t)G.bh * a.L + G.row0) * 2 : nullptr;
     Frag<T> wf[NFB][C::NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
     f4 rt[NFB][NEA];
@@ -859,8 +865,10 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(FwdSmem<C>), C::NW)) v
         f4 pq[NFB][NTB];
         fwd_tile<C>(sm, wf, rt, pq, [&](int eb, int tb, f4 acc) { put_red<C>(sm.red, eb, tb, acc); });
         __syncthreads();
-        reduce_rows_scaled<C>(sm.red, sm.qmax, nv, [&](int t, int e, f4 s, float den, bool ok) {
-            if (ok) store4<T>(Y + (size_t)(t0 + t) * C::D + e, s * (1.f / den));
+        reduce_rows_scaled<C>(sm.red, sm.qmax, nv, [&](int t, int e, f4 s, float den, float moff, bool ok) {
+            const float inv = 1.f / den;
+            if (ok) store4<T>(Y + (size_t)(t0 + t) * C::D + e, s * inv);
+            if (rs && ok && e == 0) *reinterpret_cast<float2 *>(rs + (size_t)(t0 + t) * 2) = make_float2(inv, moff);
         });
         state_update_T<C>(sm, rt);
         __syncthreads();

@@ -103,6 +103,40 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StatsSmem<C>), C::NW))
     }
 }
 
+// rowstat_kernel: the same per-row statistics from what the forward kept: its output Y
+// and, per row, 1/den at the common query offset and that offset (ChunkArgs::rstat).
+// dden = -(dY . Y) / den, since Y = Num / den; one row per VPR lanes (16-byte loads of
+// Y and dY), the dot product reduced by lane shuffles.  Grid as the chunk kernels.
+constexpr int ROWSTAT_NT = 256;
+template <class C> __global__ __launch_bounds__(ROWSTAT_NT) void rowstat_kernel(ChunkArgs a)
+{
+    typedef typename C::T T;
+    typedef typename Vec16<T>::type VT;
+    constexpr int EPV = Vec16<T>::N, VPR = C::D / EPV, RPP = ROWSTAT_NT / VPR;
+    static_assert(64 % VPR == 0, "a row's lanes stay in one wave");
+    const ChunkGeom G = chunk_geom<C>(a);
+    const T *dY = (const T *)a.dY + G.hb, *Y = (const T *)a.Yin + G.hb;
+    const float *rs = a.rstat + ((size_t)G.bh * a.L + G.row0) * 2;
+    float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
+    const int sub = threadIdx.x % VPR, rsl = threadIdx.x / VPR;
+    for (int t0 = 0; t0 < G.len; t0 += RPP) {
+        const int t = t0 + rsl;
+        float p = 0.f;
+        if (t < G.len) {
+            const VT y = gload<VT>(Y + (size_t)t * C::D + sub * EPV);
+            const VT g = gload<VT>(dY + (size_t)t * C::D + sub * EPV);
+#pragma unroll
+            for (int j = 0; j < EPV; ++j) p = fmaf((float)y[j], (float)g[j], p);
+        }
+#pragma unroll
+        for (int o = 1; o < VPR; o <<= 1) p += __shfl_xor(p, o, 64);
+        if (t < G.len && sub == 0) {
+            const float2 r = *reinterpret_cast<const float2 *>(rs + (size_t)t * 2);
+            *reinterpret_cast<f4 *>(st + (size_t)t * ROWSTAT) = f4{r.x, -p * r.x, r.y, 0.f};
+        }
+    }
+}
+
 // gstate_kernel: gslot[n+1] = (dG_n, dGs_n) = sum over chunk n of
 // (g(Q_t) dNum_t^T, dden_t g(Q_t)), the chunk's gradient w.r.t. its entry state
 // (stored like a state slot), from Q, dY and the per-row statistics.

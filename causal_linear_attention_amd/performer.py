@@ -45,16 +45,17 @@ class _StatefulAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, R_in, S_in, W, num_chunks, state_dtype):
-        Y, R, S = A.attn_fwd(q, k, v, W, "favor", num_chunks, R_in=R_in, S_in=S_in, state_dtype=state_dtype)
+        Y, R, S, rs = A.attn_fwd(q, k, v, W, "favor", num_chunks, R_in=R_in, S_in=S_in, state_dtype=state_dtype,
+                                 want_row_stats=True)
         ctx.save_for_backward(q, k, v, W, R_in if R_in is not None else torch.empty(0),
-                              S_in if S_in is not None else torch.empty(0))
+                              S_in if S_in is not None else torch.empty(0), Y, rs)
         ctx.has_state = R_in is not None
         ctx.num_chunks, ctx.state_dtype = num_chunks, R.dtype
         return Y, R, S
 
     @staticmethod
     def backward(ctx, dY, dR, dS):
-        q, k, v, W, R_in, S_in = ctx.saved_tensors
+        q, k, v, W, R_in, S_in, Y, rs = ctx.saved_tensors
         if dY is None:
             dY = torch.zeros_like(q)
         sd = ctx.state_dtype
@@ -65,7 +66,8 @@ class _StatefulAttention(torch.autograd.Function):
         st = (R_in, S_in) if ctx.has_state else (None, None)
         want_dw = ctx.needs_input_grad[5]
         g = A.attn_bwd(q, k, v, W, dY.contiguous(), "favor", ctx.num_chunks, R_in=st[0], S_in=st[1], dR_out=dR,
-                       dS_out=dS, want_state_grad=ctx.has_state, state_dtype=sd, want_dw=want_dw)
+                       dS_out=dS, want_state_grad=ctx.has_state, state_dtype=sd, want_dw=want_dw, Y=Y,
+                       row_stats=rs)
         dW = g[5].to(W.dtype) if want_dw else None
         return g[0], g[1], g[2], g[3], g[4], dW, None, None
 

@@ -164,8 +164,10 @@ def kernel_bytes(w: Workload) -> dict:
     return {
         "state": 2 * row + slot,                    # K, V -> chunk state
         "scan_prefix": 2 * slot, "scan_reverse": 2 * slot, "scan_grad": 2 * slot,  # slots in place
-        "fwd": 3 * row + slot + row,                # Q, K, V, entry state -> Y
+        # Q, K, V, entry state -> Y, and (a step with a backward) 8 bytes of row statistics
+        "fwd": 3 * row + slot + row + (8 if w.backward else 0),
         "stats": 4 * row + slot + st,               # Q, K, V, dY, entry state -> row statistics
+        "rowstat": 2 * row + 8 + st,                # Y, dY, the forward's row statistics -> row statistics
         "bwdq": 4 * row + slot + st + row,          # Q, K, V, dY, entry state, statistics -> dQ
         "gstate": 2 * row + st + slot,              # Q, dY, statistics -> gradient slot
         "bwdq_gstate": 4 * row + 2 * slot + st + row,  # Q, K, V, dY, entry state, statistics -> dQ, gradient slot

@@ -125,11 +125,18 @@ slim_status slim_featmap(const slim_desc *desc, const void *X, const void *W, fl
  * In : Q, K, V, W (NULL for elu+1); R_in, S_in = initial state (both NULL =
  *      zero, or both given).
  * Out: Y; R_out, S_out = final state R_L, S_L (required; R_out/S_out may not
- *      alias R_in/S_in).
+ *      alias R_in/S_in);
+ *      row_stats = per-row statistics for the backward, [B][H][L][2] fp32, or
+ *      NULL = not wanted: for row l, 1/den'_l and o_l, where o_l is the query
+ *      offset in the base-2 exponent domain (FAVOR+: -log2(e) max_m w_m.Q_l;
+ *      elu+1: 0) and den'_l = S_l . g'(Q_l) with the query features taken as
+ *      g'(Q_l)_m = exp(w_m.Q_l) 2^o_l (FAVOR+; elu+1: g itself), i.e.
+ *      den_l = den'_l exp(-o_l ln 2 - |Q_l|^2/2) / sqrt(M).  8 bytes per row,
+ *      the analogue of the log-sum-exp kept by softmax attention.
  * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_FWD). */
 slim_status slim_attn_fwd(const slim_desc *desc, const void *Q, const void *K, const void *V, const void *W,
-                          const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, void *ws,
-                          size_t ws_bytes, void *stream);
+                          const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, float *row_stats,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /* Backward of the loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out> of the
  * forward above (Subsection 3.3: a reverse walk over the slices that recomputes
@@ -143,6 +150,10 @@ slim_status slim_attn_fwd(const slim_desc *desc, const void *Q, const void *K, c
  * carry its rounding into every one of them.
  * In : Q, K, V, W as in the forward; dY; R_in, S_in = the forward's initial
  *      state (both NULL = zero, or both given);
+ *      Y, row_stats = the output and row statistics of a forward call on the
+ *      same inputs (any slice count), or both NULL.  Given, the backward takes
+ *      every row's denominator from them and dden_l = -(dY_l . Y_l) / den_l
+ *      from Y, instead of recomputing each slice's forward for them;
  *      dR_out, dS_out = incoming gradient of the final state (both NULL = zero).
  * Out: dQ, dK, dV; dR_in, dS_in = gradient w.r.t. the initial state (both NULL
  *      = not wanted, or both given);
@@ -157,9 +168,9 @@ slim_status slim_attn_fwd(const slim_desc *desc, const void *Q, const void *K, c
  *      adds two [B*H][window rows][M] buffers of the io dtype and the partial
  *      sums of dW). */
 slim_status slim_attn_bwd(const slim_desc *desc, const void *Q, const void *K, const void *V, const void *W,
-                          const void *dY, const void *R_in, const void *S_in, const void *dR_out,
-                          const void *dS_out, void *dQ, void *dK, void *dV, void *dR_in, void *dS_in, float *dW,
-                          void *ws, size_t ws_bytes, void *stream);
+                          const void *dY, const void *Y, const float *row_stats, const void *R_in, const void *S_in,
+                          const void *dR_out, const void *dS_out, void *dQ, void *dK, void *dV, void *dR_in,
+                          void *dS_in, float *dW, void *ws, size_t ws_bytes, void *stream);
 
 /* Recurrent decode step: the iterative prefix-sum evaluation of Subsection
  * 2.1 (eq. (3)-(4)) advanced by one position.  For every b, h and the one new
@@ -190,7 +201,8 @@ const char *slim_status_string(slim_status s);
  * slim_prof_enable(0) stops.  slim_prof_count() and slim_prof_entry() first
  * wait for the recorded events to complete (they synchronise with those
  * events), then report per kernel name ("state", "scan_prefix", "fwd",
- * "scan_window", "scan_sum", "stats", "bwdq", "gstate", "bwdq_gstate" (the dQ
+ * "scan_window", "scan_sum", "stats", "rowstat" (stats from the forward's row
+ * statistics), "bwdq", "gstate", "bwdq_gstate" (the dQ
  * kernel with the gradient state folded in, for shapes where it fits),
  * "scan_grad", "bwdkv", "featmap", "decode"; with dW: "bwdq_dw" or
  * "bwdq_gstate_dw", "bwdkv_dw", "dw" (the row contraction), "dw_sum" (the sum

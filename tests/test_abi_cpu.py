@@ -73,25 +73,48 @@ def test_validate_null(lib):
     assert lib.slim_validate(None, 1) == 1
 
 
+FWD_ARGS = ("Q", "K", "V", "W", "R_in", "S_in", "Y", "R_out", "S_out", "row_stats", "ws", "ws_bytes", "stream")
+BWD_ARGS = ("Q", "K", "V", "W", "dY", "Y", "row_stats", "R_in", "S_in", "dR_out", "dS_out", "dQ", "dK", "dV",
+            "dR_in", "dS_in", "dW", "ws", "ws_bytes", "stream")
+P = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+
+
+def fwd(lib, d, **kw):
+    """slim_attn_fwd with the named pointers; Q, K, V, W, Y, R_out, S_out, ws default to
+    a dummy address, the rest to NULL / 0."""
+    base = dict(Q=P, K=P, V=P, W=P, Y=P, R_out=P, S_out=P, ws=P, ws_bytes=1 << 40)
+    base.update(kw)
+    return lib.slim_attn_fwd(ctypes.byref(d), *[base.get(n) for n in FWD_ARGS])
+
+
+def bwd(lib, d, **kw):
+    base = dict(Q=P, K=P, V=P, W=P, dY=P, dQ=P, dK=P, dV=P, ws=P, ws_bytes=1 << 40)
+    base.update(kw)
+    return lib.slim_attn_bwd(ctypes.byref(d), *[base.get(n) for n in BWD_ARGS])
+
+
 def test_entry_points_reject_before_any_launch(lib):
     d = d_()
     # NULL inputs / workspace: rejected on the host, nothing enqueued
-    assert lib.slim_attn_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, 0,
-                           None) == 1
-    p = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
-    assert lib.slim_attn_fwd(ctypes.byref(d), p, p, p, p, None, None, p, p, p, p, 0, None) == 5
+    nulls = {n: None for n in FWD_ARGS}
+    nulls["ws_bytes"] = 0
+    assert fwd(lib, d, **nulls) == 1
+    assert fwd(lib, d, ws_bytes=0) == 5
     bad = ctypes.c_void_p((1 << 20) + 4)
-    assert lib.slim_attn_fwd(ctypes.byref(d), bad, p, p, p, None, None, p, p, p, p, 1 << 40, None) == 6
-    assert lib.slim_attn_bwd(ctypes.byref(d_(num_chunks=0)), p, p, p, p, p, p, p, None, None, p, p, p, None, None,
-                           None, p, 1 << 40, None) == 2
+    assert fwd(lib, d, Q=bad) == 6
+    assert fwd(lib, d, row_stats=bad) == 6
+    assert bwd(lib, d_(num_chunks=0)) == 2
     # only one of the paired initial-state pointers
-    assert lib.slim_attn_fwd(ctypes.byref(d), p, p, p, p, p, None, p, p, p, p, 1 << 40, None) == 1
-    assert lib.slim_attn_bwd(ctypes.byref(d), p, p, p, p, p, p, None, None, None, p, p, p, None, None,
-                           None, p, 1 << 40, None) == 1
+    assert fwd(lib, d, R_in=P) == 1
+    assert bwd(lib, d, R_in=P) == 1
+    # only one of the forward's output and row statistics
+    assert bwd(lib, d, Y=P) == 1
+    assert bwd(lib, d, row_stats=P) == 1
+    assert bwd(lib, d, Y=P, row_stats=bad) == 6
     # elu+1 takes no W
     de = d_(feat=_lib.SLIM_FEAT_ELU1, M=64)
-    assert lib.slim_attn_fwd(ctypes.byref(de), p, p, p, p, None, None, p, p, p, p, 1 << 40, None) == 2
-    assert lib.slim_featmap(ctypes.byref(de), p, None, p, p, None) == 2
+    assert fwd(lib, de) == 2
+    assert lib.slim_featmap(ctypes.byref(de), P, None, P, P, None) == 2
 
 
 def test_dw_pass_validation(lib):
@@ -113,20 +136,16 @@ def test_dw_pass_validation(lib):
 
 
 def test_dw_rejects_before_any_launch(lib):
-    p = ctypes.c_void_p(1 << 20)
     dw = ctypes.c_void_p(1 << 21)
     d = d_()
     # workspace sized for the plain backward is too small once dW is asked for
     wsb = lib.slim_workspace_bytes(ctypes.byref(d), _lib.SLIM_PASS_BWD)
-    assert lib.slim_attn_bwd(ctypes.byref(d), p, p, p, p, p, None, None, None, None, p, p, p, None, None,
-                           dw, p, wsb, None) == 5
+    assert bwd(lib, d, dW=dw, ws_bytes=wsb) == 5
     # misaligned dW
-    assert lib.slim_attn_bwd(ctypes.byref(d), p, p, p, p, p, None, None, None, None, p, p, p, None, None,
-                           ctypes.c_void_p((1 << 21) + 4), p, 1 << 40, None) == 6
+    assert bwd(lib, d, dW=ctypes.c_void_p((1 << 21) + 4)) == 6
     # elu+1 has no projection
     de = d_(feat=_lib.SLIM_FEAT_ELU1, M=64)
-    assert lib.slim_attn_bwd(ctypes.byref(de), p, p, p, None, p, None, None, None, None, p, p, p, None, None,
-                           dw, p, 1 << 40, None) == 4
+    assert bwd(lib, de, W=None, dW=dw) == 4
 
 
 def ws(lib, pass_, **kw):

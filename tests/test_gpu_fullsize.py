@@ -51,8 +51,11 @@ def test_fullsize_fwd_bwd_sampled_heads(name):
     w = WORKLOADS[name]
     print("fullsize", name, flush=True)
     x = make(w)
-    Y, R, S = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], w.feat, w.chunks)
-    dQ, dK, dV, _, _ = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], w.feat, w.chunks)
+    # as the bench step runs it: the forward keeps its row statistics for the backward
+    Y, R, S, rs = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], w.feat, w.chunks, want_row_stats=True)
+    dQ, dK, dV, _, _ = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], w.feat, w.chunks, Y=Y, row_stats=rs)
+    # and the backward that recomputes them
+    dQ0, dK0, dV0, _, _ = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], w.feat, w.chunks)
     torch.cuda.synchronize()
     sel = [(0, 0), (w.B - 1, w.H - 1)]
     Wh = None if x["W"] is None else host64(x["W"])
@@ -62,7 +65,8 @@ def test_fullsize_fwd_bwd_sampled_heads(name):
     tol = TOL[DT[w.dtype]]
     for i, (b, h) in enumerate(sel):
         for nm, got, ref in (("Y", Y, Yo), ("R", R, Ro), ("S", S, So), ("dQ", dQ, gq), ("dK", dK, gk),
-                             ("dV", dV, gv)):
+                             ("dV", dV, gv), ("dQ recomputed statistics", dQ0, gq),
+                             ("dK recomputed statistics", dK0, gk), ("dV recomputed statistics", dV0, gv)):
             e = relerr(host64(got[b, h]), ref[0, i])
             assert e < tol, (name, (b, h), nm, e)
     for t in (Y, dQ, dK, dV):
@@ -75,8 +79,8 @@ def test_fullsize_long_context_causal_prefix_and_final_state():
     print("fullsize", w.name, "L'", Lp, flush=True)
     x = make(w)
     x["dy"][:, :, Lp:] = 0
-    Y, R, S = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], w.feat, w.chunks)
-    dQ, dK, dV, _, _ = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], w.feat, w.chunks)
+    Y, R, S, rs = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], w.feat, w.chunks, want_row_stats=True)
+    dQ, dK, dV, _, _ = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], w.feat, w.chunks, Y=Y, row_stats=rs)
     torch.cuda.synchronize()
     # rows past L' receive no gradient at all
     for nm, t in (("dQ", dQ), ("dK", dK), ("dV", dV)):

@@ -246,3 +246,71 @@ def test_autograd_function():
     g = oracle.attn_bwd(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(x["W"]), host64(x["dy"]), "favor")
     for got, ref in ((q.grad, g[0]), (k.grad, g[1]), (v.grad, g[2])):
         assert relerr_heads(host64(got), ref) < 1e-4
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_forward_row_stats_give_the_denominators(case):
+    # row_stats = (1/den', o) with den = den' 2^-o exp(-|q|^2/2) / sqrt(M) (FAVOR+), den = den' (elu+1)
+    B, H, L, d, M, C, dt, feat = case
+    if not _supported(d, M, dt, feat):
+        pytest.skip("shape not compiled")
+    dtype = DT[dt]
+    x = inputs(B, H, L, d, M, dtype, feat, seed=15, dy=False)
+    Y, R, S, rs = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], feat, C, want_row_stats=True)
+    Y0, _, _ = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], feat, C)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y0)  # asking for the statistics changes nothing else
+    q = host64(x["q"])
+    _, den, _, _ = oracle.attn_fwd(q, host64(x["k"]), host64(x["v"]), None if x["W"] is None else host64(x["W"]),
+                                   feat)
+    r = host64(rs)
+    got = 1.0 / r[..., 0]
+    if feat == "favor":
+        got = got * np.exp(-r[..., 1] * np.log(2.0) - 0.5 * np.sum(q * q, axis=-1)) / np.sqrt(M)
+    else:
+        assert np.all(r[..., 1] == 0)
+    assert relerr_heads(got, den) < (1e-5 if dt == "f32" else 1e-2)
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_backward_from_forward_row_stats_matches_oracle(case):
+    # the backward that takes the forward's Y and row statistics instead of recomputing them
+    B, H, L, d, M, C, dt, feat = case
+    if not _supported(d, M, dt, feat):
+        pytest.skip("shape not compiled")
+    dtype = DT[dt]
+    x = inputs(B, H, L, d, M, dtype, feat, seed=12)
+    print("bwd from row stats", _id(case), flush=True)
+    Y, R, S, rs = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], feat, C, want_row_stats=True)
+    g = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], feat, C, Y=Y, row_stats=rs)
+    g0 = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], feat, C)
+    torch.cuda.synchronize()
+    Wh = None if x["W"] is None else host64(x["W"])
+    o = oracle.attn_bwd(host64(x["q"]), host64(x["k"]), host64(x["v"]), Wh, host64(x["dy"]), feat)
+    tol = TOL[dtype]
+    for i, name in enumerate(("dQ", "dK", "dV")):
+        e = relerr_heads(host64(g[i]), o[i])
+        e0 = relerr_heads(host64(g[i]), host64(g0[i]))
+        print(name, "vs oracle %.2e, vs recomputed statistics %.2e" % (e, e0))
+        assert e < tol, (name, e)
+
+
+def test_row_stats_across_windows_and_slice_counts():
+    # statistics from a forward with another slice count and window, a nonzero initial
+    # state and incoming state gradients
+    B, H, L, d, M = 1, 2, 300, 64, 128
+    x = inputs(B, H, L, d, M, torch.float32, "favor", seed=16)
+    rng = np.random.default_rng(17)
+    R0 = torch.from_numpy(rng.standard_normal((B, H, d, M)).astype(np.float32) * 0.2).cuda()
+    S0 = torch.from_numpy(np.abs(rng.standard_normal((B, H, M))).astype(np.float32) + 0.5).cuda()
+    dRo = torch.from_numpy(rng.standard_normal((B, H, d, M)).astype(np.float32) * 1e-2).cuda()
+    dSo = torch.from_numpy(rng.standard_normal((B, H, M)).astype(np.float32) * 1e-2).cuda()
+    Y, _, _, rs = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], "favor", 1, R_in=R0, S_in=S0, want_row_stats=True)
+    g = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], "favor", 7, R_in=R0, S_in=S0, dR_out=dRo, dS_out=dSo,
+                   want_state_grad=True, window_chunks=2, Y=Y, row_stats=rs, want_dw=True)
+    torch.cuda.synchronize()
+    o = oracle.attn_bwd(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(x["W"]), host64(x["dy"]), "favor",
+                        R0=host64(R0), S0=host64(S0), dRout=host64(dRo), dSout=host64(dSo), want_dw=True)
+    for i, name in enumerate(("dQ", "dK", "dV", "dR0", "dS0")):
+        assert relerr_heads(host64(g[i]), o[i]) < 1e-4, name
+    assert relerr(host64(g[5]), o[5]) < 1e-4
