@@ -592,6 +592,12 @@ def main():
         step(keep_stats=False)
     torch.cuda.synchronize()
     elapsed_recompute = time.perf_counter() - t1
+    # the forward alone (no row statistics kept), for the forward-only figure
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        A.attn_fwd(q, k, v, W, w.feat, w.chunks)
+    torch.cuda.synchronize()
+    elapsed_fwd = time.perf_counter() - t2
     # per-kernel times: the same number of steps again, each kernel bracketed by hipEvents
     _lib.prof_enable(True)
     for _ in range(args.steps):
@@ -613,6 +619,7 @@ def main():
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "ms_per_step_stats_recomputed": round(1e3 * elapsed_recompute / args.steps, 4),
+        "ms_forward_only": round(1e3 * elapsed_fwd / args.steps, 4),
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "M": w.M, "feat": w.feat,
                    "W": w.w_kind, "chunks": w.chunks, "chunk_len": w.chunk_len, "tile": tile,
