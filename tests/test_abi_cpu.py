@@ -64,6 +64,7 @@ def test_validate_ok(lib):
     (dict(window_chunks=-1), 2), (dict(L=1 << 31), 2), (dict(dtype=7), 3), (dict(feat=9), 3),
     (dict(feat=_lib.SLIM_FEAT_ELU1), 2),            # elu+1 needs M == d
     (dict(d=48), 4), (dict(M=96), 4), (dict(M=512), 4), (dict(d=256, M=256), 4),
+    (dict(B=65536, H=1), 4), (dict(B=256, H=257), 4),  # more heads than one launch's grid takes
 ])
 def test_validate_errors(lib, kw, code):
     assert validate(lib, **kw) == code

@@ -314,3 +314,25 @@ def test_row_stats_across_windows_and_slice_counts():
     for i, name in enumerate(("dQ", "dK", "dV", "dR0", "dS0")):
         assert relerr_heads(host64(g[i]), o[i]) < 1e-4, name
     assert relerr(host64(g[5]), o[5]) < 1e-4
+
+
+def test_most_heads_one_launch_allows():
+    # B*H = 65535 (the largest head count the chunk kernels' grid takes): forward,
+    # backward from the kept row statistics and dW; sampled heads against the oracle,
+    # dW (a sum over every head) against the oracle over all heads
+    B, H, L, d, M, C = 65535, 1, 40, 16, 16, 2
+    print("most heads", B * H, flush=True)
+    x = inputs(B, H, L, d, M, torch.bfloat16, "favor", seed=19)
+    Y, R, S, rs = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], "favor", C, want_row_stats=True)
+    g = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], "favor", C, Y=Y, row_stats=rs, want_dw=True)
+    torch.cuda.synchronize()
+    h = {n: host64(x[n]) for n in ("q", "k", "v", "dy")}
+    Wh = host64(x["W"])
+    o = oracle.attn_bwd(h["q"], h["k"], h["v"], Wh, h["dy"], "favor", form="prefix", want_dw=True)
+    idx = np.concatenate([[0, B - 1], np.random.default_rng(0).choice(B, 62, replace=False)])
+    Yo = oracle.attn_fwd(h["q"][idx], h["k"][idx], h["v"][idx], Wh, "favor")[0]
+    tol = TOL[torch.bfloat16]
+    assert relerr_heads(host64(Y)[idx], Yo) < tol
+    for i, name in enumerate(("dQ", "dK", "dV")):
+        assert relerr_heads(host64(g[i])[idx], o[i][idx]) < tol, name
+    assert relerr(host64(g[5]), o[5]) < tol
