@@ -336,3 +336,39 @@ def test_most_heads_one_launch_allows():
     for i, name in enumerate(("dQ", "dK", "dV")):
         assert relerr_heads(host64(g[i])[idx], o[i][idx]) < tol, name
     assert relerr(host64(g[5]), o[5]) < tol
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("feat", ["favor", "elu1"])
+def test_degenerate_closed_forms(dt, feat):
+    # closed forms of eq. (2), not the oracle: a one-row sequence gives Y = V, dQ = dK = 0,
+    # dV = dY; values constant along the sequence give Y = V and dQ = dK = 0, whatever
+    # the slicing, with either backward ("0" up to rounding: against the size of dV)
+    dtype = DT[dt]
+    d = 64
+    M = 128 if feat == "favor" else d
+    tol = 1e-5 if dt == "f32" else TOL[dtype]
+    zero = 5e-4 if dt == "f32" else 5e-2  # "vanishes": against the gradients' own size
+    x = inputs(2, 3, 1, d, M, dtype, feat, seed=20)
+    Y, _, _, rs = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], feat, 1, want_row_stats=True)
+    for kept in (True, False):
+        g = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], feat, 1, Y=Y if kept else None,
+                       row_stats=rs if kept else None)
+        torch.cuda.synchronize()
+        assert relerr_heads(host64(Y), host64(x["v"])) < tol
+        scale = float(x["dy"].abs().max())
+        assert float(g[0].abs().max()) < zero * scale and float(g[1].abs().max()) < zero * scale, kept
+        assert relerr_heads(host64(g[2]), host64(x["dy"])) < tol, kept
+    L = 200
+    x = inputs(1, 2, L, d, M, dtype, feat, seed=21)
+    v = x["v"][:, :, :1].expand(-1, -1, L, -1).contiguous()
+    for C, P in ((1, 0), (7, 0), (200, 3)):
+        Y, _, _, rs = A.attn_fwd(x["q"], x["k"], v, x["W"], feat, C, window_chunks=P, want_row_stats=True)
+        for kept in (True, False):
+            g = A.attn_bwd(x["q"], x["k"], v, x["W"], x["dy"], feat, C, window_chunks=P, Y=Y if kept else None,
+                           row_stats=rs if kept else None)
+            torch.cuda.synchronize()
+            assert relerr_heads(host64(Y), host64(v)) < tol, (C, P)
+            # dQ, dK vanish up to rounding: compare with the size of dV's contributions
+            scale = float(g[2].abs().max())
+            assert float(g[0].abs().max()) < zero * scale and float(g[1].abs().max()) < zero * scale, (C, P, kept)
