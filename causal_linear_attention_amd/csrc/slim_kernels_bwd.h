@@ -253,7 +253,7 @@ template <class C> struct BwdRegs {
 
 // bwdq_kernel: dQ of one chunk.  Tiles in forward order, carrying the entry state
 // [R; S] (rows e, cols m) from slot[n].  Where its registers allow (bf16 with d <= 32,
-// or d = 64 with M >= 128; fp32 with d <= 32), it also accumulates the gstate_kernel's
+// or d = 64 with M >= 64; fp32 with d <= 32), it also accumulates the gstate_kernel's
 // result from the g(Q) it already has, and the gstate_kernel is not launched.
 // dQ's W^T product: with bf16 inputs, d <= 64 and a whole number of value blocks per
 // wave count, the waves share dg(Q).g(Q) through LDS and each finishes whole output
@@ -290,7 +290,7 @@ template <class C> __device__ __forceinline__ typename C::T *pw_rows(void *buf, 
 
 template <class C> constexpr bool bwdq_fuses_gstate()
 {
-    return C::D <= 32 || (sizeof(typename C::T) == 2 && C::D <= 64 && C::M >= 128);
+    return C::D <= 32 || (sizeof(typename C::T) == 2 && C::D <= 64 && C::M >= 64);
 }
 template <class C> struct BwdqSmem {
     typedef typename C::T T;
