@@ -212,9 +212,12 @@ def cpu_baseline(w, synth, heads):
             "seconds": dt}
 
 
+MEM_SWEEP_WINDOW = 512
+
+
 def mem_sweep(torch, A, synth, w):
     """Peak HBM of one fwd+bwd step for L = 2^16 .. 2^20 at the shape of workload w
-    (B, H, d, M, slice length 512, automatic window).  Inputs (Q, K, V, dY, W) are
+    (B, H, d, M, slice length 512, a fixed window of MEM_SWEEP_WINDOW slices).  Inputs (Q, K, V, dY, W) are
     resident before the step; the step allocates the outputs Y, dQ, dK, dV (4 L d
     bf16 per head), the workspaces and the final state.  'beyond_io' = peak step
     allocation minus those outputs: what the sliced method itself needs."""
@@ -233,11 +236,12 @@ def mem_sweep(torch, A, synth, w):
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
-        Y, R, S = A.attn_fwd(q, k, v, W, w.feat, chunks)
-        g = A.attn_bwd(q, k, v, W, dy, w.feat, chunks)
+        P = MEM_SWEEP_WINDOW
+        Y, R, S = A.attn_fwd(q, k, v, W, w.feat, chunks, window_chunks=P)
+        g = A.attn_bwd(q, k, v, W, dy, w.feat, chunks, window_chunks=P)
         torch.cuda.synchronize()
         peak = torch.cuda.max_memory_allocated() - base
-        dsc = A.make_desc(q, w.M, w.feat, chunks)
+        dsc = A.make_desc(q, w.M, w.feat, chunks, P)
         outs = 4 * q.numel() * 2
         rows.append({"L": L, "chunks": chunks, "window_chunks": int(_lib.lib().slim_window_chunks(ctypes.byref(dsc))),
                      "inputs_bytes": 4 * q.numel() * 2, "step_peak_bytes": peak, "outputs_bytes": outs,

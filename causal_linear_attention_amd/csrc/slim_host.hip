@@ -281,12 +281,18 @@ static void dw_split(long long BH, long long wl, int *S, int *rows_per)
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static long long resolve_window(const slim_desc *d, long long nchunks)
+// Automatic window: enough slices for about 4096 workgroups per launch; all of them
+// when the backward's per-slice buffers (state and gradient slots, row statistics) for
+// the whole sequence fit in 1 GiB, so that it runs as one window (no extra sweep over
+// the slices, no recompute of their states per window).  Bounded for any L.
+static long long resolve_window(const slim_desc *d, long long nchunks, long long c)
 {
     long long P = d->window_chunks;
     if (P <= 0) {
         const long long BH = d->B * d->H;
-        P = (4096 + BH - 1) / BH;  // about 4096 workgroups per launch
+        const long long per_slice = BH * ((d->d + 1) * d->M * 4 * 2 + c * ROWSTAT * 4);
+        P = (4096 + BH - 1) / BH;
+        if (nchunks > P && nchunks * per_slice <= (1LL << 30)) P = nchunks;
     }
     if (P > nchunks) P = nchunks;
     if (P < 1) P = 1;
@@ -301,7 +307,7 @@ static Plan plan(const slim_desc *d, int pass)
     p.BH = d->B * d->H;
     p.c = (d->L + d->num_chunks - 1) / d->num_chunks;
     p.nchunks = (d->L + p.c - 1) / p.c;
-    p.P = resolve_window(d, p.nchunks);
+    p.P = resolve_window(d, p.nchunks, p.c);
     p.SZ = (d->d + 1) * d->M;
     const size_t slots = (size_t)p.BH * (p.P + 1) * p.SZ * 4;
     size_t off = 0;

@@ -85,7 +85,10 @@ typedef struct slim_desc {
     int64_t B, H, L;       /* batch, heads, sequence length */
     int64_t d, M;          /* head dim, number of features */
     int64_t num_chunks;    /* N slices; slice length c = ceil(L / N) */
-    int64_t window_chunks; /* slices whose states are held at once; 0 = auto */
+    int64_t window_chunks; /* slices whose states are held at once; 0 = auto: enough for
+                              about 4096 workgroups per launch, or all of them when the
+                              backward's per-slice buffers for the whole sequence fit in
+                              1 GiB */
     int32_t dtype;         /* slim_dtype of Q, K, V, W, Y, dY, dQ, dK, dV: SLIM_F32 or SLIM_BF16 */
     int32_t feat;          /* slim_feat */
     int32_t state_dtype;   /* element type of the states and their gradients (R_in, S_in,

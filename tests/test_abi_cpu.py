@@ -174,8 +174,18 @@ def test_workspace_does_not_grow_with_L_at_fixed_slice_and_window(lib):
 def test_auto_window(lib):
     d = d_(B=4, H=16, L=16384, d=64, M=256, num_chunks=32)
     assert lib.slim_window_chunks(ctypes.byref(d)) == 32
+    # the 1M-token workload fits one window within the 1 GiB budget of per-slice buffers
     d = d_(B=1, H=8, L=1 << 20, d=64, M=64, num_chunks=2048)
+    assert lib.slim_window_chunks(ctypes.byref(d)) == 2048
+    # a sequence whose per-slice buffers (slot, gradient slot, row statistics: 41 KB per
+    # slice and head here) exceed 1 GiB gets windows of about 4096 workgroups again
+    per = 8 * (65 * 64 * 4 * 2 + 512 * 16)
+    assert 2048 * per <= 1 << 30 < 4096 * per
+    d = d_(B=1, H=8, L=1 << 22, d=64, M=64, num_chunks=1 << 13)
     assert lib.slim_window_chunks(ctypes.byref(d)) == 512
+    # many heads: about 4096 workgroups per launch when that is more
+    d = d_(B=64, H=64, L=4096, d=64, M=256, num_chunks=64)
+    assert lib.slim_window_chunks(ctypes.byref(d)) == 1
 
 
 def test_tile_rows(lib):
