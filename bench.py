@@ -21,6 +21,7 @@ CPU oracle timed on a bounded sample of the same workload.
   python bench.py --chunk-sweep     # time, peak HBM and gradient discrepancy vs slice length (one JSON line)
   python bench.py --algorithm1      # the same for the page's Algorithm 1 on a multi-layer Performer
   python bench.py --dw              # the step with the backward also computing dW (FAVOR+ projection)
+  python bench.py --featmap         # the standalone feature map g(Q) with row offsets (one JSON line)
 
 roofline.traffic: HBM bytes per launch of the dominant kernel, FETCH_SIZE and
 WRITE_SIZE scaled by what the same counters read for a plain copy of known
@@ -72,6 +73,8 @@ def parse():
                     help="time the recurrent decode step (one token per sequence per step) instead")
     ap.add_argument("--dw", action="store_true",
                     help="the backward of every step also computes dW, the gradient of the FAVOR+ projection")
+    ap.add_argument("--featmap", action="store_true",
+                    help="time the standalone feature map (slim_featmap with per-row offsets) on the workload's Q")
     ap.add_argument("--pmc-summary", default=None, metavar="DIR",
                     help="DIR holds rocprofv3 counter runs F, W (FETCH_SIZE, WRITE_SIZE of --profile-run; "
                          "DF, DW with --decode; DWF, DWW with --dw) and CF, CW (the same of --copy-calib); prints "
@@ -251,6 +254,49 @@ def mem_sweep(torch, A, synth, w):
         del q, k, v, dy, W, Y, R, S, g
         torch.cuda.empty_cache()
     return {"mem_sweep": w.name, "B": w.B, "H": w.H, "d": w.d, "M": w.M, "chunk_len": 512, "rows": rows}
+
+
+def featmap_bench(torch, A, _lib, synth, w, steps, warmup):
+    """slim_featmap on the workload's Q ([B, H, L, d] io dtype -> [B, H, L, M] fp32, with
+    the per-row offsets): an HBM stream (read the rows, write M fp32 per row)."""
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q = synth.device_normal(w.seed, synth.TID_Q, (w.B, w.H, w.L, w.d), w.qkv_scale).to(dt)
+    W = torch.from_numpy(synth.projection(w.seed, w.M, w.d, w.w_kind)).to(dt).cuda() if w.feat == "favor" else None
+    favor = w.feat == "favor"
+    for _ in range(warmup):
+        out = A.featmap(q, W, w.feat, row_offset=favor)
+    del out
+    torch.cuda.synchronize()
+    _lib.prof_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        out = A.featmap(q, W, w.feat, row_offset=favor)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    _lib.prof_enable(False)
+    prof = _lib.prof_read()
+    ms, n = prof["featmap"]
+    rows = w.B * w.H * w.L
+    isz = 2 if w.dtype == "bf16" else 4
+    by = rows * (w.d * isz + w.M * 4 + (4 if favor else 0))  # X in, phi out, row offsets out
+    fl = rows * 2 * w.d * w.M if favor else 0
+    kern_s = ms / n * 1e-3
+    # a plain device copy of the same number of bytes, read + written, for scale
+    x = torch.empty(by // 8, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * x.numel() * 4 / ((time.perf_counter() - t1) / steps) / 1e9
+    return {"featmap": w.name, "rows": rows, "d": w.d, "M": w.M, "dtype": w.dtype, "row_offsets": favor,
+            "ms_per_call": round(1e3 * el, 4), "kernel_ms": round(ms / n, 5), "bytes_per_call": by,
+            "gbs": round(by / kern_s / 1e9, 1), "tflops": round(fl / kern_s / 1e12, 2),
+            "roofline": {"bound": "hbm", "achieved": round(by / kern_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(by / kern_s / 1e9 / PEAK_HBM_GBS, 4)},
+            "plain_copy_gbs": round(copy_gbs, 1)}
 
 
 DECODE_METRIC = "causal linear-attn decode tokens/s (one new token per sequence per step, state in place)"
@@ -535,6 +581,11 @@ def main():
     if args.chunk_sweep:
         print(json.dumps(chunk_sweep(torch, A, synth, WORKLOADS[args.workload or HEADLINE], args.sweep_dtype,
                                      args.sweep_window, args.sweep_cmax)))
+        return
+
+    if args.featmap:
+        print(json.dumps(featmap_bench(torch, A, _lib, synth, WORKLOADS[args.workload or HEADLINE], args.steps,
+                                       args.warmup)))
         return
 
     if args.mem_sweep:

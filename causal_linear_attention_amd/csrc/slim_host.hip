@@ -468,7 +468,7 @@ slim_status slim_featmap(const slim_desc *d, const void *X, const void *W, float
         return SLIM_ERR_ALIGN;
     const KernelTable *kt = find(d);
     const long long rows = d->B * d->H * d->L;
-    const long long nblk = (rows + kt->tt - 1) / kt->tt;
+    const long long nblk = (rows + (long long)kt->tt * FEATMAP_TILES - 1) / ((long long)kt->tt * FEATMAP_TILES);
     if (nblk > 0x7fffffffLL) return SLIM_ERR_SHAPE;
     SLIM_TIMED("featmap", (hipStream_t)stream,
                kt->featmap(dim3((unsigned)nblk), (hipStream_t)stream, X, W, phi, row_offset, rows));

@@ -440,6 +440,12 @@ template <> __device__ __forceinline__ void store4<__bf16>(__bf16 *p, f4 v)
 
 // phi[r][m] = g(X_r)_m in fp32.  With row_off non-null (FAVOR+ only) the row is
 // divided by exp(row_off[r]), row_off[r] = max_m (w_m.x_r - |x_r|^2/2).
+// A workgroup walks FEATMAP_TILES tiles of rows with W's fragments held in registers
+// and the next tile's rows in flight (one tile per workgroup re-read W from L2 for every
+// 32 rows), and each wave writes its features through LDS as whole row segments
+// (written straight from the MFMA layout, every store instruction touched 16 rows; the
+// kernel is a stream of M fp32 per row: 0.40 -> 0.24 ms at 1M rows, M = 256).
+constexpr int FEATMAP_TILES = 8;
 template <class C>
 __global__ __launch_bounds__(C::NT) void featmap_kernel(const void *Xv, const void *Wv, float *phi, float *row_off,
                                                         long long rows)
@@ -448,58 +454,71 @@ __global__ __launch_bounds__(C::NT) void featmap_kernel(const void *Xv, const vo
     __shared__ __align__(16) T xs_[C::XMat::SIZE];
     __shared__ float kn[C::TT];
     __shared__ float qmax[C::NW * C::TT];
+    __shared__ __align__(16) float fst[C::NW * C::TT * (C::MW + 4)];
     const typename C::XMat xs(xs_);
-    const long long r0 = (long long)blockIdx.x * C::TT;
-    const int nv = (int)min((long long)C::TT, rows - r0);
-    const T *X = (const T *)Xv + r0 * C::D;
+    const long long rb = (long long)blockIdx.x * C::TT * FEATMAP_TILES;
+    const long long re = min(rows, rb + (long long)C::TT * FEATMAP_TILES);
     Frag<T> wf[C::NFB][C::NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, Wv);
-    {
-        typename C::Tile rx;
-        rx.load(X, nv);
+    const float lns = 0.5f * __logf((float)C::M);
+    typename C::Tile rx;
+    rx.load((const T *)Xv + rb * C::D, (int)min((long long)C::TT, re - rb));
+    for (long long r0 = rb; r0 < re; r0 += C::TT) {
+        const int nv = (int)min((long long)C::TT, re - r0);
         if constexpr (C::FAVOR)
             rx.store(xs, false, [&](int t, float q) { kn[t] = q; });
         else
             rx.store(xs, false, nullptr);
-    }
-    __syncthreads();
-    f4 ph[C::NFB][C::NTB];
-    feat_T<C>(ph, xs, wf);
-    const float lns = 0.5f * __logf((float)C::M);
-    if constexpr (C::FAVOR) {
-#pragma unroll
-        for (int tb = 0; tb < C::NTB; ++tb)
-#pragma unroll
-            for (int fb = 0; fb < C::NFB; ++fb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) ph[fb][tb][j] -= 0.5f * kn[tb * 16 + lcol()];
-        if (row_off) q_partial_max<C>(ph, qmax);
         __syncthreads();
+        if (r0 + C::TT < re) rx.load((const T *)Xv + (r0 + C::TT) * C::D, (int)min((long long)C::TT, re - r0 - C::TT));
+        f4 ph[C::NFB][C::NTB];
+        feat_T<C>(ph, xs, wf);
+        if constexpr (C::FAVOR) {
 #pragma unroll
-        for (int tb = 0; tb < C::NTB; ++tb) {
-            const int t = tb * 16 + lcol();
-            float off = 0.f;
-            if (row_off) {
-                off = qmax[t];
+            for (int tb = 0; tb < C::NTB; ++tb)
 #pragma unroll
-                for (int w = 1; w < C::NW; ++w) off = fmaxf(off, qmax[w * C::TT + t]);
-                if (wave_id() == 0 && lgrp() == 0 && t < nv) row_off[r0 + t] = off;
+                for (int fb = 0; fb < C::NFB; ++fb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ph[fb][tb][j] -= 0.5f * kn[tb * 16 + lcol()];
+            if (row_off) q_partial_max<C>(ph, qmax);
+            __syncthreads();
+#pragma unroll
+            for (int tb = 0; tb < C::NTB; ++tb) {
+                const int t = tb * 16 + lcol();
+                float off = 0.f;
+                if (row_off) {
+                    off = qmax[t];
+#pragma unroll
+                    for (int w = 1; w < C::NW; ++w) off = fmaxf(off, qmax[w * C::TT + t]);
+                    if (wave_id() == 0 && lgrp() == 0 && t < nv) row_off[r0 + t] = off;
+                }
+                const float o2 = -(off + lns) * LOG2E;
+#pragma unroll
+                for (int fb = 0; fb < C::NFB; ++fb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ph[fb][tb][j] = __builtin_amdgcn_exp2f(fmaf(ph[fb][tb][j], LOG2E, o2));
             }
-            const float o2 = -(off + lns) * LOG2E;
-#pragma unroll
-            for (int fb = 0; fb < C::NFB; ++fb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) ph[fb][tb][j] = __builtin_amdgcn_exp2f(fmaf(ph[fb][tb][j], LOG2E, o2));
         }
-    }
+        // through this wave's LDS rows, so that each store instruction writes whole
+        // MW-feature row segments of 64 / (MW / 4) rows
+        {
+            float *wb = fst + wave_id() * C::TT * (C::MW + 4);
 #pragma unroll
-    for (int tb = 0; tb < C::NTB; ++tb) {
-        const int t = tb * 16 + lcol();
-        if (t < nv)
+            for (int tb = 0; tb < C::NTB; ++tb)
 #pragma unroll
-            for (int fb = 0; fb < C::NFB; ++fb)
-                *reinterpret_cast<f4 *>(phi + (size_t)(r0 + t) * C::M + wave_id() * C::MW + fb * 16 + 4 * lgrp()) =
-                    ph[fb][tb];
+                for (int fb = 0; fb < C::NFB; ++fb)
+                    *reinterpret_cast<f4 *>(wb + (tb * 16 + lcol()) * (C::MW + 4) + fb * 16 + 4 * lgrp()) = ph[fb][tb];
+            wave_lds_fence();
+            constexpr int LPR = C::MW / 4;  // lanes per row
+            constexpr int RPI = 64 / LPR;   // rows per instruction
+#pragma unroll
+            for (int i = 0; i < C::TT / RPI; ++i) {
+                const int t = i * RPI + lane_id() / LPR, cc = (lane_id() % LPR) * 4;
+                const f4 v = *reinterpret_cast<const f4 *>(wb + t * (C::MW + 4) + cc);
+                if (t < nv) *reinterpret_cast<f4 *>(phi + (size_t)(r0 + t) * C::M + wave_id() * C::MW + cc) = v;
+            }
+        }
+        __syncthreads();  // xs, kn and qmax are rewritten for the next tile
     }
 }
 

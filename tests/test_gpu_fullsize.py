@@ -102,3 +102,23 @@ def test_fullsize_long_context_causal_prefix_and_final_state():
     phi = oracle.featmap(kf[None, None], Wh, w.feat)[0, 0]
     assert relerr(host64(R[b, h]), vf.T @ phi) < tol
     assert relerr(host64(S[b, h]), phi.sum(axis=0)) < tol
+
+
+def test_fullsize_featmap_sampled_rows():
+    # the standalone feature map on the headline workload's Q (1M rows, as bench.py
+    # --featmap times it): sampled rows, including every workgroup boundary of the first
+    # few and the last rows, against the oracle's features
+    w = WORKLOADS["favor_bf16_L16384_d64_M256"]
+    x = make(w, dy=False)
+    phi, off = A.featmap(x["q"], x["W"], "favor", row_offset=True)
+    torch.cuda.synchronize()
+    rows = w.B * w.H * w.L
+    sel = np.unique(np.concatenate([np.arange(0, 1024, 31), [255, 256, 257, rows - 257, rows - 256, rows - 1],
+                                    np.random.default_rng(3).integers(0, rows, 500)]))
+    qf = x["q"].reshape(rows, w.d)[torch.from_numpy(sel).cuda()]
+    ref = oracle.featmap(host64(qf), host64(x["W"]), "favor")
+    got = host64(phi.reshape(rows, w.M)[torch.from_numpy(sel).cuda()])
+    o = host64(off.reshape(rows)[torch.from_numpy(sel).cuda()])
+    assert relerr(got * np.exp(o)[:, None], ref) < 1e-5
+    assert float(got.max()) <= 1.0 / np.sqrt(w.M) * (1 + 1e-5)  # the offset makes the largest feature 1/sqrt(M)
+    assert torch.isfinite(phi).all()
