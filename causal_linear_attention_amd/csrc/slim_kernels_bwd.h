@@ -686,9 +686,11 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
         }
         // next tile's inputs, fetched during the state update and the barriers
         if (t0 > 0) rg.load(Q, K, V, dY, st, t0 - TT, G.len);
-        // gradient state (after use): [dR; dS] += [dNum | dden]^T g(Q)
+        // gradient state (after use): [dR; dS] += [dNum | dden]^T g(Q), for the tiles before
+        // (skipping it after the last tile took the plain kernel from 0.564 to 0.541 ms; it
+        // slowed the dW pass's variant, which keeps it)
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb) {
+        for (int fb = 0; fb < NFB && (DW || t0 > 0); ++fb) {
 #pragma unroll
             for (int eb = 0; eb < NEA; ++eb)
                 mma_range<T>(dr[eb][fb], 0, NTB, [&](int tb) { return DN.fr(eb, tb * 16); },
