@@ -10,7 +10,6 @@ reading is taken: W iid N(0, 1) unless "orthogonal" is named.
 from __future__ import annotations
 
 import dataclasses
-import math
 
 
 @dataclasses.dataclass(frozen=True)

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import DT, TOL, host64, inputs, relerr_heads, to_dev
+from gpu_util import DT, TOL, host64, inputs, relerr_heads
 from causal_linear_attention_amd import attention as A
 
 pytestmark = pytest.mark.gpu

@@ -12,7 +12,6 @@ import sys
 import tempfile
 from concurrent.futures import ThreadPoolExecutor
 
-import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
