@@ -157,13 +157,14 @@ def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, d
     return dQ, dK, dV, dR, dS
 
 
-def decode_step(q, k, v, W=None, feat="favor", R=None, S=None, inplace=False):
+def decode_step(q, k, v, W=None, feat="favor", R=None, S=None, inplace=False, state_dtype=None):
     """One recurrent decode step for one new token per head.
 
-    q, k, v: [B, H, d] (fp32 or bf16); R [B, H, d, M], S [B, H, M] fp32: the
-    state before the token (None = zero, the first token).  Returns (y, R', S')
-    with y [B, H, d] and R' = R + v g(k)^T, S' = S + g(k).  inplace=True
-    writes R', S' into R, S (which must be given) and returns them."""
+    q, k, v: [B, H, d] (fp32 or bf16); R [B, H, d, M], S [B, H, M] (fp32, or fp64):
+    the state before the token (None = zero, the first token).  Returns (y, R', S')
+    with y [B, H, d] and R' = R + v g(k)^T, S' = S + g(k), in the state's dtype
+    (R's, else state_dtype, else fp32).  inplace=True writes R', S' into R, S (which
+    must be given) and returns them."""
     if q.dim() != 3:
         raise ValueError("decode_step takes q, k, v of shape [B, H, d]")
     B, H, d = q.shape
@@ -174,20 +175,23 @@ def decode_step(q, k, v, W=None, feat="favor", R=None, S=None, inplace=False):
         _check_io("W", W, q.dtype, (M, d))
     if (R is None) != (S is None):
         raise ValueError("give both R and S, or neither")
+    sd = R.dtype if R is not None else (state_dtype or torch.float32)
+    if sd not in _SDT:
+        raise ValueError(f"unsupported state dtype {sd}")
     if R is not None:
-        _check_io("R", R, torch.float32, (B, H, d, M))
-        _check_io("S", S, torch.float32, (B, H, M))
+        _check_io("R", R, sd, (B, H, d, M))
+        _check_io("S", S, sd, (B, H, M))
     elif inplace:
         raise ValueError("inplace needs R and S")
     if q.dtype not in _DT:
         raise ValueError(f"unsupported dtype {q.dtype}")
-    dsc = _lib.desc(B, H, 1, d, M, 1, 0, _DT[q.dtype], _FEAT[feat])
+    dsc = _lib.desc(B, H, 1, d, M, 1, 0, _DT[q.dtype], _FEAT[feat], _SDT[sd])
     y = torch.empty_like(q)
     if inplace:
         Ro, So = R, S
     else:
-        Ro = torch.empty((B, H, d, M), dtype=torch.float32, device=q.device)
-        So = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+        Ro = torch.empty((B, H, d, M), dtype=sd, device=q.device)
+        So = torch.empty((B, H, M), dtype=sd, device=q.device)
     _lib.check(_lib.lib().slim_decode_step(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(R),
                                            _ptr(S), _ptr(y), _ptr(Ro), _ptr(So), _stream()),
                "slim_decode_step")

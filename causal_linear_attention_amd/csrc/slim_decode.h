@@ -22,16 +22,24 @@ namespace slim {
 
 struct DecodeArgs {
     const void *q, *k, *v, *W;  // [BH][d] io dtype; W [M][d] (FAVOR+) or NULL
-    const float *Rin, *Sin;     // state before the token, NULL = zero
+    const void *Rin, *Sin;      // state before the token (fp32 or fp64), NULL = zero
     void *y;                    // [BH][d] io dtype
-    float *Rout, *Sout;         // state after the token (may equal Rin, Sin)
+    void *Rout, *Sout;          // state after the token (may equal Rin, Sin)
 };
 
 constexpr int DECODE_NT = 256;
 
-template <class C> __global__ __launch_bounds__(DECODE_NT) void decode_kernel(DecodeArgs a)
+// Four consecutive state entries of type S (fp32: 16 bytes, fp64: 32 bytes).
+template <typename S> struct State4;
+template <> struct State4<float> { typedef f4 type; };
+template <> struct State4<double> { typedef double type __attribute__((ext_vector_type(4))); };
+
+// S: the state's element type.  The features are fp32; with an fp64 state the update,
+// the row dot products and the division are done in fp64.
+template <class C, typename S> __global__ __launch_bounds__(DECODE_NT) void decode_kernel(DecodeArgs a)
 {
     typedef typename C::T T;
+    typedef typename State4<S>::type S4;
     constexpr int D = C::D, M = C::M;
     constexpr int TPR = M / 4;                       // threads per state row
     constexpr int RPP = DECODE_NT / TPR;             // rows per pass of the workgroup
@@ -41,21 +49,21 @@ template <class C> __global__ __launch_bounds__(DECODE_NT) void decode_kernel(De
     __shared__ float x[3][D];                        // q, k, v
     __shared__ float fk[M], pq[M];                   // g(k); w_m.q (FAVOR+) or g(q) (elu+1)
     __shared__ float wmax[NWF];
-    __shared__ float red[D + 1];                     // numerators, then the denominator
+    __shared__ S red[D + 1];                         // numerators, then the denominator
     const long long bh = blockIdx.x;
     const int tid = threadIdx.x, cg = tid % TPR, rs = tid / TPR;
-    const float *rin = a.Rin ? a.Rin + (size_t)bh * D * M : nullptr;
-    const float *sin_ = a.Sin ? a.Sin + (size_t)bh * M : nullptr;
-    float *rout = a.Rout + (size_t)bh * D * M;
-    float *sout = a.Sout + (size_t)bh * M;
+    const S *rin = a.Rin ? (const S *)a.Rin + (size_t)bh * D * M : nullptr;
+    const S *sin_ = a.Sin ? (const S *)a.Sin + (size_t)bh * M : nullptr;
+    S *rout = (S *)a.Rout + (size_t)bh * D * M;
+    S *sout = (S *)a.Sout + (size_t)bh * M;
 
-    f4 st[NP];
+    S4 st[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int row = rs + p * RPP;
-        st[p] = f4zero();
+        st[p] = S4{0, 0, 0, 0};
         if (rin && row <= D)
-            st[p] = *reinterpret_cast<const f4 *>((row < D ? rin + (size_t)row * M : sin_) + 4 * cg);
+            st[p] = *reinterpret_cast<const S4 *>((row < D ? rin + (size_t)row * M : sin_) + 4 * cg);
     }
     for (int i = tid; i < 3 * D; i += DECODE_NT) {
         const T *src = (const T *)(i < D ? a.q : i < 2 * D ? a.k : a.v);
@@ -118,18 +126,18 @@ template <class C> __global__ __launch_bounds__(DECODE_NT) void decode_kernel(De
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int row = rs + p * RPP;
-        float part = 0.f;
+        S part = 0;
         if (row <= D) {
             const float c = row < D ? x[2][row] : 1.f;
-            f4 r = st[p];
+            S4 r = st[p];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) r[j] = fmaf(c, gk[j], r[j]);
+            for (int j = 0; j < 4; ++j) r[j] += (S)c * (S)gk[j];
             // streaming store: the new state is not read again in this step, so it need not
             // occupy the caches (8-9% faster at 545 MB of state)
-            __builtin_nontemporal_store(r, reinterpret_cast<f4 *>((row < D ? rout + (size_t)row * M : sout) + 4 * cg));
-            part = r[0] * gq[0];
+            __builtin_nontemporal_store(r, reinterpret_cast<S4 *>((row < D ? rout + (size_t)row * M : sout) + 4 * cg));
+            part = r[0] * (S)gq[0];
 #pragma unroll
-            for (int j = 1; j < 4; ++j) part = fmaf(r[j], gq[j], part);
+            for (int j = 1; j < 4; ++j) part += r[j] * (S)gq[j];
         }
         // every lane of a row's group takes the same branch above; the shuffles stay
         // outside it so that the whole wave executes them
@@ -138,7 +146,7 @@ template <class C> __global__ __launch_bounds__(DECODE_NT) void decode_kernel(De
         if (row <= D && cg == 0) red[row] = part;
     }
     __syncthreads();
-    if (tid < D) ((T *)a.y)[bh * D + tid] = (T)(red[tid] / red[D]);
+    if (tid < D) ((T *)a.y)[bh * D + tid] = (T)(float)(red[tid] / red[D]);
 }
 
 }  // namespace slim

@@ -17,7 +17,7 @@ struct KernelTable {
     void (*gstate)(dim3, hipStream_t, const ChunkArgs &);  // NULL: the dQ kernel does its work
     void (*bwdq)(dim3, hipStream_t, const ChunkArgs &);
     void (*bwdkv)(dim3, hipStream_t, const ChunkArgs &);
-    void (*decode)(dim3, hipStream_t, const DecodeArgs &);
+    void (*decode)(dim3, hipStream_t, const DecodeArgs &, bool);  // bool: fp64 state
 };
 
 // The dW pass (FAVOR+): dQ and dK/dV kernels that also store dg(X) . g(X), and the

@@ -353,11 +353,12 @@ static Plan plan(const slim_desc *d, int pass)
 
 static bool misaligned(const void *p, uintptr_t a) { return p && ((uintptr_t)p % a) != 0; }
 
-// Two fp32 ranges of n elements that overlap without being the same range.
-static bool overlaps_partly(const float *x, const float *y, long long n)
+// Two ranges of n bytes that overlap without being the same range.
+static bool overlaps_partly(const void *x, const void *y, long long n)
 {
     if (!x || !y || x == y) return false;
-    return x < y + n && y < x + n;
+    const char *a = (const char *)x, *b = (const char *)y;
+    return a < b + n && b < a + n;
 }
 
 }  // namespace slim
@@ -366,7 +367,7 @@ using namespace slim;
 
 extern "C" {
 
-int slim_version(void) { return (2 << 16) | 0; }
+int slim_version(void) { return (2 << 16) | 1; }
 
 slim_status slim_prof_enable(int enable)
 {
@@ -428,7 +429,6 @@ slim_status slim_validate(const slim_desc *d, int pass)
     if (d->feat == SLIM_FEAT_ELU1 && d->M != d->d) return SLIM_ERR_SHAPE;
     if (d->state_dtype != SLIM_F32 && d->state_dtype != SLIM_F64) return SLIM_ERR_DTYPE;
     if (pass == SLIM_PASS_DECODE && d->L != 1) return SLIM_ERR_SHAPE;
-    if (pass == SLIM_PASS_DECODE && d->state_dtype != SLIM_F32) return SLIM_ERR_UNSUPPORTED;
     const long long BH = d->B * d->H;
     if (pass == SLIM_PASS_DECODE ? BH > (1LL << 24) : (BH > 65535 && pass != SLIM_PASS_FEATMAP))
         return SLIM_ERR_UNSUPPORTED;
@@ -649,8 +649,7 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
 }
 
 slim_status slim_decode_step(const slim_desc *d, const void *q, const void *k, const void *v, const void *W,
-                             const float *R_in, const float *S_in, void *y, float *R_out, float *S_out,
-                             void *stream)
+                             const void *R_in, const void *S_in, void *y, void *R_out, void *S_out, void *stream)
 {
     slim_status st = slim_validate(d, SLIM_PASS_DECODE);
     if (st != SLIM_OK) return st;
@@ -663,14 +662,16 @@ slim_status slim_decode_step(const slim_desc *d, const void *q, const void *k, c
         return SLIM_ERR_ALIGN;
     // the state may be updated in place, but not through partly overlapping ranges
     const long long BH = d->B * d->H;
-    if (overlaps_partly(R_in, R_out, BH * d->d * d->M) || overlaps_partly(S_in, S_out, BH * d->M))
+    const bool f64 = d->state_dtype == SLIM_F64;
+    const long long es = f64 ? 8 : 4;
+    if (overlaps_partly(R_in, R_out, BH * d->d * d->M * es) || overlaps_partly(S_in, S_out, BH * d->M * es))
         return SLIM_ERR_SHAPE;
     const KernelTable *kt = find(d);
     hipStream_t s = (hipStream_t)stream;
     DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.W = W;
     a.Rin = R_in; a.Sin = S_in; a.y = y; a.Rout = R_out; a.Sout = S_out;
-    SLIM_TIMED("decode", s, kt->decode(dim3((unsigned)(d->B * d->H)), s, a));
+    SLIM_TIMED("decode", s, kt->decode(dim3((unsigned)(d->B * d->H)), s, a, f64));
     return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
 

@@ -93,14 +93,13 @@ typedef struct slim_desc {
     int32_t feat;          /* slim_feat */
     int32_t state_dtype;   /* element type of the states and their gradients (R_in, S_in,
                               R_out, S_out, dR_out, dS_out, dR_in, dS_in): SLIM_F32, or
-                              SLIM_F64 for slim_attn_fwd / slim_attn_bwd (states passed
-                              between calls then keep the precision of the internal
-                              fp64 carries) */
+                              SLIM_F64 (states passed between calls then keep the
+                              precision of the internal fp64 carries; the decode step
+                              then updates the state in fp64) */
 } slim_desc;
 
 /* Host-only check of a descriptor for a pass; touches no GPU.  SLIM_PASS_DECODE
- * requires L == 1 (one token per head) and fp32 states, and allows B*H up to
- * 2^24. */
+ * requires L == 1 (one token per head) and allows B*H up to 2^24. */
 slim_status slim_validate(const slim_desc *desc, int pass);
 
 /* Workspace bytes the pass needs (0 for SLIM_PASS_FEATMAP and SLIM_PASS_DECODE); 0 if the
@@ -183,18 +182,19 @@ slim_status slim_attn_bwd(const slim_desc *desc, const void *Q, const void *K, c
  * steps gives the same outputs and state as one slim_attn_fwd over the same
  * tokens (up to fp32 rounding order).
  * desc: L must be 1 (num_chunks therefore 1); window_chunks is ignored;
- *       state_dtype must be SLIM_F32.
+ *       state_dtype SLIM_F32 or SLIM_F64 (the state's type; with fp64 the
+ *       update, the row dot products and the division are done in fp64, the
+ *       features in fp32).
  * In : q, k, v [B][H][d] (desc dtype); W as in the forward (NULL for elu+1);
- *      R_in [B][H][d][M], S_in [B][H][M] fp32 = the state before the token
- *      (both NULL = zero, i.e. the first token, or both given).
+ *      R_in [B][H][d][M], S_in [B][H][M] (state_dtype) = the state before the
+ *      token (both NULL = zero, i.e. the first token, or both given).
  * Out: y [B][H][d]; R_out, S_out = the state after the token (required).
  *      R_out may be the same pointer as R_in and S_out as S_in (update in
  *      place); no other overlap of inputs and outputs is allowed.
  * No workspace.  Two calls that update the same state must be ordered (same
  * stream or synchronised). */
 slim_status slim_decode_step(const slim_desc *desc, const void *q, const void *k, const void *v, const void *W,
-                             const float *R_in, const float *S_in, void *y, float *R_out, float *S_out,
-                             void *stream);
+                             const void *R_in, const void *S_in, void *y, void *R_out, void *S_out, void *stream);
 
 const char *slim_status_string(slim_status s);
 

@@ -17,7 +17,8 @@ def to_dev(x: np.ndarray, dtype) -> torch.Tensor:
 
 
 def host64(t: torch.Tensor) -> np.ndarray:
-    return t.detach().float().cpu().numpy().astype(np.float64)
+    # widened on the host: an fp64 tensor keeps every bit
+    return t.detach().cpu().double().numpy()
 
 
 def inputs(B, H, L, d, M, dtype, feat="favor", seed=0, scale=None, w_kind="gaussian", dy=True):

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.slim_version() >> 16 == 2
+    assert lib.slim_version() >> 16 == 2 and lib.slim_version() & 0xffff >= 1
     for code in range(8):
         assert lib.slim_status_string(code)
     assert lib.slim_status_string(0) == b"ok"
@@ -224,6 +224,10 @@ def test_decode_rejects_before_any_launch(lib):
     r_out = ctypes.c_void_p((1 << 24) + 256)
     s_ = ctypes.c_void_p(1 << 28)
     assert lib.slim_decode_step(ctypes.byref(d), p, p, p, p, r_in, s_, p, r_out, s_, None) == 2
+    # with an fp64 state the ranges are twice as long: one state's length in fp32 bytes apart overlaps
+    d64 = d_(L=1, num_chunks=1, state_dtype=_lib.SLIM_F64)
+    r_far = ctypes.c_void_p((1 << 24) + 2 * 3 * 64 * 128 * 4)
+    assert lib.slim_decode_step(ctypes.byref(d64), p, p, p, p, r_in, s_, p, r_far, s_, None) == 2
     de = d_(L=1, num_chunks=1, feat=_lib.SLIM_FEAT_ELU1, M=64)
     assert lib.slim_decode_step(ctypes.byref(de), p, p, p, p, None, None, p, p, p, None) == 2    # elu+1: no W
 
@@ -233,6 +237,6 @@ def test_state_dtype_validation(lib):
     assert validate(lib, _lib.SLIM_PASS_BWD, state_dtype=_lib.SLIM_F64) == 0
     assert validate(lib, _lib.SLIM_PASS_FWD, state_dtype=_lib.SLIM_BF16) == 3     # states are fp32 or fp64
     assert validate(lib, _lib.SLIM_PASS_FWD, state_dtype=7) == 3
-    assert validate(lib, _lib.SLIM_PASS_DECODE, L=1, num_chunks=1, state_dtype=_lib.SLIM_F64) == 4
+    assert validate(lib, _lib.SLIM_PASS_DECODE, L=1, num_chunks=1, state_dtype=_lib.SLIM_F64) == 0  # fp64 state
     # the workspace does not depend on the state type (the carries are fp64 either way)
     assert ws(lib, 2, state_dtype=_lib.SLIM_F64) == ws(lib, 2)

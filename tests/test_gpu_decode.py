@@ -145,3 +145,66 @@ def test_many_heads():
     yo, Ro, So = oracle.decode_step(sel(q), sel(k), sel(v), W, "favor", sel(R), sel(S))
     assert relerr_heads(sel(y), yo) < TOL[torch.bfloat16]
     assert relerr_heads(sel(R2), Ro) < TOL_STATE and relerr_heads(sel(S2), So) < TOL_STATE
+
+
+@pytest.mark.parametrize("dt,feat,d,M", [("bf16", "favor", 64, 256), ("f32", "favor", 16, 32),
+                                         ("f32", "elu1", 128, 128), ("bf16", "favor", 128, 64)])
+def test_fp64_state_matches_oracle(dt, feat, d, M):
+    # fp64 states: the update R + v g(k)^T, S + g(k) is taken in fp64, so the
+    # state is the oracle's up to the fp32 rounding of the features themselves
+    B, H = 2, 3
+    print("decode f64", dt, feat, d, M, flush=True)
+    q, k, v, W = _token(B, H, d, M, dt, feat, seed=41)
+    R, S = (t.double() for t in _state(B, H, d, M, dt, feat, 42, W))
+    y, R2, S2 = A.decode_step(q, k, v, W, feat, R, S)
+    torch.cuda.synchronize()
+    assert R2.dtype == torch.float64 and S2.dtype == torch.float64
+    yo, Ro, So = oracle.decode_step(q, k, v, W, feat, host64(R), host64(S))
+    assert relerr_heads(host64(y), yo) < TOL[DT[dt]]
+    assert relerr_heads(host64(R2), Ro) < TOL_STATE and relerr_heads(host64(S2), So) < TOL_STATE
+    # the first token, with the state dtype asked for
+    y1, R1, S1 = A.decode_step(q, k, v, W, feat, state_dtype=torch.float64)
+    torch.cuda.synchronize()
+    assert R1.dtype == torch.float64
+    _, Ro1, So1 = oracle.decode_step(q, k, v, W, feat)
+    assert relerr_heads(host64(R1), Ro1) < TOL_STATE and relerr_heads(host64(S1), So1) < TOL_STATE
+
+
+def test_fp64_state_keeps_small_increments():
+    # after a very long prefix the state is large and one token's increment is
+    # below fp32's resolution of it; an fp64 state still records the increment
+    B, H, d, M = 2, 2, 64, 128
+    q, k, v, W = _token(B, H, d, M, "f32", "favor", seed=43)
+    rng = np.random.default_rng(44)
+    R = torch.from_numpy(rng.standard_normal((B, H, d, M)) * 1e7 + 3e8).cuda()
+    S = torch.from_numpy(np.abs(rng.standard_normal((B, H, M))) * 1e7 + 3e8).cuda()
+    _, R2, S2 = A.decode_step(q, k, v, W, "favor", R, S)
+    _, R2f, S2f = A.decode_step(q, k, v, W, "favor", R.float(), S.float())
+    torch.cuda.synchronize()
+    _, Ro, So = oracle.decode_step(q, k, v, W, "favor", host64(R), host64(S))
+    inc_o = Ro - host64(R)
+    assert relerr_heads(host64(R2) - host64(R), inc_o) < 1e-5
+    assert relerr_heads(host64(S2) - host64(S), So - host64(S)) < 1e-5
+    # the fp32 state loses it (its spacing at 3e8 is 32, the increments are O(1))
+    assert relerr_heads(host64(R2f) - host64(R.float()), inc_o) > 1e-1
+
+
+def test_fp64_decode_run_equals_fp64_chunked_forward():
+    B, H, T, d, M = 2, 3, 40, 64, 256
+    t = inputs(B, H, T, d, M, torch.bfloat16, "favor", seed=45, dy=False)
+    R0, S0 = (x.double() for x in _state(B, H, d, M, "bf16", "favor", 46, t["W"]))
+    R, S = R0.clone(), S0.clone()
+    ys = []
+    for l in range(T):
+        tok = [t[n][:, :, l, :].contiguous() for n in ("q", "k", "v")]
+        y, _, _ = A.decode_step(*tok, t["W"], "favor", R, S, inplace=True)
+        ys.append(y)
+    Yd = torch.stack(ys, dim=2)
+    Yc, Rc, Sc = A.attn_fwd(t["q"], t["k"], t["v"], t["W"], "favor", num_chunks=4, R_in=R0, S_in=S0)
+    torch.cuda.synchronize()
+    assert Rc.dtype == torch.float64
+    Yo, _, Ro, So = oracle.attn_fwd(t["q"], t["k"], t["v"], t["W"], "favor", R0=host64(R0), S0=host64(S0))
+    tol = TOL[torch.bfloat16]
+    assert relerr_heads(host64(Yd), Yo) < tol and relerr_heads(host64(Yc), Yo) < tol
+    assert relerr_heads(host64(R), Ro) < TOL_STATE and relerr_heads(host64(S), So) < TOL_STATE
+    assert relerr_heads(host64(R), host64(Rc)) < tol and relerr_heads(host64(S), host64(Sc)) < tol
