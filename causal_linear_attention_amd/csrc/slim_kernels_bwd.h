@@ -260,8 +260,13 @@ template <class C> struct BwdRegs {
 // blocks from W^T fragments it holds (no partial sums); elsewhere (where the held
 // fragments would cost spills) each wave reduces its own features' partial sums
 // across waves through LDS.
+// A wave owns value blocks w mod NEB + k NW (k < EBW): with fewer waves than value
+// blocks it holds EBW x M/16 = NEB x NFB W^T fragments, as many as the partial-sum
+// form does.
 template <class C> struct DqShared {
-    static constexpr bool value = C::FAVOR && sizeof(typename C::T) == 2 && C::D <= 64 && C::NW % C::NEB == 0;
+    static constexpr bool value = C::FAVOR && sizeof(typename C::T) == 2 && C::D <= 64 &&
+                                  (C::NW % C::NEB == 0 || C::NEB % C::NW == 0);
+    static constexpr int EBW = C::NEB > C::NW ? C::NEB / C::NW : 1;
 };
 // W^T fragments of value block eb over all M features (free index e, contraction m),
 // from the packed W^T.
@@ -347,10 +352,13 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
     constexpr bool SH = DqShared<C>::value;
     constexpr int NB = NTB * NEB, MB = C::M / 16;
     const LMat<T, TT, C::M> Gq(sm.gqm);
-    Frag<T> wt[C::FAVOR ? (SH ? MB : NEB * NFB) : 1];
+    constexpr int EBW = DqShared<C>::EBW;
+    Frag<T> wt[C::FAVOR ? (SH ? EBW * MB : NEB * NFB) : 1];
     if constexpr (C::FAVOR) {
         if constexpr (SH)
-            load_wt_col<C>(wt, a.Wt, w % NEB);
+#pragma unroll
+            for (int k = 0; k < EBW; ++k)
+                load_wt_col<C>(*reinterpret_cast<Frag<T>(*)[MB]>(wt + k * MB), a.Wt, w % NEB + k * C::NW);
         else
 #pragma unroll
             for (int eb = 0; eb < NEB; ++eb) load_wtfrag_block<C>(*reinterpret_cast<Frag<T>(*)[NFB]>(wt + eb * NFB), a.Wt, eb);
@@ -411,10 +419,13 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
                         if constexpr (DW) store_pw<C>(pw + (size_t)t0 * C::M, tb * 16 + lc, nv, w * MW + fb * 16 + 4 * g, v);
                     }
                 __syncthreads();
-                for (int blk = w; blk < NB; blk += C::NW) {
-                    const int tb = blk / NEB, eb = blk % NEB;
+#pragma unroll
+                for (int j = 0; j < (NB + C::NW - 1) / C::NW; ++j) {
+                    const int blk = w + j * C::NW, tb = blk / NEB, eb = blk % NEB;
+                    if (blk >= NB) break;  // more waves than blocks
+                    const int k = NEB > C::NW ? j % EBW : 0;  // eb = w mod NEB + k NW
                     f4 acc = f4zero();
-                    mma_range<T>(acc, 0, MB, [&](int mb) { return wt[mb]; },
+                    mma_range<T>(acc, 0, MB, [&](int mb) { return wt[k * MB + mb]; },
                                  [&](int mb) { return Gq.frag_c(tb * 16, mb * 16); });
                     const int t = tb * 16 + lc;
                     if (t < nv) store4<T>(dQ + (size_t)(t0 + t) * D + eb * 16 + 4 * g, acc);
@@ -493,6 +504,20 @@ template <class C> struct BwdkvSmem {
     __align__(16) T dna[C::AuxMat::SIZE];
     __align__(16) T fq[C::NW * C::FMat::SIZE];
     float kn2[C::TT], qoff[C::TT];
+};
+// dK's W^T product with shared operands: the waves put dg(K) . g(K) (bf16, all
+// features) and their row-sum partials in the reduction rows, which are free once dV
+// is stored, and each wave finishes whole dK blocks of the value blocks it owns from
+// W^T fragments over all features, instead of reducing fp32 partial sums.  Used up to
+// 64 features: there the fp32 reduction weighs most beside a tile's feature work (at
+// d = 64, M = 64 the kernel goes from 1.91 to 1.67 ms on 1M tokens x 8 heads); at
+// M = 256 the W^T fragments over all features cost more than the reduction saves
+// (0.548 -> 0.60 ms at the 16K-token, 64-head shape).
+template <class C> struct DkShared {
+    typedef LMat<typename C::T, C::TT, C::M> GMat;
+    static constexpr bool value = C::FAVOR && sizeof(typename C::T) == 2 && C::D <= 64 && C::M <= 64 &&
+                                  GMat::SIZE * sizeof(typename C::T) + C::NW * C::TT * sizeof(float) <=
+                                      (size_t)C::NW * C::TT * C::LDR * sizeof(float);
 };
 // DW: also store dg(K) . g(K) for the projection gradient (slim_dw.h).
 template <class C, bool DW = false>
@@ -637,7 +662,67 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                     dk[fb][sb] = acc;
                 }
         }
-        if constexpr (C::FAVOR) {
+        if constexpr (DkShared<C>::value) {
+            // dK = W^T-product of dg(K) . g(K) over all features - K * its row sum
+            typedef typename DkShared<C>::GMat GMat;
+            constexpr int MB = C::M / 16;
+            const GMat Gk(reinterpret_cast<T *>(red));
+            float *rsp = red + GMat::SIZE * sizeof(T) / sizeof(float);  // [NW][TT] row-sum partials
+#pragma unroll
+            for (int sb = 0; sb < NTB; ++sb) {
+                float rsum = 0.f;
+#pragma unroll
+                for (int fb = 0; fb < NFB; ++fb) {
+                    const f4 v = dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]);
+                    rsum += (v[0] + v[1]) + (v[2] + v[3]);
+                    const Frag<T> gf = cfrag<T>(v);
+                    Gk.put_frag(sb * 16 + lc, w * MW + fb * 16 + 4 * g, gf);
+                    if constexpr (DW) store_pw<C>(pw + (size_t)t0 * C::M, sb * 16 + lc, nv, w * MW + fb * 16 + 4 * g, gf);
+                }
+                rsum += __shfl_xor(rsum, 16, 64);
+                rsum += __shfl_xor(rsum, 32, 64);
+                if (g == 0) rsp[w * TT + sb * 16 + lc] = rsum;
+            }
+            // value blocks eb = w mod NW (all row blocks), or, with more waves than value
+            // blocks, eb = w mod NEB and the row blocks sb = w / NEB mod NW / NEB
+            constexpr int TB_STEP = C::NW > NEB ? C::NW / NEB : 1;
+            constexpr int MH = MB >= 8 ? 8 : MB;  // W^T fragments held at once
+            const T *Wp = (const T *)a.Wt;
+            __syncthreads();
+            constexpr int EBW = NEB > C::NW ? NEB / C::NW : 1;  // value blocks per wave
+#pragma unroll 1
+            for (int k = 0; k < EBW; ++k) {
+                const int eb = w % NEB + k * C::NW;
+                f4 acc[NTB];
+#pragma unroll
+                for (int sb = 0; sb < NTB; ++sb) acc[sb] = f4zero();
+#pragma unroll 1
+                for (int m0 = 0; m0 < MB; m0 += MH) {
+                    Frag<T> wt[MH];
+#pragma unroll
+                    for (int j = 0; j < MH; ++j)
+                        wt[j] = *reinterpret_cast<const Frag<T> *>(
+                            Wp + (((size_t)eb * MB + m0 + j) * 64 + threadIdx.x % 64) * 4);
+#pragma unroll
+                    for (int sb = 0; sb < NTB; ++sb) {
+                        if (sb % TB_STEP != (w / NEB) % TB_STEP) continue;
+                        mma_range<T>(acc[sb], 0, MH, [&](int mb) { return wt[mb]; },
+                                     [&](int mb) { return Gk.frag_c(sb * 16, (m0 + mb) * 16); });
+                    }
+                }
+#pragma unroll
+                for (int sb = 0; sb < NTB; ++sb) {
+                    if (sb % TB_STEP != (w / NEB) % TB_STEP) continue;
+                    const int s = sb * 16 + lc;
+                    float rs = rsp[s];
+#pragma unroll
+                    for (int w2 = 1; w2 < C::NW; ++w2) rs += rsp[w2 * TT + s];
+                    if (s < nv)
+                        store4<T>(dK + (size_t)(t0 + s) * D + eb * 16 + 4 * g,
+                                  acc[sb] - xk.get4(s, eb * 16 + 4 * g) * rs);
+                }
+            }
+        } else if constexpr (C::FAVOR) {
             // dK^T = W^T (dg(K) . g(K))^T and the row sums of dg(K) . g(K), reduced across
             // waves (the sums in column D of the reduction rows); dK = that - K * rowsum.
             Frag<T> gk[NFB][NTB];
