@@ -83,10 +83,12 @@ def parse():
 
 
 def kernel_source_hash():
-    """sha256 of the kernel sources and the C-ABI header (what the traffic figures depend on)."""
+    """sha256 of the kernel sources, the C-ABI header and the build script with its compiler
+    flags (what the traffic figures depend on)."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(ROOT, "causal_linear_attention_amd", "csrc", "*")))
     files.append(os.path.join(ROOT, "include", "slim.h"))
+    files.append(os.path.join(ROOT, "causal_linear_attention_amd", "build.py"))
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:

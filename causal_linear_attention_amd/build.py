@@ -22,8 +22,12 @@ ARCH = "gfx950"
 SOURCES = ["slim_bf16_favor.hip", "slim_f32_favor.hip", "slim_bf16_favor_dw.hip", "slim_f32_favor_dw.hip",
            "slim_f32_elu1.hip", "slim_bf16_elu1.hip", "slim_host.hip"]
 
+# -amdgpu-use-amdgpu-trackers: the scheduler's AMDGPU register-pressure tracking; it
+# spills less in the dQ kernel at 64 features (1.30 -> 1.17 ms on 1M tokens x 8 heads)
+# and changes nothing measurable at the 16K-token, 64-head shape.
 CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-use-amdgpu-trackers=1",
           "-I", os.path.join(ROOT, "include")]
 
 
