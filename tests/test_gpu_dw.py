@@ -145,3 +145,28 @@ def test_dw_fullsize_rotation_symmetry_and_sampled_heads():
     o = oracle.attn_bwd(*(host64(t) for t in sel), host64(x["W"]), host64(dys), "favor", form="prefix",
                         want_dw=True)
     assert relerr(host64(dW2), o[5]) < TOL[torch.bfloat16]
+
+
+# bf16 FAVOR+ shapes for every way the dQ and dK kernels split their W^T products over
+# waves when the waves share dg(X) . g(X): one wave for several value blocks (d = 64 with
+# M = 16 or 32; d = 32, M = 16), as many waves as value blocks (d = 32, M = 64; d = 16,
+# M = 16), more waves than value blocks (d = 16, M = 64), and the 64-feature shape of the
+# long-sequence workload; ragged tiles and slices.
+SHARED_SHAPES = [(16, 16), (16, 64), (32, 16), (32, 64), (64, 16), (64, 32), (64, 64)]
+
+
+@pytest.mark.parametrize("d,M", SHARED_SHAPES, ids=lambda v: str(v))
+def test_shared_operand_products_all_wave_splits(d, M):
+    B, H, L, C = 1, 2, 173, 3
+    print("shared", d, M, flush=True)
+    x = inputs(B, H, L, d, M, torch.bfloat16, "favor", seed=56)
+    g = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], "favor", C, want_dw=True)
+    p = A.attn_bwd(x["q"], x["k"], x["v"], x["W"], x["dy"], "favor", C)
+    torch.cuda.synchronize()
+    o = oracle.attn_bwd(host64(x["q"]), host64(x["k"]), host64(x["v"]), host64(x["W"]), host64(x["dy"]), "favor",
+                        want_dw=True)
+    tol = TOL[torch.bfloat16]
+    for i, name in enumerate(("dQ", "dK", "dV")):
+        assert relerr_heads(host64(g[i]), o[i]) < tol, name
+        assert relerr_heads(host64(p[i]), o[i]) < tol, name
+    assert relerr(host64(g[5]), o[5]) < tol
