@@ -60,7 +60,7 @@ def lib(path: str | None = None):
     L.slim_tile_rows.restype = i64
     L.slim_featmap.argtypes = [D, vp, vp, vp, vp, vp]
     L.slim_featmap.restype = i32
-    L.slim_attn_fwd.argtypes = [D] + [vp] * 11 + [sz, vp]
+    L.slim_attn_fwd.argtypes = [D] + [vp] * 12 + [sz, vp]
     L.slim_attn_fwd.restype = i32
     L.slim_attn_bwd.argtypes = [D] + [vp] * 18 + [sz, vp]
     L.slim_attn_bwd.restype = i32

@@ -79,11 +79,13 @@ def featmap(x, W=None, feat="favor", row_offset=False):
 
 
 def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, window_chunks=0,
-             state_dtype=None, want_row_stats=False):
+             state_dtype=None, want_row_stats=False, koff_out=None):
     """Forward.  Returns (Y, R_out [B,H,d,M], S_out [B,H,M]).  States are fp32, or
-    fp64 when R_in is fp64 or state_dtype=torch.float64.  want_row_stats: a fourth
-    value, the per-row statistics [B,H,L,2] fp32 that let attn_bwd skip recomputing
-    the denominators (pass it with Y)."""
+    fp64 when R_in is fp64 or state_dtype=torch.float64; like R_in, S_in they hold
+    the state times exp(-koff), the key-side offset of W (0 unless some row of W has
+    |w_m|^2 > 120).  want_row_stats: a fourth value, the per-row statistics
+    [B,H,L,2] fp32 that let attn_bwd skip recomputing the denominators (pass it
+    with Y).  koff_out: a one-element fp32 GPU tensor that receives koff."""
     B, H, L, d = q.shape
     M = _feat_M(W, feat, d)
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -100,9 +102,11 @@ def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, 
     R = torch.empty((B, H, d, M), dtype=sd, device=q.device)
     S = torch.empty((B, H, M), dtype=sd, device=q.device)
     rs = torch.empty((B, H, L, 2), dtype=torch.float32, device=q.device) if want_row_stats else None
+    if koff_out is not None:
+        _check_io("koff_out", koff_out, torch.float32, (1,))
     _lib.check(_lib.lib().slim_attn_fwd(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(R_in),
-                                        _ptr(S_in), _ptr(Y), _ptr(R), _ptr(S), _ptr(rs), _ptr(ws), ws.numel(),
-                                        _stream()),
+                                        _ptr(S_in), _ptr(Y), _ptr(R), _ptr(S), _ptr(koff_out), _ptr(rs), _ptr(ws),
+                                        ws.numel(), _stream()),
                "slim_attn_fwd")
     if want_row_stats:
         return Y, R, S, rs

@@ -47,8 +47,8 @@ template <class C, typename S> __global__ __launch_bounds__(DECODE_NT) void deco
     constexpr int NWF = (M + 63) / 64;               // waves that compute features
     static_assert(M % 16 == 0 && M <= DECODE_NT, "decode feature count");
     __shared__ float x[3][D];                        // q, k, v
-    __shared__ float fk[M], pq[M];                   // g(k); w_m.q (FAVOR+) or g(q) (elu+1)
-    __shared__ float wmax[NWF];
+    __shared__ float fk[M], pq[M];                   // g(k) (FAVOR+: its exponent); w_m.q (FAVOR+) or g(q) (elu+1)
+    __shared__ float wmax[NWF], nmax[NWF];           // per wave: max_m w_m.q, max_m |w_m|^2
     __shared__ S red[D + 1];                         // numerators, then the denominator
     const long long bh = blockIdx.x;
     const int tid = threadIdx.x, cg = tid % TPR, rs = tid / TPR;
@@ -72,7 +72,7 @@ template <class C, typename S> __global__ __launch_bounds__(DECODE_NT) void deco
     __syncthreads();
 
     if constexpr (C::FAVOR) {
-        float qm = -__builtin_inff();
+        float qm = -__builtin_inff(), nn = 0.f;
         if (tid < M) {
             typedef typename Vec16<T>::type VT;
             constexpr int VN = Vec16<T>::N;
@@ -87,17 +87,25 @@ template <class C, typename S> __global__ __launch_bounds__(DECODE_NT) void deco
                     sk = fmaf(we, ke, sk);
                     sq = fmaf(we, x[0][e0 + j], sq);
                     kk = fmaf(ke, ke, kk);
+                    nn = fmaf(we, we, nn);  // |w_m|^2 in index order, as key_offset_block sums it
                 }
             }
-            // g(k)_m = exp(w_m.k - |k|^2/2) / sqrt(M), exactly (no offset: it would not cancel)
+            // g(k)_m = exp(w_m.k - |k|^2/2 - koff) / sqrt(M): its exponent (base 2) here,
+            // the key-side offset koff of W once the maximum of |w_m|^2 is known
             const float kn2 = (0.5f * kk + 0.5f * __logf((float)M)) * LOG2E;
-            fk[tid] = __builtin_amdgcn_exp2f(fmaf(sk, LOG2E, -kn2));
+            fk[tid] = fmaf(sk, LOG2E, -kn2);
             pq[tid] = sq;
             qm = sq;
         }
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) qm = fmaxf(qm, __shfl_xor(qm, o, 64));
-        if (tid < M && lane_id() == 0) wmax[wave_id()] = qm;
+        for (int o = 32; o >= 1; o >>= 1) {
+            qm = fmaxf(qm, __shfl_xor(qm, o, 64));
+            nn = fmaxf(nn, __shfl_xor(nn, o, 64));
+        }
+        if (tid < M && lane_id() == 0) {
+            wmax[wave_id()] = qm;
+            nmax[wave_id()] = nn;
+        }
     } else {
         if (tid < M) {
             fk[tid] = elu1(x[1][tid]);
@@ -110,16 +118,21 @@ template <class C, typename S> __global__ __launch_bounds__(DECODE_NT) void deco
     // without the |q|^2/2 and sqrt(M) factors: y is invariant to any positive factor
     // on g(q), and the largest feature becomes 1.
     float gk[4], gq[4];
-    float qoff = 0.f;
+    float qoff = 0.f, koff2 = 0.f;
     if constexpr (C::FAVOR) {
         qoff = wmax[0];
+        float n2 = nmax[0];
 #pragma unroll
-        for (int w = 1; w < NWF; ++w) qoff = fmaxf(qoff, wmax[w]);
+        for (int w = 1; w < NWF; ++w) {
+            qoff = fmaxf(qoff, wmax[w]);
+            n2 = fmaxf(n2, nmax[w]);
+        }
         qoff *= -LOG2E;
+        koff2 = fmaxf(0.f, 0.5f * n2 - KOFF_MARGIN) * LOG2E;  // the key-side offset of W (slim_device.h)
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        gk[j] = fk[4 * cg + j];
+        gk[j] = C::FAVOR ? __builtin_amdgcn_exp2f(fk[4 * cg + j] - koff2) : fk[4 * cg + j];
         gq[j] = C::FAVOR ? __builtin_amdgcn_exp2f(fmaf(pq[4 * cg + j], LOG2E, qoff)) : pq[4 * cg + j];
     }
 

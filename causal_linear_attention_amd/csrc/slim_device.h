@@ -253,6 +253,47 @@ __device__ __forceinline__ void wave_lds_fence()
 // feature offset (exp2 domain) and one unused.
 constexpr int ROWSTAT = 4;
 
+// Key-side offset of the FAVOR+ map, one number per projection W.  For every key
+// k and feature m, w_m.k - |k|^2/2 = |w_m|^2/2 - |k - w_m|^2/2 <= |w_m|^2/2, so
+// with koff = max(0, max_m |w_m|^2/2 - KOFF_MARGIN) every key feature evaluated
+// as exp(w_m.k - |k|^2/2 - koff)/sqrt(M) is at most exp(KOFF_MARGIN)/sqrt(M),
+// whatever the keys: fp32 cannot overflow, and the prefix sums of up to 2^31 rows
+// of such features times values of moderate size stay finite.  A factor common to
+// all key features cancels in Y and in every input gradient (eq. (2) is
+// homogeneous of degree 0 in the keys' features taken together), so only the
+// states that cross the boundary carry it.  For the usual draws (|w_m|^2 near d,
+// d <= 64) koff is 0 and nothing changes.
+constexpr float KOFF_MARGIN = 60.f;
+
+// koff of W [M][D] (fp32, or bf16 when wbf16), computed by a whole workgroup of
+// at least M threads (every thread must call it; it synchronises the workgroup).
+// Thread m sums its row's squares in index order; the maximum over rows is exact in
+// any order, so every kernel that calls this gets the same value bit for bit.
+// red: LDS scratch of one float per wave of the workgroup, plus one.
+__device__ __forceinline__ float key_offset_block(const void *W, int wbf16, int M, int D, float *red)
+{
+    float n2 = 0.f;
+    if ((int)threadIdx.x < M) {
+        for (int e = 0; e < D; ++e) {
+            const size_t i = (size_t)threadIdx.x * D + e;
+            const float x = wbf16 ? __uint_as_float((unsigned)((const uint16_t *)W)[i] << 16) : ((const float *)W)[i];
+            n2 = fmaf(x, x, n2);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n2 = fmaxf(n2, __shfl_xor(n2, o, 64));
+    const int nw = (blockDim.x + 63) / 64;
+    if (lane_id() == 0) red[wave_id()] = n2;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float m = red[0];
+        for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
+        red[nw] = fmaxf(0.f, 0.5f * m - KOFF_MARGIN);
+    }
+    __syncthreads();
+    return red[nw];
+}
+
 // A [TT][D] tile of a row-major tensor held in registers: thread i owns the
 // 16-byte vectors i, i+NT, ... (row t = idx / VPR, columns c..c+EPV-1).  load()
 // issues the global reads (rows >= nvalid read as zero) and returns at once, so a

@@ -154,14 +154,28 @@ __global__ __launch_bounds__(256) void narrow2_kernel(S *d0, const double *s0, l
     else if (i - n0 < n1)
         d1[i - n0] = (S)s1[i - n0];
 }
-// Up to four carries loaded in one launch (each from its source, or zero).
+// Up to four carries loaded in one launch (each from its source, or zero).  The
+// same launch's first workgroup computes the key-side offset of W (FAVOR+) into the
+// workspace and, if wanted, the caller's koff (0 for elu+1, which has no W).
 struct WidenSet {
     double *dst[4];
     const void *src[4];
     long long n[4];
+    const void *W;  // FAVOR+ projection [M][D], or NULL
+    int wbf16, M, D;
+    float *kws, *kout;  // key offset: workspace copy (read by the chunk kernels), caller's copy
 };
 template <typename S> __global__ __launch_bounds__(256) void widen_set_kernel(WidenSet w)
 {
+    if (blockIdx.x == 0) {
+        __shared__ float red[5];
+        float koff = 0.f;
+        if (w.W) koff = key_offset_block(w.W, w.wbf16, w.M, w.D, red);
+        if (threadIdx.x == 0) {
+            if (w.kws) *w.kws = koff;
+            if (w.kout) *w.kout = koff;
+        }
+    }
     long long i = (long long)blockIdx.x * 256 + threadIdx.x;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -175,8 +189,8 @@ template <typename S> __global__ __launch_bounds__(256) void widen_set_kernel(Wi
 static void widen(const WidenSet &w, bool f64, hipStream_t s)
 {
     const long long n = w.n[0] + w.n[1] + w.n[2] + w.n[3];
-    if (n <= 0) return;
-    const dim3 g((unsigned)((n + 255) / 256));
+    if (n <= 0 && !w.kws && !w.kout) return;
+    const dim3 g((unsigned)(n > 0 ? (n + 255) / 256 : 1));
     if (f64)
         hipLaunchKernelGGL(widen_set_kernel<double>, g, dim3(256), 0, s, w);
     else
@@ -256,7 +270,7 @@ static const DwTable *find_dw(const slim_desc *d)
 struct Plan {
     long long BH, c, nchunks, P, SZ;
     long long dw_parts;  // dW pass: partial sums per window (2 sides x BH x workgroups per head)
-    size_t slots_off, gslots_off, stats_off, cR_off, cS_off, gR_off, gS_off, wt_off;
+    size_t slots_off, gslots_off, stats_off, cR_off, cS_off, gR_off, gS_off, wt_off, koff_off;
     size_t pq_off, pk_off, part_off, part2_off, total;
 };
 
@@ -282,17 +296,25 @@ static void dw_split(long long BH, long long wl, int *S, int *rows_per)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Automatic window: enough slices for about 4096 workgroups per launch; all of them
-// when the backward's per-slice buffers (state and gradient slots, row statistics) for
-// the whole sequence fit in 1 GiB, so that it runs as one window (no extra sweep over
-// the slices, no recompute of their states per window).  Bounded for any L.
-static long long resolve_window(const slim_desc *d, long long nchunks, long long c)
+// when the backward's per-slice buffers for the whole sequence fit the budget, so that
+// it runs as one window (no extra sweep over the slices, no recompute of their states
+// per window); and never more slices than fit it (at least one).  The budget is 1 GiB
+// for the state and gradient slots with the row statistics, and with dW another 1 GiB
+// for its two [c][M] rows of dg(X) . g(X) per slice and head.  The workspace is
+// therefore bounded for any L at a given slice length.
+constexpr long long WINDOW_BUDGET = 1LL << 30;
+static long long resolve_window(const slim_desc *d, long long nchunks, long long c, int pass)
 {
     long long P = d->window_chunks;
     if (P <= 0) {
         const long long BH = d->B * d->H;
-        const long long per_slice = BH * ((d->d + 1) * d->M * 4 * 2 + c * ROWSTAT * 4);
+        const long long per_state = BH * ((d->d + 1) * d->M * 4 * 2 + c * ROWSTAT * 4);
+        const long long per_dw = pass == SLIM_PASS_BWD_DW ? BH * 2 * c * d->M * (d->dtype == SLIM_BF16 ? 2 : 4) : 0;
+        long long most = WINDOW_BUDGET / per_state;  // slices that fit the budgets
+        if (per_dw > 0 && WINDOW_BUDGET / per_dw < most) most = WINDOW_BUDGET / per_dw;
         P = (4096 + BH - 1) / BH;
-        if (nchunks > P && nchunks * per_slice <= (1LL << 30)) P = nchunks;
+        if (nchunks > P && nchunks <= most) P = nchunks;
+        if (P > most) P = most;
     }
     if (P > nchunks) P = nchunks;
     if (P < 1) P = 1;
@@ -307,7 +329,7 @@ static Plan plan(const slim_desc *d, int pass)
     p.BH = d->B * d->H;
     p.c = (d->L + d->num_chunks - 1) / d->num_chunks;
     p.nchunks = (d->L + p.c - 1) / p.c;
-    p.P = resolve_window(d, p.nchunks, p.c);
+    p.P = resolve_window(d, p.nchunks, p.c, pass);
     p.SZ = (d->d + 1) * d->M;
     const size_t slots = (size_t)p.BH * (p.P + 1) * p.SZ * 4;
     size_t off = 0;
@@ -318,6 +340,8 @@ static Plan plan(const slim_desc *d, int pass)
     off = align256(off + (size_t)p.BH * d->d * d->M * 8);
     p.cS_off = off;
     off = align256(off + (size_t)p.BH * d->M * 8);
+    p.koff_off = off;  // the key-side offset of W, one float
+    off = align256(off + 4);
     if (pass == SLIM_PASS_BWD || pass == SLIM_PASS_BWD_DW) {
         p.gslots_off = off;
         off = align256(off + slots);
@@ -367,7 +391,7 @@ using namespace slim;
 
 extern "C" {
 
-int slim_version(void) { return (2 << 16) | 1; }
+int slim_version(void) { return (3 << 16) | 0; }
 
 slim_status slim_prof_enable(int enable)
 {
@@ -476,8 +500,8 @@ slim_status slim_featmap(const slim_desc *d, const void *X, const void *W, float
 }
 
 slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
-                          const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, float *row_stats,
-                          void *ws, size_t ws_bytes, void *stream)
+                          const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, float *koff,
+                          float *row_stats, void *ws, size_t ws_bytes, void *stream)
 {
     slim_status st = slim_validate(d, SLIM_PASS_FWD);
     if (st != SLIM_OK) return st;
@@ -487,7 +511,7 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
     if ((R_in == nullptr) != (S_in == nullptr)) return SLIM_ERR_NULL;
     if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(W, 16) || misaligned(Y, 16) ||
         misaligned(R_out, 16) || misaligned(S_out, 16) || misaligned(R_in, 16) || misaligned(S_in, 16) ||
-        misaligned(row_stats, 16) || misaligned(ws, 256))
+        misaligned(row_stats, 16) || misaligned(koff, 4) || misaligned(ws, 256))
         return SLIM_ERR_ALIGN;
     const Plan p = plan(d, SLIM_PASS_FWD);
     if (ws_bytes < p.total) return SLIM_ERR_WORKSPACE;
@@ -501,9 +525,13 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
     a.rstat = row_stats;
     a.slots = (float *)(base + p.slots_off);
     a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
+    a.koff = (const float *)(base + p.koff_off);
     double *cR = (double *)(base + p.cR_off), *cS = (double *)(base + p.cS_off);
     const bool f64 = d->state_dtype == SLIM_F64;
-    widen(WidenSet{{cR, cS, nullptr, nullptr}, {R_in, S_in, nullptr, nullptr}, {p.BH * D * M, p.BH * M, 0, 0}},
+    widen(WidenSet{{cR, cS, nullptr, nullptr},
+                   {R_in, S_in, nullptr, nullptr},
+                   {p.BH * D * M, p.BH * M, 0, 0},
+                   W, d->dtype == SLIM_BF16, M, D, (float *)(base + p.koff_off), koff},
           f64, s);
     for (long long n0 = 0; n0 < p.nchunks; n0 += p.P) {
         const int np = (int)(p.nchunks - n0 < p.P ? p.nchunks - n0 : p.P);
@@ -553,6 +581,7 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
     a.gslots = (float *)(base + p.gslots_off);
     a.stats = (float *)(base + p.stats_off);
     a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
+    a.koff = (const float *)(base + p.koff_off);
     if (dt) {
         a.pq = base + p.pq_off;
         a.pk = base + p.pk_off;
@@ -564,7 +593,10 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
         pack_wt(W, base + p.wt_off, M, D, d->dtype == SLIM_BF16, s);
     }
     const bool f64 = d->state_dtype == SLIM_F64;
-    widen(WidenSet{{cR, cS, gR, gS}, {R_in, S_in, dR_out, dS_out}, {p.BH * D * M, p.BH * M, p.BH * D * M, p.BH * M}},
+    widen(WidenSet{{cR, cS, gR, gS},
+                   {R_in, S_in, dR_out, dS_out},
+                   {p.BH * D * M, p.BH * M, p.BH * D * M, p.BH * M},
+                   W, d->dtype == SLIM_BF16, M, D, (float *)(base + p.koff_off), nullptr},
           f64, s);
     const long long nwin = (p.nchunks + p.P - 1) / p.P;
     auto window = [&](long long wi) {

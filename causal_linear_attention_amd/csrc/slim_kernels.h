@@ -60,6 +60,7 @@ struct ChunkArgs {
     float *rstat;              // [BH][L][2] per row (1/den, query offset): written by the forward,
                                // read by the backward instead of recomputing them (or NULL)
     const void *Yin;           // backward with the forward's row statistics: its output Y
+    const float *koff;         // FAVOR+: the key-side offset of W (key_offset_block), one float
     long long L;
     int c;   // chunk length
     int n0;  // first chunk of the window
@@ -334,15 +335,26 @@ template <class C> __device__ __forceinline__ void k_finish_S(f4 (&ph)[C::NTB][C
     }
 }
 
-// Row function for staging K: kn2[t] as above.
+// Row function for staging K: kn2[t] as above, plus the key-side offset koff of W
+// (every key feature scaled by exp(-koff); see key_offset_block).
 template <class C> struct KnormFn {
     float *kn2;
     int nv;
+    float koff;
     __device__ __forceinline__ void operator()(int t, float q) const
     {
-        kn2[t] = t < nv ? (0.5f * q + 0.5f * __logf((float)C::M)) * LOG2E : __builtin_inff();
+        kn2[t] = t < nv ? (0.5f * q + 0.5f * __logf((float)C::M) + koff) * LOG2E : __builtin_inff();
     }
 };
+
+// The key-side offset of the call (0 for elu+1), a uniform scalar load.
+template <class C> __device__ __forceinline__ float key_off(const ChunkArgs &a)
+{
+    if constexpr (C::FAVOR)
+        return *a.koff;
+    else
+        return 0.f;
+}
 
 // Write this wave's feature blocks ph[fb][tb] (rows m, cols t) into F (rows t, cols m).
 template <class C>
@@ -549,10 +561,11 @@ template <class C> __device__ __forceinline__ float *slot_ptr(float *base, const
 // Stage a K tile: rows past the chunk give g = 0 (kn2 = +inf for FAVOR+, -inf
 // inputs for elu+1).
 template <class C>
-__device__ __forceinline__ void store_k_tile(typename C::Tile &rk, const typename C::XMat &xk, float *kn2, int nv)
+__device__ __forceinline__ void store_k_tile(typename C::Tile &rk, const typename C::XMat &xk, float *kn2, int nv,
+                                             float koff)
 {
     if constexpr (C::FAVOR) {
-        rk.store(xk, false, KnormFn<C>{kn2, nv});
+        rk.store(xk, false, KnormFn<C>{kn2, nv, koff});
     } else {
         rk.fill_invalid(nv, -__builtin_inff());
         rk.store(xk, false, nullptr);
@@ -614,6 +627,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StateSmem<C>), C::NW))
     const T *Kp = (const T *)a.K + G.hb, *Vp = (const T *)a.V + G.hb;
     Frag<T> wf[NFB][C::NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
+    const float koff = key_off<C>(a);
     f4 rt[NFB][NEA];
 #pragma unroll
     for (int fb = 0; fb < NFB; ++fb)
@@ -634,7 +648,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StateSmem<C>), C::NW))
             const int t0 = t00 + i * TT;
             if (t0 >= G.len) break;
             const int nv = min(TT, G.len - t0);
-            store_k_tile<C>(rk[i], xk, kn2, nv);
+            store_k_tile<C>(rk[i], xk, kn2, nv, koff);
             store_v_tile<C>(rv[i], V, nv);
             __syncthreads();
             if (t0 + 2 * TT < G.len) {  // prefetch two tiles ahead
@@ -709,14 +723,17 @@ __global__ __launch_bounds__(256) void scan_kernel(float *slots, double *carryR,
 #pragma unroll
     for (int j = 0; j < 4; ++j) tot[threadIdx.x][j] = seg[j];
     __syncthreads();
-    // totals of the segments before (and after) this one, and of all of them
-    double before[4] = {0.0, 0.0, 0.0, 0.0}, all[4] = {0.0, 0.0, 0.0, 0.0};
+    // totals of the segments before this one, after it, and of all of them (each a sum
+    // of its own segments, never a difference, so that one non-finite contribution
+    // reaches only the slices whose prefix or suffix contains it)
+    double before[4] = {0.0, 0.0, 0.0, 0.0}, after[4] = {0.0, 0.0, 0.0, 0.0}, all[4] = {0.0, 0.0, 0.0, 0.0};
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const double t = tot[h * E + el][j];
             all[j] += t;
             if (h < g) before[j] += t;
+            if (h > g) after[j] += t;
         }
     if (!active) return;
     const bool last = g == G - 1;
@@ -746,7 +763,7 @@ __global__ __launch_bounds__(256) void scan_kernel(float *slots, double *carryR,
     } else {  // MODE 2
         double run[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) run[j] = cur[j] + (all[j] - before[j] - seg[j]);
+        for (int j = 0; j < 4; ++j) run[j] = cur[j] + after[j];
         for (int n = nb - 1; n >= na; --n) {
             const f4 dl = *slot(n + 1);
             put(n + 1, run);
@@ -786,10 +803,10 @@ template <class C> struct FwdRegs {
         k.load(K + (size_t)t0 * C::D, nv);
         v.load(V + (size_t)t0 * C::D, nv);
     }
-    template <class SM> __device__ __forceinline__ void store(SM &sm, int nv)
+    template <class SM> __device__ __forceinline__ void store(SM &sm, int nv, float koff)
     {
         q.store(typename C::XMat(sm.xq), false, nullptr);
-        store_k_tile<C>(k, typename C::XMat(sm.xk), sm.kn2, nv);
+        store_k_tile<C>(k, typename C::XMat(sm.xk), sm.kn2, nv, koff);
         store_v_tile<C>(v, AugTile<C>(sm.xv, sm.xva), nv);
     }
 };
@@ -872,13 +889,14 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(FwdSmem<C>), C::NW)) v
     float *rs = a.rstat ? a.rstat + ((size_t)G.bh * a.L + G.row0) * 2 : nullptr;
     Frag<T> wf[NFB][C::NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
+    const float koff = key_off<C>(a);
     f4 rt[NFB][NEA];
     load_state_T<C>(rt, slot_ptr<C>(a.slots, a, G.bh, G.nl));
     FwdRegs<C> rg;
     rg.load(Q, K, V, 0, G.len);
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        rg.store(sm, nv);
+        rg.store(sm, nv, koff);
         __syncthreads();
         if (t0 + TT < G.len) rg.load(Q, K, V, t0 + TT, G.len);
         f4 pq[NFB][NTB];

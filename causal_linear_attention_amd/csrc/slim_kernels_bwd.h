@@ -42,6 +42,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StatsSmem<C>), C::NW))
     float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
     Frag<T> wf[NFB][NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
+    const float koff = key_off<C>(a);
     f4 rt[NFB][NEA];
     load_state_T<C>(rt, slot_ptr<C>(a.slots, a, G.bh, G.nl));
     FwdRegs<C> rg;
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StatsSmem<C>), C::NW))
     rdy.load(dY, min(TT, G.len));
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        rg.store(sm.f, nv);
+        rg.store(sm.f, nv, koff);
         rdy.store(xdy, false, nullptr);
         __syncthreads();
         if (t0 + TT < G.len) {
@@ -238,10 +239,11 @@ template <class C> struct BwdRegs {
         rs.load(st + (size_t)t0 * ROWSTAT, n);
     }
     __device__ __forceinline__ void store(const typename C::XMat &xq, const typename C::XMat &xk,
-                                          const AugTile<C> &Vt, const AugTile<C> &DN, float *kn2, float *qoff, int nv)
+                                          const AugTile<C> &Vt, const AugTile<C> &DN, float *kn2, float *qoff, int nv,
+                                          float koff)
     {
         q.store(xq, false, nullptr);
-        store_k_tile<C>(k, xk, kn2, nv);
+        store_k_tile<C>(k, xk, kn2, nv, koff);
         store_v_tile<C>(v, Vt, nv);
         dy.store(DN.x, true, nullptr);
         if (threadIdx.x < C::TT) {
@@ -341,6 +343,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
     const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
     Frag<T> wf[NFB][NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
+    const float koff = key_off<C>(a);
     f4 r[NEA][NFB];
     load_state_E<C>(r, slot_ptr<C>(a.slots, a, G.bh, G.nl));
     BwdRegs<C> rg;
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
     }
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        rg.store(xq, xk, Vt, DN, kn2, qoff, nv);
+        rg.store(xq, xk, Vt, DN, kn2, qoff, nv, koff);
         __syncthreads();
         if (t0 + TT < G.len) rg.load(Q, K, V, dY, st, t0 + TT, G.len);
         f4 pq[NFB][NTB];
@@ -541,6 +544,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
     T *pw = DW ? pw_rows<C>(a.pk, a, G) : nullptr;
     const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
     const float *gsl = slot_ptr<C>(a.gslots, a, G.bh, G.nl + 1);
+    const float koff = key_off<C>(a);
     f4 dr[NEA][NFB];                       // [dR; dS], rows e, cols m
     f4 drt[DRL ? 1 : NFB][DRL ? 1 : NEB];  // dR^T (rows m, cols e) when not copied through LDS
     load_state_E<C>(dr, gsl);
@@ -562,7 +566,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
         // issued before the tile's staging and barrier, which cover their latency
         Frag<T> wf[NFB][NEB];
         if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
-        rg.store(xq, xk, Vt, DN, kn2, qoff, nv);
+        rg.store(xq, xk, Vt, DN, kn2, qoff, nv, koff);
         __syncthreads();
         Frag<T> fq[NFB][NTB], fkT[NFB][NTB];
         {
@@ -673,9 +677,12 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                 float rsum = 0.f;
 #pragma unroll
                 for (int fb = 0; fb < NFB; ++fb) {
-                    const f4 v = dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]);
+                    // the row sum is taken over the same rounded values that enter the W^T
+                    // product, so that W^T G - k sum(G) = sum_m G_m (w_m - k) cancels
+                    // consistently for a key close to a row of W
+                    const Frag<T> gf = cfrag<T>(dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]));
+                    const f4 v = frag_to_f4<T>(gf);
                     rsum += (v[0] + v[1]) + (v[2] + v[3]);
-                    const Frag<T> gf = cfrag<T>(v);
                     Gk.put_frag(sb * 16 + lc, w * MW + fb * 16 + 4 * g, gf);
                     if constexpr (DW) store_pw<C>(pw + (size_t)t0 * C::M, sb * 16 + lc, nv, w * MW + fb * 16 + 4 * g, gf);
                 }
@@ -731,9 +738,9 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                 float rsum = 0.f;
 #pragma unroll
                 for (int fb = 0; fb < NFB; ++fb) {
-                    const f4 v = dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]);
+                    gk[fb][sb] = cfrag<T>(dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]));
+                    const f4 v = frag_to_f4<T>(gk[fb][sb]);  // as rounded for the W^T product
                     rsum += (v[0] + v[1]) + (v[2] + v[3]);
-                    gk[fb][sb] = cfrag<T>(v);
                     if constexpr (DW)
                         store_pw<C>(pw + (size_t)t0 * C::M, sb * 16 + lc, nv, w * MW + fb * 16 + 4 * g, gk[fb][sb]);
                 }

@@ -47,6 +47,22 @@
  *     (FAVOR+) or M == d (elu+1); 1 <= num_chunks <= L; L < 2^31.  Other
  *     shapes return SLIM_ERR_UNSUPPORTED.
  *   - Results are deterministic: no atomics, fixed reduction order.
+ *
+ * Key-side offset (FAVOR+; Subsection 2.1 relies on positive features for a
+ * well-defined, stable division).  exp(w_m.k - |k|^2/2) can exceed the fp32
+ * range for a W row of large norm and a key near it; since
+ * w_m.k - |k|^2/2 <= |w_m|^2/2 for every key, every call evaluates the key
+ * features as g(K) exp(-koff) with the one number
+ *     koff = max(0, max_m |w_m|^2/2 - 60)
+ * (computed on the device from W in fp32), which bounds each of them by
+ * exp(60)/sqrt(M).  A factor common to all key features cancels in Y and in
+ * dQ, dK, dV; it stays only in the states, so every state argument (R_in,
+ * S_in, R_out, S_out of the forward and the decode step) holds the state
+ * times exp(-koff), and every state-gradient argument (dR_out, dS_out,
+ * dR_in, dS_in) the gradient with respect to that scaled state.  koff depends
+ * on W alone, so calls that pass states between them with the same W agree;
+ * for W with every |w_m|^2 <= 120 (Gaussian or orthogonal draws at d <= 64)
+ * koff = 0 and the states are the plain sums.  elu+1: koff = 0.
  */
 #ifndef SLIM_H
 #define SLIM_H
@@ -88,7 +104,8 @@ typedef struct slim_desc {
     int64_t window_chunks; /* slices whose states are held at once; 0 = auto: enough for
                               about 4096 workgroups per launch, or all of them when the
                               backward's per-slice buffers for the whole sequence fit in
-                              1 GiB */
+                              1 GiB, and never more than those buffers fit in 1 GiB (the
+                              dW pass's own per-slice rows within another 1 GiB) */
     int32_t dtype;         /* slim_dtype of Q, K, V, W, Y, dY, dQ, dK, dV: SLIM_F32 or SLIM_BF16 */
     int32_t feat;          /* slim_feat */
     int32_t state_dtype;   /* element type of the states and their gradients (R_in, S_in,
@@ -106,7 +123,8 @@ slim_status slim_validate(const slim_desc *desc, int pass);
  * descriptor is invalid.  Host-only. */
 size_t slim_workspace_bytes(const slim_desc *desc, int pass);
 
-/* Slices whose states one window holds (the resolved window_chunks). */
+/* Slices whose states one window holds (the resolved window_chunks) in the forward
+ * and the plain backward; the backward with dW may hold fewer (see window_chunks). */
 int64_t slim_window_chunks(const slim_desc *desc);
 
 /* Rows per tile with which the chunk kernels walk a slice for this
@@ -125,20 +143,23 @@ slim_status slim_featmap(const slim_desc *desc, const void *X, const void *W, fl
 
 /* Forward (eq. (2) evaluated slice by slice, Subsection 3.2).
  * In : Q, K, V, W (NULL for elu+1); R_in, S_in = initial state (both NULL =
- *      zero, or both given).
- * Out: Y; R_out, S_out = final state R_L, S_L (required; R_out/S_out may not
- *      alias R_in/S_in);
+ *      zero, or both given), scaled by exp(-koff) (see "Key-side offset").
+ * Out: Y; R_out, S_out = final state R_L, S_L times exp(-koff) (required;
+ *      R_out/S_out may not alias R_in/S_in);
+ *      koff = the key-side offset of W, one fp32 value on the device (NULL =
+ *      not wanted);
  *      row_stats = per-row statistics for the backward, [B][H][L][2] fp32, or
  *      NULL = not wanted: for row l, 1/den'_l and o_l, where o_l is the query
  *      offset in the base-2 exponent domain (FAVOR+: -log2(e) max_m w_m.Q_l;
- *      elu+1: 0) and den'_l = S_l . g'(Q_l) with the query features taken as
+ *      elu+1: 0) and den'_l = S'_l . g'(Q_l) with the scaled state S'_l =
+ *      S_l exp(-koff) and the query features taken as
  *      g'(Q_l)_m = exp(w_m.Q_l) 2^o_l (FAVOR+; elu+1: g itself), i.e.
- *      den_l = den'_l exp(-o_l ln 2 - |Q_l|^2/2) / sqrt(M).  8 bytes per row,
- *      the analogue of the log-sum-exp kept by softmax attention.
+ *      den_l = den'_l exp(koff - o_l ln 2 - |Q_l|^2/2) / sqrt(M).  8 bytes per
+ *      row, the analogue of the log-sum-exp kept by softmax attention.
  * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_FWD). */
 slim_status slim_attn_fwd(const slim_desc *desc, const void *Q, const void *K, const void *V, const void *W,
-                          const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, float *row_stats,
-                          void *ws, size_t ws_bytes, void *stream);
+                          const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, float *koff,
+                          float *row_stats, void *ws, size_t ws_bytes, void *stream);
 
 /* Backward of the loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out> of the
  * forward above (Subsection 3.3: a reverse walk over the slices that recomputes
@@ -163,6 +184,9 @@ slim_status slim_attn_fwd(const slim_desc *desc, const void *Q, const void *K, c
  *      batch rows and heads (they share W), overwritten; NULL = not wanted.
  *      g depends on W only through w_m, with d g(x)_m / d w_m = g(x)_m x, so
  *      dW[m] = sum over the query and key rows x of (dL/dg(x)_m) g(x)_m x.
+ *      The key-side offset is held constant: exact whenever koff = 0, and for
+ *      states handed between calls with the same W (its factor cancels
+ *      between the call that scales a state and the call that reads it).
  *      FAVOR+ only (SLIM_ERR_UNSUPPORTED for elu+1).  Deterministic: the
  *      per-row products are summed in a fixed order.
  * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_BWD),
@@ -187,8 +211,10 @@ slim_status slim_attn_bwd(const slim_desc *desc, const void *Q, const void *K, c
  *       features in fp32).
  * In : q, k, v [B][H][d] (desc dtype); W as in the forward (NULL for elu+1);
  *      R_in [B][H][d][M], S_in [B][H][M] (state_dtype) = the state before the
- *      token (both NULL = zero, i.e. the first token, or both given).
- * Out: y [B][H][d]; R_out, S_out = the state after the token (required).
+ *      token, times exp(-koff) like every state argument (both NULL = zero,
+ *      i.e. the first token, or both given).
+ * Out: y [B][H][d]; R_out, S_out = the state after the token, scaled likewise
+ *      (required).
  *      R_out may be the same pointer as R_in and S_out as S_in (update in
  *      place); no other overlap of inputs and outputs is allowed.
  * No workspace.  Two calls that update the same state must be ordered (same

@@ -96,4 +96,4 @@ def loss_and_grads(params: dict, tokens: np.ndarray, heads: int, layers: int, tr
     logp = logits - torch.logsumexp(logits, dim=-1, keepdim=True)
     loss = -logp.gather(-1, tok[:, 1:, None]).sum()
     loss.backward()
-    return float(loss), {n: t.grad.numpy().copy() for n, t in P.items() if t.requires_grad}
+    return float(loss.detach()), {n: t.grad.numpy().copy() for n, t in P.items() if t.requires_grad}

@@ -494,13 +494,61 @@ def pin_bwd_quadratic_equals_prefix():
             assert _relerr(x, y) < 1e-11, feat
 
 
+def pin_performer_ref_loss_by_hand():
+    # The model reference's loss on a one-layer, d_model = 2 model whose parameters make
+    # every step a closed form (page "Sub-Linear Memory: How to Make Performers SLiM",
+    # Subsection 2.2, eq. (5)-(10), in the reading the reference takes):
+    #  * LN1 with zero gain gives the bias beta at every position, so Q, K, V are the
+    #    same at every position and attention returns V itself, c = beta W_V, whatever
+    #    W_Q, W_K and the features (Y_l is a weighted average of equal values);
+    #  * LN2 (gain 1, bias 0) of a 2-vector [a, b] is s [1, -1] with
+    #    s = ((a - b)/2) / sqrt(((a - b)/2)^2 + 1e-5), the biased variance being ((a-b)/2)^2;
+    #  * W1 = W2 = I and b1 = 0 leave the FFN as GeLU (exact, erf) of that, plus b2;
+    #  * the loss sums, over l = 1 .. L-1, logsumexp(z_l) - z_l[p_{l+1}] with
+    #    z_l = X_l W_out + b_out, positions from 1: pos(l) = [sin l, cos l].
+    # Written with scalars (math), it fails on: positions from 0, a target not shifted,
+    # a mean instead of the sum, the unbiased variance, a tanh GeLU, W_V transposed, a
+    # missing residual.
+    import math
+
+    from oracle import performer_ref
+    emb = [[0.3, -0.2], [0.1, 0.4], [-0.5, 0.25]]
+    beta, wv = [0.6, -0.3], [[1.0, 0.5], [0.2, -1.0]]
+    b2 = [0.05, -0.1]
+    wout, bout = [[1.0, -1.0, 0.5], [0.0, 2.0, -1.0]], [0.1, 0.0, -0.2]
+    tokens = [2, 0, 1]
+    params = {
+        "emb": np.array(emb), "ln1_g.0": np.zeros(2), "ln1_b.0": np.array(beta),
+        "wq.0": np.array([[0.2, 0.1], [-0.3, 0.4]]), "wk.0": np.array([[0.7, -0.2], [0.1, 0.3]]),
+        "wv.0": np.array(wv), "wf.0": np.array([[0.5, -0.5], [1.0, 0.2]]),
+        "ln2_g.0": np.ones(2), "ln2_b.0": np.zeros(2), "w1.0": np.eye(2), "b1.0": np.zeros(2),
+        "w2.0": np.eye(2), "b2.0": np.array(b2), "wout": np.array(wout), "bout": np.array(bout),
+    }
+    got, _ = performer_ref.loss_and_grads(params, np.array([tokens]), heads=1, layers=1)
+
+    c = [beta[0] * wv[0][j] + beta[1] * wv[1][j] for j in range(2)]  # the attention output
+
+    def gelu(x):
+        return 0.5 * x * (1.0 + math.erf(x / math.sqrt(2.0)))
+
+    want = 0.0
+    for l in (1, 2):
+        x1 = [emb[tokens[l - 1]][j] + (math.sin(l), math.cos(l))[j] + c[j] for j in range(2)]
+        h = (x1[0] - x1[1]) / 2.0
+        s = h / math.sqrt(h * h + 1e-5)
+        x2 = [x1[0] + gelu(s) + b2[0], x1[1] + gelu(-s) + b2[1]]
+        z = [x2[0] * wout[0][v] + x2[1] * wout[1][v] + bout[v] for v in range(3)]
+        want += math.log(sum(math.exp(zv) for zv in z)) - z[tokens[l]]
+    assert abs(got - want) <= 1e-12 * abs(want), (got, want)
+
+
 ALL_PINS = [
     pin_featmap_golden, pin_featmap_zero_input, pin_elu1_values, pin_favor_unbiased,
     pin_featmap_vjp_fd, pin_featmap_wgrad_fd, pin_fwd_golden, pin_single_row_is_value, pin_identical_keys_give_running_mean,
     pin_constant_values, pin_causality, pin_convex_hull, pin_quadratic_equals_prefix,
     pin_initial_state_is_a_prefix, pin_rows_match_full, pin_decode_golden, pin_decode_steps_equal_quadratic,
     pin_decode_first_token_is_value, pin_performer_ref_finite_differences, pin_performer_ref_feature_gradients,
-    pin_performer_ref_no_target,
+    pin_performer_ref_no_target, pin_performer_ref_loss_by_hand,
     pin_softmax_special_cases,
     pin_favor_converges_to_softmax, pin_bwd_finite_differences, pin_bwd_dw_finite_differences,
     pin_dw_rotation_symmetry, pin_bwd_special_cases, pin_bwd_quadratic_equals_prefix,

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.slim_version() >> 16 == 2 and lib.slim_version() & 0xffff >= 1
+    assert lib.slim_version() >> 16 == 3
     for code in range(8):
         assert lib.slim_status_string(code)
     assert lib.slim_status_string(0) == b"ok"
@@ -74,7 +74,8 @@ def test_validate_null(lib):
     assert lib.slim_validate(None, 1) == 1
 
 
-FWD_ARGS = ("Q", "K", "V", "W", "R_in", "S_in", "Y", "R_out", "S_out", "row_stats", "ws", "ws_bytes", "stream")
+FWD_ARGS = ("Q", "K", "V", "W", "R_in", "S_in", "Y", "R_out", "S_out", "koff", "row_stats", "ws", "ws_bytes",
+            "stream")
 BWD_ARGS = ("Q", "K", "V", "W", "dY", "Y", "row_stats", "R_in", "S_in", "dR_out", "dS_out", "dQ", "dK", "dV",
             "dR_in", "dS_in", "dW", "ws", "ws_bytes", "stream")
 P = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
@@ -104,6 +105,7 @@ def test_entry_points_reject_before_any_launch(lib):
     bad = ctypes.c_void_p((1 << 20) + 4)
     assert fwd(lib, d, Q=bad) == 6
     assert fwd(lib, d, row_stats=bad) == 6
+    assert fwd(lib, d, koff=ctypes.c_void_p((1 << 20) + 2)) == 6
     assert bwd(lib, d_(num_chunks=0)) == 2
     # only one of the paired initial-state pointers
     assert fwd(lib, d, R_in=P) == 1
@@ -134,6 +136,28 @@ def test_dw_pass_validation(lib):
     # bounded by the window, not by L
     big = [ws(lib, DW, B=1, H=8, L=n, d=64, M=64, num_chunks=n // 512, window_chunks=64) for n in (1 << 16, 1 << 20)]
     assert big[0] == big[1]
+
+
+@pytest.mark.parametrize("dtype", [_lib.SLIM_F32, _lib.SLIM_BF16])
+def test_automatic_window_bounds_every_pass(lib, dtype):
+    # the automatic window keeps each pass's per-slice buffers within 1 GiB (with dW the
+    # two rows of dg(X) . g(X) per slice row within another 1 GiB), for any L at a given
+    # slice length
+    GiB = 1 << 30
+    for c in (512, 4096):
+        sizes = {}
+        for p in (_lib.SLIM_PASS_FWD, _lib.SLIM_PASS_BWD, _lib.SLIM_PASS_BWD_DW):
+            sizes[p] = [ws(lib, p, dtype=dtype, B=1, H=8, L=n, d=64, M=256, num_chunks=n // c)
+                        for n in (1 << 16, 1 << 20, 1 << 22, 1 << 24)]
+            # per-slice buffers within the budget, plus what does not grow with L: the
+            # carries, W^T and the dW partial sums (at most about 1024 fp32 [M][d] blocks)
+            budget = (2 if p == _lib.SLIM_PASS_BWD_DW else 1) * GiB
+            assert max(sizes[p]) <= budget + (192 << 20), (c, p, sizes[p])
+            # constant once L is past what fits whole
+            assert sizes[p][-1] == sizes[p][-2], (c, p, sizes[p])
+    # a few long slices of many rows: the window shrinks to what fits (at least one slice)
+    one = ws(lib, _lib.SLIM_PASS_BWD_DW, dtype=dtype, B=1, H=1, L=1 << 22, d=64, M=256, num_chunks=1024)
+    assert 0 < one <= 2 * GiB + (192 << 20)
 
 
 def test_dw_rejects_before_any_launch(lib):

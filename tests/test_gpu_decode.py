@@ -3,15 +3,17 @@
 The oracle's decode step is its prefix-sum recurrence run over one position
 (page "Sub-Linear Memory: How to Make Performers SLiM", Subsection 2.1,
 eq. (3)-(4)); it receives exactly the values the GPU received (io-dtype
-inputs, the fp32 state).  Outputs y are compared normwise per head at the
-io dtype's tolerance; the fp32 states at 1e-5.
+inputs, the fp32 state).  Outputs y are checked at the io dtype's tolerance,
+the fp32 states at 1e-5 (gpu_util.check: normwise, max-abs/max-ref, worst row).
+States cross the boundary times exp(-koff), the key-side offset of W: the
+oracle gets them multiplied back by exp(koff), and so are the results.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import DT, TOL, host64, inputs, relerr_heads
+from gpu_util import DT, TOL, check, gpu_koff, host64, inputs, relerr_heads
 from causal_linear_attention_amd import attention as A
 
 pytestmark = pytest.mark.gpu
@@ -42,10 +44,12 @@ def _token(B, H, d, M, dt, feat, seed, scale=None):
 
 
 def _state(B, H, d, M, dt, feat, seed, W, L=12):
-    """A state reached by a real prefix of L tokens (fp32 on the device)."""
+    """A state reached by a real prefix of L tokens (fp32 on the device), scaled by
+    exp(-koff) as the library holds states."""
     t = inputs(B, H, L, d, M, DT[dt], feat, seed=seed, dy=False)
     _, _, R, S = oracle.attn_fwd(t["q"], t["k"], t["v"], W, feat, form="prefix")
-    return (torch.from_numpy(R).float().cuda().contiguous(), torch.from_numpy(S).float().cuda().contiguous())
+    sc = np.exp(-gpu_koff(W))
+    return (torch.from_numpy(R * sc).float().cuda().contiguous(), torch.from_numpy(S * sc).float().cuda().contiguous())
 
 
 @pytest.mark.parametrize("case", CASES, ids=_ids)
@@ -56,10 +60,11 @@ def test_decode_step_matches_oracle(case):
     R, S = _state(B, H, d, M, dt, feat, 32, W)
     y, R2, S2 = A.decode_step(q, k, v, W, feat, R, S)
     torch.cuda.synchronize()
-    yo, Ro, So = oracle.decode_step(q, k, v, W, feat, host64(R), host64(S))
-    assert relerr_heads(host64(y), yo) < TOL[DT[dt]]
-    assert relerr_heads(host64(R2), Ro) < TOL_STATE
-    assert relerr_heads(host64(S2), So) < TOL_STATE
+    sc = np.exp(gpu_koff(W))
+    yo, Ro, So = oracle.decode_step(q, k, v, W, feat, host64(R) * sc, host64(S) * sc)
+    check(("decode y", case), host64(y), yo, TOL[DT[dt]])
+    check(("decode R", case), host64(R2) * sc, Ro, TOL_STATE)
+    check(("decode S", case), host64(S2) * sc, So, TOL_STATE)
     # inputs untouched (not in place)
     assert torch.equal(R, _state(B, H, d, M, dt, feat, 32, W)[0])
 
@@ -75,10 +80,10 @@ def test_first_token_gives_its_value(dt, feat):
     if dt == "bf16":  # v (1 + O(1e-7)) rounds back to v
         assert torch.equal(y, v)
     else:
-        assert relerr_heads(host64(y), host64(v)) < 1e-6
+        check(("first token y = v", feat), host64(y), host64(v), 1e-6)
     _, Ro, So = oracle.decode_step(q, k, v, W, feat)
-    assert relerr_heads(host64(R), Ro) < TOL_STATE
-    assert relerr_heads(host64(S), So) < TOL_STATE
+    check(("first token R", dt, feat), host64(R), Ro, TOL_STATE)
+    check(("first token S", dt, feat), host64(S), So, TOL_STATE)
 
 
 @pytest.mark.parametrize("dt,feat,d,M", [("bf16", "favor", 64, 256), ("f32", "favor", 32, 64),
@@ -101,9 +106,10 @@ def test_decode_run_equals_chunked_forward_and_oracle(dt, feat, d, M):
     torch.cuda.synchronize()
     Yo, _, Ro, So = oracle.attn_fwd(t["q"], t["k"], t["v"], t["W"], feat, R0=host64(R0), S0=host64(S0))
     tol = TOL[DT[dt]]
-    assert relerr_heads(host64(Yd), Yo) < tol
-    assert relerr_heads(host64(Yc), Yo) < tol
-    assert relerr_heads(host64(R), Ro) < TOL_STATE and relerr_heads(host64(S), So) < TOL_STATE
+    check(("decode run Y", dt, feat, d, M), host64(Yd), Yo, tol)
+    check(("chunked Y", dt, feat, d, M), host64(Yc), Yo, tol)
+    check(("decode run R", dt, feat, d, M), host64(R), Ro, TOL_STATE)
+    check(("decode run S", dt, feat, d, M), host64(S), So, TOL_STATE)
     # the chunked forward multiplies bf16 copies of the features on the matrix cores, so
     # its state carries bf16 rounding; the decode step keeps them in fp32
     assert relerr_heads(host64(R), host64(Rc)) < tol
@@ -129,7 +135,7 @@ def test_wide_query_range():
     torch.cuda.synchronize()
     assert torch.isfinite(y).all()
     yo, _, _ = oracle.decode_step(q, k, v, W, "favor", host64(R), host64(S))
-    assert relerr_heads(host64(y), yo) < 1e-4
+    check("wide query range y", host64(y), yo, 1e-4)
 
 
 def test_many_heads():
@@ -143,8 +149,9 @@ def test_many_heads():
     idx = np.random.default_rng(0).choice(B * H, 64, replace=False)
     sel = lambda x: host64(x).reshape((B * H,) + tuple(x.shape[2:]))[idx][:, None]  # noqa: E731
     yo, Ro, So = oracle.decode_step(sel(q), sel(k), sel(v), W, "favor", sel(R), sel(S))
-    assert relerr_heads(sel(y), yo) < TOL[torch.bfloat16]
-    assert relerr_heads(sel(R2), Ro) < TOL_STATE and relerr_heads(sel(S2), So) < TOL_STATE
+    check("many heads y", sel(y), yo, TOL[torch.bfloat16])
+    check("many heads R", sel(R2), Ro, TOL_STATE)
+    check("many heads S", sel(S2), So, TOL_STATE)
 
 
 @pytest.mark.parametrize("dt,feat,d,M", [("bf16", "favor", 64, 256), ("f32", "favor", 16, 32),
@@ -159,15 +166,18 @@ def test_fp64_state_matches_oracle(dt, feat, d, M):
     y, R2, S2 = A.decode_step(q, k, v, W, feat, R, S)
     torch.cuda.synchronize()
     assert R2.dtype == torch.float64 and S2.dtype == torch.float64
-    yo, Ro, So = oracle.decode_step(q, k, v, W, feat, host64(R), host64(S))
-    assert relerr_heads(host64(y), yo) < TOL[DT[dt]]
-    assert relerr_heads(host64(R2), Ro) < TOL_STATE and relerr_heads(host64(S2), So) < TOL_STATE
+    sc = np.exp(gpu_koff(W))
+    yo, Ro, So = oracle.decode_step(q, k, v, W, feat, host64(R) * sc, host64(S) * sc)
+    check(("fp64 decode y", dt, feat, d, M), host64(y), yo, TOL[DT[dt]])
+    check(("fp64 decode R", dt, feat, d, M), host64(R2) * sc, Ro, TOL_STATE)
+    check(("fp64 decode S", dt, feat, d, M), host64(S2) * sc, So, TOL_STATE)
     # the first token, with the state dtype asked for
     y1, R1, S1 = A.decode_step(q, k, v, W, feat, state_dtype=torch.float64)
     torch.cuda.synchronize()
     assert R1.dtype == torch.float64
     _, Ro1, So1 = oracle.decode_step(q, k, v, W, feat)
-    assert relerr_heads(host64(R1), Ro1) < TOL_STATE and relerr_heads(host64(S1), So1) < TOL_STATE
+    check(("fp64 first token R", dt, feat, d, M), host64(R1) * sc, Ro1, TOL_STATE)
+    check(("fp64 first token S", dt, feat, d, M), host64(S1) * sc, So1, TOL_STATE)
 
 
 def test_fp64_state_keeps_small_increments():
@@ -183,8 +193,8 @@ def test_fp64_state_keeps_small_increments():
     torch.cuda.synchronize()
     _, Ro, So = oracle.decode_step(q, k, v, W, "favor", host64(R), host64(S))
     inc_o = Ro - host64(R)
-    assert relerr_heads(host64(R2) - host64(R), inc_o) < 1e-5
-    assert relerr_heads(host64(S2) - host64(S), So - host64(S)) < 1e-5
+    check("fp64 increment R", host64(R2) - host64(R), inc_o, 1e-5)
+    check("fp64 increment S", host64(S2) - host64(S), So - host64(S), 1e-5)
     # the fp32 state loses it (its spacing at 3e8 is 32, the increments are O(1))
     assert relerr_heads(host64(R2f) - host64(R.float()), inc_o) > 1e-1
 
@@ -205,6 +215,8 @@ def test_fp64_decode_run_equals_fp64_chunked_forward():
     assert Rc.dtype == torch.float64
     Yo, _, Ro, So = oracle.attn_fwd(t["q"], t["k"], t["v"], t["W"], "favor", R0=host64(R0), S0=host64(S0))
     tol = TOL[torch.bfloat16]
-    assert relerr_heads(host64(Yd), Yo) < tol and relerr_heads(host64(Yc), Yo) < tol
-    assert relerr_heads(host64(R), Ro) < TOL_STATE and relerr_heads(host64(S), So) < TOL_STATE
+    check("fp64 decode run Y", host64(Yd), Yo, tol)
+    check("fp64 chunked Y", host64(Yc), Yo, tol)
+    check("fp64 decode run R", host64(R), Ro, TOL_STATE)
+    check("fp64 decode run S", host64(S), So, TOL_STATE)
     assert relerr_heads(host64(R), host64(Rc)) < tol and relerr_heads(host64(S), host64(Sc)) < tol

@@ -13,6 +13,7 @@ import torch
 
 from causal_linear_attention_amd import synth
 from causal_linear_attention_amd.performer import Performer
+from gpu_util import check
 from oracle import performer_ref
 
 pytestmark = pytest.mark.gpu
@@ -67,6 +68,8 @@ def test_full_pass_matches_fp64_reference():
     g = _grads(m)
     assert abs(float(loss) - ref_loss) <= 1e-5 * abs(ref_loss)
     assert _relerr(g, ref) < 1e-5, _worst(g, ref)
+    for n in ref:  # each parameter's gradient, element by element, at the fp32 bounds
+        check(("full pass", n), g[n], ref[n], 1e-4)
 
 
 @pytest.mark.parametrize("C", [256, 64, 16, 1])
@@ -90,6 +93,8 @@ def test_algorithm1_matches_full_pass_and_reference(C):
     print("discrepancy vs full pass %.2e, vs fp64 reference %.2e" % (_relerr(gc, gf), _relerr(gc, ref)))
     assert _relerr(gc, gf) < 1e-5, _worst(gc, gf)
     assert _relerr(gc, ref) < 1e-5, _worst(gc, ref)
+    for n in ref:
+        check(("algorithm 1", C, n), gc[n], ref[n], 1e-4)
 
 
 def test_algorithm1_ragged_last_slice():
@@ -120,3 +125,5 @@ def test_algorithm1_with_trainable_features(C):
           (_relerr(gc, ref), _relerr({n: gc[n] for n in ("wf.0", "wf.1")}, {n: ref[n] for n in ("wf.0", "wf.1")})))
     assert _relerr(gc, ref) < 1e-5, _worst(gc, ref)
     assert _relerr({n: gc[n] for n in ("wf.0", "wf.1")}, {n: ref[n] for n in ("wf.0", "wf.1")}) < 1e-5
+    for n in ref:
+        check(("algorithm 1 with trainable features", C, n), gc[n], ref[n], 1e-4)
