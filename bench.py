@@ -55,6 +55,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-mem-sweep", action="store_true", help="skip the peak-HBM-vs-L rows of the JSON line")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU oracle sample (0 = H)")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
@@ -188,9 +189,29 @@ def make_inputs(w, torch, synth):
     return q, k, v, W, dy
 
 
+def host_cpu():
+    """The host's logical CPU count and model name (from /proc/cpuinfo)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
+QUAD_SAMPLE_ROWS = 16
+
+
 def cpu_baseline(w, synth, heads):
     """The fp64 oracle's linear-time (prefix) form, fwd+bwd, on batch row 0 and
-    `heads` heads at full length, one thread per head."""
+    `heads` heads at full length, one thread per head; beside it, the oracle's
+    quadratic form (the definition, eq. (2)) timed on QUAD_SAMPLE_ROWS evenly spaced
+    rows of one head (its cost per row grows with the row index, so the sample mean
+    is the mean over all rows) and extrapolated to the forward of every row."""
     import numpy as np
 
     import oracle
@@ -211,10 +232,21 @@ def cpu_baseline(w, synth, heads):
     dt = time.perf_counter() - t0
     # one token needs all H heads: a sample of `heads` heads covers heads/H of L tokens
     tok = w.L * heads / w.H
+    rows = (np.arange(QUAD_SAMPLE_ROWS) * w.L) // QUAD_SAMPLE_ROWS + w.L // (2 * QUAD_SAMPLE_ROWS)
+    t1 = time.perf_counter()
+    oracle.attn_fwd_rows(q[0, 0], k[0, 0], v[0, 0], W, rows, w.feat)
+    dq = time.perf_counter() - t1
+    quad_fwd_s = dq / QUAD_SAMPLE_ROWS * w.L * w.H  # every row of every head of one batch row, one thread
+    ncpu, model = host_cpu()
     return {"value": tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle, iterative prefix-sum form, fwd+bwd of batch row 0, {heads} of {w.H} heads, "
                       f"full L={w.L}, one thread per head ({dt:.1f} s); tokens credited = L*{heads}/{w.H}",
-            "seconds": dt}
+            "seconds": dt, "host_logical_cpus": ncpu, "host_cpu_model": model,
+            "quadratic_fwd": {"value": w.L / quad_fwd_s, "unit": "tokens/s", "threads": 1,
+                              "sample": f"fp64 oracle, quadratic form (the definition), forward of "
+                                        f"{QUAD_SAMPLE_ROWS} evenly spaced rows of one head ({dq:.1f} s), "
+                                        f"extrapolated to all {w.L} rows x {w.H} heads of one batch row",
+                              "extrapolated": True}}
 
 
 MEM_SWEEP_WINDOW = 512
@@ -505,19 +537,26 @@ def algorithm1_sweep(torch, synth):
             "full_ms": round(ms_f, 1), "full_peak_bytes": mem_f, "rows": rows}
 
 
-def kernel_records(w, prof, steps, tile):
+DW_PASS_KERNELS = ("bwdq_dw", "bwdq_gstate_dw", "bwdkv_dw", "dw", "dw_sum")
+
+
+def kernel_records(w, prof, steps, tile, nwin):
     """Per-kernel records from the library's hipEvent timings {name: (ms total, launches)}
-    over `steps` steps, and the roofline record of the dominant kernel."""
+    over `steps` steps, and the roofline record of the dominant kernel.  Every chunk and
+    scan kernel is launched once per window and covers that window's slices, so one
+    launch processes head_tokens / (windows of its pass) token-heads; nwin = windows of
+    the forward and plain backward, and the dW pass's are counted from its row
+    contraction, launched once per window."""
     from causal_linear_attention_amd.workloads import kernel_bytes, kernel_flops
     fl = kernel_flops(w, tile)
     by = kernel_bytes(w)
-    passes = {"state": 2 if w.backward else 1}
+    nwin_dw = prof["dw"][1] / steps if "dw" in prof else nwin
     peak_t = PEAK_TFLOPS[w.dtype]
     kernels = {}
     for name, (ms, n) in prof.items():
-        rec = {"ms_total": round(ms, 4), "launches": n, "ms_avg": round(ms / n, 5),
-               "ms_per_step": round(ms / steps, 5)}
-        units = w.head_tokens * passes.get(name, 1) * steps / n  # token-heads per launch
+        rec = {"ms_total": round(ms, 4), "launches": n, "launches_per_step": round(n / steps, 3),
+               "ms_avg": round(ms / n, 5), "ms_per_step": round(ms / steps, 5)}
+        units = w.head_tokens / (nwin_dw if name in DW_PASS_KERNELS else nwin)  # token-heads per launch
         if name in fl:
             rec["flop_per_launch"] = fl[name] * units
             rec["tflops"] = round(rec["flop_per_launch"] / (rec["ms_avg"] * 1e-3) / 1e12, 2)
@@ -665,7 +704,11 @@ def main():
 
     ms_step = 1e3 * elapsed / args.steps
     tokens_per_s = w.tokens * args.steps / elapsed
-    kernels, roofline = kernel_records(w, prof, args.steps, tile)
+    dsc = A.make_desc(q, w.M, w.feat, w.chunks)
+    window = int(_lib.lib().slim_window_chunks(__import__("ctypes").byref(dsc)))
+    nchunks = -(-w.L // -(-w.L // w.chunks))  # slices actually used: ceil(L / ceil(L / chunks))
+    nwin = -(-nchunks // window)
+    kernels, roofline = kernel_records(w, prof, args.steps, tile, nwin)
     isz = 2 if w.dtype == "bf16" else 4
     # minimum HBM traffic of a step: read Q K V (fwd) and Q K V dY (bwd), write Y dQ dK dV
     io = w.head_tokens * w.d * isz * (11 if w.backward else 4)
@@ -680,8 +723,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "M": w.M, "feat": w.feat,
                    "W": w.w_kind, "chunks": w.chunks, "chunk_len": w.chunk_len, "tile": tile,
-                   "window_chunks": int(_lib.lib().slim_window_chunks(
-                       __import__("ctypes").byref(A.make_desc(q, w.M, w.feat, w.chunks)))),
+                   "window_chunks": window, "windows": nwin,
                    "dW": want_dw, "global_batch": w.B, "seq_len": w.L, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "step_tflops": round(step_flop / (ms_step * 1e-3) / 1e12, 2),
@@ -691,6 +733,16 @@ def main():
         "io_footprint_bytes": footprint,
         "kernels": kernels,
     }
+    if not args.no_mem_sweep:
+        # the sub-linear memory claim, measured in the same run: peak HBM of one fwd+bwd
+        # step vs L at the 1M-token workload's shape (fixed window of 512 slices)
+        del q, k, v, W, dy
+        torch.cuda.empty_cache()
+        sw = mem_sweep(torch, A, synth, WORKLOADS["favor_bf16_L1048576_d64_M64"])
+        rec["peak_hbm_vs_L"] = {k2: sw[k2] for k2 in ("mem_sweep", "B", "H", "d", "M", "chunk_len")}
+        rec["peak_hbm_vs_L"]["window_chunks"] = MEM_SWEEP_WINDOW
+        rec["peak_hbm_vs_L"]["rows"] = [{k2: r[k2] for k2 in ("L", "step_peak_bytes", "outputs_bytes",
+                                                              "beyond_io_bytes")} for r in sw["rows"]]
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_heads or w.H)
     print(json.dumps(rec))

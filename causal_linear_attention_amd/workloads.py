@@ -163,6 +163,7 @@ def kernel_bytes(w: Workload) -> dict:
     return {
         "state": 2 * row + slot,                    # K, V -> chunk state
         "scan_prefix": 2 * slot, "scan_reverse": 2 * slot, "scan_grad": 2 * slot,  # slots in place
+        "scan_window": 2 * slot, "scan_sum": slot,  # several windows: start states; the final-state sweep
         # Q, K, V, entry state -> Y, and (a step with a backward) 8 bytes of row statistics
         "fwd": 3 * row + slot + row + (8 if w.backward else 0),
         "stats": 4 * row + slot + st,               # Q, K, V, dY, entry state -> row statistics

@@ -22,7 +22,7 @@ def test_roofline_record_of_the_dominant_kernel():
     prof = {"state": (0.46, 2 * steps), "scan_prefix": (0.19, 2 * steps), "fwd": (1.1, steps),
             "rowstat": (0.22, steps), "bwdq_gstate": (1.8, steps), "scan_grad": (0.2, steps),
             "bwdkv": (2.24, steps)}
-    kernels, roof = bench.kernel_records(w, prof, steps, 32)
+    kernels, roof = bench.kernel_records(w, prof, steps, 32, 1)
     assert roof["kernel"] == "bwdkv"
     d = kernels["bwdkv"]
     assert d["ms_avg"] == pytest.approx(0.56)
@@ -35,8 +35,25 @@ def test_roofline_record_of_the_dominant_kernel():
     assert t_hbm > t_mfma and roof["bound"] == "hbm" and roof["unit"] == "GB/s"
     assert roof["achieved"] == pytest.approx(d["bytes_per_launch"] / 0.56e-3 / 1e9, rel=1e-3)
     assert roof["frac"] == pytest.approx(roof["achieved"] / 8000.0, rel=1e-3)
-    # the state kernel runs in both passes: its launches each cover all rows too
+    # the state kernel and the prefix scan run in both passes: their launches each cover
+    # all rows too (one window)
     assert kernels["state"]["bytes_per_launch"] == pytest.approx(kernel_bytes(w)["state"] * units)
+    assert kernels["scan_prefix"]["bytes_per_launch"] == pytest.approx(kernel_bytes(w)["scan_prefix"] * units)
+    assert kernels["scan_prefix"]["launches_per_step"] == 2
+
+
+def test_units_per_launch_with_several_windows():
+    # four windows: each launch of a chunk or scan kernel covers a quarter of the rows;
+    # the dW pass's window count comes from its row contraction's launches
+    w = WORKLOADS[HEADLINE]
+    steps = 2
+    prof = {"state": (1.0, 3 * 4 * steps), "scan_sum": (0.1, 4 * steps), "scan_window": (0.1, 4 * steps),
+            "fwd": (1.0, 4 * steps), "bwdkv_dw": (2.0, 2 * steps), "dw": (0.5, 2 * steps)}
+    kernels, _ = bench.kernel_records(w, prof, steps, 32, 4)
+    units = w.B * w.H * w.L
+    assert kernels["fwd"]["bytes_per_launch"] == pytest.approx(kernel_bytes(w)["fwd"] * units / 4)
+    assert kernels["state"]["bytes_per_launch"] == pytest.approx(kernel_bytes(w)["state"] * units / 4)
+    assert kernels["bwdkv_dw"]["bytes_per_launch"] == pytest.approx(kernel_bytes(w)["bwdkv_dw"] * units / 2)
 
 
 def _counter_csv(path, rows):
