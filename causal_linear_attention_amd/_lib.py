@@ -14,12 +14,13 @@ LIB_PATH = os.path.join(_HERE, "libslim.so")
 SLIM_F32, SLIM_BF16, SLIM_F64 = 0, 1, 2
 SLIM_FEAT_FAVOR, SLIM_FEAT_ELU1 = 0, 1
 SLIM_PASS_FEATMAP, SLIM_PASS_FWD, SLIM_PASS_BWD, SLIM_PASS_DECODE, SLIM_PASS_BWD_DW = 0, 1, 2, 3, 4
+SLIM_NOALLOC_SCRATCH_BYTES = 64 << 20
 STATUS = {0: "SLIM_OK", 1: "SLIM_ERR_NULL", 2: "SLIM_ERR_SHAPE", 3: "SLIM_ERR_DTYPE",
           4: "SLIM_ERR_UNSUPPORTED", 5: "SLIM_ERR_WORKSPACE", 6: "SLIM_ERR_ALIGN", 7: "SLIM_ERR_HIP"}
 
 # every symbol declared in include/slim.h
 EXPORTS = ["slim_validate", "slim_workspace_bytes", "slim_window_chunks", "slim_tile_rows", "slim_featmap", "slim_attn_fwd",
-           "slim_attn_bwd", "slim_decode_step", "slim_status_string", "slim_version", "slim_prof_enable", "slim_prof_count",
+           "slim_attn_fwd_noalloc", "slim_attn_bwd", "slim_decode_step", "slim_status_string", "slim_version", "slim_prof_enable", "slim_prof_count",
            "slim_prof_entry"]
 
 
@@ -62,6 +63,8 @@ def lib(path: str | None = None):
     L.slim_featmap.restype = i32
     L.slim_attn_fwd.argtypes = [D] + [vp] * 12 + [sz, vp]
     L.slim_attn_fwd.restype = i32
+    L.slim_attn_fwd_noalloc.argtypes = [D] + [vp] * 12
+    L.slim_attn_fwd_noalloc.restype = i32
     L.slim_attn_bwd.argtypes = [D] + [vp] * 18 + [sz, vp]
     L.slim_attn_bwd.restype = i32
     L.slim_decode_step.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]

@@ -113,6 +113,47 @@ def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, 
     return Y, R, S
 
 
+def attn_fwd_noalloc(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, window_chunks=0,
+                     state_dtype=None, want_row_stats=False, koff_out=None, out=None):
+    """attn_fwd through slim_attn_fwd_noalloc: the library allocates no workspace (it
+    works in its own fixed device array).  out: optional (Y, R_out, S_out[, row_stats])
+    tensors to write into, so that a caller can avoid every allocation; else they are
+    allocated here.  Same results as attn_fwd."""
+    B, H, L, d = q.shape
+    M = _feat_M(W, feat, d)
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_io(n, t, q.dtype, q.shape)
+    if W is not None:
+        _check_io("W", W, q.dtype, (M, d))
+    sd = R_in.dtype if R_in is not None else (state_dtype or torch.float32)
+    if R_in is not None:
+        _check_io("R_in", R_in, sd, (B, H, d, M))
+        _check_io("S_in", S_in, sd, (B, H, M))
+    dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd)
+    if out is None:
+        Y = torch.empty_like(q)
+        R = torch.empty((B, H, d, M), dtype=sd, device=q.device)
+        S = torch.empty((B, H, M), dtype=sd, device=q.device)
+        rs = torch.empty((B, H, L, 2), dtype=torch.float32, device=q.device) if want_row_stats else None
+    else:
+        Y, R, S = out[:3]
+        rs = out[3] if len(out) > 3 else None
+        _check_io("Y", Y, q.dtype, q.shape)
+        _check_io("R_out", R, sd, (B, H, d, M))
+        _check_io("S_out", S, sd, (B, H, M))
+        if rs is not None:
+            _check_io("row_stats", rs, torch.float32, (B, H, L, 2))
+    if koff_out is not None:
+        _check_io("koff_out", koff_out, torch.float32, (1,))
+    _lib.check(_lib.lib().slim_attn_fwd_noalloc(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(R_in),
+                                                _ptr(S_in), _ptr(Y), _ptr(R), _ptr(S), _ptr(koff_out), _ptr(rs),
+                                                _stream()),
+               "slim_attn_fwd_noalloc")
+    if rs is not None:
+        return Y, R, S, rs
+    return Y, R, S
+
+
 def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, dR_out=None, dS_out=None,
              want_state_grad=False, window_chunks=0, state_dtype=None, want_dw=False, Y=None, row_stats=None):
     """Backward of attn_fwd(q, k, v, W, feat, num_chunks, R_in, S_in) for the

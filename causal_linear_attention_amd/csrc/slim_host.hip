@@ -322,14 +322,15 @@ static long long resolve_window(const slim_desc *d, long long nchunks, long long
     return P;
 }
 
-static Plan plan(const slim_desc *d, int pass)
+// window > 0: hold that many slices per window instead of the resolved window.
+static Plan plan(const slim_desc *d, int pass, long long window = 0)
 {
     Plan p;
     memset(&p, 0, sizeof(p));
     p.BH = d->B * d->H;
     p.c = (d->L + d->num_chunks - 1) / d->num_chunks;
     p.nchunks = (d->L + p.c - 1) / p.c;
-    p.P = resolve_window(d, p.nchunks, p.c, pass);
+    p.P = window > 0 ? (window < p.nchunks ? window : p.nchunks) : resolve_window(d, p.nchunks, p.c, pass);
     p.SZ = (d->d + 1) * d->M;
     const size_t slots = (size_t)p.BH * (p.P + 1) * p.SZ * 4;
     size_t off = 0;
@@ -499,26 +500,35 @@ slim_status slim_featmap(const slim_desc *d, const void *X, const void *W, float
     return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
 
-slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
-                          const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, float *koff,
-                          float *row_stats, void *ws, size_t ws_bytes, void *stream)
+}  // extern "C"
+
+namespace slim {
+
+// Argument checks shared by the two forward entry points (host only, no HIP call).
+static slim_status check_fwd_args(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
+                                  const void *R_in, const void *S_in, const void *Y, const void *R_out,
+                                  const void *S_out, const float *koff, const float *row_stats)
 {
     slim_status st = slim_validate(d, SLIM_PASS_FWD);
     if (st != SLIM_OK) return st;
-    if (!Q || !K || !V || !Y || !R_out || !S_out || !ws) return SLIM_ERR_NULL;
+    if (!Q || !K || !V || !Y || !R_out || !S_out) return SLIM_ERR_NULL;
     if (d->feat == SLIM_FEAT_FAVOR && !W) return SLIM_ERR_NULL;
     if (d->feat == SLIM_FEAT_ELU1 && W) return SLIM_ERR_SHAPE;
     if ((R_in == nullptr) != (S_in == nullptr)) return SLIM_ERR_NULL;
     if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(W, 16) || misaligned(Y, 16) ||
         misaligned(R_out, 16) || misaligned(S_out, 16) || misaligned(R_in, 16) || misaligned(S_in, 16) ||
-        misaligned(row_stats, 16) || misaligned(koff, 4) || misaligned(ws, 256))
+        misaligned(row_stats, 16) || misaligned(koff, 4))
         return SLIM_ERR_ALIGN;
-    const Plan p = plan(d, SLIM_PASS_FWD);
-    if (ws_bytes < p.total) return SLIM_ERR_WORKSPACE;
+    return SLIM_OK;
+}
+
+// The forward's launch sequence over a workspace laid out by p (checked arguments).
+static slim_status fwd_launch(const slim_desc *d, const Plan &p, const void *Q, const void *K, const void *V,
+                              const void *W, const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out,
+                              float *koff, float *row_stats, char *base, hipStream_t s)
+{
     const KernelTable *kt = find(d);
-    hipStream_t s = (hipStream_t)stream;
     const int D = (int)d->d, M = (int)d->M, BH = (int)p.BH;
-    char *base = (char *)ws;
     ChunkArgs a;
     memset(&a, 0, sizeof(a));
     a.Q = Q; a.K = K; a.V = V; a.W = W; a.out0 = Y;
@@ -542,6 +552,88 @@ slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, cons
     }
     narrow2(R_out, cR, p.BH * D * M, S_out, cS, p.BH * M, f64, s);
     return hipGetLastError() == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
+}
+
+// The allocation-free forward's workspace: one array per GPU the library runs on, held
+// until the process ends.  Host code never uses this name as an address (on the host it
+// is only a stand-in for the symbol): scratch_base() looks up each device's own copy
+// with hipGetSymbolAddress once, with that device current, and keeps it.
+constexpr size_t NOALLOC_SCRATCH_BYTES = SLIM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+static std::mutex scratch_mu;
+static std::vector<void *> scratch_ptr;  // per device ordinal; null until looked up
+
+// The scratch array of the device that runs `s` (the current device for the null stream).
+static hipError_t scratch_base(hipStream_t s, char **out)
+{
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (s) {
+        e = hipStreamGetDevice(s, &dev);
+        if (e != hipSuccess) return e;
+    }
+    std::lock_guard<std::mutex> g(scratch_mu);
+    if (dev < 0) return hipErrorInvalidDevice;
+    if ((size_t)dev >= scratch_ptr.size()) scratch_ptr.resize(dev + 1, nullptr);
+    if (!scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        scratch_ptr[dev] = p;
+    }
+    *out = (char *)scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace slim
+
+extern "C" {
+
+slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
+                          const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, float *koff,
+                          float *row_stats, void *ws, size_t ws_bytes, void *stream)
+{
+    slim_status st = check_fwd_args(d, Q, K, V, W, R_in, S_in, Y, R_out, S_out, koff, row_stats);
+    if (st != SLIM_OK) return st;
+    if (!ws) return SLIM_ERR_NULL;
+    if (misaligned(ws, 256)) return SLIM_ERR_ALIGN;
+    const Plan p = plan(d, SLIM_PASS_FWD);
+    if (ws_bytes < p.total) return SLIM_ERR_WORKSPACE;
+    return fwd_launch(d, p, Q, K, V, W, R_in, S_in, Y, R_out, S_out, koff, row_stats, (char *)ws,
+                      (hipStream_t)stream);
+}
+
+slim_status slim_attn_fwd_noalloc(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
+                                  const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out,
+                                  float *koff, float *row_stats, void *stream)
+{
+    slim_status st = check_fwd_args(d, Q, K, V, W, R_in, S_in, Y, R_out, S_out, koff, row_stats);
+    if (st != SLIM_OK) return st;
+    // the resolved window, or (automatic window) the most slices that fit the scratch
+    Plan p = plan(d, SLIM_PASS_FWD);
+    if (p.total > NOALLOC_SCRATCH_BYTES) {
+        if (d->window_chunks > 0) return SLIM_ERR_WORKSPACE;
+        long long lo = 1, hi = p.P - 1;  // the plan's size grows with the window
+        if (plan(d, SLIM_PASS_FWD, 1).total > NOALLOC_SCRATCH_BYTES) return SLIM_ERR_WORKSPACE;
+        while (lo < hi) {
+            const long long mid = (lo + hi + 1) / 2;
+            if (plan(d, SLIM_PASS_FWD, mid).total <= NOALLOC_SCRATCH_BYTES)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        p = plan(d, SLIM_PASS_FWD, lo);
+    }
+    char *base = nullptr;
+    if (scratch_base((hipStream_t)stream, &base) != hipSuccess) return SLIM_ERR_HIP;
+    return fwd_launch(d, p, Q, K, V, W, R_in, S_in, Y, R_out, S_out, koff, row_stats, base, (hipStream_t)stream);
 }
 
 slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,

@@ -161,6 +161,31 @@ slim_status slim_attn_fwd(const slim_desc *desc, const void *Q, const void *K, c
                           const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, float *koff,
                           float *row_stats, void *ws, size_t ws_bytes, void *stream);
 
+/* Size of the device array slim_attn_fwd_noalloc works in, per GPU: 64 MiB. */
+#define SLIM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* The forward above for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as slim_attn_fwd, without ws and ws_bytes: the
+ * workspace is a file-scope device array of SLIM_NOALLOC_SCRATCH_BYTES that each
+ * GPU the library runs on holds until the process ends (its address is looked up
+ * once per device, on the first call there).  The call allocates and frees
+ * nothing.
+ * Window: the automatic window (desc.window_chunks == 0), shrunk to the most
+ * slices whose workspace fits the array; or desc.window_chunks itself, which must
+ * fit.  Returns SLIM_ERR_WORKSPACE, before anything is enqueued, when it does not
+ * fit, or when even one slice per window does not (about 16*B*H*(d+1)*M bytes: two
+ * state slots and the fp64 carries per head, so B*H up to about 250 at d = 64,
+ * M = 256).  Results equal slim_attn_fwd's with the same window exactly, and with
+ * another window up to the rounding of the fp64 carries to fp32 slots.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one GPU
+ * (other streams, other host threads) race and must be ordered by the caller.
+ * Nothing in the array needs clearing between calls: every byte a call reads it
+ * has written first. */
+slim_status slim_attn_fwd_noalloc(const slim_desc *desc, const void *Q, const void *K, const void *V,
+                                  const void *W, const void *R_in, const void *S_in, void *Y, void *R_out,
+                                  void *S_out, float *koff, float *row_stats, void *stream);
+
 /* Backward of the loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out> of the
  * forward above (Subsection 3.3: a reverse walk over the slices that recomputes
  * each slice's forward and carries the gradient of the state).  Every slice's

@@ -264,3 +264,22 @@ def test_state_dtype_validation(lib):
     assert validate(lib, _lib.SLIM_PASS_DECODE, L=1, num_chunks=1, state_dtype=_lib.SLIM_F64) == 0  # fp64 state
     # the workspace does not depend on the state type (the carries are fp64 either way)
     assert ws(lib, 2, state_dtype=_lib.SLIM_F64) == ws(lib, 2)
+
+
+def test_noalloc_forward_rejects_before_any_launch(lib):
+    # the allocation-free forward checks its arguments and the fit of its workspace in
+    # the fixed scratch array on the host, before any HIP call
+    args = [P] * 3 + [P, None, None, P, P, P, None, None, None]  # Q K V W R_in S_in Y R_out S_out koff rs stream
+    assert lib.slim_attn_fwd_noalloc(None, *args) == 1
+    assert lib.slim_attn_fwd_noalloc(ctypes.byref(d_(num_chunks=0)), *args) == 2
+    null_q = [None] + args[1:]
+    assert lib.slim_attn_fwd_noalloc(ctypes.byref(d_()), *null_q) == 1
+    bad = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.slim_attn_fwd_noalloc(ctypes.byref(d_()), bad, *args[1:]) == 6
+    # two state slots and the fp64 carries of 600 heads at d = 64, M = 256 exceed 64 MiB
+    too_many = d_(B=600, H=1, L=16, d=64, M=256, num_chunks=1)
+    assert lib.slim_attn_fwd_noalloc(ctypes.byref(too_many), *args) == 5
+    # an explicit window that does not fit is refused, not shrunk
+    wide = d_(B=64, H=1, L=16384, d=64, M=256, num_chunks=32, window_chunks=32)
+    assert lib.slim_attn_fwd_noalloc(ctypes.byref(wide), *args) == 5
+    assert _lib.SLIM_NOALLOC_SCRATCH_BYTES == 64 << 20
