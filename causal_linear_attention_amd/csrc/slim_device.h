@@ -274,10 +274,31 @@ __device__ __forceinline__ float key_offset_block(const void *W, int wbf16, int 
 {
     float n2 = 0.f;
     if ((int)threadIdx.x < M) {
-        for (int e = 0; e < D; ++e) {
-            const size_t i = (size_t)threadIdx.x * D + e;
-            const float x = wbf16 ? __uint_as_float((unsigned)((const uint16_t *)W)[i] << 16) : ((const float *)W)[i];
-            n2 = fmaf(x, x, n2);
+        // row m's squares summed in index order; its elements fetched 16 bytes at a time
+        // (rows start 16-byte aligned: W is, and D is a multiple of 16)
+        if (wbf16) {
+            const uint4 *row = reinterpret_cast<const uint4 *>((const uint16_t *)W + (size_t)threadIdx.x * D);
+#pragma unroll 4
+            for (int j = 0; j < D / 8; ++j) {
+                const uint4 u = row[j];
+                const unsigned p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float lo = __uint_as_float(p[h] << 16), hi = __uint_as_float(p[h] & 0xffff0000u);
+                    n2 = fmaf(lo, lo, n2);
+                    n2 = fmaf(hi, hi, n2);
+                }
+            }
+        } else {
+            const float4 *row = reinterpret_cast<const float4 *>((const float *)W + (size_t)threadIdx.x * D);
+#pragma unroll 4
+            for (int j = 0; j < D / 4; ++j) {
+                const float4 u = row[j];
+                n2 = fmaf(u.x, u.x, n2);
+                n2 = fmaf(u.y, u.y, n2);
+                n2 = fmaf(u.z, u.z, n2);
+                n2 = fmaf(u.w, u.w, n2);
+            }
         }
     }
 #pragma unroll
