@@ -2,10 +2,12 @@
 
 One step = slim_attn_fwd + slim_attn_bwd over one batch of synthetic inputs
 already resident in HBM (every kernel of the path: feature maps, chunk states,
-scans, outputs, statistics, dQ, dK/dV); the forward keeps its output and per-row
-denominator statistics for the backward, as the autograd function does (the
-step with the backward recomputing them is timed too, ms_per_step_stats_recomputed).  Default workload: FAVOR+, bf16 I/O with
-fp32 state, B=4, H=16, L=16384, d=64, M=256, 32 slices of 512.
+scans, outputs, statistics, dQ, dK/dV); the forward keeps its output, per-row
+denominator statistics and, where one window holds every slice, the slices'
+entry states for the backward, as the autograd function does (the step with the
+backward rebuilding all of them is timed too, ms_per_step_stats_recomputed).
+Default workload: FAVOR+, bf16 I/O with fp32 state, B=4, H=16, L=16384, d=64,
+M=256, 32 slices of 512.
 
 Prints ONE JSON line (rank 0): throughput (tokens/s = B*L per step time, timed
 over plain steps), the roofline record of the dominant kernel (its launches
@@ -274,8 +276,11 @@ def mem_sweep(torch, A, synth, w):
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
         P = MEM_SWEEP_WINDOW
-        Y, R, S = A.attn_fwd(q, k, v, W, w.feat, chunks, window_chunks=P)
-        g = A.attn_bwd(q, k, v, W, dy, w.feat, chunks, window_chunks=P)
+        # as the bench step runs it: the forward keeps Y, the row statistics and (where one
+        # window holds every slice) the slices' entry states for the backward
+        Y, R, S, rs, st = A.attn_fwd(q, k, v, W, w.feat, chunks, window_chunks=P, want_row_stats=True,
+                                     want_states=True)
+        g = A.attn_bwd(q, k, v, W, dy, w.feat, chunks, window_chunks=P, Y=Y, row_stats=rs, states=st)
         torch.cuda.synchronize()
         peak = torch.cuda.max_memory_allocated() - base
         dsc = A.make_desc(q, w.M, w.feat, chunks, P)
@@ -283,9 +288,10 @@ def mem_sweep(torch, A, synth, w):
         rows.append({"L": L, "chunks": chunks, "window_chunks": int(_lib.lib().slim_window_chunks(ctypes.byref(dsc))),
                      "inputs_bytes": 4 * q.numel() * 2, "step_peak_bytes": peak, "outputs_bytes": outs,
                      "beyond_io_bytes": peak - outs,
-                     "ws_fwd_bytes": int(A.workspace_bytes(dsc, _lib.SLIM_PASS_FWD)),
-                     "ws_bwd_bytes": int(A.workspace_bytes(dsc, _lib.SLIM_PASS_BWD))})
-        del q, k, v, dy, W, Y, R, S, g
+                     "states_kept_bytes": 0 if st is None else st.numel() * 4,
+                     "ws_fwd_bytes": int(A.workspace_bytes(dsc, _lib.SLIM_PASS_FWD, st is not None)),
+                     "ws_bwd_bytes": int(A.workspace_bytes(dsc, _lib.SLIM_PASS_BWD, st is not None))})
+        del q, k, v, dy, W, Y, R, S, rs, st, g
         torch.cuda.empty_cache()
     return {"mem_sweep": w.name, "B": w.B, "H": w.H, "d": w.d, "M": w.M, "chunk_len": 512, "rows": rows}
 
@@ -644,14 +650,15 @@ def main():
     want_dw = bool(args.dw and w.backward and w.feat == "favor")
 
     def step(keep_stats=True):
-        # the forward keeps its output and per-row denominator statistics for the
-        # backward (as autograd does); keep_stats=False: the backward recomputes them
+        # the forward keeps its output, per-row denominator statistics and (one window)
+        # the slices' entry states for the backward, as autograd does; keep_stats=False:
+        # the backward rebuilds all of them
         keep = keep_stats and w.backward
-        out = A.attn_fwd(q, k, v, W, w.feat, w.chunks, want_row_stats=keep)
+        out = A.attn_fwd(q, k, v, W, w.feat, w.chunks, want_row_stats=keep, want_states=keep)
         Y = out[0]
         if w.backward:
             A.attn_bwd(q, k, v, W, dy, w.feat, w.chunks, want_dw=want_dw, Y=Y if keep else None,
-                       row_stats=out[3] if keep else None)
+                       row_stats=out[3] if keep else None, states=out[4] if keep else None)
         return Y
 
     if args.profile_run:

@@ -19,9 +19,10 @@ STATUS = {0: "SLIM_OK", 1: "SLIM_ERR_NULL", 2: "SLIM_ERR_SHAPE", 3: "SLIM_ERR_DT
           4: "SLIM_ERR_UNSUPPORTED", 5: "SLIM_ERR_WORKSPACE", 6: "SLIM_ERR_ALIGN", 7: "SLIM_ERR_HIP"}
 
 # every symbol declared in include/slim.h
-EXPORTS = ["slim_validate", "slim_workspace_bytes", "slim_window_chunks", "slim_tile_rows", "slim_featmap", "slim_attn_fwd",
-           "slim_attn_fwd_noalloc", "slim_attn_bwd", "slim_decode_step", "slim_status_string", "slim_version", "slim_prof_enable", "slim_prof_count",
-           "slim_prof_entry"]
+EXPORTS = ["slim_validate", "slim_workspace_bytes", "slim_workspace_bytes_states", "slim_state_bytes",
+           "slim_window_chunks", "slim_tile_rows", "slim_featmap", "slim_attn_fwd", "slim_attn_fwd_noalloc",
+           "slim_attn_bwd", "slim_decode_step", "slim_status_string", "slim_version", "slim_prof_enable",
+           "slim_prof_count", "slim_prof_entry"]
 
 
 class SlimDesc(ctypes.Structure):
@@ -55,17 +56,21 @@ def lib(path: str | None = None):
     L.slim_validate.restype = i32
     L.slim_workspace_bytes.argtypes = [D, i32]
     L.slim_workspace_bytes.restype = sz
+    L.slim_workspace_bytes_states.argtypes = [D, i32]
+    L.slim_workspace_bytes_states.restype = sz
+    L.slim_state_bytes.argtypes = [D]
+    L.slim_state_bytes.restype = sz
     L.slim_window_chunks.argtypes = [D]
     L.slim_window_chunks.restype = i64
     L.slim_tile_rows.argtypes = [D]
     L.slim_tile_rows.restype = i64
     L.slim_featmap.argtypes = [D, vp, vp, vp, vp, vp]
     L.slim_featmap.restype = i32
-    L.slim_attn_fwd.argtypes = [D] + [vp] * 12 + [sz, vp]
+    L.slim_attn_fwd.argtypes = [D] + [vp] * 13 + [sz, vp]
     L.slim_attn_fwd.restype = i32
     L.slim_attn_fwd_noalloc.argtypes = [D] + [vp] * 12
     L.slim_attn_fwd_noalloc.restype = i32
-    L.slim_attn_bwd.argtypes = [D] + [vp] * 18 + [sz, vp]
+    L.slim_attn_bwd.argtypes = [D] + [vp] * 19 + [sz, vp]
     L.slim_attn_bwd.restype = i32
     L.slim_decode_step.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.slim_decode_step.restype = i32

@@ -56,11 +56,20 @@ def _feat_M(W, feat, d):
     return d
 
 
-def workspace_bytes(desc, pass_):
-    n = _lib.lib().slim_workspace_bytes(ctypes.byref(desc), pass_)
+def workspace_bytes(desc, pass_, states=False):
+    """Workspace bytes of a pass; states: with a states buffer given to the call."""
+    fn = _lib.lib().slim_workspace_bytes_states if states else _lib.lib().slim_workspace_bytes
+    n = fn(ctypes.byref(desc), pass_)
     if n == 0 and pass_ != _lib.SLIM_PASS_FEATMAP:
         _lib.check(_lib.lib().slim_validate(ctypes.byref(desc), pass_), "slim_workspace_bytes")
     return n
+
+
+def state_shape(q, M, num_chunks):
+    """Shape of the per-slice states attn_fwd(want_states=True) returns."""
+    B, H, L, d = q.shape
+    c = -(-L // num_chunks)
+    return (B, H, -(-L // c) + 1, d + 1, M)
 
 
 def featmap(x, W=None, feat="favor", row_offset=False):
@@ -79,13 +88,17 @@ def featmap(x, W=None, feat="favor", row_offset=False):
 
 
 def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, window_chunks=0,
-             state_dtype=None, want_row_stats=False, koff_out=None):
+             state_dtype=None, want_row_stats=False, koff_out=None, want_states=False):
     """Forward.  Returns (Y, R_out [B,H,d,M], S_out [B,H,M]).  States are fp32, or
     fp64 when R_in is fp64 or state_dtype=torch.float64; like R_in, S_in they hold
     the state times exp(-koff), the key-side offset of W (0 unless some row of W has
     |w_m|^2 > 120).  want_row_stats: a fourth value, the per-row statistics
     [B,H,L,2] fp32 that let attn_bwd skip recomputing the denominators (pass it
-    with Y).  koff_out: a one-element fp32 GPU tensor that receives koff."""
+    with Y).  want_states: a fifth value (the fourth None unless want_row_stats),
+    the state entering every slice [B,H,slices+1,d+1,M] fp32 (rows < d: R, row d:
+    S, times exp(-koff)) for attn_bwd to read instead of rebuilding them, or None
+    where the slices span several windows.  koff_out: a one-element fp32 GPU
+    tensor that receives koff."""
     B, H, L, d = q.shape
     M = _feat_M(W, feat, d)
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -97,7 +110,12 @@ def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, 
         _check_io("R_in", R_in, sd, (B, H, d, M))
         _check_io("S_in", S_in, sd, (B, H, M))
     dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd)
-    ws = torch.empty(max(1, workspace_bytes(dsc, _lib.SLIM_PASS_FWD)), dtype=torch.uint8, device=q.device)
+    st = None
+    if want_states and _lib.lib().slim_state_bytes(ctypes.byref(dsc)) > 0:
+        st = torch.empty(state_shape(q, M, num_chunks), dtype=torch.float32, device=q.device)
+        assert st.numel() * 4 == _lib.lib().slim_state_bytes(ctypes.byref(dsc))
+    ws = torch.empty(max(1, workspace_bytes(dsc, _lib.SLIM_PASS_FWD, st is not None)), dtype=torch.uint8,
+                     device=q.device)
     Y = torch.empty_like(q)
     R = torch.empty((B, H, d, M), dtype=sd, device=q.device)
     S = torch.empty((B, H, M), dtype=sd, device=q.device)
@@ -105,9 +123,11 @@ def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, 
     if koff_out is not None:
         _check_io("koff_out", koff_out, torch.float32, (1,))
     _lib.check(_lib.lib().slim_attn_fwd(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(R_in),
-                                        _ptr(S_in), _ptr(Y), _ptr(R), _ptr(S), _ptr(koff_out), _ptr(rs), _ptr(ws),
-                                        ws.numel(), _stream()),
+                                        _ptr(S_in), _ptr(Y), _ptr(R), _ptr(S), _ptr(koff_out), _ptr(rs), _ptr(st),
+                                        _ptr(ws), ws.numel(), _stream()),
                "slim_attn_fwd")
+    if want_states:
+        return Y, R, S, rs, st
     if want_row_stats:
         return Y, R, S, rs
     return Y, R, S
@@ -155,7 +175,8 @@ def attn_fwd_noalloc(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_i
 
 
 def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, dR_out=None, dS_out=None,
-             want_state_grad=False, window_chunks=0, state_dtype=None, want_dw=False, Y=None, row_stats=None):
+             want_state_grad=False, window_chunks=0, state_dtype=None, want_dw=False, Y=None, row_stats=None,
+             states=None):
     """Backward of attn_fwd(q, k, v, W, feat, num_chunks, R_in, S_in) for the
     loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out>.  Returns (dQ, dK, dV,
     dR_in, dS_in); the last two are None unless want_state_grad.  With want_dw
@@ -163,7 +184,10 @@ def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, d
     projection W.  The state tensors share one dtype (fp32, or fp64), taken
     from those given.  Y, row_stats: the output and row statistics of attn_fwd on
     the same inputs (want_row_stats=True); given, the backward reuses the
-    forward's denominators instead of recomputing them."""
+    forward's denominators instead of recomputing them.  states: what
+    attn_fwd(want_states=True) returned for the same inputs and slices; the
+    backward then reads every slice's entry state instead of rebuilding it
+    (same results)."""
     B, H, L, d = q.shape
     M = _feat_M(W, feat, d)
     for n, t in (("q", q), ("k", k), ("v", v), ("dY", dY)):
@@ -184,8 +208,10 @@ def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, d
         _check_io("Y", Y, q.dtype, q.shape)
         _check_io("row_stats", row_stats, torch.float32, (B, H, L, 2))
     dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd)
+    if states is not None:
+        _check_io("states", states, torch.float32, state_shape(q, M, num_chunks))
     ps = _lib.SLIM_PASS_BWD_DW if want_dw else _lib.SLIM_PASS_BWD
-    ws = torch.empty(max(1, workspace_bytes(dsc, ps)), dtype=torch.uint8, device=q.device)
+    ws = torch.empty(max(1, workspace_bytes(dsc, ps, states is not None)), dtype=torch.uint8, device=q.device)
     dQ, dK, dV = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dW = torch.empty((M, d), dtype=torch.float32, device=q.device) if want_dw else None
     dR = dS = None
@@ -193,7 +219,7 @@ def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, d
         dR = torch.empty((B, H, d, M), dtype=sd, device=q.device)
         dS = torch.empty((B, H, M), dtype=sd, device=q.device)
     _lib.check(_lib.lib().slim_attn_bwd(ctypes.byref(dsc), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(dY),
-                                        _ptr(Y), _ptr(row_stats), _ptr(R_in), _ptr(S_in), _ptr(dR_out),
+                                        _ptr(Y), _ptr(row_stats), _ptr(states), _ptr(R_in), _ptr(S_in), _ptr(dR_out),
                                         _ptr(dS_out), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dR), _ptr(dS), _ptr(dW),
                                         _ptr(ws), ws.numel(), _stream()),
                "slim_attn_bwd")
@@ -245,27 +271,36 @@ def decode_step(q, k, v, W=None, feat="favor", R=None, S=None, inplace=False, st
 
 class _SlimAttention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, W, feat, num_chunks, window_chunks):
-        Y, _, _, rs = attn_fwd(q, k, v, W, feat, num_chunks, window_chunks=window_chunks, want_row_stats=True)
-        # Kept for the backward: the inputs, the output and 8 bytes per row of
-        # denominator statistics; the backward rebuilds every slice's entry state
-        # and recomputes the slice (no per-slice state is stored).
-        ctx.save_for_backward(q, k, v, W if W is not None else torch.empty(0), Y, rs)
+    def forward(ctx, q, k, v, W, feat, num_chunks, window_chunks, keep_states):
+        out = attn_fwd(q, k, v, W, feat, num_chunks, window_chunks=window_chunks, want_row_stats=True,
+                       want_states=keep_states)
+        Y, rs, st = out[0], out[3], out[4] if keep_states else None
+        # Kept for the backward: the inputs, the output, 8 bytes per row of
+        # denominator statistics and, where one window holds every slice and
+        # keep_states is set, each slice's entry state ((d+1) M fp32 per slice);
+        # else the backward rebuilds the entry states.  The slices are recomputed
+        # either way.
+        ctx.save_for_backward(q, k, v, W if W is not None else torch.empty(0), Y, rs,
+                              st if st is not None else torch.empty(0))
         ctx.feat, ctx.num_chunks, ctx.window_chunks, ctx.has_w = feat, num_chunks, window_chunks, W is not None
+        ctx.has_st = st is not None
         return Y
 
     @staticmethod
     def backward(ctx, dY):
-        q, k, v, W, Y, rs = ctx.saved_tensors
+        q, k, v, W, Y, rs, st = ctx.saved_tensors
         want_dw = ctx.has_w and ctx.needs_input_grad[3]
         g = attn_bwd(q, k, v, W if ctx.has_w else None, dY.contiguous(), ctx.feat, ctx.num_chunks,
-                     window_chunks=ctx.window_chunks, want_dw=want_dw, Y=Y, row_stats=rs)
+                     window_chunks=ctx.window_chunks, want_dw=want_dw, Y=Y, row_stats=rs,
+                     states=st if ctx.has_st else None)
         dW = g[5].to(W.dtype) if want_dw else None
-        return g[0], g[1], g[2], dW, None, None, None
+        return g[0], g[1], g[2], dW, None, None, None, None
 
 
-def slim_attention(q, k, v, W=None, feat="favor", num_chunks=1, window_chunks=0):
+def slim_attention(q, k, v, W=None, feat="favor", num_chunks=1, window_chunks=0, keep_states=True):
     """Causal linear attention with autograd: gradients for q, k, v, and for
     the FAVOR+ projection W when it requires one (the page keeps W a fixed
-    random projection; a caller may train it)."""
-    return _SlimAttention.apply(q, k, v, W, feat, num_chunks, window_chunks)
+    random projection; a caller may train it).  keep_states: where one window
+    holds every slice, keep each slice's entry state from the forward for the
+    backward ((d+1) M fp32 per slice and head) instead of rebuilding them."""
+    return _SlimAttention.apply(q, k, v, W, feat, num_chunks, window_chunks, keep_states)

@@ -271,7 +271,11 @@ struct Plan {
     long long BH, c, nchunks, P, SZ;
     long long dw_parts;  // dW pass: partial sums per window (2 sides x BH x workgroups per head)
     size_t slots_off, gslots_off, stats_off, cR_off, cS_off, gR_off, gS_off, wt_off, koff_off;
-    size_t pq_off, pk_off, part_off, part2_off, total;
+    size_t pq_off, pk_off, part_off, part2_off;
+    size_t total;         // workspace bytes
+    size_t total_states;  // workspace bytes when the caller holds the slices' states (the
+                          // slot array is the last region; equal to total for several windows)
+    bool one_window() const { return P == nchunks; }
 };
 
 // dW pass: the row contraction runs about 1024 workgroups (at least 256 rows each).
@@ -334,8 +338,6 @@ static Plan plan(const slim_desc *d, int pass, long long window = 0)
     p.SZ = (d->d + 1) * d->M;
     const size_t slots = (size_t)p.BH * (p.P + 1) * p.SZ * 4;
     size_t off = 0;
-    p.slots_off = off;
-    off = align256(off + slots);
     // fp64 carries of the state (both passes) and of its gradient (backward)
     p.cR_off = off;
     off = align256(off + (size_t)p.BH * d->d * d->M * 8);
@@ -372,7 +374,14 @@ static Plan plan(const slim_desc *d, int pass, long long window = 0)
         p.part2_off = off;
         off = align256(off + (size_t)((p.dw_parts + 31) / 32) * pmd);
     }
-    p.total = (pass == SLIM_PASS_FEATMAP || pass == SLIM_PASS_DECODE) ? 0 : off;
+    // the state slots last: a call handed every slice's state by the caller (one
+    // window) needs no room for them
+    p.slots_off = off;
+    const size_t without = off;
+    off = align256(off + slots);
+    const bool none = pass == SLIM_PASS_FEATMAP || pass == SLIM_PASS_DECODE;
+    p.total = none ? 0 : off;
+    p.total_states = none ? 0 : p.one_window() ? without : off;
     return p;
 }
 
@@ -392,7 +401,7 @@ using namespace slim;
 
 extern "C" {
 
-int slim_version(void) { return (3 << 16) | 0; }
+int slim_version(void) { return (4 << 16) | 0; }
 
 slim_status slim_prof_enable(int enable)
 {
@@ -469,6 +478,19 @@ size_t slim_workspace_bytes(const slim_desc *d, int pass)
     return plan(d, pass).total;
 }
 
+size_t slim_state_bytes(const slim_desc *d)
+{
+    if (slim_validate(d, SLIM_PASS_FWD) != SLIM_OK) return 0;
+    const Plan p = plan(d, SLIM_PASS_FWD);
+    return p.one_window() ? (size_t)p.BH * (p.nchunks + 1) * p.SZ * 4 : 0;
+}
+
+size_t slim_workspace_bytes_states(const slim_desc *d, int pass)
+{
+    if (slim_validate(d, pass) != SLIM_OK) return 0;
+    return plan(d, pass).total_states;
+}
+
 int64_t slim_window_chunks(const slim_desc *d)
 {
     if (slim_validate(d, SLIM_PASS_FWD) != SLIM_OK) return 0;
@@ -507,7 +529,8 @@ namespace slim {
 // Argument checks shared by the two forward entry points (host only, no HIP call).
 static slim_status check_fwd_args(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
                                   const void *R_in, const void *S_in, const void *Y, const void *R_out,
-                                  const void *S_out, const float *koff, const float *row_stats)
+                                  const void *S_out, const float *koff, const float *row_stats,
+                                  const float *states = nullptr)
 {
     slim_status st = slim_validate(d, SLIM_PASS_FWD);
     if (st != SLIM_OK) return st;
@@ -517,7 +540,7 @@ static slim_status check_fwd_args(const slim_desc *d, const void *Q, const void 
     if ((R_in == nullptr) != (S_in == nullptr)) return SLIM_ERR_NULL;
     if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(W, 16) || misaligned(Y, 16) ||
         misaligned(R_out, 16) || misaligned(S_out, 16) || misaligned(R_in, 16) || misaligned(S_in, 16) ||
-        misaligned(row_stats, 16) || misaligned(koff, 4))
+        misaligned(row_stats, 16) || misaligned(koff, 4) || misaligned(states, 16))
         return SLIM_ERR_ALIGN;
     return SLIM_OK;
 }
@@ -525,7 +548,7 @@ static slim_status check_fwd_args(const slim_desc *d, const void *Q, const void 
 // The forward's launch sequence over a workspace laid out by p (checked arguments).
 static slim_status fwd_launch(const slim_desc *d, const Plan &p, const void *Q, const void *K, const void *V,
                               const void *W, const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out,
-                              float *koff, float *row_stats, char *base, hipStream_t s)
+                              float *koff, float *row_stats, float *states, char *base, hipStream_t s)
 {
     const KernelTable *kt = find(d);
     const int D = (int)d->d, M = (int)d->M, BH = (int)p.BH;
@@ -533,7 +556,7 @@ static slim_status fwd_launch(const slim_desc *d, const Plan &p, const void *Q, 
     memset(&a, 0, sizeof(a));
     a.Q = Q; a.K = K; a.V = V; a.W = W; a.out0 = Y;
     a.rstat = row_stats;
-    a.slots = (float *)(base + p.slots_off);
+    a.slots = states ? states : (float *)(base + p.slots_off);  // the caller's: one window
     a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
     a.koff = (const float *)(base + p.koff_off);
     double *cR = (double *)(base + p.cR_off), *cS = (double *)(base + p.cS_off);
@@ -598,15 +621,16 @@ extern "C" {
 
 slim_status slim_attn_fwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
                           const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, float *koff,
-                          float *row_stats, void *ws, size_t ws_bytes, void *stream)
+                          float *row_stats, float *states, void *ws, size_t ws_bytes, void *stream)
 {
-    slim_status st = check_fwd_args(d, Q, K, V, W, R_in, S_in, Y, R_out, S_out, koff, row_stats);
+    slim_status st = check_fwd_args(d, Q, K, V, W, R_in, S_in, Y, R_out, S_out, koff, row_stats, states);
     if (st != SLIM_OK) return st;
     if (!ws) return SLIM_ERR_NULL;
     if (misaligned(ws, 256)) return SLIM_ERR_ALIGN;
     const Plan p = plan(d, SLIM_PASS_FWD);
-    if (ws_bytes < p.total) return SLIM_ERR_WORKSPACE;
-    return fwd_launch(d, p, Q, K, V, W, R_in, S_in, Y, R_out, S_out, koff, row_stats, (char *)ws,
+    if (states && !p.one_window()) return SLIM_ERR_SHAPE;  // the states of every slice need one window
+    if (ws_bytes < (states ? p.total_states : p.total)) return SLIM_ERR_WORKSPACE;
+    return fwd_launch(d, p, Q, K, V, W, R_in, S_in, Y, R_out, S_out, koff, row_stats, states, (char *)ws,
                       (hipStream_t)stream);
 }
 
@@ -633,13 +657,15 @@ slim_status slim_attn_fwd_noalloc(const slim_desc *d, const void *Q, const void 
     }
     char *base = nullptr;
     if (scratch_base((hipStream_t)stream, &base) != hipSuccess) return SLIM_ERR_HIP;
-    return fwd_launch(d, p, Q, K, V, W, R_in, S_in, Y, R_out, S_out, koff, row_stats, base, (hipStream_t)stream);
+    return fwd_launch(d, p, Q, K, V, W, R_in, S_in, Y, R_out, S_out, koff, row_stats, nullptr, base,
+                      (hipStream_t)stream);
 }
 
 slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, const void *V, const void *W,
-                          const void *dY, const void *Y, const float *row_stats, const void *R_in, const void *S_in,
-                          const void *dR_out, const void *dS_out, void *dQ, void *dK, void *dV, void *dR_in,
-                          void *dS_in, float *dW, void *ws, size_t ws_bytes, void *stream)
+                          const void *dY, const void *Y, const float *row_stats, const float *states,
+                          const void *R_in, const void *S_in, const void *dR_out, const void *dS_out, void *dQ,
+                          void *dK, void *dV, void *dR_in, void *dS_in, float *dW, void *ws, size_t ws_bytes,
+                          void *stream)
 {
     const int pass = dW ? SLIM_PASS_BWD_DW : SLIM_PASS_BWD;
     slim_status st = slim_validate(d, pass);
@@ -651,14 +677,17 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
     if ((dR_out == nullptr) != (dS_out == nullptr)) return SLIM_ERR_NULL;
     if ((dR_in == nullptr) != (dS_in == nullptr)) return SLIM_ERR_NULL;
     if ((Y == nullptr) != (row_stats == nullptr)) return SLIM_ERR_NULL;
-    if (misaligned(Y, 16) || misaligned(row_stats, 16)) return SLIM_ERR_ALIGN;
+    if (misaligned(Y, 16) || misaligned(row_stats, 16) || misaligned(states, 16)) return SLIM_ERR_ALIGN;
     if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(W, 16) || misaligned(dY, 16) ||
         misaligned(R_in, 16) || misaligned(S_in, 16) || misaligned(dR_out, 16) || misaligned(dS_out, 16) ||
         misaligned(dQ, 16) || misaligned(dK, 16) || misaligned(dV, 16) || misaligned(dR_in, 16) ||
         misaligned(dS_in, 16) || misaligned(dW, 16) || misaligned(ws, 256))
         return SLIM_ERR_ALIGN;
     const Plan p = plan(d, pass);
-    if (ws_bytes < p.total) return SLIM_ERR_WORKSPACE;
+    // the forward's states of every slice, used where this pass holds them all in one window
+    // (else rebuilt as without them, to the same values)
+    const bool kept = states && p.one_window();
+    if (ws_bytes < (kept ? p.total_states : p.total)) return SLIM_ERR_WORKSPACE;
     const KernelTable *kt = find(d);
     const DwTable *dt = dW ? find_dw(d) : nullptr;
     hipStream_t s = (hipStream_t)stream;
@@ -669,7 +698,7 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
     a.Q = Q; a.K = K; a.V = V; a.W = W; a.dY = dY;
     a.Yin = Y; a.rstat = const_cast<float *>(row_stats);
     a.out0 = dQ; a.out1 = dK; a.out2 = dV;
-    a.slots = (float *)(base + p.slots_off);
+    a.slots = kept ? const_cast<float *>(states) : (float *)(base + p.slots_off);  // read only when kept
     a.gslots = (float *)(base + p.gslots_off);
     a.stats = (float *)(base + p.stats_off);
     a.L = d->L; a.c = (int)p.c; a.P = (int)p.P;
@@ -709,9 +738,11 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
     }
     for (long long wi = nwin - 1; wi >= 0; --wi) {
         const int np = window(wi);
-        if (nwin == 1) {  // entry states forward from the initial state
-            SLIM_TIMED("state", s, kt->state(dim3(np, BH), s, a));
-            scan(0, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
+        if (nwin == 1) {  // entry states forward from the initial state (unless the forward's are kept)
+            if (!kept) {
+                SLIM_TIMED("state", s, kt->state(dim3(np, BH), s, a));
+                scan(0, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
+            }
         } else {  // window start = state after it minus its chunks; entry states forward from there
             if (wi != nwin - 1) SLIM_TIMED("state", s, kt->state(dim3(np, BH), s, a));
             scan(1, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);

@@ -19,7 +19,9 @@
  * recovering each slice's entry state from the final state by subtraction and
  * carrying the gradient of the state.  No L x d x M prefix tensor is stored:
  * the workspace holds per-slice states for a bounded window of slices, so it
- * does not grow with L once L exceeds window_chunks * c.
+ * does not grow with L once L exceeds window_chunks * c.  Where one window
+ * holds every slice, the forward can hand its per-slice states to the
+ * backward (slim_state_bytes), which then skips rebuilding them.
  *
  * Feature maps (Subsection 2.1 names both kinds):
  *   SLIM_FEAT_FAVOR: g(x)_m = exp(w_m . x - |x|^2/2) / sqrt(M), w_m = row m of
@@ -127,6 +129,21 @@ size_t slim_workspace_bytes(const slim_desc *desc, int pass);
  * and the plain backward; the backward with dW may hold fewer (see window_chunks). */
 int64_t slim_window_chunks(const slim_desc *desc);
 
+/* Bytes of the `states` buffer slim_attn_fwd can fill for the backward: the state
+ * entering every slice, [B*H][num_chunks' + 1][d + 1][M] fp32 (num_chunks' =
+ * ceil(L / c), the slices there are), entry n of a head holding R (rows e < d,
+ * stored [e][m] = R[e][m]) and S (row d) before slice n, scaled by exp(-koff):
+ * entry 0 the initial state, the last entry the final state.  Only when one
+ * window holds every slice (slim_window_chunks(desc) == num_chunks'); else 0,
+ * and states cannot be kept.  Host-only; 0 for an invalid descriptor. */
+size_t slim_state_bytes(const slim_desc *desc);
+
+/* Workspace bytes of a pass (SLIM_PASS_FWD, SLIM_PASS_BWD, SLIM_PASS_BWD_DW) when
+ * the call is given a states buffer: slim_workspace_bytes less the room for the
+ * slices' states, where the pass holds every slice in one window; otherwise
+ * slim_workspace_bytes itself.  Host-only; 0 for an invalid descriptor. */
+size_t slim_workspace_bytes_states(const slim_desc *desc, int pass);
+
 /* Rows per tile with which the chunk kernels walk a slice for this
  * descriptor's (dtype, feat, d, M): 32, or 16 where 32-row tiles would not fit
  * a compute unit's LDS.  0 if the descriptor is invalid.  Host-only. */
@@ -155,18 +172,24 @@ slim_status slim_featmap(const slim_desc *desc, const void *X, const void *W, fl
  *      S_l exp(-koff) and the query features taken as
  *      g'(Q_l)_m = exp(w_m.Q_l) 2^o_l (FAVOR+; elu+1: g itself), i.e.
  *      den_l = den'_l exp(koff - o_l ln 2 - |Q_l|^2/2) / sqrt(M).  8 bytes per
- *      row, the analogue of the log-sum-exp kept by softmax attention.
- * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_FWD). */
+ *      row, the analogue of the log-sum-exp kept by softmax attention;
+ *      states = the state entering every slice, slim_state_bytes(desc) bytes
+ *      in the layout given there, for the backward to read instead of
+ *      rebuilding them; NULL = not wanted.  SLIM_ERR_SHAPE where
+ *      slim_state_bytes(desc) is 0 (the slices span several windows).
+ * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_FWD), or
+ *      slim_workspace_bytes_states(desc, SLIM_PASS_FWD) with states (the
+ *      slices' states are then built in states itself). */
 slim_status slim_attn_fwd(const slim_desc *desc, const void *Q, const void *K, const void *V, const void *W,
                           const void *R_in, const void *S_in, void *Y, void *R_out, void *S_out, float *koff,
-                          float *row_stats, void *ws, size_t ws_bytes, void *stream);
+                          float *row_stats, float *states, void *ws, size_t ws_bytes, void *stream);
 
 /* Size of the device array slim_attn_fwd_noalloc works in, per GPU: 64 MiB. */
 #define SLIM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* The forward above for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
- * arguments, results and errors as slim_attn_fwd, without ws and ws_bytes: the
+ * arguments, results and errors as slim_attn_fwd, without states, ws and ws_bytes: the
  * workspace is a file-scope device array of SLIM_NOALLOC_SCRATCH_BYTES that each
  * GPU the library runs on holds until the process ends (its address is looked up
  * once per device, on the first call there).  The call allocates and frees
@@ -202,6 +225,13 @@ slim_status slim_attn_fwd_noalloc(const slim_desc *desc, const void *Q, const vo
  *      same inputs (any slice count), or both NULL.  Given, the backward takes
  *      every row's denominator from them and dden_l = -(dY_l . Y_l) / den_l
  *      from Y, instead of recomputing each slice's forward for them;
+ *      states = what a forward call with the same descriptor and inputs wrote
+ *      to its states argument, or NULL.  Where this pass holds every slice in
+ *      one window (always so for SLIM_PASS_BWD when slim_state_bytes(desc) is
+ *      not 0) the backward reads each slice's entry state from it instead of
+ *      rebuilding them (the chunk-state pass and its prefix sum are skipped);
+ *      the values are the ones the rebuild gives, bit for bit, so the results
+ *      are the same.  Elsewhere it is ignored;
  *      dR_out, dS_out = incoming gradient of the final state (both NULL = zero).
  * Out: dQ, dK, dV; dR_in, dS_in = gradient w.r.t. the initial state (both NULL
  *      = not wanted, or both given);
@@ -217,11 +247,12 @@ slim_status slim_attn_fwd_noalloc(const slim_desc *desc, const void *Q, const vo
  * ws : device workspace of at least slim_workspace_bytes(desc, SLIM_PASS_BWD),
  *      or slim_workspace_bytes(desc, SLIM_PASS_BWD_DW) when dW is given (it
  *      adds two [B*H][window rows][M] buffers of the io dtype and the partial
- *      sums of dW). */
+ *      sums of dW); with states, slim_workspace_bytes_states of the same pass. */
 slim_status slim_attn_bwd(const slim_desc *desc, const void *Q, const void *K, const void *V, const void *W,
-                          const void *dY, const void *Y, const float *row_stats, const void *R_in, const void *S_in,
-                          const void *dR_out, const void *dS_out, void *dQ, void *dK, void *dV, void *dR_in,
-                          void *dS_in, float *dW, void *ws, size_t ws_bytes, void *stream);
+                          const void *dY, const void *Y, const float *row_stats, const float *states,
+                          const void *R_in, const void *S_in, const void *dR_out, const void *dS_out, void *dQ,
+                          void *dK, void *dV, void *dR_in, void *dS_in, float *dW, void *ws, size_t ws_bytes,
+                          void *stream);
 
 /* Recurrent decode step: the iterative prefix-sum evaluation of Subsection
  * 2.1 (eq. (3)-(4)) advanced by one position.  For every b, h and the one new

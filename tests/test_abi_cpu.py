@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.slim_version() >> 16 == 3
+    assert lib.slim_version() >> 16 == 4
     for code in range(8):
         assert lib.slim_status_string(code)
     assert lib.slim_status_string(0) == b"ok"
@@ -74,10 +74,10 @@ def test_validate_null(lib):
     assert lib.slim_validate(None, 1) == 1
 
 
-FWD_ARGS = ("Q", "K", "V", "W", "R_in", "S_in", "Y", "R_out", "S_out", "koff", "row_stats", "ws", "ws_bytes",
-            "stream")
-BWD_ARGS = ("Q", "K", "V", "W", "dY", "Y", "row_stats", "R_in", "S_in", "dR_out", "dS_out", "dQ", "dK", "dV",
-            "dR_in", "dS_in", "dW", "ws", "ws_bytes", "stream")
+FWD_ARGS = ("Q", "K", "V", "W", "R_in", "S_in", "Y", "R_out", "S_out", "koff", "row_stats", "states", "ws",
+            "ws_bytes", "stream")
+BWD_ARGS = ("Q", "K", "V", "W", "dY", "Y", "row_stats", "states", "R_in", "S_in", "dR_out", "dS_out", "dQ", "dK",
+            "dV", "dR_in", "dS_in", "dW", "ws", "ws_bytes", "stream")
 P = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
 
 
@@ -195,6 +195,35 @@ def test_workspace_does_not_grow_with_L_at_fixed_slice_and_window(lib):
     assert fw[0] == fw[1]
 
 
+def test_state_handoff_sizes_and_checks(lib):
+    # one window holds every slice: the states buffer holds (slices + 1) states of
+    # (d + 1) x M fp32 per head, and a call given it needs that much less workspace
+    d = d_(B=4, H=16, L=16384, d=64, M=256, num_chunks=32)
+    slot = 65 * 256 * 4
+    assert lib.slim_state_bytes(ctypes.byref(d)) == 64 * 33 * slot
+    for p in (_lib.SLIM_PASS_FWD, _lib.SLIM_PASS_BWD):
+        full = lib.slim_workspace_bytes(ctypes.byref(d), p)
+        assert 0 < lib.slim_workspace_bytes_states(ctypes.byref(d), p) <= full - 64 * 33 * slot
+    # a ragged last slice counts as a slice: L = 1000 in slices of 334 -> 3 slices
+    dr = d_(B=1, H=2, L=1000, d=64, M=128, num_chunks=3)
+    assert lib.slim_state_bytes(ctypes.byref(dr)) == 2 * 4 * 65 * 128 * 4
+    # several windows: no states, and the workspace is the usual one
+    dm = d_(B=1, H=8, L=1 << 20, d=64, M=64, num_chunks=2048, window_chunks=512)
+    assert lib.slim_state_bytes(ctypes.byref(dm)) == 0
+    for p in (_lib.SLIM_PASS_FWD, _lib.SLIM_PASS_BWD):
+        assert lib.slim_workspace_bytes_states(ctypes.byref(dm), p) == lib.slim_workspace_bytes(ctypes.byref(dm), p)
+    # the forward rejects states it cannot fill, and a workspace sized without them is
+    # too small when no states are given; both before anything is enqueued
+    assert fwd(lib, dm, states=P) == 2
+    small = lib.slim_workspace_bytes_states(ctypes.byref(d), _lib.SLIM_PASS_FWD)
+    assert fwd(lib, d, ws_bytes=small) == 5
+    assert bwd(lib, d, ws_bytes=lib.slim_workspace_bytes_states(ctypes.byref(d), _lib.SLIM_PASS_BWD)) == 5
+    assert fwd(lib, d, states=ctypes.c_void_p((1 << 20) + 4)) == 6
+    assert bwd(lib, d, states=ctypes.c_void_p((1 << 20) + 4)) == 6
+    assert lib.slim_state_bytes(ctypes.byref(d_(B=0))) == 0
+    assert lib.slim_workspace_bytes_states(ctypes.byref(d_(B=0)), _lib.SLIM_PASS_FWD) == 0
+
+
 def test_auto_window(lib):
     d = d_(B=4, H=16, L=16384, d=64, M=256, num_chunks=32)
     assert lib.slim_window_chunks(ctypes.byref(d)) == 32
@@ -216,7 +245,10 @@ def test_tile_rows(lib):
     def tr(**kw):
         return lib.slim_tile_rows(ctypes.byref(d_(**kw)))
     assert tr(d=64, M=256) == 32                                   # bf16 FAVOR+ d=64 M=256
-    assert tr(d=128, M=128, feat=_lib.SLIM_FEAT_ELU1) == 32
+    # bf16 elu+1 at d = M = 128: 32-row tiles would take more than 80 KB of LDS in the
+    # dK/dV kernel, so two workgroups could not share a compute unit
+    assert tr(d=128, M=128, feat=_lib.SLIM_FEAT_ELU1) == 16
+    assert tr(d=128, M=128, feat=_lib.SLIM_FEAT_ELU1, dtype=_lib.SLIM_F32) == 32
     assert tr(d=64, M=256, dtype=_lib.SLIM_F32) == 32
     assert tr(d=128, M=256) == 16                                  # 8 waves of d+4 fp32 reduction rows
     assert tr(d=128, M=256, dtype=_lib.SLIM_F32) == 16
