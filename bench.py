@@ -53,8 +53,10 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first (a few do not let the clocks settle: after 3, 1.52 ms per step at "
+                         "the default workload, after 20, 1.46)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-mem-sweep", action="store_true", help="skip the peak-HBM-vs-L rows of the JSON line")
@@ -546,16 +548,17 @@ def algorithm1_sweep(torch, synth):
 DW_PASS_KERNELS = ("bwdq_dw", "bwdq_gstate_dw", "bwdkv_dw", "dw", "dw_sum")
 
 
-def kernel_records(w, prof, steps, tile, nwin):
+def kernel_records(w, prof, steps, tile, nwin, group=1):
     """Per-kernel records from the library's hipEvent timings {name: (ms total, launches)}
     over `steps` steps, and the roofline record of the dominant kernel.  Every chunk and
     scan kernel is launched once per window and covers that window's slices, so one
     launch processes head_tokens / (windows of its pass) token-heads; nwin = windows of
     the forward and plain backward, and the dW pass's are counted from its row
-    contraction, launched once per window."""
+    contraction, launched once per window.  group: slices per workgroup (one state
+    slot per group)."""
     from causal_linear_attention_amd.workloads import kernel_bytes, kernel_flops
     fl = kernel_flops(w, tile)
-    by = kernel_bytes(w)
+    by = kernel_bytes(w, group)
     nwin_dw = prof["dw"][1] / steps if "dw" in prof else nwin
     peak_t = PEAK_TFLOPS[w.dtype]
     kernels = {}
@@ -713,9 +716,10 @@ def main():
     tokens_per_s = w.tokens * args.steps / elapsed
     dsc = A.make_desc(q, w.M, w.feat, w.chunks)
     window = int(_lib.lib().slim_window_chunks(__import__("ctypes").byref(dsc)))
+    group = int(_lib.lib().slim_group_slices(__import__("ctypes").byref(dsc)))
     nchunks = -(-w.L // -(-w.L // w.chunks))  # slices actually used: ceil(L / ceil(L / chunks))
     nwin = -(-nchunks // window)
-    kernels, roofline = kernel_records(w, prof, args.steps, tile, nwin)
+    kernels, roofline = kernel_records(w, prof, args.steps, tile, nwin, group)
     isz = 2 if w.dtype == "bf16" else 4
     # minimum HBM traffic of a step: read Q K V (fwd) and Q K V dY (bwd), write Y dQ dK dV
     io = w.head_tokens * w.d * isz * (11 if w.backward else 4)
@@ -730,7 +734,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "M": w.M, "feat": w.feat,
                    "W": w.w_kind, "chunks": w.chunks, "chunk_len": w.chunk_len, "tile": tile,
-                   "window_chunks": window, "windows": nwin,
+                   "group_slices": group, "window_chunks": window, "windows": nwin,
                    "dW": want_dw, "global_batch": w.B, "seq_len": w.L, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "step_tflops": round(step_flop / (ms_step * 1e-3) / 1e12, 2),

@@ -20,7 +20,7 @@ STATUS = {0: "SLIM_OK", 1: "SLIM_ERR_NULL", 2: "SLIM_ERR_SHAPE", 3: "SLIM_ERR_DT
 
 # every symbol declared in include/slim.h
 EXPORTS = ["slim_validate", "slim_workspace_bytes", "slim_workspace_bytes_states", "slim_state_bytes",
-           "slim_window_chunks", "slim_tile_rows", "slim_featmap", "slim_attn_fwd", "slim_attn_fwd_noalloc",
+           "slim_window_chunks", "slim_group_slices", "slim_tile_rows", "slim_featmap", "slim_attn_fwd", "slim_attn_fwd_noalloc",
            "slim_attn_bwd", "slim_decode_step", "slim_status_string", "slim_version", "slim_prof_enable",
            "slim_prof_count", "slim_prof_entry"]
 
@@ -28,7 +28,8 @@ EXPORTS = ["slim_validate", "slim_workspace_bytes", "slim_workspace_bytes_states
 class SlimDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("L", ctypes.c_int64), ("d", ctypes.c_int64),
                 ("M", ctypes.c_int64), ("num_chunks", ctypes.c_int64), ("window_chunks", ctypes.c_int64),
-                ("dtype", ctypes.c_int32), ("feat", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("feat", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
+                ("group_slices", ctypes.c_int32)]
 
 
 class SlimError(RuntimeError):
@@ -62,6 +63,8 @@ def lib(path: str | None = None):
     L.slim_state_bytes.restype = sz
     L.slim_window_chunks.argtypes = [D]
     L.slim_window_chunks.restype = i64
+    L.slim_group_slices.argtypes = [D]
+    L.slim_group_slices.restype = i64
     L.slim_tile_rows.argtypes = [D]
     L.slim_tile_rows.restype = i64
     L.slim_featmap.argtypes = [D, vp, vp, vp, vp, vp]
@@ -103,9 +106,9 @@ def check(code: int, where: str):
 
 
 def desc(B, H, L, d, M, num_chunks=1, window_chunks=0, dtype=SLIM_F32, feat=SLIM_FEAT_FAVOR,
-         state_dtype=SLIM_F32) -> SlimDesc:
+         state_dtype=SLIM_F32, group_slices=0) -> SlimDesc:
     return SlimDesc(int(B), int(H), int(L), int(d), int(M), int(num_chunks), int(window_chunks), int(dtype),
-                    int(feat), int(state_dtype))
+                    int(feat), int(state_dtype), int(group_slices))
 
 
 def prof_enable(on: bool):

@@ -37,13 +37,14 @@ def _check_io(name, t, dtype, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def make_desc(q, M, feat, num_chunks, window_chunks=0, state_dtype=torch.float32):
+def make_desc(q, M, feat, num_chunks, window_chunks=0, state_dtype=torch.float32, group_slices=0):
     B, H, L, d = q.shape
     if q.dtype not in _DT:
         raise ValueError(f"unsupported dtype {q.dtype}")
     if state_dtype not in _SDT:
         raise ValueError(f"unsupported state dtype {state_dtype}")
-    return _lib.desc(B, H, L, d, M, num_chunks, window_chunks, _DT[q.dtype], _FEAT[feat], _SDT[state_dtype])
+    return _lib.desc(B, H, L, d, M, num_chunks, window_chunks, _DT[q.dtype], _FEAT[feat], _SDT[state_dtype],
+                     group_slices)
 
 
 def _feat_M(W, feat, d):
@@ -65,11 +66,12 @@ def workspace_bytes(desc, pass_, states=False):
     return n
 
 
-def state_shape(q, M, num_chunks):
-    """Shape of the per-slice states attn_fwd(want_states=True) returns."""
-    B, H, L, d = q.shape
-    c = -(-L // num_chunks)
-    return (B, H, -(-L // c) + 1, d + 1, M)
+def state_shape(dsc):
+    """Shape of the per-group states attn_fwd(want_states=True) returns for a
+    descriptor: one entry per group of slices (slim_group_slices) and the final state."""
+    c = -(-dsc.L // dsc.num_chunks)
+    G = _lib.lib().slim_group_slices(ctypes.byref(dsc))
+    return (dsc.B, dsc.H, -(-dsc.L // min(c * G, dsc.L)) + 1, dsc.d + 1, dsc.M)
 
 
 def featmap(x, W=None, feat="favor", row_offset=False):
@@ -88,17 +90,18 @@ def featmap(x, W=None, feat="favor", row_offset=False):
 
 
 def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, window_chunks=0,
-             state_dtype=None, want_row_stats=False, koff_out=None, want_states=False):
+             state_dtype=None, want_row_stats=False, koff_out=None, want_states=False, group_slices=0):
     """Forward.  Returns (Y, R_out [B,H,d,M], S_out [B,H,M]).  States are fp32, or
     fp64 when R_in is fp64 or state_dtype=torch.float64; like R_in, S_in they hold
     the state times exp(-koff), the key-side offset of W (0 unless some row of W has
     |w_m|^2 > 120).  want_row_stats: a fourth value, the per-row statistics
     [B,H,L,2] fp32 that let attn_bwd skip recomputing the denominators (pass it
     with Y).  want_states: a fifth value (the fourth None unless want_row_stats),
-    the state entering every slice [B,H,slices+1,d+1,M] fp32 (rows < d: R, row d:
-    S, times exp(-koff)) for attn_bwd to read instead of rebuilding them, or None
-    where the slices span several windows.  koff_out: a one-element fp32 GPU
-    tensor that receives koff."""
+    the state entering every group of slices [B,H,groups+1,d+1,M] fp32 (rows < d:
+    R, row d: S, times exp(-koff)) for attn_bwd to read instead of rebuilding them,
+    or None where the slices span several windows.  koff_out: a one-element fp32
+    GPU tensor that receives koff.  group_slices: consecutive slices one workgroup
+    walks (0 = automatic, 1 = one slice each); pass the same to attn_bwd."""
     B, H, L, d = q.shape
     M = _feat_M(W, feat, d)
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -109,10 +112,10 @@ def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, 
     if R_in is not None:
         _check_io("R_in", R_in, sd, (B, H, d, M))
         _check_io("S_in", S_in, sd, (B, H, M))
-    dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd)
+    dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd, group_slices)
     st = None
     if want_states and _lib.lib().slim_state_bytes(ctypes.byref(dsc)) > 0:
-        st = torch.empty(state_shape(q, M, num_chunks), dtype=torch.float32, device=q.device)
+        st = torch.empty(state_shape(dsc), dtype=torch.float32, device=q.device)
         assert st.numel() * 4 == _lib.lib().slim_state_bytes(ctypes.byref(dsc))
     ws = torch.empty(max(1, workspace_bytes(dsc, _lib.SLIM_PASS_FWD, st is not None)), dtype=torch.uint8,
                      device=q.device)
@@ -134,7 +137,7 @@ def attn_fwd(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, 
 
 
 def attn_fwd_noalloc(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_in=None, window_chunks=0,
-                     state_dtype=None, want_row_stats=False, koff_out=None, out=None):
+                     state_dtype=None, want_row_stats=False, koff_out=None, out=None, group_slices=0):
     """attn_fwd through slim_attn_fwd_noalloc: the library allocates no workspace (it
     works in its own fixed device array).  out: optional (Y, R_out, S_out[, row_stats])
     tensors to write into, so that a caller can avoid every allocation; else they are
@@ -149,7 +152,7 @@ def attn_fwd_noalloc(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_i
     if R_in is not None:
         _check_io("R_in", R_in, sd, (B, H, d, M))
         _check_io("S_in", S_in, sd, (B, H, M))
-    dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd)
+    dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd, group_slices)
     if out is None:
         Y = torch.empty_like(q)
         R = torch.empty((B, H, d, M), dtype=sd, device=q.device)
@@ -176,7 +179,7 @@ def attn_fwd_noalloc(q, k, v, W=None, feat="favor", num_chunks=1, R_in=None, S_i
 
 def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, dR_out=None, dS_out=None,
              want_state_grad=False, window_chunks=0, state_dtype=None, want_dw=False, Y=None, row_stats=None,
-             states=None):
+             states=None, group_slices=0):
     """Backward of attn_fwd(q, k, v, W, feat, num_chunks, R_in, S_in) for the
     loss <dY, Y> + <dR_out, R_out> + <dS_out, S_out>.  Returns (dQ, dK, dV,
     dR_in, dS_in); the last two are None unless want_state_grad.  With want_dw
@@ -207,9 +210,9 @@ def attn_bwd(q, k, v, W, dY, feat="favor", num_chunks=1, R_in=None, S_in=None, d
     if Y is not None:
         _check_io("Y", Y, q.dtype, q.shape)
         _check_io("row_stats", row_stats, torch.float32, (B, H, L, 2))
-    dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd)
+    dsc = make_desc(q, M, feat, num_chunks, window_chunks, sd, group_slices)
     if states is not None:
-        _check_io("states", states, torch.float32, state_shape(q, M, num_chunks))
+        _check_io("states", states, torch.float32, state_shape(dsc))
     ps = _lib.SLIM_PASS_BWD_DW if want_dw else _lib.SLIM_PASS_BWD
     ws = torch.empty(max(1, workspace_bytes(dsc, ps, states is not None)), dtype=torch.uint8, device=q.device)
     dQ, dK, dV = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -271,9 +274,9 @@ def decode_step(q, k, v, W=None, feat="favor", R=None, S=None, inplace=False, st
 
 class _SlimAttention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, W, feat, num_chunks, window_chunks, keep_states):
+    def forward(ctx, q, k, v, W, feat, num_chunks, window_chunks, keep_states, group_slices):
         out = attn_fwd(q, k, v, W, feat, num_chunks, window_chunks=window_chunks, want_row_stats=True,
-                       want_states=keep_states)
+                       want_states=keep_states, group_slices=group_slices)
         Y, rs, st = out[0], out[3], out[4] if keep_states else None
         # Kept for the backward: the inputs, the output, 8 bytes per row of
         # denominator statistics and, where one window holds every slice and
@@ -283,7 +286,7 @@ class _SlimAttention(torch.autograd.Function):
         ctx.save_for_backward(q, k, v, W if W is not None else torch.empty(0), Y, rs,
                               st if st is not None else torch.empty(0))
         ctx.feat, ctx.num_chunks, ctx.window_chunks, ctx.has_w = feat, num_chunks, window_chunks, W is not None
-        ctx.has_st = st is not None
+        ctx.has_st, ctx.group_slices = st is not None, group_slices
         return Y
 
     @staticmethod
@@ -292,15 +295,16 @@ class _SlimAttention(torch.autograd.Function):
         want_dw = ctx.has_w and ctx.needs_input_grad[3]
         g = attn_bwd(q, k, v, W if ctx.has_w else None, dY.contiguous(), ctx.feat, ctx.num_chunks,
                      window_chunks=ctx.window_chunks, want_dw=want_dw, Y=Y, row_stats=rs,
-                     states=st if ctx.has_st else None)
+                     states=st if ctx.has_st else None, group_slices=ctx.group_slices)
         dW = g[5].to(W.dtype) if want_dw else None
-        return g[0], g[1], g[2], dW, None, None, None, None
+        return g[0], g[1], g[2], dW, None, None, None, None, None
 
 
-def slim_attention(q, k, v, W=None, feat="favor", num_chunks=1, window_chunks=0, keep_states=True):
+def slim_attention(q, k, v, W=None, feat="favor", num_chunks=1, window_chunks=0, keep_states=True, group_slices=0):
     """Causal linear attention with autograd: gradients for q, k, v, and for
     the FAVOR+ projection W when it requires one (the page keeps W a fixed
     random projection; a caller may train it).  keep_states: where one window
     holds every slice, keep each slice's entry state from the forward for the
-    backward ((d+1) M fp32 per slice and head) instead of rebuilding them."""
-    return _SlimAttention.apply(q, k, v, W, feat, num_chunks, window_chunks, keep_states)
+    backward ((d+1) M fp32 per group of slices and head) instead of rebuilding them.
+    group_slices: consecutive slices one workgroup walks (0 = automatic)."""
+    return _SlimAttention.apply(q, k, v, W, feat, num_chunks, window_chunks, keep_states, group_slices)

@@ -252,6 +252,8 @@ __device__ __forceinline__ void wave_lds_fence()
 // Floats per row of the backward's row statistics: 1/den, dden, the query
 // feature offset (exp2 domain) and one unused.
 constexpr int ROWSTAT = 4;
+// Rows per workgroup of the row-statistics kernel (its grid splits each chunk in parts).
+constexpr int ROWSTAT_ROWS = 256;
 
 // Key-side offset of the FAVOR+ map, one number per projection W.  For every key
 // k and feature m, w_m.k - |k|^2/2 = |w_m|^2/2 - |k - w_m|^2/2 <= |w_m|^2/2, so

@@ -268,7 +268,12 @@ static const DwTable *find_dw(const slim_desc *d)
 }
 
 struct Plan {
-    long long BH, c, nchunks, P, SZ;
+    long long BH;
+    long long G;        // slices per group: one workgroup walks G consecutive slices
+    long long c;        // rows per group (G slices, at most L)
+    long long nchunks;  // groups
+    long long P;        // groups per window
+    long long SZ;
     long long dw_parts;  // dW pass: partial sums per window (2 sides x BH x workgroups per head)
     size_t slots_off, gslots_off, stats_off, cR_off, cS_off, gR_off, gS_off, wt_off, koff_off;
     size_t pq_off, pk_off, part_off, part2_off;
@@ -307,9 +312,9 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // for its two [c][M] rows of dg(X) . g(X) per slice and head.  The workspace is
 // therefore bounded for any L at a given slice length.
 constexpr long long WINDOW_BUDGET = 1LL << 30;
-static long long resolve_window(const slim_desc *d, long long nchunks, long long c, int pass)
+static long long resolve_window(const slim_desc *d, long long nchunks, long long c, long long G, int pass)
 {
-    long long P = d->window_chunks;
+    long long P = d->window_chunks > 0 ? (d->window_chunks / G > 0 ? d->window_chunks / G : 1) : 0;
     if (P <= 0) {
         const long long BH = d->B * d->H;
         const long long per_state = BH * ((d->d + 1) * d->M * 4 * 2 + c * ROWSTAT * 4);
@@ -326,15 +331,34 @@ static long long resolve_window(const slim_desc *d, long long nchunks, long long
     return P;
 }
 
-// window > 0: hold that many slices per window instead of the resolved window.
+// Slices per group: the chunk kernels run one workgroup per group of G consecutive
+// slices, walking them in order and carrying the state from one slice to the next (the
+// slice loop of Subsection 3.2, G slices at a time), so that one state per group is
+// written, scanned and read back, and a workgroup's start-up (loading its entry state)
+// is paid once per group.  Automatic: G a power of two with groups of at most 1024
+// rows, while at least 1024 workgroups per launch remain (at the 16K-token, 64-head
+// shape in slices of 512 the step goes from 1.62 to 1.47 ms with two slices per group;
+// at d = M = 128 elu+1 in slices of 256 from 1.43 to 1.24 ms).
+static long long group_of(const slim_desc *d, long long nslices, long long c)
+{
+    if (d->group_slices > 0) return d->group_slices < nslices ? d->group_slices : nslices;
+    const long long BH = d->B * d->H;
+    long long G = 1;
+    while (2 * G * c <= 1024 && (nslices + 2 * G - 1) / (2 * G) * BH >= 1024) G *= 2;
+    return G;
+}
+
+// window > 0: hold that many groups per window instead of the resolved window.
 static Plan plan(const slim_desc *d, int pass, long long window = 0)
 {
     Plan p;
     memset(&p, 0, sizeof(p));
     p.BH = d->B * d->H;
-    p.c = (d->L + d->num_chunks - 1) / d->num_chunks;
+    const long long cs = (d->L + d->num_chunks - 1) / d->num_chunks;  // rows per slice
+    p.G = group_of(d, (d->L + cs - 1) / cs, cs);
+    p.c = cs * p.G < d->L ? cs * p.G : d->L;
     p.nchunks = (d->L + p.c - 1) / p.c;
-    p.P = window > 0 ? (window < p.nchunks ? window : p.nchunks) : resolve_window(d, p.nchunks, p.c, pass);
+    p.P = window > 0 ? (window < p.nchunks ? window : p.nchunks) : resolve_window(d, p.nchunks, p.c, p.G, pass);
     p.SZ = (d->d + 1) * d->M;
     const size_t slots = (size_t)p.BH * (p.P + 1) * p.SZ * 4;
     size_t off = 0;
@@ -459,7 +483,7 @@ slim_status slim_validate(const slim_desc *d, int pass)
     if (d->B < 1 || d->H < 1 || d->L < 1 || d->d < 1 || d->M < 1) return SLIM_ERR_SHAPE;
     if (d->L >= (1LL << 31) || d->B > (1LL << 31) || d->H > (1LL << 31)) return SLIM_ERR_SHAPE;
     if (pass != SLIM_PASS_FEATMAP && (d->num_chunks < 1 || d->num_chunks > d->L)) return SLIM_ERR_SHAPE;
-    if (d->window_chunks < 0) return SLIM_ERR_SHAPE;
+    if (d->window_chunks < 0 || d->group_slices < 0) return SLIM_ERR_SHAPE;
     if (d->feat == SLIM_FEAT_ELU1 && d->M != d->d) return SLIM_ERR_SHAPE;
     if (d->state_dtype != SLIM_F32 && d->state_dtype != SLIM_F64) return SLIM_ERR_DTYPE;
     if (pass == SLIM_PASS_DECODE && d->L != 1) return SLIM_ERR_SHAPE;
@@ -494,7 +518,15 @@ size_t slim_workspace_bytes_states(const slim_desc *d, int pass)
 int64_t slim_window_chunks(const slim_desc *d)
 {
     if (slim_validate(d, SLIM_PASS_FWD) != SLIM_OK) return 0;
-    return plan(d, SLIM_PASS_FWD).P;
+    const Plan p = plan(d, SLIM_PASS_FWD);
+    const long long cs = (d->L + d->num_chunks - 1) / d->num_chunks, ns = (d->L + cs - 1) / cs;
+    return p.P * p.G < ns ? p.P * p.G : ns;
+}
+
+int64_t slim_group_slices(const slim_desc *d)
+{
+    if (slim_validate(d, SLIM_PASS_FWD) != SLIM_OK) return 0;
+    return plan(d, SLIM_PASS_FWD).G;
 }
 
 int64_t slim_tile_rows(const slim_desc *d)
@@ -749,7 +781,7 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
         }
         const dim3 cg(np, BH);
         if (Y)  // the forward's denominators and query offsets, and dden from its output
-            SLIM_TIMED("rowstat", s, kt->rowstat(cg, s, a));
+            SLIM_TIMED("rowstat", s, kt->rowstat(dim3(np * (unsigned)((p.c + ROWSTAT_ROWS - 1) / ROWSTAT_ROWS), BH), s, a));
         else
             SLIM_TIMED("stats", s, kt->stats(cg, s, a));
         if (kt->gstate) {

@@ -107,7 +107,9 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StatsSmem<C>), C::NW))
 // rowstat_kernel: the same per-row statistics from what the forward kept: its output Y
 // and, per row, 1/den at the common query offset and that offset (ChunkArgs::rstat).
 // dden = -(dY . Y) / den, since Y = Num / den; one row per VPR lanes (16-byte loads of
-// Y and dY), the dot product reduced by lane shuffles.  Grid as the chunk kernels.
+// Y and dY), the dot product reduced by lane shuffles.  Grid: (chunks of the window x
+// parts of ROWSTAT_ROWS rows, heads), so that the launch has as many workgroups for
+// long chunks as for short ones.
 constexpr int ROWSTAT_NT = 256;
 template <class C> __global__ __launch_bounds__(ROWSTAT_NT) void rowstat_kernel(ChunkArgs a)
 {
@@ -115,15 +117,20 @@ template <class C> __global__ __launch_bounds__(ROWSTAT_NT) void rowstat_kernel(
     typedef typename Vec16<T>::type VT;
     constexpr int EPV = Vec16<T>::N, VPR = C::D / EPV, RPP = ROWSTAT_NT / VPR;
     static_assert(64 % VPR == 0, "a row's lanes stay in one wave");
-    const ChunkGeom G = chunk_geom<C>(a);
-    const T *dY = (const T *)a.dY + G.hb, *Y = (const T *)a.Yin + G.hb;
-    const float *rs = a.rstat + ((size_t)G.bh * a.L + G.row0) * 2;
-    float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
+    const int parts = (a.c + ROWSTAT_ROWS - 1) / ROWSTAT_ROWS;
+    const int nl = blockIdx.x / parts, bh = blockIdx.y;
+    const long long row0 = (long long)(a.n0 + nl) * a.c;
+    const int len = (int)min((long long)a.c, a.L - row0);
+    const int r0 = (blockIdx.x % parts) * ROWSTAT_ROWS, r1 = min(len, r0 + ROWSTAT_ROWS);
+    const size_t hb = ((size_t)bh * (size_t)a.L + (size_t)row0) * C::D;
+    const T *dY = (const T *)a.dY + hb, *Y = (const T *)a.Yin + hb;
+    const float *rs = a.rstat + ((size_t)bh * a.L + row0) * 2;
+    float *st = a.stats + ((size_t)bh * a.P + nl) * (size_t)a.c * ROWSTAT;
     const int sub = threadIdx.x % VPR, rsl = threadIdx.x / VPR;
-    for (int t0 = 0; t0 < G.len; t0 += RPP) {
+    for (int t0 = r0; t0 < r1; t0 += RPP) {
         const int t = t0 + rsl;
         float p = 0.f;
-        if (t < G.len) {
+        if (t < r1) {
             const VT y = gload<VT>(Y + (size_t)t * C::D + sub * EPV);
             const VT g = gload<VT>(dY + (size_t)t * C::D + sub * EPV);
 #pragma unroll
@@ -131,7 +138,7 @@ template <class C> __global__ __launch_bounds__(ROWSTAT_NT) void rowstat_kernel(
         }
 #pragma unroll
         for (int o = 1; o < VPR; o <<= 1) p += __shfl_xor(p, o, 64);
-        if (t < G.len && sub == 0) {
+        if (t < r1 && sub == 0) {
             const float2 r = *reinterpret_cast<const float2 *>(rs + (size_t)t * 2);
             *reinterpret_cast<f4 *>(st + (size_t)t * ROWSTAT) = f4{r.x, -p * r.x, r.y, 0.f};
         }

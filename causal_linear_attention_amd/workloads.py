@@ -150,15 +150,15 @@ def kernel_flops(w: Workload, tile: int) -> dict:
     }
 
 
-def kernel_bytes(w: Workload) -> dict:
+def kernel_bytes(w: Workload, group: int = 1) -> dict:
     """Algorithmic HBM bytes per (token, head) of each chunk kernel and scan: every
     input tensor row read once, every output row written once, one (d+1) x M fp32
-    state slot read or written per chunk (so per row: slot / c), 16 bytes of row
-    statistics (1/den, dden, query offset, one unused float) per row where used.  No
-    re-reads, no caches."""
+    state slot read or written per workgroup's group of `group` slices (so per row:
+    slot / (group c)), 16 bytes of row statistics (1/den, dden, query offset, one
+    unused float) per row where used.  No re-reads, no caches."""
     s = 2 if w.dtype == "bf16" else 4
     row = w.d * s                                   # one Q/K/V/Y/dY/dQ/dK/dV row
-    slot = (w.d + 1) * w.M * 4 / w.chunk_len        # one chunk state, per row of the chunk
+    slot = (w.d + 1) * w.M * 4 / min(w.chunk_len * group, w.L)  # one group's state, per row
     st = 16
     return {
         "state": 2 * row + slot,                    # K, V -> chunk state

@@ -115,6 +115,12 @@ typedef struct slim_desc {
                               SLIM_F64 (states passed between calls then keep the
                               precision of the internal fp64 carries; the decode step
                               then updates the state in fp64) */
+    int32_t group_slices;  /* consecutive slices one workgroup walks, carrying the state
+                              from one to the next (the page's slice loop, that many
+                              slices at a time): one state per group is stored, scanned
+                              and read back.  0 = automatic (slim_group_slices); 1 = one
+                              slice per workgroup.  Results differ between groupings
+                              only in fp32 rounding order. */
 } slim_desc;
 
 /* Host-only check of a descriptor for a pass; touches no GPU.  SLIM_PASS_DECODE
@@ -125,17 +131,25 @@ slim_status slim_validate(const slim_desc *desc, int pass);
  * descriptor is invalid.  Host-only. */
 size_t slim_workspace_bytes(const slim_desc *desc, int pass);
 
-/* Slices whose states one window holds (the resolved window_chunks) in the forward
- * and the plain backward; the backward with dW may hold fewer (see window_chunks). */
+/* Slices whose states one window holds (the resolved window_chunks, a whole number of
+ * groups) in the forward and the plain backward; the backward with dW may hold fewer
+ * (see window_chunks).  A given window_chunks is rounded down to whole groups (at
+ * least one). */
 int64_t slim_window_chunks(const slim_desc *desc);
 
+/* Slices per group (desc.group_slices, or the automatic choice: a power of two with
+ * groups of at most 1024 rows while at least 1024 workgroups per launch remain, else
+ * 1).  0 if the descriptor is invalid.  Host-only. */
+int64_t slim_group_slices(const slim_desc *desc);
+
 /* Bytes of the `states` buffer slim_attn_fwd can fill for the backward: the state
- * entering every slice, [B*H][num_chunks' + 1][d + 1][M] fp32 (num_chunks' =
- * ceil(L / c), the slices there are), entry n of a head holding R (rows e < d,
- * stored [e][m] = R[e][m]) and S (row d) before slice n, scaled by exp(-koff):
- * entry 0 the initial state, the last entry the final state.  Only when one
- * window holds every slice (slim_window_chunks(desc) == num_chunks'); else 0,
- * and states cannot be kept.  Host-only; 0 for an invalid descriptor. */
+ * entering every group of slices, [B*H][n + 1][d + 1][M] fp32 (n = ceil(L / (G c)),
+ * the groups there are, G = slim_group_slices(desc), c the slice length), entry j
+ * of a head holding R (rows e < d, stored [e][m] = R[e][m]) and S (row d) before
+ * group j, i.e. after the first j G slices, scaled by exp(-koff): entry 0 the
+ * initial state, the last entry the final state.  Only when one window holds every
+ * slice (slim_window_chunks(desc) equal to the number of slices); else 0, and states
+ * cannot be kept.  Host-only; 0 for an invalid descriptor. */
 size_t slim_state_bytes(const slim_desc *desc);
 
 /* Workspace bytes of a pass (SLIM_PASS_FWD, SLIM_PASS_BWD, SLIM_PASS_BWD_DW) when

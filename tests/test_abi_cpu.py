@@ -133,9 +133,13 @@ def test_dw_pass_validation(lib):
     d = dict(B=2, H=3, L=4096, d=64, M=128, num_chunks=16, window_chunks=16)
     extra = ws(lib, DW, **d) - ws(lib, BWD, **d)
     assert extra >= 2 * 6 * 4096 * 128 * 2
-    # bounded by the window, not by L
-    big = [ws(lib, DW, B=1, H=8, L=n, d=64, M=64, num_chunks=n // 512, window_chunks=64) for n in (1 << 16, 1 << 20)]
+    # bounded by the window, not by L (one slice per workgroup: the automatic grouping
+    # depends on L and only shrinks the per-group buffers)
+    big = [ws(lib, DW, B=1, H=8, L=n, d=64, M=64, num_chunks=n // 512, window_chunks=64, group_slices=1)
+           for n in (1 << 16, 1 << 20)]
     assert big[0] == big[1]
+    auto = [ws(lib, DW, B=1, H=8, L=n, d=64, M=64, num_chunks=n // 512, window_chunks=64) for n in (1 << 16, 1 << 20)]
+    assert max(auto) <= big[0]
 
 
 @pytest.mark.parametrize("dtype", [_lib.SLIM_F32, _lib.SLIM_BF16])
@@ -188,10 +192,18 @@ def test_workspace_sizes(lib):
 
 def test_workspace_does_not_grow_with_L_at_fixed_slice_and_window(lib):
     # slice length 512, window of 64 slices: once L exceeds 64 * 512 the workspace is flat
-    sizes = [ws(lib, 2, B=1, H=8, L=n, d=64, M=64, num_chunks=n // 512, window_chunks=64)
-             for n in (1 << 15, 1 << 16, 1 << 18, 1 << 20)]
-    assert len(set(sizes)) == 1, sizes
-    fw = [ws(lib, 1, B=1, H=8, L=n, d=64, M=64, num_chunks=n // 512, window_chunks=64) for n in (1 << 15, 1 << 20)]
+    # (one slice per workgroup); with the automatic grouping, which takes two slices per
+    # workgroup once there are enough of them, it never exceeds that
+    for g in (1, 0):
+        sizes = [ws(lib, 2, B=1, H=8, L=n, d=64, M=64, num_chunks=n // 512, window_chunks=64, group_slices=g)
+                 for n in (1 << 15, 1 << 16, 1 << 18, 1 << 20)]
+        if g == 1:
+            assert len(set(sizes)) == 1, sizes
+            flat = sizes[0]
+        else:
+            assert max(sizes) <= flat and sizes[-1] == sizes[-2], sizes
+    fw = [ws(lib, 1, B=1, H=8, L=n, d=64, M=64, num_chunks=n // 512, window_chunks=64, group_slices=1)
+          for n in (1 << 15, 1 << 20)]
     assert fw[0] == fw[1]
 
 
@@ -200,13 +212,21 @@ def test_state_handoff_sizes_and_checks(lib):
     # (d + 1) x M fp32 per head, and a call given it needs that much less workspace
     d = d_(B=4, H=16, L=16384, d=64, M=256, num_chunks=32)
     slot = 65 * 256 * 4
-    assert lib.slim_state_bytes(ctypes.byref(d)) == 64 * 33 * slot
-    for p in (_lib.SLIM_PASS_FWD, _lib.SLIM_PASS_BWD):
-        full = lib.slim_workspace_bytes(ctypes.byref(d), p)
-        assert 0 < lib.slim_workspace_bytes_states(ctypes.byref(d), p) <= full - 64 * 33 * slot
-    # a ragged last slice counts as a slice: L = 1000 in slices of 334 -> 3 slices
+    assert lib.slim_group_slices(ctypes.byref(d)) == 2  # 16 groups of two slices of 512
+    assert lib.slim_state_bytes(ctypes.byref(d)) == 64 * 17 * slot
+    d1 = d_(B=4, H=16, L=16384, d=64, M=256, num_chunks=32, group_slices=1)
+    assert lib.slim_state_bytes(ctypes.byref(d1)) == 64 * 33 * slot
+    for dd, n in ((d, 17), (d1, 33)):
+        for p in (_lib.SLIM_PASS_FWD, _lib.SLIM_PASS_BWD):
+            full = lib.slim_workspace_bytes(ctypes.byref(dd), p)
+            assert 0 < lib.slim_workspace_bytes_states(ctypes.byref(dd), p) <= full - 64 * n * slot
+    # a ragged last slice counts as a slice: L = 1000 in slices of 334 -> 3 slices, and
+    # in groups of two: 2 groups (668 rows, then 332)
     dr = d_(B=1, H=2, L=1000, d=64, M=128, num_chunks=3)
+    assert lib.slim_group_slices(ctypes.byref(dr)) == 1
     assert lib.slim_state_bytes(ctypes.byref(dr)) == 2 * 4 * 65 * 128 * 4
+    dr2 = d_(B=1, H=2, L=1000, d=64, M=128, num_chunks=3, group_slices=2)
+    assert lib.slim_state_bytes(ctypes.byref(dr2)) == 2 * 3 * 65 * 128 * 4
     # several windows: no states, and the workspace is the usual one
     dm = d_(B=1, H=8, L=1 << 20, d=64, M=64, num_chunks=2048, window_chunks=512)
     assert lib.slim_state_bytes(ctypes.byref(dm)) == 0
@@ -234,11 +254,38 @@ def test_auto_window(lib):
     # slice and head here) exceed 1 GiB gets windows of about 4096 workgroups again
     per = 8 * (65 * 64 * 4 * 2 + 512 * 16)
     assert 2048 * per <= 1 << 30 < 4096 * per
-    d = d_(B=1, H=8, L=1 << 22, d=64, M=64, num_chunks=1 << 13)
+    d = d_(B=1, H=8, L=1 << 22, d=64, M=64, num_chunks=1 << 13, group_slices=1)
     assert lib.slim_window_chunks(ctypes.byref(d)) == 512
-    # many heads: about 4096 workgroups per launch when that is more
-    d = d_(B=64, H=64, L=4096, d=64, M=256, num_chunks=64)
+    # in groups of two slices (the automatic choice there): 512 workgroups of two slices
+    d = d_(B=1, H=8, L=1 << 22, d=64, M=64, num_chunks=1 << 13)
+    assert lib.slim_group_slices(ctypes.byref(d)) == 2
+    assert lib.slim_window_chunks(ctypes.byref(d)) == 1024
+    # many heads: about 4096 workgroups per launch when that is more; one group of
+    # slices each (slices of 64 rows go 16 to a group)
+    d = d_(B=64, H=64, L=4096, d=64, M=256, num_chunks=64, group_slices=1)
     assert lib.slim_window_chunks(ctypes.byref(d)) == 1
+    d = d_(B=64, H=64, L=4096, d=64, M=256, num_chunks=64)
+    assert lib.slim_group_slices(ctypes.byref(d)) == 16
+    assert lib.slim_window_chunks(ctypes.byref(d)) == 16
+
+
+def test_group_slices(lib):
+    def g(**kw):
+        return lib.slim_group_slices(ctypes.byref(d_(**kw)))
+    # groups of at most 1024 rows while at least 1024 workgroups per launch remain
+    assert g(B=4, H=16, L=16384, d=64, M=256, num_chunks=32) == 2        # 16 x 64 = 1024 workgroups
+    assert g(B=1, H=8, L=1 << 20, d=64, M=64, num_chunks=2048) == 2      # 1024 x 8
+    assert g(B=8, H=12, L=8192, d=128, M=128, num_chunks=32, feat=_lib.SLIM_FEAT_ELU1) == 2  # not 4: 768
+    assert g(B=2, H=8, L=4096, d=64, M=128, num_chunks=16) == 1          # 256 workgroups already
+    assert g(B=1, H=8, L=1 << 20, d=64, M=64, num_chunks=8192) == 8      # slices of 128: groups of 1024 rows
+    assert g(B=64, H=64, L=4096, d=64, M=64, num_chunks=4) == 1          # slices of 1024 rows
+    # given: taken as is, at most the slices there are
+    assert g(group_slices=3) == 3
+    assert g(L=1000, num_chunks=3, group_slices=5) == 3
+    assert validate(lib, group_slices=-1) == 2
+    # a window given in slices holds whole groups, at least one
+    assert lib.slim_window_chunks(ctypes.byref(d_(L=4096, num_chunks=16, window_chunks=5, group_slices=2))) == 4
+    assert lib.slim_window_chunks(ctypes.byref(d_(L=4096, num_chunks=16, window_chunks=1, group_slices=4))) == 4
 
 
 def test_tile_rows(lib):
