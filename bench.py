@@ -102,9 +102,9 @@ def kernel_source_hash():
 
 
 def short_kernel(name):
-    m = re.match(r"void slim::scan_kernel<(\d)>", name)
+    m = re.match(r"void slim::scan_kernel<(\d)(?:, (?:true|false))?>", name)
     if m:
-        return ("scan_prefix", "scan_reverse", "scan_grad")[int(m.group(1))]
+        return ("scan_prefix", "scan_window", "scan_grad", "scan_sum")[int(m.group(1))]
     m = re.match(r"void slim::(\w+?)_kernel<", name) or re.match(r"_ZN4slim\d+(\w+?)_kernel", name)
     if m:
         return m.group(1)

@@ -690,7 +690,11 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StateSmem<C>), C::NW))
 // segment, the segment totals are exchanged through LDS, and each thread then sweeps
 // its segment starting from the carry plus the totals of the segments before it
 // (after it, for the suffix).
-template <int MODE>
+// SCAN_KEEP: segments of at most that many slots are read once, held in registers from
+// the totals pass to the sweep (KEEP, for when there is a totals pass); the variant
+// without keeps its registers low for the single sweep.
+constexpr int SCAN_KEEP = 32;
+template <int MODE, bool KEEP>
 __global__ __launch_bounds__(256) void scan_kernel(float *slots, double *carryR, double *carryS, int DM, int M, int P,
                                                    int np, int G)
 {
@@ -710,14 +714,28 @@ __global__ __launch_bounds__(256) void scan_kernel(float *slots, double *carryR,
     // segment totals: needed by the window-start and accumulate modes, and by every
     // mode when the chunks are split over several segments
     const bool totals = MODE == 1 || MODE == 3 || G > 1;
+    // (the sums keep their order either way)
+    const bool keep = KEEP && totals && sl <= SCAN_KEEP;
+    f4 buf[KEEP ? SCAN_KEEP : 1];
     double cur[4] = {0.0, 0.0, 0.0, 0.0}, seg[4] = {0.0, 0.0, 0.0, 0.0};
     if (active) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) cur[j] = cp[j];
-        for (int n = na; totals && n < nb; ++n) {
-            const f4 dl = *slot(n + 1);
+        if (keep) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) seg[j] += (double)dl[j];
+            for (int u = 0; u < (KEEP ? SCAN_KEEP : 0); ++u)
+                if (na + u < nb) buf[u] = *slot(na + u + 1);
+#pragma unroll
+            for (int u = 0; u < (KEEP ? SCAN_KEEP : 0); ++u)
+                if (na + u < nb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) seg[j] += (double)buf[u][j];
+        } else {
+            for (int n = na; totals && n < nb; ++n) {
+                const f4 dl = *slot(n + 1);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) seg[j] += (double)dl[j];
+            }
         }
     }
 #pragma unroll
@@ -751,11 +769,21 @@ __global__ __launch_bounds__(256) void scan_kernel(float *slots, double *carryR,
             run[j] = start[j] + before[j];
         }
         if (g == 0) put(0, start);
-        for (int n = na; n < nb; ++n) {
-            const f4 dl = *slot(n + 1);
+        if (keep) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) run[j] += (double)dl[j];
-            put(n + 1, run);
+            for (int u = 0; u < (KEEP ? SCAN_KEEP : 0); ++u)
+                if (na + u < nb) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) run[j] += (double)buf[u][j];
+                    put(na + u + 1, run);
+                }
+        } else {
+            for (int n = na; n < nb; ++n) {
+                const f4 dl = *slot(n + 1);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) run[j] += (double)dl[j];
+                put(n + 1, run);
+            }
         }
         if (last)
 #pragma unroll
@@ -764,11 +792,21 @@ __global__ __launch_bounds__(256) void scan_kernel(float *slots, double *carryR,
         double run[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) run[j] = cur[j] + after[j];
-        for (int n = nb - 1; n >= na; --n) {
-            const f4 dl = *slot(n + 1);
-            put(n + 1, run);
+        if (keep) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) run[j] += (double)dl[j];
+            for (int u = (KEEP ? SCAN_KEEP : 0) - 1; u >= 0; --u)
+                if (na + u < nb) {
+                    put(na + u + 1, run);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) run[j] += (double)buf[u][j];
+                }
+        } else {
+            for (int n = nb - 1; n >= na; --n) {
+                const f4 dl = *slot(n + 1);
+                put(n + 1, run);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) run[j] += (double)dl[j];
+            }
         }
         if (g == 0) {
             put(0, run);
