@@ -558,7 +558,8 @@ def kernel_records(w, prof, steps, tile, nwin, group=1):
     slot per group)."""
     from causal_linear_attention_amd.workloads import kernel_bytes, kernel_flops
     fl = kernel_flops(w, tile)
-    by = kernel_bytes(w, group)
+    # the row statistics: made by the dQ kernel unless a pass of their own ran
+    by = kernel_bytes(w, group, fr="rowstat" not in prof and "stats" not in prof)
     nwin_dw = prof["dw"][1] / steps if "dw" in prof else nwin
     peak_t = PEAK_TFLOPS[w.dtype]
     kernels = {}

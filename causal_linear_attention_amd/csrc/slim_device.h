@@ -349,8 +349,10 @@ template <typename T, int D, int TT, int NT> struct TileRegs {
     V v[PER];
     float s[PER];
 
-    // stats (optional): per-row (scale, unused) pairs; row t's scale goes with its vectors.
-    __device__ __forceinline__ void load(const T *__restrict__ src, int nvalid, const float *stats = nullptr)
+    // stats (optional): per-row records of sstride floats whose first is the row's
+    // scale; row t's scale goes with its vectors.
+    __device__ __forceinline__ void load(const T *__restrict__ src, int nvalid, const float *stats = nullptr,
+                                         int sstride = ROWSTAT)
     {
         const T *base = uniform_ptr(src);
         const float *sbase = stats ? uniform_ptr(stats) : nullptr;
@@ -360,7 +362,7 @@ template <typename T, int D, int TT, int NT> struct TileRegs {
             const int t = idx / VPR, c = (idx % VPR) * EPV;
             const bool ok = idx < NV && t < nvalid;
             v[i] = ok ? gload<V>(base + (unsigned)(t * D + c)) : zero16<T>();
-            if (stats) s[i] = ok ? gload<float>(sbase + (unsigned)(t * ROWSTAT)) : 0.f;
+            if (stats) s[i] = ok ? gload<float>(sbase + (unsigned)(t * sstride)) : 0.f;
         }
     }
     // Move the tile into an LDS matrix (rows t, columns e); scaled: multiply row t

@@ -13,7 +13,9 @@ struct KernelTable {
     void (*state)(dim3, hipStream_t, const ChunkArgs &);
     void (*fwd)(dim3, hipStream_t, const ChunkArgs &);
     void (*stats)(dim3, hipStream_t, const ChunkArgs &);
-    void (*rowstat)(dim3, hipStream_t, const ChunkArgs &);  // stats from the forward's row statistics
+    // the row statistics from the forward's output and row records; NULL: the dQ
+    // kernel makes them itself when ChunkArgs::Yin is set
+    void (*rowstat)(dim3, hipStream_t, const ChunkArgs &);
     void (*gstate)(dim3, hipStream_t, const ChunkArgs &);  // NULL: the dQ kernel does its work
     void (*bwdq)(dim3, hipStream_t, const ChunkArgs &);
     void (*bwdkv)(dim3, hipStream_t, const ChunkArgs &);

@@ -2,15 +2,18 @@
 // workspace planning and the slice-window launch sequence, plus the two small
 // shape-independent kernels (state scan, copy/zero).
 //
-// Launch sequence (page "Sub-Linear Memory: How to Make Performers SLiM"):
-//   forward  (Subsection 3.2): for each window of P slices in order:
+// Launch sequence (page "Sub-Linear Memory: How to Make Performers SLiM"); the
+// chunk kernels run one workgroup per group of G consecutive slices:
+//   forward  (Subsection 3.2): for each window of P groups in order:
 //       state -> forward prefix scan (carry = running final state) -> fwd
 //   backward (Subsection 3.3): for each window in reverse order:
 //       state -> entry states (one window: forward prefix from the initial
-//       state; several: the window's start state recovered from the state
-//       after it by subtraction, update (19) at window granularity, then a
-//       forward prefix) -> stats (recompute forward, per-row statistics; or, when
-//       the caller kept the forward's output and row statistics, rowstat) -> dQ
+//       state, or the forward's when the caller kept them; several: the window's
+//       start state recovered from the state after it by subtraction, update (19)
+//       at window granularity, then a forward prefix) -> stats (recompute
+//       forward, per-row statistics; when the caller kept the forward's output
+//       and row records, made from them by the dQ kernel itself or by a pass of
+//       their own, rowstat) -> dQ
 //       -> gstate (the slice's gradient w.r.t. its entry state; folded into the
 //       dQ kernel where its registers allow) -> gradient suffix scan (update
 //       (20)) -> dK, dV.  With several windows, a forward
@@ -783,10 +786,15 @@ slim_status slim_attn_bwd(const slim_desc *d, const void *Q, const void *K, cons
             scan(1, a.slots, cR, cS, D, M, (int)p.P, np, BH, s);
         }
         const dim3 cg(np, BH);
-        if (Y)  // the forward's denominators and query offsets, and dden from its output
-            SLIM_TIMED("rowstat", s, kt->rowstat(dim3(np * (unsigned)((p.c + ROWSTAT_ROWS - 1) / ROWSTAT_ROWS), BH), s, a));
-        else
+        // the row statistics: from the forward's output and row records (denominators,
+        // query offsets; dden from Y), made by the dQ kernel itself where it has the room,
+        // else by a pass of their own; without them, a pass that recomputes each slice's
+        // forward
+        if (!Y)
             SLIM_TIMED("stats", s, kt->stats(cg, s, a));
+        else if (kt->rowstat)
+            SLIM_TIMED("rowstat", s,
+                       kt->rowstat(dim3(np * (unsigned)((p.c + ROWSTAT_ROWS - 1) / ROWSTAT_ROWS), BH), s, a));
         if (kt->gstate) {
             if (dt)
                 SLIM_TIMED("bwdq_dw", s, dt->bwdq(cg, s, a));

@@ -104,8 +104,9 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(StatsSmem<C>), C::NW))
     }
 }
 
-// rowstat_kernel: the same per-row statistics from what the forward kept: its output Y
-// and, per row, 1/den at the common query offset and that offset (ChunkArgs::rstat).
+// rowstat_kernel: the per-row statistics from what the forward kept: its output Y and,
+// per row, 1/den at the common query offset and that offset (ChunkArgs::rstat); for the
+// shapes whose dQ kernel does not make them itself (bwdq_makes_rowstats).
 // dden = -(dY . Y) / den, since Y = Num / den; one row per VPR lanes (16-byte loads of
 // Y and dY), the dot product reduced by lane shuffles.  Grid: (chunks of the window x
 // parts of ROWSTAT_ROWS rows, heads), so that the launch has as many workgroups for
@@ -235,6 +236,10 @@ template <class C> struct BwdRegs {
     typedef typename C::T T;
     typename C::Tile q, k, v, dy;
     RowStatRegs<C::TT> rs;
+    // With the forward's output and its 8-byte row records (1/den', query offset): the
+    // output tile and each vector's row offset, for the row statistics made here
+    typename C::Tile y;
+    float qo[C::Tile::PER];
     __device__ __forceinline__ void load(const T *Q, const T *K, const T *V, const T *dY, const float *st, int t0,
                                          int len)
     {
@@ -256,6 +261,55 @@ template <class C> struct BwdRegs {
         if (threadIdx.x < C::TT) {
             DN.set_aux(threadIdx.x, rs.dd);
             qoff[threadIdx.x] = rs.qoff;
+        }
+    }
+    // The same from the forward's output Y and row records fr ([row][2]: 1/den', offset):
+    // each row's statistics (1/den, dden = -(dY . Y) / den, offset) are made here, put in
+    // LDS for this tile and stored to st (the row-statistics layout) for the dK/dV pass.
+    __device__ __forceinline__ void load_fwd(const T *Q, const T *K, const T *V, const T *dY, const float *fr,
+                                             int t0, int len)
+    {
+        const int n = min(C::TT, len - t0);
+        q.load(Q + (size_t)t0 * C::D, n);
+        k.load(K + (size_t)t0 * C::D, n);
+        v.load(V + (size_t)t0 * C::D, n);
+        dy.load(dY + (size_t)t0 * C::D, n, fr + (size_t)t0 * 2, 2);
+        const float *ob = uniform_ptr(fr + (size_t)t0 * 2);
+#pragma unroll
+        for (int i = 0; i < C::Tile::PER; ++i) {
+            const int idx = threadIdx.x + i * C::NT, t = idx / C::Tile::VPR;
+            qo[i] = idx < C::Tile::NV && t < n ? gload<float>(ob + (unsigned)(t * 2 + 1)) : 0.f;
+        }
+    }
+    __device__ __forceinline__ void load_y(const T *Y, int t0, int len)
+    {
+        y.load(Y + (size_t)t0 * C::D, min(C::TT, len - t0));
+    }
+    __device__ __forceinline__ void store_fwd(const typename C::XMat &xq, const typename C::XMat &xk,
+                                              const AugTile<C> &Vt, const AugTile<C> &DN, float *kn2, float *qoff,
+                                              int nv, float koff, float *st)
+    {
+        constexpr int EPV = C::Tile::EPV, VPR = C::Tile::VPR;
+        q.store(xq, false, nullptr);
+        store_k_tile<C>(k, xk, kn2, nv, koff);
+        store_v_tile<C>(v, Vt, nv);
+        dy.store(DN.x, true, nullptr);
+#pragma unroll
+        for (int i = 0; i < C::Tile::PER; ++i) {
+            const int idx = threadIdx.x + i * C::NT;
+            const int t = idx / VPR, c = (idx % VPR) * EPV;
+            float p = 0.f;  // dY . Y over the row: this lane's elements, then the row's lanes
+#pragma unroll
+            for (int j = 0; j < EPV; ++j) p = fmaf((float)y.v[i][j], (float)dy.v[i][j], p);
+#pragma unroll
+            for (int o = 1; o < VPR; o <<= 1) p += __shfl_xor(p, o, 64);
+            if (idx < C::Tile::NV && c == 0) {
+                const bool ok = t < nv;
+                const float inv = dy.s[i], dd = ok ? -p * inv : 0.f;
+                DN.set_aux(t, dd);
+                qoff[t] = qo[i];
+                if (ok) *reinterpret_cast<f4 *>(st + (size_t)t * ROWSTAT) = f4{inv, dd, qo[i], 0.f};
+            }
         }
     }
 };
@@ -302,6 +356,17 @@ template <class C> __device__ __forceinline__ typename C::T *pw_rows(void *buf, 
     return (typename C::T *)buf + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * C::M;
 }
 
+// The dQ kernel makes the row statistics itself (from the forward's output and row
+// records) where that costs it no spills: one vector of each input tile per thread
+// (bf16), or fp32 (whose dQ kernel holds its registers at one wave per SIMD anyway).
+// At d = 64, M = 64 (two waves, two vectors per thread) the extra tile spilled and the
+// kernel went from 1.19 to 1.73 ms on 1M tokens x 8 heads, more than the separate
+// pass costs (0.46 ms); at the 16K-token, 64-head shape the separate pass took 47 us
+// and the dQ kernel gained 16.
+template <class C> constexpr bool bwdq_makes_rowstats()
+{
+    return sizeof(typename C::T) == 4 || C::Tile::PER == 1;
+}
 template <class C> constexpr bool bwdq_fuses_gstate()
 {
     return C::D <= 32 || (sizeof(typename C::T) == 2 && C::D <= 64 && C::M >= 64);
@@ -322,8 +387,10 @@ template <class C> struct BwdqSmem {
     __align__(16) float red[C::FAVOR && !DqShared<C>::value ? C::NW * C::TT * C::LDR : 4];
     float kn2[C::TT], qoff[C::TT];
 };
-// DW: also store dg(Q) . g(Q) for the projection gradient (slim_dw.h).
-template <class C, bool DW = false>
+// DW: also store dg(Q) . g(Q) for the projection gradient (slim_dw.h).  FR: the row
+// statistics from the forward's output and row records (ChunkArgs::Yin, rstat), made
+// per tile here and stored for the dK/dV pass; else read from ChunkArgs::stats.
+template <class C, bool DW = false, bool FR = false>
 __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) void bwdq_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
@@ -347,14 +414,21 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
             for (int eb = 0; eb < NEA; ++eb) dg[fb][eb] = f4zero();
-    const float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
+    float *st = a.stats + ((size_t)G.bh * a.P + G.nl) * (size_t)a.c * ROWSTAT;
+    const T *Yf = FR ? (const T *)a.Yin + G.hb : nullptr;
+    const float *fr = FR ? a.rstat + ((size_t)G.bh * a.L + G.row0) * 2 : nullptr;
     Frag<T> wf[NFB][NEB];
     if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
     const float koff = key_off<C>(a);
     f4 r[NEA][NFB];
     load_state_E<C>(r, slot_ptr<C>(a.slots, a, G.bh, G.nl));
     BwdRegs<C> rg;
-    rg.load(Q, K, V, dY, st, 0, G.len);
+    if constexpr (FR) {
+        rg.load_fwd(Q, K, V, dY, fr, 0, G.len);
+        rg.load_y(Yf, 0, G.len);
+    } else {
+        rg.load(Q, K, V, dY, st, 0, G.len);
+    }
     // W^T fragments held over the tile loop (reloading them per tile put their cache
     // latency on the dQ chain).  Shared dg(Q).g(Q): a wave finishes the dQ^T blocks
     // (16 value columns x 16 rows) of value block w % NEB, over all features.
@@ -375,9 +449,18 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
     }
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
-        rg.store(xq, xk, Vt, DN, kn2, qoff, nv, koff);
+        if constexpr (FR)
+            rg.store_fwd(xq, xk, Vt, DN, kn2, qoff, nv, koff, st + (size_t)t0 * ROWSTAT);
+        else
+            rg.store(xq, xk, Vt, DN, kn2, qoff, nv, koff);
         __syncthreads();
-        if (t0 + TT < G.len) rg.load(Q, K, V, dY, st, t0 + TT, G.len);
+        if (t0 + TT < G.len) {
+            if constexpr (FR) {
+                rg.load_fwd(Q, K, V, dY, fr, t0 + TT, G.len);
+                rg.load_y(Yf, t0 + TT, G.len);
+            } else
+                rg.load(Q, K, V, dY, st, t0 + TT, G.len);
+        }
         f4 pq[NFB][NTB];
         feat_T<C>(pq, xq, wf);
         q_finish_off<C>(pq, qoff);

@@ -150,17 +150,19 @@ def kernel_flops(w: Workload, tile: int) -> dict:
     }
 
 
-def kernel_bytes(w: Workload, group: int = 1) -> dict:
+def kernel_bytes(w: Workload, group: int = 1, fr: bool = False) -> dict:
     """Algorithmic HBM bytes per (token, head) of each chunk kernel and scan: every
     input tensor row read once, every output row written once, one (d+1) x M fp32
     state slot read or written per workgroup's group of `group` slices (so per row:
     slot / (group c)), 16 bytes of row statistics (1/den, dden, query offset, one
-    unused float) per row where used.  No re-reads, no caches."""
+    unused float) per row where used.  fr: the dQ kernel makes the row statistics
+    itself from the forward's output row and 8-byte row record (and stores them for
+    the dK/dV kernel) instead of reading them.  No re-reads, no caches."""
     s = 2 if w.dtype == "bf16" else 4
     row = w.d * s                                   # one Q/K/V/Y/dY/dQ/dK/dV row
     slot = (w.d + 1) * w.M * 4 / min(w.chunk_len * group, w.L)  # one group's state, per row
     st = 16
-    return {
+    out = {
         "state": 2 * row + slot,                    # K, V -> chunk state
         "scan_prefix": 2 * slot, "scan_reverse": 2 * slot, "scan_grad": 2 * slot,  # slots in place
         "scan_window": 2 * slot, "scan_sum": slot,  # several windows: start states; the final-state sweep
@@ -179,6 +181,10 @@ def kernel_bytes(w: Workload, group: int = 1) -> dict:
         "bwdkv_dw": 4 * row + st + slot + 2 * row + w.M * s,
         "dw": 2 * (w.M * s + row),
     }
+    if fr:  # + the output row and the 8-byte record read, the statistics written, not read
+        for k in ("bwdq", "bwdq_gstate", "bwdq_dw", "bwdq_gstate_dw"):
+            out[k] += row + 8
+    return out
 
 
 def survey_flops(w: Workload) -> float:
