@@ -454,8 +454,9 @@ def chunk_sweep(torch, A, synth, w, dtype, window, cmax):
     W = torch.from_numpy(synth.projection(w.seed, w.M, w.d, w.w_kind)).cuda().to(dt).contiguous()
 
     def step(qq, kk, vv, dd, chunks, win):
-        A.attn_fwd(qq, kk, vv, W, w.feat, chunks, window_chunks=win)
-        return A.attn_bwd(qq, kk, vv, W, dd, w.feat, chunks, window_chunks=win)[:3]
+        # one slice per workgroup: the sweep measures the page's slice length itself
+        A.attn_fwd(qq, kk, vv, W, w.feat, chunks, window_chunks=win, group_slices=1)
+        return A.attn_bwd(qq, kk, vv, W, dd, w.feat, chunks, window_chunks=win, group_slices=1)[:3]
 
     def measure(qq, kk, vv, dd, chunks, win, reps):
         torch.cuda.synchronize()
