@@ -103,6 +103,33 @@ __device__ __forceinline__ void mma_range(f4 &acc, int k0, int k1, FA fa, FB fb)
     if (kb < k1) mma1(acc, fa(kb), fb(kb));
 }
 
+// The same over two contraction lists (blocks k0..k1-1 of fa/fb, then j0..j1-1 of
+// ga/gb) into one accumulator, paired across the lists: an odd block of the first
+// pairs with the second's first instead of going through a zero-padded product.
+template <typename T, typename FA, typename FB, typename GA, typename GB>
+__device__ __forceinline__ void mma_range2(f4 &acc, int k0, int k1, FA fa, FB fb, int j0, int j1, GA ga, GB gb)
+{
+    int kb = k0, jb = j0;
+    for (; kb + 1 < k1; kb += 2) mma2(acc, fa(kb), fa(kb + 1), fb(kb), fb(kb + 1));
+    if (kb < k1) {
+        if (jb < j1) {
+            mma2(acc, fa(kb), ga(jb), fb(kb), gb(jb));
+            ++jb;
+        } else {
+            mma1(acc, fa(kb), fb(kb));
+        }
+    }
+    for (; jb + 1 < j1; jb += 2) mma2(acc, ga(jb), ga(jb + 1), gb(jb), gb(jb + 1));
+    if (jb < j1) mma1(acc, ga(jb), gb(jb));
+}
+// A-operand fragment of a 16-row block whose row 0 is all ones (the others zero):
+// the product with it sums the B operand's contraction index into output row 0.
+template <typename T> __device__ __forceinline__ Frag<T> ones_row0()
+{
+    const float o = lcol() == 0 ? 1.f : 0.f;
+    return cfrag<T>(f4{o, o, o, o});
+}
+
 // Operand fragment from an LDS array stored [n][k] with row stride ld elements:
 // free index n0 + i%16, contraction indices k0 + 4*(i/16) .. +3.
 template <typename T> __device__ __forceinline__ Frag<T> lds_frag(const T *base, int ld, int n0, int k0)

@@ -494,6 +494,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) {
                 f4 acc = f4zero();
+                // (pairing these two lists, as the dK/dV kernel does, made this kernel spill:
+                // 0.443 -> 0.508 ms at the 16K-token, 64-head shape)
                 mma_range<T>(acc, 0, tb + 1, [&](int sb) { return Fk.frag_r(fb * 16, sb * 16); },
                              [&](int sb) { return at[sb][tb]; });
                 mma_range<T>(acc, 0, NEA, [&](int eb) { return cfrag<T>(r[eb][fb]); },
@@ -749,10 +751,10 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
 #pragma unroll
                 for (int sb = 0; sb < NTB; ++sb) {
                     f4 acc = f4zero();
-                    mma_range<T>(acc, sb, NTB, [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); },
-                                 [&](int tb) { return fa[tb][sb]; });
-                    mma_range<T>(acc, 0, NEA, [&](int eb) { return cfrag<T>(dr[eb][fb]); },
-                                 [&](int eb) { return Vt.fc(sb * 16, eb); });
+                    mma_range2<T>(acc, sb, NTB, [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); },
+                                  [&](int tb) { return fa[tb][sb]; }, 0, NEA,
+                                  [&](int eb) { return cfrag<T>(dr[eb][fb]); },
+                                  [&](int eb) { return Vt.fc(sb * 16, eb); });
                     dk[fb][sb] = acc;
                 }
         }
@@ -764,21 +766,20 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
             float *rsp = red + GMat::SIZE * sizeof(T) / sizeof(float);  // [NW][TT] row-sum partials
 #pragma unroll
             for (int sb = 0; sb < NTB; ++sb) {
-                float rsum = 0.f;
+                Frag<T> gf[NFB];
 #pragma unroll
                 for (int fb = 0; fb < NFB; ++fb) {
-                    // the row sum is taken over the same rounded values that enter the W^T
-                    // product, so that W^T G - k sum(G) = sum_m G_m (w_m - k) cancels
-                    // consistently for a key close to a row of W
-                    const Frag<T> gf = cfrag<T>(dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]));
-                    const f4 v = frag_to_f4<T>(gf);
-                    rsum += (v[0] + v[1]) + (v[2] + v[3]);
-                    Gk.put_frag(sb * 16 + lc, w * MW + fb * 16 + 4 * g, gf);
-                    if constexpr (DW) store_pw<C>(pw + (size_t)t0 * C::M, sb * 16 + lc, nv, w * MW + fb * 16 + 4 * g, gf);
+                    gf[fb] = cfrag<T>(dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]));
+                    Gk.put_frag(sb * 16 + lc, w * MW + fb * 16 + 4 * g, gf[fb]);
+                    if constexpr (DW)
+                        store_pw<C>(pw + (size_t)t0 * C::M, sb * 16 + lc, nv, w * MW + fb * 16 + 4 * g, gf[fb]);
                 }
-                rsum += __shfl_xor(rsum, 16, 64);
-                rsum += __shfl_xor(rsum, 32, 64);
-                if (g == 0) rsp[w * TT + sb * 16 + lc] = rsum;
+                // the row sums over the same rounded values that enter the W^T product (so
+                // that W^T G - k sum(G) = sum_m G_m (w_m - k) cancels consistently for a key
+                // close to a row of W), on the matrix cores: a row of ones times G
+                f4 rs = f4zero();
+                mma_range<T>(rs, 0, NFB, [&](int) { return ones_row0<T>(); }, [&](int fb) { return gf[fb]; });
+                if (g == 0) rsp[w * TT + sb * 16 + lc] = rs[0];
             }
             // value blocks eb = w mod NW (all row blocks), or, with more waves than value
             // blocks, eb = w mod NEB and the row blocks sb = w / NEB mod NW / NEB
@@ -825,18 +826,17 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
             Frag<T> gk[NFB][NTB];
 #pragma unroll
             for (int sb = 0; sb < NTB; ++sb) {
-                float rsum = 0.f;
 #pragma unroll
                 for (int fb = 0; fb < NFB; ++fb) {
                     gk[fb][sb] = cfrag<T>(dk[fb][sb] * frag_to_f4<T>(fkT[fb][sb]));
-                    const f4 v = frag_to_f4<T>(gk[fb][sb]);  // as rounded for the W^T product
-                    rsum += (v[0] + v[1]) + (v[2] + v[3]);
                     if constexpr (DW)
                         store_pw<C>(pw + (size_t)t0 * C::M, sb * 16 + lc, nv, w * MW + fb * 16 + 4 * g, gk[fb][sb]);
                 }
-                rsum += __shfl_xor(rsum, 16, 64);
-                rsum += __shfl_xor(rsum, 32, 64);
-                if (g == 0) red[(w * TT + sb * 16 + lc) * C::LDR + D] = rsum;
+                // row sums of the values as rounded for the W^T product, on the matrix
+                // cores: a row of ones times dg(K) . g(K)
+                f4 rs = f4zero();
+                mma_range<T>(rs, 0, NFB, [&](int) { return ones_row0<T>(); }, [&](int fb) { return gk[fb][sb]; });
+                if (g == 0) red[(w * TT + sb * 16 + lc) * C::LDR + D] = rs[0];
             }
 #pragma unroll 1
             for (int eb = 0; eb < NEB; ++eb) {  // one W^T block at a time
