@@ -750,11 +750,13 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
             for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
                 for (int sb = 0; sb < NTB; ++sb) {
+                    // the state list first, so that its blocks pair the same way for every
+                    // sb (one set of operand registers for them)
                     f4 acc = f4zero();
-                    mma_range2<T>(acc, sb, NTB, [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); },
-                                  [&](int tb) { return fa[tb][sb]; }, 0, NEA,
-                                  [&](int eb) { return cfrag<T>(dr[eb][fb]); },
-                                  [&](int eb) { return Vt.fc(sb * 16, eb); });
+                    mma_range2<T>(acc, 0, NEA, [&](int eb) { return cfrag<T>(dr[eb][fb]); },
+                                  [&](int eb) { return Vt.fc(sb * 16, eb); }, sb, NTB,
+                                  [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); },
+                                  [&](int tb) { return fa[tb][sb]; });
                     dk[fb][sb] = acc;
                 }
         }
