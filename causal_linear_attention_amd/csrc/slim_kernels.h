@@ -873,12 +873,17 @@ __device__ __forceinline__ void fwd_tile(SM &sm, const Frag<typename C::T> (&wf)
     to_frags<C>(fq, pq);
     to_frags<C>(fkT, pkT);
     put_feature_frags<C>(Fk, fkT);
-    // P^T blocks (rows s, cols t), s-block <= t-block, over this wave's features.
+    // P^T blocks (rows s, cols t) over this wave's features; the blocks above the
+    // diagonal (s-block > t-block) are zero
     Frag<T> pt[NTB][NTB];
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-        for (int sb = 0; sb <= tb; ++sb) {
+        for (int sb = 0; sb < NTB; ++sb) {
+            if (sb > tb) {
+                pt[sb][tb] = cfrag<T>(f4zero());
+                continue;
+            }
             f4 acc = f4zero();
             mma_range<T>(acc, 0, NFB, [&](int kb) { return fkT[kb][sb]; }, [&](int kb) { return fq[kb][tb]; });
             if (sb == tb)
@@ -887,13 +892,16 @@ __device__ __forceinline__ void fwd_tile(SM &sm, const Frag<typename C::T> (&wf)
                     if (4 * g + j > lc) acc[j] = 0.f;
             pt[sb][tb] = cfrag<T>(acc);
         }
-    // partial numerators^T (rows e, cols t; e = D is the denominator): V^T P^T + R g(Q)^T
+    // partial numerators^T (rows e, cols t; e = D is the denominator): V^T P^T + R g(Q)^T.
+    // The product with P^T runs over all s-blocks of the tile, the zero ones included:
+    // the V operand pairs then are the same for every t-block, and no block goes
+    // through a zero-padded product
 #pragma unroll
     for (int eb = 0; eb < NEA; ++eb)
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
             f4 acc = f4zero();
-            mma_range<T>(acc, 0, tb + 1, [&](int sb) { return V.fr(eb, sb * 16); }, [&](int sb) { return pt[sb][tb]; });
+            mma_range<T>(acc, 0, NTB, [&](int sb) { return V.fr(eb, sb * 16); }, [&](int sb) { return pt[sb][tb]; });
             mma_range<T>(acc, 0, NFB, [&](int fb) { return cfrag<T>(rt[fb][eb]); }, [&](int fb) { return fq[fb][tb]; });
             emit(eb, tb, acc);
         }

@@ -686,11 +686,15 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
         }
         // dV^T blocks (rows e, cols s): dNum^T P + dR g(K)^T, reduced across waves.
         {
-            Frag<T> fp[NTB][NTB];  // P[t][s] = g(Q_t).g(K_s) over own features, s <= t
+            Frag<T> fp[NTB][NTB];  // P[t][s] = g(Q_t).g(K_s) over own features; 0 for s > t
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-                for (int sb = 0; sb <= tb; ++sb) {
+                for (int sb = 0; sb < NTB; ++sb) {
+                    if (sb > tb) {
+                        fp[tb][sb] = cfrag<T>(f4zero());
+                        continue;
+                    }
                     f4 acc = f4zero();
                     mma_range<T>(acc, 0, NFB, [&](int fb) { return fq[fb][tb]; }, [&](int fb) { return fkT[fb][sb]; });
                     if (sb == tb)
@@ -705,8 +709,10 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
             for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
                 for (int sb = 0; sb < NTB; ++sb) {
+                    // over all t-blocks, the zero ones included (one dNum operand pairing
+                    // for every s-block, no zero-padded product)
                     f4 acc = f4zero();
-                    mma_range<T>(acc, sb, NTB, [&](int tb) { return DN.fr(eb, tb * 16); },
+                    mma_range<T>(acc, 0, NTB, [&](int tb) { return DN.fr(eb, tb * 16); },
                                  [&](int tb) { return fp[tb][sb]; });
                     if constexpr (DRL)
                         mma_range<T>(acc, 0, NFB, [&](int fb) { return Dr.frag_r(eb * 16, fb * 16); },
