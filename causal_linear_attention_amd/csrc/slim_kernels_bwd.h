@@ -472,11 +472,15 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
             put_features<C>(Fk, pkT);
         }
         // A^T blocks (rows s, cols t), s <= t: [V | 1] [dNum | dden]^T
-        Frag<T> at[NTB][NTB];
+        Frag<T> at[NTB][NTB];  // 0 above the diagonal (s-block > t-block)
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-            for (int sb = 0; sb <= tb; ++sb) {
+            for (int sb = 0; sb < NTB; ++sb) {
+                if (sb > tb) {
+                    at[sb][tb] = cfrag<T>(f4zero());
+                    continue;
+                }
                 f4 acc = f4zero();
                 mma_range<T>(acc, 0, NEA, [&](int eb) { return Vt.fc(sb * 16, eb); },
                              [&](int eb) { return DN.fc(tb * 16, eb); });
@@ -496,7 +500,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) 
                 f4 acc = f4zero();
                 // (pairing these two lists, as the dK/dV kernel does, made this kernel spill:
                 // 0.443 -> 0.508 ms at the 16K-token, 64-head shape)
-                mma_range<T>(acc, 0, tb + 1, [&](int sb) { return Fk.frag_r(fb * 16, sb * 16); },
+                // over all s-blocks, the zero ones included (as in the forward)
+                mma_range<T>(acc, 0, NTB, [&](int sb) { return Fk.frag_r(fb * 16, sb * 16); },
                              [&](int sb) { return at[sb][tb]; });
                 mma_range<T>(acc, 0, NEA, [&](int eb) { return cfrag<T>(r[eb][fb]); },
                              [&](int eb) { return DN.fc(tb * 16, eb); });
