@@ -3,8 +3,8 @@ the C ABI, on two calls in a row, the second with a smaller input.
 
 slim_attn_fwd_noalloc works in a fixed 64 MiB device array instead of a caller's
 workspace.  The first call (the 16K-token, 64-head workload's shape: its automatic
-window of 32 slices needs 140 MB of slots) has to shrink its window to fit, so it runs
-in several windows: its outputs are bitwise those of slim_attn_fwd given the same
+window, all 32 slices in 16 groups of two, needs 72 MB of slots) has to shrink its
+window to fit, so it runs in several windows: its outputs are bitwise those of slim_attn_fwd given the same
 window, and within the bf16 bound (2e-2, gpu_util.check) of slim_attn_fwd with the
 automatic window and of the fp64 oracle on sampled heads.  The second call (smaller,
 fp32) fits whole: bitwise equal to slim_attn_fwd.  Both calls share the array, so the
