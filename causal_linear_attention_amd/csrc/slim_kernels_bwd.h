@@ -359,10 +359,18 @@ template <class C> __device__ __forceinline__ typename C::T *pw_rows(void *buf, 
 // The dQ kernel makes the row statistics itself (from the forward's output and row
 // records) where that costs it no spills: one vector of each input tile per thread
 // (bf16), or fp32 (whose dQ kernel holds its registers at one wave per SIMD anyway).
-// At d = 64, M = 64 (two waves, two vectors per thread) the extra tile spilled and the
-// kernel went from 1.19 to 1.73 ms on 1M tokens x 8 heads, more than the separate
-// pass costs (0.46 ms); at the 16K-token, 64-head shape the separate pass took 47 us
-// and the dQ kernel gained 16.
+// With two vectors per thread (two waves at d = 64, M = 64 before that shape moved to
+// 16 features per wave) the extra tile spilled and the kernel went from 1.19 to 1.73 ms
+// on 1M tokens x 8 heads, more than the separate pass costs (0.46 ms); at the 16K-token,
+// 64-head shape the separate pass took 47 us and the dQ kernel gained 16.
+// Features per wave of the dQ kernel.  At bf16, M = 64, 16 features per wave (four
+// waves) instead of 32 (two) let it make the row statistics with no spill: on 1M tokens
+// x 8 heads the dQ kernel went from 1.19 to 1.43 ms (it also reads Y now) and the 0.46 ms
+// statistics pass went away.
+template <typename T, int M> constexpr int bwdq_features_per_wave()
+{
+    return sizeof(T) == 2 && M == 64 ? 16 : 32;
+}
 template <class C> constexpr bool bwdq_makes_rowstats()
 {
     return sizeof(typename C::T) == 4 || C::Tile::PER == 1;
@@ -387,11 +395,18 @@ template <class C> struct BwdqSmem {
     __align__(16) float red[C::FAVOR && !DqShared<C>::value ? C::NW * C::TT * C::LDR : 4];
     float kn2[C::TT], qoff[C::TT];
 };
+// Waves per SIMD the dQ kernel is compiled for: three where 16 features per wave leave
+// room for them (in registers and in LDS), else as the other chunk kernels.
+template <class C> constexpr int bwdq_waves_per_simd()
+{
+    return C::MW == 16 && C::NW <= 4 && 3 * sizeof(BwdqSmem<C>) <= 160 * 1024 ? 3
+                                                                                : waves_per_simd(sizeof(BwdqSmem<C>), C::NW);
+}
 // DW: also store dg(Q) . g(Q) for the projection gradient (slim_dw.h).  FR: the row
 // statistics from the forward's output and row records (ChunkArgs::Yin, rstat), made
 // per tile here and stored for the dK/dV pass; else read from ChunkArgs::stats.
 template <class C, bool DW = false, bool FR = false>
-__global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdqSmem<C>), C::NW)) void bwdq_kernel(ChunkArgs a)
+__global__ __launch_bounds__(C::NT, bwdq_waves_per_simd<C>()) void bwdq_kernel(ChunkArgs a)
 {
     typedef typename C::T T;
     constexpr int NFB = C::NFB, NEB = C::NEB, NEA = C::NEA, NTB = C::NTB, TT = C::TT, D = C::D, MW = C::MW;
