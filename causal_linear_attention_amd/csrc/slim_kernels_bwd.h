@@ -671,6 +671,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
 
     const int last = ((G.len - 1) / TT) * TT;
     BwdRegs<C> rg;
+    constexpr bool EARLY = C::Tile::PER == 1;
     rg.load(Q, K, V, dY, st, last, G.len);
     for (int t0 = last; t0 >= 0; t0 -= TT) {
         const int nv = min(TT, G.len - t0);
@@ -680,6 +681,13 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
         if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
         rg.store(xq, xk, Vt, DN, kn2, qoff, nv, koff);
         __syncthreads();
+        // the next tile's inputs: with one vector of each input tile per thread, in flight
+        // over this whole tile (issued after the dK/dV products instead, their memory
+        // latency showed: 0.521 -> 0.495 ms at the 16K-token, 64-head shape, 0.421 -> 0.401
+        // for d = 128 elu+1); with two, the registers they hold cost more than that (1M
+        // tokens at M = 64: 1.765 -> 1.810 ms), and they are fetched during the state update
+        if constexpr (EARLY)
+            if (t0 > 0) rg.load(Q, K, V, dY, st, t0 - TT, G.len);
         Frag<T> fq[NFB][NTB], fkT[NFB][NTB];
         {
             f4 pq[NFB][NTB];
@@ -894,8 +902,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                     if (s < nv) store4<T>(dK + (size_t)(t0 + s) * D + w * MW + fb * 16 + 4 * g, v);
                 }
         }
-        // next tile's inputs, fetched during the state update and the barriers
-        if (t0 > 0) rg.load(Q, K, V, dY, st, t0 - TT, G.len);
+        if constexpr (!EARLY)
+            if (t0 > 0) rg.load(Q, K, V, dY, st, t0 - TT, G.len);
         // gradient state (after use): [dR; dS] += [dNum | dden]^T g(Q), for the tiles before
         // (skipping it after the last tile took the plain kernel from 0.564 to 0.541 ms; it
         // slowed the dW pass's variant, which keeps it)
