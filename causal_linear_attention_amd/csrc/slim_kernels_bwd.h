@@ -671,7 +671,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
 
     const int last = ((G.len - 1) / TT) * TT;
     BwdRegs<C> rg;
-    constexpr bool EARLY = C::Tile::PER == 1;
+    constexpr bool EARLY = C::Tile::PER == 1 && !DW;
     rg.load(Q, K, V, dY, st, last, G.len);
     for (int t0 = last; t0 >= 0; t0 -= TT) {
         const int nv = min(TT, G.len - t0);
@@ -685,7 +685,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
         // over this whole tile (issued after the dK/dV products instead, their memory
         // latency showed: 0.521 -> 0.495 ms at the 16K-token, 64-head shape, 0.421 -> 0.401
         // for d = 128 elu+1); with two, the registers they hold cost more than that (1M
-        // tokens at M = 64: 1.765 -> 1.810 ms), and they are fetched during the state update
+        // tokens at M = 64: 1.765 -> 1.810 ms), and in the dW pass's variant (0.706 ->
+        // 0.718 ms); those fetch them during the gradient-state update
         if constexpr (EARLY)
             if (t0 > 0) rg.load(Q, K, V, dY, st, t0 - TT, G.len);
         Frag<T> fq[NFB][NTB], fkT[NFB][NTB];
@@ -793,6 +794,34 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                                   [&](int tb) { return fa[tb][sb]; });
                     dk[fb][sb] = acc;
                 }
+        }
+        // the gradient state (its last use, in the dg(K) products, is above): [dR; dS] +=
+        // [dNum | dden]^T g(Q), for the tiles before (skipping it after the last tile took
+        // the plain kernel from 0.564 to 0.541 ms; it slowed the dW pass's variant, which
+        // keeps it)
+        auto grad_state = [&]() {
+#pragma unroll
+            for (int fb = 0; fb < NFB && (DW || t0 > 0); ++fb) {
+#pragma unroll
+                for (int eb = 0; eb < NEA; ++eb)
+                    mma_range<T>(dr[eb][fb], 0, NTB, [&](int tb) { return DN.fr(eb, tb * 16); },
+                                 [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); });
+                if constexpr (!DRL) {
+#pragma unroll
+                    for (int eb = 0; eb < NEB; ++eb)
+                        mma_range<T>(drt[fb][eb], 0, NTB, [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); },
+                                     [&](int tb) { return DN.fr(eb, tb * 16); });
+                }
+            }
+        };
+        // Issued before dK's W^T product and reduction rather than after them, so that these
+        // matrix-core products overlap that work: at the 16K-token, 64-head shape 0.497 ->
+        // 0.480 ms, on 1M tokens x 8 heads (M = 64) 1.708 -> 1.663 ms.  Not for the dW
+        // pass's variant, whose extra stores fill that part (0.718 -> 0.752 ms there).
+        if constexpr (!DW) {
+            if constexpr (!EARLY)
+                if (t0 > 0) rg.load(Q, K, V, dY, st, t0 - TT, G.len);
+            grad_state();
         }
         if constexpr (DkShared<C>::value) {
             // dK = W^T-product of dg(K) . g(K) over all features - K * its row sum
@@ -902,23 +931,9 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                     if (s < nv) store4<T>(dK + (size_t)(t0 + s) * D + w * MW + fb * 16 + 4 * g, v);
                 }
         }
-        if constexpr (!EARLY)
+        if constexpr (DW) {
             if (t0 > 0) rg.load(Q, K, V, dY, st, t0 - TT, G.len);
-        // gradient state (after use): [dR; dS] += [dNum | dden]^T g(Q), for the tiles before
-        // (skipping it after the last tile took the plain kernel from 0.564 to 0.541 ms; it
-        // slowed the dW pass's variant, which keeps it)
-#pragma unroll
-        for (int fb = 0; fb < NFB && (DW || t0 > 0); ++fb) {
-#pragma unroll
-            for (int eb = 0; eb < NEA; ++eb)
-                mma_range<T>(dr[eb][fb], 0, NTB, [&](int tb) { return DN.fr(eb, tb * 16); },
-                             [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); });
-            if constexpr (!DRL) {
-#pragma unroll
-                for (int eb = 0; eb < NEB; ++eb)
-                    mma_range<T>(drt[fb][eb], 0, NTB, [&](int tb) { return Fq.frag_r(fb * 16, tb * 16); },
-                                 [&](int tb) { return DN.fr(eb, tb * 16); });
-            }
+            grad_state();
         }
         __syncthreads();
     }
