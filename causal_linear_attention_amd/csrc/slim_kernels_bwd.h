@@ -379,10 +379,13 @@ template <class C> constexpr bool bwdq_makes_rowstats()
 // separate pass over Q and dY) where its registers allow: at bf16, d = 128 with elu+1
 // (no W fragments) it spills 40 B with the row statistics made in the kernel and still
 // saves more than the pass costs (dQ + gstate 0.388 -> 0.368 ms at 8K tokens x 64
-// heads, M = 128); FAVOR+ at d = 128 would spill 180-240 B.
+// heads, M = 128); FAVOR+ at d = 128 would spill 180-240 B.  At fp32 (one wave per
+// SIMD, the accumulation registers in use) up to d = 64: 0.114 -> 0.097 ms at 4K tokens
+// x 64 heads, M = 128; not at M = 256, where the g(Q) copy in LDS would leave 32-row
+// tiles without room.
 template <class C> constexpr bool bwdq_fuses_gstate()
 {
-    return C::D <= 32 ||
+    return C::D <= 32 || (sizeof(typename C::T) == 4 && C::D <= 64 && C::M >= 64 && C::M <= 128) ||
            (sizeof(typename C::T) == 2 && C::M >= 64 && (C::D <= 64 || (C::D <= 128 && !C::FAVOR)));
 }
 template <class C, bool FR = false> struct BwdqSmem {
