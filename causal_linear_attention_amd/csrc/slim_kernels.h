@@ -408,27 +408,6 @@ template <class C> __device__ __forceinline__ float reduce_col(const float *red,
     for (int w = 1; w < C::NW; ++w) s += red[(w * C::TT + t) * C::LDR + C::D];
     return s;
 }
-// As reduce_rows, with each wave's partial rescaled by its factor (wave_scales) and
-// the rescaled sum of column D (denominator) and the common query offset handed over
-// too: emit(t, e, s, den, moff, ok).
-template <class C, typename F>
-__device__ __forceinline__ void reduce_rows_scaled(const float *red, const float *qmax, int nv, F emit)
-{
-    constexpr int Q4 = C::D / 4;
-    for (int v = threadIdx.x; v < C::TT * Q4; v += C::NT) {
-        const int t = v / Q4, e = (v % Q4) * 4;
-        float sc[C::NW], moff;
-        wave_scales<C>(qmax, t, sc, &moff);
-        f4 s = f4zero();
-        float den = 0.f;
-#pragma unroll
-        for (int w = 0; w < C::NW; ++w) {
-            s += *reinterpret_cast<const f4 *>(red + (w * C::TT + t) * C::LDR + e) * sc[w];
-            den += red[(w * C::TT + t) * C::LDR + C::D] * sc[w];
-        }
-        emit(t, e, s, den, moff, t < nv);
-    }
-}
 // Write a value-indexed block acc (rows e = eb*16 + 4g + j, cols t = tb*16 + i%16) of
 // this wave's partial to red; the auxiliary block contributes only column D.
 template <class C> __device__ __forceinline__ void put_red(float *red, int eb, int tb, f4 acc)
@@ -939,23 +918,64 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(FwdSmem<C>), C::NW)) v
     f4 rt[NFB][NEA];
     load_state_T<C>(rt, slot_ptr<C>(a.slots, a, G.bh, G.nl));
     FwdRegs<C> rg;
+    // Y (and the row records) of a tile, held in registers as stored, are written at the
+    // start of the next tile, after the wait for that tile's inputs (a wait for a load
+    // also waits for every store issued before it): fwd 1.048 -> 0.986 ms on 1M tokens x
+    // 8 heads, 0.226 -> 0.212 ms for elu+1 at d = 128, 0.275 -> 0.272 ms at the 16K-token,
+    // 64-head shape
+    constexpr int Q4 = C::D / 4, YI = (TT * Q4 + C::NT - 1) / C::NT;
+    typedef std::conditional_t<sizeof(T) == 2, bf4, f4> YV;
+    YV yv[YI];
+    float2 yr[YI];
+    int pt0 = -1, pnv = 0;
+    auto store_y = [&]() {
+#pragma unroll
+        for (int k = 0; k < YI; ++k) {
+            const int v = threadIdx.x + k * C::NT, t = v / Q4, e = (v % Q4) * 4;
+            if (v < TT * Q4 && t < pnv) {
+                *reinterpret_cast<YV *>(Y + (size_t)(pt0 + t) * C::D + e) = yv[k];
+                if (rs && e == 0) *reinterpret_cast<float2 *>(rs + (size_t)(pt0 + t) * 2) = yr[k];
+            }
+        }
+    };
     rg.load(Q, K, V, 0, G.len);
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
         rg.store(sm, nv, koff);
+        if (pt0 >= 0) store_y();
         __syncthreads();
         if (t0 + TT < G.len) rg.load(Q, K, V, t0 + TT, G.len);
         f4 pq[NFB][NTB];
         fwd_tile<C>(sm, wf, rt, pq, [&](int eb, int tb, f4 acc) { put_red<C>(sm.red, eb, tb, acc); });
         __syncthreads();
-        reduce_rows_scaled<C>(sm.red, sm.qmax, nv, [&](int t, int e, f4 s, float den, float moff, bool ok) {
-            const float inv = 1.f / den;
-            if (ok) store4<T>(Y + (size_t)(t0 + t) * C::D + e, s * inv);
-            if (rs && ok && e == 0) *reinterpret_cast<float2 *>(rs + (size_t)(t0 + t) * 2) = make_float2(inv, moff);
-        });
+#pragma unroll
+        for (int k = 0; k < YI; ++k) {
+            const int v = threadIdx.x + k * C::NT, t = v / Q4, e = (v % Q4) * 4;
+            if (v < TT * Q4) {
+                float sc[C::NW], moff;
+                wave_scales<C>(sm.qmax, t, sc, &moff);
+                f4 sum = f4zero();
+                float den = 0.f;
+#pragma unroll
+                for (int w = 0; w < C::NW; ++w) {
+                    sum += *reinterpret_cast<const f4 *>(sm.red + (w * TT + t) * C::LDR + e) * sc[w];
+                    den += sm.red[(w * TT + t) * C::LDR + C::D] * sc[w];
+                }
+                const float inv = 1.f / den;
+                const f4 y = sum * inv;
+                if constexpr (sizeof(T) == 2)
+                    yv[k] = YV{(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+                else
+                    yv[k] = y;
+                yr[k] = make_float2(inv, moff);
+            }
+        }
+        pt0 = t0;
+        pnv = nv;
         state_update_T<C>(sm, rt);
         __syncthreads();
     }
+    store_y();
 }
 
 }  // namespace slim
