@@ -729,6 +729,39 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
     const int last = ((G.len - 1) / TT) * TT;
     BwdRegs<C> rg;
     constexpr bool EARLY = C::Tile::PER == 1 && !DW;
+    // dK of a tile, held in registers as stored, written during the next tile (after its
+    // feature maps, whose waits for their W fragments would also wait for these stores):
+    // where dK is made from each wave's own blocks (the shared-operand and elu+1 paths)
+    // and a few registers hold it: 1.711 -> 1.613 ms on 1M tokens x 8 heads (M = 64),
+    // 0.404 -> 0.400 ms for elu+1 at d = 128; the other path's values spill
+    constexpr bool SHK = DkShared<C>::value;
+    constexpr int EBW_ = NEB > C::NW ? NEB / C::NW : 1, TBS_ = C::NW > NEB ? C::NW / NEB : 1;
+    constexpr int NDK_ = SHK ? EBW_ * NTB : NFB * NTB;
+    constexpr bool DEFER_DK = !DW && (SHK || !C::FAVOR) && NDK_ <= 4;
+    constexpr int NDK = DEFER_DK ? NDK_ : 1;
+    typedef std::conditional_t<sizeof(T) == 2, bf4, f4> DkV;
+    DkV dkv[NDK];
+    int pt0 = -1, pnv = 0;
+    auto pack = [](f4 x) -> DkV {
+        if constexpr (sizeof(T) == 2)
+            return DkV{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+        else
+            return x;
+    };
+    auto store_dk = [&]() {
+#pragma unroll
+        for (int i = 0; i < NDK; ++i) {
+            const int sb = i % NTB, s = sb * 16 + lc;
+            int col;
+            if constexpr (SHK) {
+                if (sb % TBS_ != (w / NEB) % TBS_) continue;
+                col = (w % NEB + (i / NTB) * C::NW) * 16 + 4 * g;
+            } else {
+                col = w * MW + (i / NTB) * 16 + 4 * g;
+            }
+            if (s < pnv) *reinterpret_cast<DkV *>(dK + (size_t)(pt0 + s) * D + col) = dkv[i];
+        }
+    };
     rg.load(Q, K, V, dY, st, last, G.len);
     for (int t0 = last; t0 >= 0; t0 -= TT) {
         const int nv = min(TT, G.len - t0);
@@ -758,6 +791,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
             k_finish_T<C>(pkT, kn2);
             to_frags<C>(fkT, pkT);
         }
+        if constexpr (DEFER_DK)
+            if (pt0 >= 0) store_dk();
         if constexpr (DRL) {
 #pragma unroll
             for (int eb = 0; eb < NEB; ++eb)
@@ -910,8 +945,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
             const T *Wp = (const T *)a.Wt;
             __syncthreads();
             constexpr int EBW = NEB > C::NW ? NEB / C::NW : 1;  // value blocks per wave
-#pragma unroll 1
-            for (int k = 0; k < EBW; ++k) {
+            auto dk_blocks = [&](int k) {
                 const int eb = w % NEB + k * C::NW;
                 f4 acc[NTB];
 #pragma unroll
@@ -937,10 +971,19 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                     float rs = rsp[s];
 #pragma unroll
                     for (int w2 = 1; w2 < C::NW; ++w2) rs += rsp[w2 * TT + s];
-                    if (s < nv)
-                        store4<T>(dK + (size_t)(t0 + s) * D + eb * 16 + 4 * g,
-                                  acc[sb] - xk.get4(s, eb * 16 + 4 * g) * rs);
+                    const f4 r = acc[sb] - xk.get4(s, eb * 16 + 4 * g) * rs;
+                    if constexpr (DEFER_DK)
+                        dkv[k * NTB + sb] = pack(r);
+                    else if (s < nv)
+                        store4<T>(dK + (size_t)(t0 + s) * D + eb * 16 + 4 * g, r);
                 }
+            };
+            if constexpr (DEFER_DK) {
+#pragma unroll
+                for (int k = 0; k < EBW; ++k) dk_blocks(k);
+            } else {
+#pragma unroll 1
+                for (int k = 0; k < EBW; ++k) dk_blocks(k);
             }
         } else if constexpr (C::FAVOR) {
             // dK^T = W^T (dg(K) . g(K))^T and the row sums of dg(K) . g(K), reduced across
@@ -985,15 +1028,23 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                     f4 v;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) v[j] = dk[fb][sb][j] * elu1_grad(x[j]);
-                    if (s < nv) store4<T>(dK + (size_t)(t0 + s) * D + w * MW + fb * 16 + 4 * g, v);
+                    if constexpr (DEFER_DK)
+                        dkv[fb * NTB + sb] = pack(v);
+                    else if (s < nv)
+                        store4<T>(dK + (size_t)(t0 + s) * D + w * MW + fb * 16 + 4 * g, v);
                 }
         }
         if constexpr (DW) {
             if (t0 > 0) rg.load(Q, K, V, dY, st, t0 - TT, G.len);
             grad_state();
         }
+        if constexpr (DEFER_DK) {
+            pt0 = t0;
+            pnv = nv;
+        }
         __syncthreads();
     }
+    if constexpr (DEFER_DK) store_dk();
 }
 
 }  // namespace slim
