@@ -9,6 +9,9 @@ namespace slim {
 struct KernelTable {
     int nt;  // threads per workgroup
     int tt;  // rows per tile
+    // workgroups the chip holds at once (256 CUs) of the forward, dQ and dK/dV kernels
+    // (their occupancy: waves per SIMD and LDS per CU)
+    int slots_fwd, slots_q, slots_kv;
     void (*featmap)(dim3, hipStream_t, const void *, const void *, float *, float *, long long);
     void (*state)(dim3, hipStream_t, const ChunkArgs &);
     void (*fwd)(dim3, hipStream_t, const ChunkArgs &);

@@ -341,17 +341,34 @@ static long long resolve_window(const slim_desc *d, long long nchunks, long long
 // slices, walking them in order and carrying the state from one slice to the next (the
 // slice loop of Subsection 3.2, G slices at a time), so that one state per group is
 // written, scanned and read back, and a workgroup's start-up (loading its entry state)
-// is paid once per group.  Automatic: G a power of two with groups of at most 1024
-// rows, while at least 1024 workgroups per launch remain (at the 16K-token, 64-head
-// shape in slices of 512 the step goes from 1.62 to 1.47 ms with two slices per group;
-// at d = M = 128 elu+1 in slices of 256 from 1.43 to 1.24 ms).
+// is paid once per group.  Automatic: the largest G, a power of two with groups of at
+// most 2048 rows, whose launches still fill the chip in whole rounds, within 10%, for
+// each of the forward, dQ and dK/dV kernels: at least as many workgroups as the chip
+// holds of that kernel at once (its slots: 512 for two 4-wave workgroups per CU, 768
+// for the dQ kernel's three at bf16, M = 64, ...), and workgroups / (rounds x slots)
+// >= 0.9.  Measured step times (fwd+bwd, forward states kept):
+// 16K tokens x 64 heads in slices of 512, G = 1, 2, 4, 8: 1.45, 1.35, 1.29, 1.72 ms
+// (4: 512 workgroups, one round; 8 leaves half the chip idle); elu+1 at d = M = 128,
+// 8K tokens x 96 heads in slices of 256: 1.32, 1.17, 1.21, 1.43 ms (4: 768 workgroups,
+// a second round half empty); 1M tokens x 8 heads in slices of 512: 4.81, 4.55, 4.57,
+// 4.52 ms (at 8 the dQ kernel's last round of 768 is two-thirds full: 1.44 -> 1.53 ms).
+// Few heads and slices (under 512 workgroups even at G = 1): 1.
 static long long group_of(const slim_desc *d, long long nslices, long long c)
 {
     if (d->group_slices > 0) return d->group_slices < nslices ? d->group_slices : nslices;
+    const KernelTable *kt = find(d);
+    if (!kt) return 1;
     const long long BH = d->B * d->H;
-    long long G = 1;
-    while (2 * G * c <= 1024 && (nslices + 2 * G - 1) / (2 * G) * BH >= 1024) G *= 2;
-    return G;
+    auto fills = [](long long wgs, long long slots) {
+        const long long rounds = (wgs + slots - 1) / slots;
+        return wgs >= slots && 10 * wgs >= 9 * rounds * slots;
+    };
+    long long best = 1;
+    for (long long G = 1; G <= nslices && G * c <= 2048; G *= 2) {
+        const long long wgs = (nslices + G - 1) / G * BH;
+        if (fills(wgs, kt->slots_fwd) && fills(wgs, kt->slots_q) && fills(wgs, kt->slots_kv)) best = G;
+    }
+    return best;
 }
 
 // window > 0: hold that many groups per window instead of the resolved window.

@@ -137,9 +137,10 @@ size_t slim_workspace_bytes(const slim_desc *desc, int pass);
  * least one). */
 int64_t slim_window_chunks(const slim_desc *desc);
 
-/* Slices per group (desc.group_slices, or the automatic choice: a power of two with
- * groups of at most 1024 rows while at least 1024 workgroups per launch remain, else
- * 1).  0 if the descriptor is invalid.  Host-only. */
+/* Slices per group (desc.group_slices, or the automatic choice: the largest power of
+ * two with groups of at most 2048 rows whose launches have at least 512 workgroups and
+ * fill whole rounds of 512 workgroups, and for bf16 with M = 64 also of 768, to within
+ * 10%; else 1).  0 if the descriptor is invalid.  Host-only. */
 int64_t slim_group_slices(const slim_desc *desc);
 
 /* Bytes of the `states` buffer slim_attn_fwd can fill for the backward: the state

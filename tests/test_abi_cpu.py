@@ -201,7 +201,7 @@ def test_workspace_does_not_grow_with_L_at_fixed_slice_and_window(lib):
             assert len(set(sizes)) == 1, sizes
             flat = sizes[0]
         else:
-            assert max(sizes) <= flat and sizes[-1] == sizes[-2], sizes
+            assert max(sizes) <= flat and all(b <= a for a, b in zip(sizes, sizes[1:])), sizes
     fw = [ws(lib, 1, B=1, H=8, L=n, d=64, M=64, num_chunks=n // 512, window_chunks=64, group_slices=1)
           for n in (1 << 15, 1 << 20)]
     assert fw[0] == fw[1]
@@ -212,11 +212,11 @@ def test_state_handoff_sizes_and_checks(lib):
     # (d + 1) x M fp32 per head, and a call given it needs that much less workspace
     d = d_(B=4, H=16, L=16384, d=64, M=256, num_chunks=32)
     slot = 65 * 256 * 4
-    assert lib.slim_group_slices(ctypes.byref(d)) == 2  # 16 groups of two slices of 512
-    assert lib.slim_state_bytes(ctypes.byref(d)) == 64 * 17 * slot
+    assert lib.slim_group_slices(ctypes.byref(d)) == 4  # 8 groups of four slices of 512
+    assert lib.slim_state_bytes(ctypes.byref(d)) == 64 * 9 * slot
     d1 = d_(B=4, H=16, L=16384, d=64, M=256, num_chunks=32, group_slices=1)
     assert lib.slim_state_bytes(ctypes.byref(d1)) == 64 * 33 * slot
-    for dd, n in ((d, 17), (d1, 33)):
+    for dd, n in ((d, 9), (d1, 33)):
         for p in (_lib.SLIM_PASS_FWD, _lib.SLIM_PASS_BWD):
             full = lib.slim_workspace_bytes(ctypes.byref(dd), p)
             assert 0 < lib.slim_workspace_bytes_states(ctypes.byref(dd), p) <= full - 64 * n * slot
@@ -256,29 +256,33 @@ def test_auto_window(lib):
     assert 2048 * per <= 1 << 30 < 4096 * per
     d = d_(B=1, H=8, L=1 << 22, d=64, M=64, num_chunks=1 << 13, group_slices=1)
     assert lib.slim_window_chunks(ctypes.byref(d)) == 512
-    # in groups of two slices (the automatic choice there): 512 workgroups of two slices
+    # in groups of four slices (the automatic choice there): 512 workgroups of four slices
     d = d_(B=1, H=8, L=1 << 22, d=64, M=64, num_chunks=1 << 13)
-    assert lib.slim_group_slices(ctypes.byref(d)) == 2
-    assert lib.slim_window_chunks(ctypes.byref(d)) == 1024
+    assert lib.slim_group_slices(ctypes.byref(d)) == 4
+    assert lib.slim_window_chunks(ctypes.byref(d)) == 2048
     # many heads: about 4096 workgroups per launch when that is more; one group of
-    # slices each (slices of 64 rows go 16 to a group)
+    # slices each (slices of 64 rows go 32 to a group)
     d = d_(B=64, H=64, L=4096, d=64, M=256, num_chunks=64, group_slices=1)
     assert lib.slim_window_chunks(ctypes.byref(d)) == 1
     d = d_(B=64, H=64, L=4096, d=64, M=256, num_chunks=64)
-    assert lib.slim_group_slices(ctypes.byref(d)) == 16
-    assert lib.slim_window_chunks(ctypes.byref(d)) == 16
+    assert lib.slim_group_slices(ctypes.byref(d)) == 32
+    assert lib.slim_window_chunks(ctypes.byref(d)) == 32
 
 
 def test_group_slices(lib):
     def g(**kw):
         return lib.slim_group_slices(ctypes.byref(d_(**kw)))
-    # groups of at most 1024 rows while at least 1024 workgroups per launch remain
-    assert g(B=4, H=16, L=16384, d=64, M=256, num_chunks=32) == 2        # 16 x 64 = 1024 workgroups
-    assert g(B=1, H=8, L=1 << 20, d=64, M=64, num_chunks=2048) == 2      # 1024 x 8
-    assert g(B=8, H=12, L=8192, d=128, M=128, num_chunks=32, feat=_lib.SLIM_FEAT_ELU1) == 2  # not 4: 768
-    assert g(B=2, H=8, L=4096, d=64, M=128, num_chunks=16) == 1          # 256 workgroups already
+    # the largest power of two with groups of at most 2048 rows whose launches fill whole
+    # rounds of each kernel's resident workgroups (512 for two 4-wave workgroups per CU,
+    # 256 for the 8-wave dQ kernel at M = 256, 768 for three dQ workgroups at bf16 M = 64)
+    # to within 10%
+    assert g(B=4, H=16, L=16384, d=64, M=256, num_chunks=32) == 4        # 8 x 64 = 512: one round
+    assert g(B=1, H=8, L=1 << 20, d=64, M=64, num_chunks=2048) == 2      # at 4, 4096 = 5.3 rounds of 768
+    assert g(B=8, H=12, L=8192, d=128, M=128, num_chunks=32, feat=_lib.SLIM_FEAT_ELU1) == 2  # 4: 768 = 1.5 x 512
+    assert g(B=2, H=8, L=4096, d=64, M=128, num_chunks=16) == 1          # 256 workgroups, not a round
     assert g(B=1, H=8, L=1 << 20, d=64, M=64, num_chunks=8192) == 8      # slices of 128: groups of 1024 rows
-    assert g(B=64, H=64, L=4096, d=64, M=64, num_chunks=4) == 1          # slices of 1024 rows
+    assert g(B=64, H=64, L=4096, d=64, M=64, num_chunks=4) == 2          # slices of 1024 rows, 8192 workgroups
+    assert g(B=64, H=16, L=1024, d=64, M=64, num_chunks=8) == 1          # 1024 at 8: 1.3 rounds of 768
     # given: taken as is, at most the slices there are
     assert g(group_slices=3) == 3
     assert g(L=1000, num_chunks=3, group_slices=5) == 3
@@ -358,7 +362,8 @@ def test_noalloc_forward_rejects_before_any_launch(lib):
     # two state slots and the fp64 carries of 600 heads at d = 64, M = 256 exceed 64 MiB
     too_many = d_(B=600, H=1, L=16, d=64, M=256, num_chunks=1)
     assert lib.slim_attn_fwd_noalloc(ctypes.byref(too_many), *args) == 5
-    # an explicit window that does not fit is refused, not shrunk
-    wide = d_(B=64, H=1, L=16384, d=64, M=256, num_chunks=32, window_chunks=32)
+    # an explicit window that does not fit is refused, not shrunk (one slice per
+    # workgroup: 33 slots per head)
+    wide = d_(B=64, H=1, L=16384, d=64, M=256, num_chunks=32, window_chunks=32, group_slices=1)
     assert lib.slim_attn_fwd_noalloc(ctypes.byref(wide), *args) == 5
     assert _lib.SLIM_NOALLOC_SCRATCH_BYTES == 64 << 20

@@ -8,7 +8,7 @@ including the row statistics kernel, which splits a group into parts of 256 rows
     initial state and incoming state gradients, the forward's row statistics and
     kept states, and dW;
   * several windows of groups (a window given in slices holds whole groups);
-  * the automatic grouping where it walks eight slices per workgroup, against one
+  * the automatic grouping where it walks four slices per workgroup, against one
     slice per workgroup and the oracle."""
 import ctypes
 
@@ -107,12 +107,13 @@ def test_groups_in_several_windows():
 
 
 def test_automatic_grouping_matches_one_slice_per_workgroup():
-    # 1024 heads in 8 slices of 128: the automatic choice walks 8 slices per workgroup
-    # (groups of 1024 rows, still 1024 workgroups); against one slice per workgroup
-    B, H, L, d, M, C = 64, 16, 1024, 64, 64, 8
+    # 64 heads in 32 slices of 256 (M = 256): the automatic choice walks 4 slices per
+    # workgroup (groups of 1024 rows, 512 workgroups: one round of the chip); against one
+    # slice per workgroup
+    B, H, L, d, M, C = 4, 16, 8192, 64, 256, 32
     x = inputs(B, H, L, d, M, torch.bfloat16, "favor", seed=94)
     dsc = A.make_desc(x["q"], M, "favor", C)
-    assert _lib.lib().slim_group_slices(ctypes.byref(dsc)) == 8
+    assert _lib.lib().slim_group_slices(ctypes.byref(dsc)) == 4
     print("automatic grouping", flush=True)
     outs = []
     for G in (0, 1):
@@ -131,4 +132,4 @@ def test_automatic_grouping_matches_one_slice_per_workgroup():
     o = oracle.attn_bwd(h["q"], h["k"], h["v"], host64(x["W"]), h["dy"], "favor", form="prefix")
     for name, a, ref in zip(("Y", "dQ", "dK", "dV"), (outs[0][0],) + outs[0][3:], (Yo,) + o[:3]):
         got = np.stack([host64(a[b, hh]) for b, hh in sel])[None]
-        check(("automatic grouping vs oracle", name), got, ref, 2e-2, positions=(1024, tile_rows(x["q"], M, "favor", C)))
+        check(("automatic grouping vs oracle", name), got, ref, 2e-2, positions=(1024, tile_rows(x["q"], M, "favor", C)))  # noqa: E501

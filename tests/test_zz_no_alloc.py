@@ -2,11 +2,11 @@
 the C ABI, on two calls in a row, the second with a smaller input.
 
 slim_attn_fwd_noalloc works in a fixed 64 MiB device array instead of a caller's
-workspace.  The first call (the 16K-token, 64-head workload's shape: its automatic
-window, all 32 slices in 16 groups of two, needs 72 MB of slots) has to shrink its
-window to fit, so it runs in several windows: its outputs are bitwise those of slim_attn_fwd given the same
-window, and within the bf16 bound (2e-2, gpu_util.check) of slim_attn_fwd with the
-automatic window and of the fp64 oracle on sampled heads.  The second call (smaller,
+workspace.  The first call (the 16K-token, 64-head workload's shape, one slice per
+workgroup: its automatic window, all 32 slices, needs 140 MB of slots) has to shrink
+its window to fit, so it runs in several windows: its outputs are bitwise those of
+slim_attn_fwd given the same window, and within the bf16 bound (2e-2, gpu_util.check)
+of slim_attn_fwd with the automatic window and of the fp64 oracle on sampled heads.  The second call (smaller,
 fp32) fits whole: bitwise equal to slim_attn_fwd.  Both calls share the array, so the
 second also shows that nothing left in it by the first leaks into its result."""
 import ctypes
@@ -23,10 +23,10 @@ from gpu_util import TOL, check, host64, inputs
 pytestmark = pytest.mark.gpu
 
 
-def _noalloc_window(q, M, feat, C):
+def _noalloc_window(q, M, feat, C, G=0):
     """The window slim_attn_fwd_noalloc takes: the largest whose forward workspace fits."""
-    P = int(_lib.lib().slim_window_chunks(ctypes.byref(A.make_desc(q, M, feat, C))))
-    while P > 1 and A.workspace_bytes(A.make_desc(q, M, feat, C, P), _lib.SLIM_PASS_FWD) > \
+    P = int(_lib.lib().slim_window_chunks(ctypes.byref(A.make_desc(q, M, feat, C, group_slices=G))))
+    while P > 1 and A.workspace_bytes(A.make_desc(q, M, feat, C, P, group_slices=G), _lib.SLIM_PASS_FWD) > \
             _lib.SLIM_NOALLOC_SCRATCH_BYTES:
         P -= 1
     return P
@@ -37,16 +37,18 @@ def _same(a, b):
 
 
 def test_noalloc_forward_two_calls():
-    # call 1: B=4, H=16, L=16384, d=64, M=256, bf16, 32 slices of 512
-    B, H, L, d, M, C = 4, 16, 16384, 64, 256, 32
+    # call 1: B=4, H=16, L=16384, d=64, M=256, bf16, 32 slices of 512, one per workgroup
+    B, H, L, d, M, C, G = 4, 16, 16384, 64, 256, 32, 1
     print("no-alloc forward, call 1", (B, H, L, d, M, C), flush=True)
     x = inputs(B, H, L, d, M, torch.bfloat16, "favor", seed=81, dy=False)
     ko = torch.full((1,), -1.0, device="cuda")
-    got = A.attn_fwd_noalloc(x["q"], x["k"], x["v"], x["W"], "favor", C, want_row_stats=True, koff_out=ko)
-    P = _noalloc_window(x["q"], M, "favor", C)
+    got = A.attn_fwd_noalloc(x["q"], x["k"], x["v"], x["W"], "favor", C, want_row_stats=True, koff_out=ko,
+                             group_slices=G)
+    P = _noalloc_window(x["q"], M, "favor", C, G)
     assert P < C  # the automatic window does not fit the array: several windows
-    same_window = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], "favor", C, window_chunks=P, want_row_stats=True)
-    auto = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], "favor", C, want_row_stats=True)
+    same_window = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], "favor", C, window_chunks=P, want_row_stats=True,
+                             group_slices=G)
+    auto = A.attn_fwd(x["q"], x["k"], x["v"], x["W"], "favor", C, want_row_stats=True, group_slices=G)
     torch.cuda.synchronize()
     print("window", P, "of", C, "slices", flush=True)
     assert float(ko) == 0.0
