@@ -292,6 +292,30 @@ def test_group_slices(lib):
     assert lib.slim_window_chunks(ctypes.byref(d_(L=4096, num_chunks=16, window_chunks=1, group_slices=4))) == 4
 
 
+def test_group_slices_invariants(lib):
+    # over a grid of shapes: G is a power of two (or all the slices), at most 2048 rows per
+    # group, and G > 1 only with at least one workgroup per CU (256; 512 where two
+    # 4-wave workgroups share a CU: bf16 at d = 64, M = 256); the group count and the
+    # states buffer follow from it
+    for dtype in (_lib.SLIM_BF16, _lib.SLIM_F32):
+        for B, H in ((1, 1), (1, 8), (4, 16), (8, 12), (64, 64)):
+            for L, C in ((300, 3), (4096, 16), (16384, 32), (1 << 20, 2048), (1 << 20, 8192)):
+                for d, M in ((64, 64), (64, 256), (128, 128)):
+                    if B * H * L > (1 << 24):
+                        continue
+                    dd = d_(B=B, H=H, L=L, d=d, M=M, num_chunks=C, dtype=dtype)
+                    G = lib.slim_group_slices(ctypes.byref(dd))
+                    c = -(-L // C)
+                    n = -(-L // c)
+                    assert 1 <= G <= n and (G & (G - 1)) == 0, (B, H, L, C, d, M, G)
+                    if G > 1:
+                        least = 512 if (dtype == _lib.SLIM_BF16 and d == 64 and M == 256) else 256
+                        assert G * c <= 2048 and -(-n // G) * B * H >= least, (B, H, L, C, d, M, G)
+                    groups = -(-L // min(G * c, L))
+                    if lib.slim_window_chunks(ctypes.byref(dd)) >= n:  # one window: states kept
+                        assert lib.slim_state_bytes(ctypes.byref(dd)) == B * H * (groups + 1) * (d + 1) * M * 4
+
+
 def test_tile_rows(lib):
     def tr(**kw):
         return lib.slim_tile_rows(ctypes.byref(d_(**kw)))
