@@ -29,6 +29,7 @@ CASES = [
     (1, 2, 2100, 64, 256, 7, 3, "bf16", "favor"),  # slices of 300: groups of 900 (four row-statistics parts)
     (2, 1, 700, 32, 32, 9, 5, "f32", "elu1"),      # slices of 78: 2 groups, the second of 4 slices
     (1, 2, 1536, 128, 128, 6, 2, "bf16", "elu1"),
+    (2, 2, 1500, 64, 64, 7, 2, "bf16", "favor"),   # slices of 215: the shared-operand dK path
 ]
 
 
