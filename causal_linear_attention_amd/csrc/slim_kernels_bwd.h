@@ -738,6 +738,13 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
     constexpr int EBW_ = NEB > C::NW ? NEB / C::NW : 1, TBS_ = C::NW > NEB ? C::NW / NEB : 1;
     constexpr int NDK_ = SHK ? EBW_ * NTB : NFB * NTB;
     constexpr bool DEFER_DK = !DW && (SHK || !C::FAVOR) && NDK_ <= 4;
+    // Where dK is reduced across waves, the waves of a workgroup take raised issue priority
+    // from dK's W^T products through both reductions (the phases that end a tile, paced by
+    // LDS and memory latency), so that the other workgroup on the compute unit fills their
+    // gaps rather than delaying them: 0.474 -> 0.444 ms at the 16K-token, 64-head shape
+    // (the reductions alone 0.465, one level for all of it 0.444).  Not on the shared-operand
+    // path, where it cost 1% on 1M tokens x 8 heads (M = 64), nor for elu+1 (no change).
+    constexpr bool PRIO = C::FAVOR && !SHK;
     constexpr int NDK = DEFER_DK ? NDK_ : 1;
     typedef std::conditional_t<sizeof(T) == 2, bf4, f4> DkV;
     DkV dkv[NDK];
@@ -851,9 +858,11 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                 for (int sb = 0; sb < NTB; ++sb) put_red<C>(red, eb, sb, dv[eb][sb]);
         }
         __syncthreads();
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(2);
         reduce_rows<C>(red, nv, [&](int s, int e, f4 v, bool ok) {
             if (ok) store4<T>(dV + (size_t)(t0 + s) * D + e, v);
         });
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
         __syncthreads();
         // dg(K)^T blocks (rows m, cols s) = g(Q)^T A + [dR; dS]^T [V | 1]^T,
         // A[t][s] = [dNum | dden]_t . [V | 1]_s for s <= t.
@@ -1003,6 +1012,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                 mma_range<T>(rs, 0, NFB, [&](int) { return ones_row0<T>(); }, [&](int fb) { return gk[fb][sb]; });
                 if (g == 0) red[(w * TT + sb * 16 + lc) * C::LDR + D] = rs[0];
             }
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll 1
             for (int eb = 0; eb < NEB; ++eb) {  // one W^T block at a time
                 Frag<T> wt[NFB];
@@ -1015,9 +1025,11 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                 }
             }
             __syncthreads();
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(2);
             reduce_rows<C>(red, nv, [&](int s, int e, f4 v, bool ok) {
                 if (ok) store4<T>(dK + (size_t)(t0 + s) * D + e, v - xk.get4(s, e) * reduce_col<C>(red, s));
             });
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
         } else {
 #pragma unroll
             for (int fb = 0; fb < NFB; ++fb)
