@@ -939,8 +939,13 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(FwdSmem<C>), C::NW)) v
         }
     };
     rg.load(Q, K, V, 0, G.len);
+    // The phases that end a tile (the reduction of Y, then the state update) run at raised
+    // wave priority, so that the other workgroup on the compute unit fills their gaps rather
+    // than delaying them: fwd 0.272 -> 0.267 ms at the 16K-token, 64-head shape, 1.00 ->
+    // 0.98 ms on 1M tokens x 8 heads (M = 64); no change for elu+1 or fp32.
     for (int t0 = 0; t0 < G.len; t0 += TT) {
         const int nv = min(TT, G.len - t0);
+        __builtin_amdgcn_s_setprio(0);
         rg.store(sm, nv, koff);
         if (pt0 >= 0) store_y();
         __syncthreads();
@@ -948,6 +953,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(FwdSmem<C>), C::NW)) v
         f4 pq[NFB][NTB];
         fwd_tile<C>(sm, wf, rt, pq, [&](int eb, int tb, f4 acc) { put_red<C>(sm.red, eb, tb, acc); });
         __syncthreads();
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int k = 0; k < YI; ++k) {
             const int v = threadIdx.x + k * C::NT, t = v / Q4, e = (v % Q4) * 4;
@@ -972,6 +978,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(FwdSmem<C>), C::NW)) v
         }
         pt0 = t0;
         pnv = nv;
+        __builtin_amdgcn_s_setprio(1);
         state_update_T<C>(sm, rt);
         __syncthreads();
     }
