@@ -608,7 +608,7 @@ def main():
     from causal_linear_attention_amd import _lib
     from causal_linear_attention_amd import attention as A
     from causal_linear_attention_amd import synth
-    from causal_linear_attention_amd.workloads import HEADLINE, WORKLOADS, survey_flops
+    from causal_linear_attention_amd.workloads import HEADLINE, WORKLOADS, unsliced_flops
 
     if args.copy_calib:
         # plain device-to-device copy of 1 GiB (reads 1 GiB, writes 1 GiB): the
@@ -740,7 +740,7 @@ def main():
                    "dW": want_dw, "global_batch": w.B, "seq_len": w.L, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "step_tflops": round(step_flop / (ms_step * 1e-3) / 1e12, 2),
-        "step_tflops_unsliced_accounting": round(survey_flops(w) * w.head_tokens / (ms_step * 1e-3) / 1e12, 2),
+        "step_tflops_unsliced_accounting": round(unsliced_flops(w) * w.head_tokens / (ms_step * 1e-3) / 1e12, 2),
         "peak_hbm_bytes": peak, "resident_before_step_bytes": base, "step_extra_bytes": peak - base,
         "io_traffic_bytes_per_step": io, "io_gbs": round(io / (ms_step * 1e-3) / 1e9, 1),
         "io_footprint_bytes": footprint,

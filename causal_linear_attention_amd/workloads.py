@@ -187,7 +187,7 @@ def kernel_bytes(w: Workload, group: int = 1, fr: bool = False) -> dict:
     return out
 
 
-def survey_flops(w: Workload) -> float:
+def unsliced_flops(w: Workload) -> float:
     """The per-(token, head) fwd+bwd count of the unsliced-tile accounting:
     28 d M + 4 c (M + d) for FAVOR+, 16 d M + 4 c (M + d) for elu+1."""
     c = w.chunk_len
