@@ -481,6 +481,11 @@ __global__ __launch_bounds__(C::NT, bwdq_waves_per_simd<C>()) void bwdq_kernel(C
     // 16K-token, 64-head shape, the dW pass's dQ kernel 0.601 -> 0.592 ms.  Where the row
     // statistics are made here it spills (0.434 -> 0.449 ms).
     constexpr bool DEFER_DQ = BwdqSmem<C, FR>::DEFER_DQ;
+    // Where several workgroups share a compute unit, the phases after the dQ exchange (the
+    // W^T products, then the state updates) run at raised wave priority, as in the other
+    // chunk kernels: 1.443 -> 1.424 ms on 1M tokens x 8 heads (M = 64, three workgroups per
+    // CU).  Not for elu+1 (0.366 -> 0.371 ms at d = 128).
+    constexpr bool PRIO_Q = C::FAVOR && SH && 4 * bwdq_waves_per_simd<C>() / C::NW >= 2;
     int pt0 = -1, pnv = 0;
     auto store_dq = [&]() {  // the values this lane staged in sm.dqs
 #pragma unroll
@@ -502,6 +507,7 @@ __global__ __launch_bounds__(C::NT, bwdq_waves_per_simd<C>()) void bwdq_kernel(C
         if constexpr (DEFER_DQ)
             if (pt0 >= 0) store_dq();
         __syncthreads();
+        if constexpr (PRIO_Q) __builtin_amdgcn_s_setprio(0);
         if (t0 + TT < G.len) {
             if constexpr (FR) {
                 rg.load_fwd(Q, K, V, dY, fr, t0 + TT, G.len);
@@ -583,6 +589,7 @@ __global__ __launch_bounds__(C::NT, bwdq_waves_per_simd<C>()) void bwdq_kernel(C
                     }
                 if constexpr (EARLY_R) update_r();
                 __syncthreads();
+                if constexpr (PRIO_Q) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
                 for (int j = 0; j < (NB + C::NW - 1) / C::NW; ++j) {
                     const int blk = w + j * C::NW, tb = blk / NEB, eb = blk % NEB;
@@ -641,6 +648,7 @@ __global__ __launch_bounds__(C::NT, bwdq_waves_per_simd<C>()) void bwdq_kernel(C
                     if (t < nv) store4<T>(dQ + (size_t)(t0 + t) * D + w * MW + fb * 16 + 4 * g, v);
                 }
         }
+        if constexpr (PRIO_Q) __builtin_amdgcn_s_setprio(1);
         if constexpr (!EARLY_R) update_r();
         // fused: [dG | dGs] += g(Q)^T [dNum | dden]
         if constexpr (FG)
