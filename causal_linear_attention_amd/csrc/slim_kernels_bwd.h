@@ -753,6 +753,26 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
     // (the reductions alone 0.465, one level for all of it 0.444).  Not on the shared-operand
     // path, where it cost 1% on 1M tokens x 8 heads (M = 64), nor for elu+1 (no change).
     constexpr bool PRIO = C::FAVOR && !SHK;
+    // On the shared-operand path with few features (W^T fragments of at most four feature
+    // blocks for at most two value blocks per wave) the W and W^T fragments are loaded once
+    // and held in registers over the tile loop instead of re-read every tile, where the
+    // products right after the tile's barriers waited for them: on 1M tokens x 8 heads
+    // (d = M = 64) 1.623 -> 1.525 ms for W^T, 1.48 ms with W too, still two waves per SIMD.
+    // Not in the dW pass's variant, where they spill.
+    constexpr int WR_EBW = NEB > C::NW ? NEB / C::NW : 1, WR_MB = C::M / 16;
+    constexpr bool WT_REG = SHK && !DW && WR_MB <= 4 && WR_EBW <= 2;
+    Frag<T> wtr[WT_REG ? WR_EBW : 1][WT_REG ? WR_MB : 1];
+    Frag<T> wfr[WT_REG ? NFB : 1][WT_REG ? NEB : 1];
+    if constexpr (WT_REG) {
+        load_wfrag<C>(wfr, a.W);
+#pragma unroll
+        for (int k = 0; k < WR_EBW; ++k)
+#pragma unroll
+            for (int j = 0; j < WR_MB; ++j)
+                wtr[k][j] = *reinterpret_cast<const Frag<T> *>((const T *)a.Wt +
+                                                               (((size_t)(w % NEB + k * C::NW) * WR_MB + j) * 64 +
+                                                                threadIdx.x % 64) * 4);
+    }
     constexpr int NDK = DEFER_DK ? NDK_ : 1;
     typedef std::conditional_t<sizeof(T) == 2, bf4, f4> DkV;
     DkV dkv[NDK];
@@ -780,10 +800,17 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
     rg.load(Q, K, V, dY, st, last, G.len);
     for (int t0 = last; t0 >= 0; t0 -= TT) {
         const int nv = min(TT, G.len - t0);
-        // W fragments are re-read (from cache) every tile rather than held over the loop;
-        // issued before the tile's staging and barrier, which cover their latency
+        // W fragments, unless held (above), are re-read (from cache) every tile rather than
+        // held over the loop; issued before the tile's staging and barrier, which cover their
+        // latency
         Frag<T> wf[NFB][NEB];
-        if constexpr (C::FAVOR) load_wfrag<C>(wf, a.W);
+        if constexpr (WT_REG) {
+#pragma unroll
+            for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+                for (int eb = 0; eb < NEB; ++eb) wf[fb][eb] = wfr[fb][eb];
+        } else if constexpr (C::FAVOR)
+            load_wfrag<C>(wf, a.W);
         rg.store(xq, xk, Vt, DN, kn2, qoff, nv, koff);
         __syncthreads();
         // the next tile's inputs: with one vector of each input tile per thread, in flight
@@ -971,9 +998,13 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                 for (int m0 = 0; m0 < MB; m0 += MH) {
                     Frag<T> wt[MH];
 #pragma unroll
-                    for (int j = 0; j < MH; ++j)
-                        wt[j] = *reinterpret_cast<const Frag<T> *>(
-                            Wp + (((size_t)eb * MB + m0 + j) * 64 + threadIdx.x % 64) * 4);
+                    for (int j = 0; j < MH; ++j) {
+                        if constexpr (WT_REG)
+                            wt[j] = wtr[k][m0 + j];
+                        else
+                            wt[j] = *reinterpret_cast<const Frag<T> *>(
+                                Wp + (((size_t)eb * MB + m0 + j) * 64 + threadIdx.x % 64) * 4);
+                    }
 #pragma unroll
                     for (int sb = 0; sb < NTB; ++sb) {
                         if (sb % TB_STEP != (w / NEB) % TB_STEP) continue;
