@@ -426,6 +426,29 @@ template <> __device__ __forceinline__ void store4<__bf16>(__bf16 *p, f4 v)
     bf4 r = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
     *reinterpret_cast<bf4 *>(p) = r;
 }
+// Store of an 8- or 16-byte value at byte offset off of base, which the hardware drops
+// when it does not lie within the first nbytes: row-bounded output stores without a
+// branch, so that the compiler counts them exactly in its memory waits.
+template <typename V> __device__ __forceinline__ void bstore(void *base, int nbytes, int off, V x)
+{
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, nbytes, 0x00020000);
+    if constexpr (sizeof(V) == 8) {
+        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, x), r, off, 0, 0);
+    } else {
+        static_assert(sizeof(V) == 16, "8- or 16-byte values");
+        typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x), r, off, 0, 0);
+    }
+}
+// Four values as the I/O type, row-bounded as bstore.
+template <typename T> __device__ __forceinline__ void bstore4(T *base, int nbytes, int off, f4 v)
+{
+    if constexpr (sizeof(T) == 2)
+        bstore(base, nbytes, off, bf4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]});
+    else
+        bstore(base, nbytes, off, v);
+}
 
 // ----------------------------------------------------------- featmap ---
 
@@ -932,10 +955,10 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(FwdSmem<C>), C::NW)) v
 #pragma unroll
         for (int k = 0; k < YI; ++k) {
             const int v = threadIdx.x + k * C::NT, t = v / Q4, e = (v % Q4) * 4;
-            if (v < TT * Q4 && t < pnv) {
-                *reinterpret_cast<YV *>(Y + (size_t)(pt0 + t) * C::D + e) = yv[k];
-                if (rs && e == 0) *reinterpret_cast<float2 *>(rs + (size_t)(pt0 + t) * 2) = yr[k];
-            }
+            const int ny = pnv * C::D * (int)sizeof(T), nr = pnv * 8;
+            const bool in = v < TT * Q4;
+            bstore(Y + (size_t)pt0 * C::D, ny, in ? (t * C::D + e) * (int)sizeof(T) : ny, yv[k]);
+            if (rs) bstore(rs + (size_t)pt0 * 2, nr, in && e == 0 ? t * 8 : nr, yr[k]);
         }
     };
     rg.load(Q, K, V, 0, G.len);

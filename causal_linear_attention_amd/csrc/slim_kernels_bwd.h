@@ -493,9 +493,8 @@ __global__ __launch_bounds__(C::NT, bwdq_waves_per_simd<C>()) void bwdq_kernel(C
             const int blk = w + j * C::NW, tb = blk / NEB, eb = blk % NEB;
             if (blk >= NB) break;
             const int t = tb * 16 + lc;
-            if (t < pnv)
-                *reinterpret_cast<bf4 *>(dQ + (size_t)(pt0 + t) * D + eb * 16 + 4 * g) =
-                    *reinterpret_cast<const bf4 *>(sm.dqs + ((size_t)j * C::NT + threadIdx.x) * 4);
+            bstore(dQ + (size_t)pt0 * D, pnv * D * (int)sizeof(T), (t * D + eb * 16 + 4 * g) * (int)sizeof(T),
+                   *reinterpret_cast<const bf4 *>(sm.dqs + ((size_t)j * C::NT + threadIdx.x) * 4));
         }
     };
     for (int t0 = 0; t0 < G.len; t0 += TT) {
@@ -603,7 +602,7 @@ __global__ __launch_bounds__(C::NT, bwdq_waves_per_simd<C>()) void bwdq_kernel(C
                             bf4{(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
                     } else {
                         const int t = tb * 16 + lc;
-                        if (t < nv) store4<T>(dQ + (size_t)(t0 + t) * D + eb * 16 + 4 * g, acc);
+                        bstore4<T>(dQ + (size_t)t0 * D, nv * D * (int)sizeof(T), (t * D + eb * 16 + 4 * g) * (int)sizeof(T), acc);
                     }
                 }
                 if constexpr (DEFER_DQ) {
@@ -632,7 +631,7 @@ __global__ __launch_bounds__(C::NT, bwdq_waves_per_simd<C>()) void bwdq_kernel(C
                 }
                 __syncthreads();
                 reduce_rows<C>(red, nv, [&](int t, int e, f4 s, bool ok) {
-                    if (ok) store4<T>(dQ + (size_t)(t0 + t) * D + e, s);
+                    bstore4<T>(dQ + (size_t)t0 * D, nv * D * (int)sizeof(T), (t * D + e) * (int)sizeof(T), s);
                 });
             }
         } else {
@@ -645,7 +644,7 @@ __global__ __launch_bounds__(C::NT, bwdq_waves_per_simd<C>()) void bwdq_kernel(C
                     f4 v;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) v[j] = dq[fb][tb][j] * elu1_grad(x[j]);
-                    if (t < nv) store4<T>(dQ + (size_t)(t0 + t) * D + w * MW + fb * 16 + 4 * g, v);
+                    bstore4<T>(dQ + (size_t)t0 * D, nv * D * (int)sizeof(T), (t * D + w * MW + fb * 16 + 4 * g) * (int)sizeof(T), v);
                 }
         }
         if constexpr (PRIO_Q) __builtin_amdgcn_s_setprio(1);
@@ -794,7 +793,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
             } else {
                 col = w * MW + (i / NTB) * 16 + 4 * g;
             }
-            if (s < pnv) *reinterpret_cast<DkV *>(dK + (size_t)(pt0 + s) * D + col) = dkv[i];
+            bstore(dK + (size_t)pt0 * D, pnv * D * (int)sizeof(T), (s * D + col) * (int)sizeof(T), dkv[i]);
         }
     };
     rg.load(Q, K, V, dY, st, last, G.len);
@@ -895,7 +894,7 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
         __syncthreads();
         if constexpr (PRIO) __builtin_amdgcn_s_setprio(2);
         reduce_rows<C>(red, nv, [&](int s, int e, f4 v, bool ok) {
-            if (ok) store4<T>(dV + (size_t)(t0 + s) * D + e, v);
+            bstore4<T>(dV + (size_t)t0 * D, nv * D * (int)sizeof(T), (s * D + e) * (int)sizeof(T), v);
         });
         if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
         __syncthreads();
@@ -1022,8 +1021,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                     const f4 r = acc[sb] - xk.get4(s, eb * 16 + 4 * g) * rs;
                     if constexpr (DEFER_DK)
                         dkv[k * NTB + sb] = pack(r);
-                    else if (s < nv)
-                        store4<T>(dK + (size_t)(t0 + s) * D + eb * 16 + 4 * g, r);
+                    else
+                        bstore4<T>(dK + (size_t)t0 * D, nv * D * (int)sizeof(T), (s * D + eb * 16 + 4 * g) * (int)sizeof(T), r);
                 }
             };
             if constexpr (DEFER_DK) {
@@ -1075,7 +1074,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
             __syncthreads();
             if constexpr (PRIO) __builtin_amdgcn_s_setprio(2);
             reduce_rows<C>(red, nv, [&](int s, int e, f4 v, bool ok) {
-                if (ok) store4<T>(dK + (size_t)(t0 + s) * D + e, v - xk.get4(s, e) * reduce_col<C>(red, s));
+                bstore4<T>(dK + (size_t)t0 * D, nv * D * (int)sizeof(T), (s * D + e) * (int)sizeof(T),
+                           v - xk.get4(s, e) * reduce_col<C>(red, s));
             });
             if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
         } else {
@@ -1090,8 +1090,8 @@ __global__ __launch_bounds__(C::NT, waves_per_simd(sizeof(BwdkvSmem<C>), C::NW))
                     for (int j = 0; j < 4; ++j) v[j] = dk[fb][sb][j] * elu1_grad(x[j]);
                     if constexpr (DEFER_DK)
                         dkv[fb * NTB + sb] = pack(v);
-                    else if (s < nv)
-                        store4<T>(dK + (size_t)(t0 + s) * D + w * MW + fb * 16 + 4 * g, v);
+                    else
+                        bstore4<T>(dK + (size_t)t0 * D, nv * D * (int)sizeof(T), (s * D + w * MW + fb * 16 + 4 * g) * (int)sizeof(T), v);
                 }
         }
         if constexpr (DW) {
