@@ -348,7 +348,7 @@ __device__ __forceinline__ void load_wt_col(Frag<typename C::T> (&wt)[C::M / 16]
 template <class C>
 __device__ __forceinline__ void store_pw(typename C::T *rows, int t, int nv, int m, Frag<typename C::T> v)
 {
-    if (t < nv) *reinterpret_cast<Frag<typename C::T> *>(rows + (size_t)t * C::M + m) = v;
+    bstore(rows, nv * C::M * (int)sizeof(typename C::T), (t * C::M + m) * (int)sizeof(typename C::T), v.v);
 }
 // The chunk's first row in a dW buffer (see ChunkArgs::pq).
 template <class C> __device__ __forceinline__ typename C::T *pw_rows(void *buf, const ChunkArgs &a, const ChunkGeom &G)
